@@ -1,0 +1,201 @@
+/*
+ * moe_mxfp4.h - C ABI of the routed MXFP4 Mixture-of-Experts block on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The block (pages: turbospark-runtime `src/families/gptoss/mod.rs`, module
+ * doc "One decoder layer"; goosedump `src/engine/model/gpt_oss.rs`,
+ * `mixture_of_experts` and `mixture_of_experts_batch`):
+ *
+ *   xn   = norm_w ? rms_norm(hidden, norm_w, rms_eps) : hidden
+ *   l    = xn . router_w^T + router_b                    (logits, fp64)
+ *   idx  = top-k of l, ties to the lower expert index
+ *   w    = route_scale * softmax(l[idx])                 (over the k selected)
+ *   y_j  = down_j(swiglu(gate_j(xn) + bg_j, up_j(xn) + bu_j)) + bd_j
+ *   out  = hidden + sum_j w_j * y_j  (+ shared experts, weight 1)
+ *
+ *   swiglu(g, u) = min(g, L) * sigmoid(alpha * min(g, L)) * (clamp(u, -L, L) + o)
+ *
+ * Conventions for every call below:
+ * - Device pointers are caller-owned device allocations; the library never
+ *   allocates, frees or keeps device memory between calls. Host pointers are
+ *   marked "host".
+ * - Compute calls enqueue work on `stream` and return without synchronising.
+ *   Arguments are validated on the host before anything is enqueued; on an
+ *   invalid argument nothing is enqueued, a negative moe_status is returned
+ *   and moe_last_error() describes the problem.
+ * - Row-major layouts; [A,B] means A rows of B contiguous elements.
+ * - Shape limits: 1 <= E <= 256, 1 <= k <= min(E, 8), H and F multiples of
+ *   32 and at most 16384, 0 <= T, n_shared in {0, 1}. T = 0 is a no-op.
+ *   Decode additionally needs T <= 64 and H, F <= 8192. With T = 0 a call
+ *   only validates the shape and returns MOE_OK.
+ */
+#ifndef MOE_MXFP4_H
+#define MOE_MXFP4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum moe_status {
+    MOE_OK = 0,
+    MOE_ERR_INVALID_ARG = -1, /* null pointer, bad shape or constant */
+    MOE_ERR_UNSUPPORTED = -2, /* valid request outside the supported limits */
+    MOE_ERR_WORKSPACE = -3,   /* workspace missing, too small or misaligned */
+    MOE_ERR_HIP = -4          /* a HIP launch or runtime call failed */
+} moe_status;
+
+typedef enum moe_dtype {
+    MOE_F32 = 0,  /* float32 hidden/residual */
+    MOE_BF16 = 1  /* bfloat16 hidden/residual (bits), widened exactly */
+} moe_dtype;
+
+/* Shape and constants of one MoE block.
+ * alpha / limit / up_offset: gpt-oss uses 1.702 / 7.0 / 1.0 (goosedump
+ * constants SWIGLU_ALPHA, SWIGLU_LIMIT); the DeepSeek-V4-Flash shape uses
+ * 1.0 / 10.0 / 0.0 (antirez ds4.c DS4_DEFAULT_SWIGLU_CLAMP_EXP).
+ * route_scale: 1.0 for gpt-oss, 1.5 for DeepSeek-V4-Flash (ds4.c
+ * DS4_SHAPE_FLASH expert_weight_scale). rms_eps is used only when a norm
+ * weight is passed (1e-5 for gpt-oss). */
+typedef struct moe_shape {
+    int32_t T;          /* tokens */
+    int32_t H;          /* hidden size */
+    int32_t F;          /* expert hidden size */
+    int32_t E;          /* routed experts */
+    int32_t k;          /* experts per token */
+    int32_t act_dtype;  /* moe_dtype of hidden */
+    int32_t n_shared;   /* always-on shared experts (0 or 1) */
+    float swiglu_alpha;
+    float swiglu_limit;
+    float swiglu_up_offset;
+    float route_scale;
+    float rms_eps;
+} moe_shape;
+
+/* Byte layout of one packed expert blob. Offsets are from the blob start;
+ * every plane is 256-byte aligned. Expert e of a packed set starts at
+ * base + e * stride.
+ *   gate_q [F, H/2]  up_q [F, H/2]  down_q [H, F/2]   E2M1 codes, element 2i
+ *                                                     in the low nibble of byte i
+ *   gate_s [F, H/32] up_s [F, H/32] down_s [H, F/32]  E8M0 scale bytes,
+ *                                                     value 2^(b-127)
+ *   gate_b [F]       up_b [F]       down_b [H]        float32 biases
+ * The weight of gate row f, column h is E2M1(code) * 2^(gate_s[f][h/32]-127)
+ * (MXFP4: blocks of 32 sharing one power-of-two scale; pages: ds4.c
+ * `dsv4_e2m1fn_value_cpu`, `dsv4_fp4_act_quantize_row_inplace_cpu`;
+ * goosedump `validate_tensors`, Mxfp4 expert tensors with F32 biases).
+ * Supported scale bytes: 2..252 (every E2M1 product is then a normal,
+ * finite float32/bfloat16; outside that range results are unspecified). */
+typedef struct moe_blob_layout {
+    uint64_t gate_q, up_q, down_q;
+    uint64_t gate_s, up_s, down_s;
+    uint64_t gate_b, up_b, down_b;
+    uint64_t bytes;   /* end of the last plane: bytes the block reads per expert */
+    uint64_t stride;  /* bytes rounded up to 4096 */
+} moe_blob_layout;
+
+/* Host-side planar MXFP4 weights of n experts, as produced by a quantiser:
+ * gate_q/up_q [n, F, H/2], down_q [n, H, F/2]; gate_s/up_s [n, F, H/32],
+ * down_s [n, H, F/32]; gate_b/up_b [n, F], down_b [n, H]. All host. */
+typedef struct moe_expert_planes {
+    const uint8_t *gate_q, *up_q, *down_q;
+    const uint8_t *gate_s, *up_s, *down_s;
+    const float *gate_b, *up_b, *down_b;
+} moe_expert_planes;
+
+/* Routing results (all device, caller-owned; any field may be NULL to skip it).
+ *   topk_idx [T, k] int32  expert of slot j of token t, by descending logit,
+ *                          equal logits ordered by ascending expert index
+ *   topk_w   [T, k] float  route weight (route_scale * softmax of the selected)
+ *   counts   [E]    int32  routes per expert
+ *   offsets  [E+1]  int32  exclusive prefix sum of counts
+ *   perm     [T*k]  int32  route id t*k+j at each position, grouped by expert,
+ *                          ascending token inside a group
+ *   inv      [T*k]  int32  position of route t*k+j, perm[inv[r]] == r
+ * Pages: goosedump `top_experts` (strict-greater insertion: descending value,
+ * lower index first on ties), `mixture_of_experts_batch` (routes pushed per
+ * expert in token order), `route_output_index` (route id token*k + slot). */
+typedef struct moe_route_out {
+    int32_t *topk_idx;
+    float *topk_w;
+    int32_t *counts;
+    int32_t *offsets;
+    int32_t *perm;
+    int32_t *inv;
+} moe_route_out;
+
+/* Fill *layout for experts of this shape (uses H and F only). Host only.
+ * Returns MOE_OK or MOE_ERR_INVALID_ARG. */
+int moe_blob_layout_get(const moe_shape *shape, moe_blob_layout *layout);
+
+/* Pack n experts from planes into dst (host, n * layout.stride bytes,
+ * padding zeroed). Host only; MOE_OK or MOE_ERR_INVALID_ARG. */
+int moe_pack_experts(const moe_shape *shape, int32_t n, const moe_expert_planes *planes,
+                     uint8_t *dst);
+
+/* Device workspace bytes that moe_route / moe_forward_decode /
+ * moe_forward_prefill need for this shape (the largest of the three).
+ * Returns 0 for an invalid shape. Host only. */
+size_t moe_workspace_bytes(const moe_shape *shape);
+
+/* Routing only: optional RMSNorm, router logits in fp64, top-k, route weights,
+ * per-expert histogram, exclusive scan and stable permutation.
+ *   x        [T, H] float32 or bfloat16 (shape->act_dtype), device
+ *   norm_w   [H] float32 RMSNorm weight or NULL (no norm), device
+ *   router_w [E, H] float32, router_b [E] float32, device
+ *   out      non-NULL; NULL fields are not written (see moe_route_out)
+ *   ws       >= moe_workspace_bytes(shape) bytes, 256-byte aligned, device
+ * Pages: goosedump `mixture_of_experts_batch` (router matmul, add_bias_batch,
+ * top_experts, softmax, routes_by_expert). */
+int moe_route(const moe_shape *shape, const void *x, const float *norm_w,
+              const float *router_w, const float *router_b, const moe_route_out *out,
+              void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* The whole block for a few tokens (T <= 64): streams only the k selected
+ * experts' bytes per token with GEMV kernels.
+ *   hidden   [T, H] float32 or bfloat16, device; it is also the residual
+ *   experts  E packed blobs, layout.stride bytes apart, device
+ *   shared   n_shared packed blobs (same layout) or NULL when n_shared == 0
+ *   out      [T, H] float32, device; may alias a float32 hidden
+ *   route_out NULL, or routing results to export (fields may be NULL)
+ * Pages: goosedump `mixture_of_experts` (router matvec, add_bias,
+ * top_experts, softmax, per expert: matrix_vector_pair, biases, swiglu,
+ * matrix_vector, bias, times the route weight, summed over slots). */
+int moe_forward_decode(const moe_shape *shape, const void *hidden, const float *norm_w,
+                       const float *router_w, const float *router_b, const uint8_t *experts,
+                       const uint8_t *shared, float *out, const moe_route_out *route_out,
+                       void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* The whole block for a token batch: routing, permutation, grouped GEMMs on
+ * the matrix cores (gate/up with bias and clamped SwiGLU fused; down with
+ * bias, route weight and scatter-add into out fused). Same arguments as
+ * moe_forward_decode; any T. out may alias a float32 hidden.
+ * Pages: goosedump `mixture_of_experts_batch`, `expert_batch_output`,
+ * `mix_expert_outputs`. */
+int moe_forward_prefill(const moe_shape *shape, const void *hidden, const float *norm_w,
+                        const float *router_w, const float *router_b, const uint8_t *experts,
+                        const uint8_t *shared, float *out, const moe_route_out *route_out,
+                        void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Export the weights the kernels compute with, for bit-exact checks.
+ *   blob   one packed expert, device
+ *   which  0 gate [F, H], 1 up [F, H], 2 down [H, F]
+ *   path   0: the float32 decoding the GEMV (decode) kernels use;
+ *          1: the bfloat16 decoding the matrix-core (prefill) kernels use,
+ *             widened to float32
+ *   out    float32 [rows, cols], device */
+int moe_dequant_debug(const moe_shape *shape, const uint8_t *blob, int32_t which, int32_t path,
+                      float *out, hipStream_t stream);
+
+/* Message of the last failing call on this thread ("" if none). */
+const char *moe_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MXFP4_H */

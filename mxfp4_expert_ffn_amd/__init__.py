@@ -1,0 +1,156 @@
+"""Routed MXFP4 Mixture-of-Experts block for AMD Instinct MI355X (gfx950).
+
+A thin binding over the C ABI of `libmoe_mxfp4.so` (include/moe_mxfp4.h):
+each function has the C name, turns torch device tensors into pointers and
+the current HIP stream, and raises `MoeError` on a negative status. Every
+step of the block runs in the library's HIP kernels; PyTorch only provides
+device memory and streams. There is no CPU fallback: without the built
+library every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+
+import numpy as np
+
+from . import _lib
+from ._lib import MOE_BF16, MOE_F32, MoeBlobLayout, MoeExpertPlanes, MoeRouteOut, MoeShape
+
+__all__ = [
+    "MoeError", "MoeShape", "make_shape", "moe_blob_layout_get", "moe_pack_experts",
+    "moe_workspace_bytes", "moe_route", "moe_forward_decode", "moe_forward_prefill",
+    "moe_dequant_debug", "moe_last_error", "ROUTE_FIELDS",
+]
+
+ROUTE_FIELDS = ("topk_idx", "topk_w", "counts", "offsets", "perm", "inv")
+
+
+class MoeError(RuntimeError):
+    def __init__(self, code: int, message: str):
+        super().__init__(f"[{code}] {message}")
+        self.code = code
+
+
+def make_shape(T, H, F, E, k, act_dtype="f32", n_shared=0, alpha=1.702, limit=7.0,
+               up_offset=1.0, route_scale=1.0, rms_eps=0.0) -> MoeShape:
+    return MoeShape(int(T), int(H), int(F), int(E), int(k),
+                    MOE_BF16 if act_dtype == "bf16" else MOE_F32, int(n_shared),
+                    float(alpha), float(limit), float(up_offset), float(route_scale),
+                    float(rms_eps))
+
+
+def moe_last_error() -> str:
+    return _lib.load().moe_last_error().decode()
+
+
+def _check(rc: int):
+    if rc != 0:
+        raise MoeError(rc, moe_last_error())
+
+
+def _ptr(t, name: str, dtype=None, optional: bool = False):
+    if t is None:
+        if optional:
+            return None
+        raise ValueError(f"{name} is required")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _route_out(route_out):
+    import torch
+    if route_out is None:
+        return None
+    ro = MoeRouteOut()
+    for f in ROUTE_FIELDS:
+        t = route_out.get(f)
+        dt = torch.float32 if f == "topk_w" else torch.int32
+        setattr(ro, f, None if t is None else _ptr(t, f, dt).value)
+    return ctypes.byref(ro)
+
+
+def moe_blob_layout_get(shape: MoeShape) -> dict:
+    L = MoeBlobLayout()
+    _check(_lib.load().moe_blob_layout_get(ctypes.byref(shape), ctypes.byref(L)))
+    return {name: getattr(L, name) for name, _ in L._fields_}
+
+
+def moe_pack_experts(shape: MoeShape, planes) -> np.ndarray:
+    """Pack host planar MXFP4 experts (attributes or keys gate_codes, gate_scales,
+    gate_bias, up_*, down_*) into n blobs; returns uint8 [n * stride] (host)."""
+    get = (lambda k: planes[k]) if isinstance(planes, dict) else (lambda k: getattr(planes, k))
+    names = {"gate_q": "gate_codes", "up_q": "up_codes", "down_q": "down_codes",
+             "gate_s": "gate_scales", "up_s": "up_scales", "down_s": "down_scales",
+             "gate_b": "gate_bias", "up_b": "up_bias", "down_b": "down_bias"}
+    arrs = {}
+    for cname, pname in names.items():
+        a = get(pname)
+        want = np.float32 if cname.endswith("_b") else np.uint8
+        arrs[cname] = np.ascontiguousarray(a, dtype=want)
+    n = arrs["gate_q"].shape[0]
+    stride = moe_blob_layout_get(shape)["stride"]
+    dst = np.empty(n * stride, dtype=np.uint8)
+    p = MoeExpertPlanes(**{k: v.ctypes.data for k, v in arrs.items()})
+    _check(_lib.load().moe_pack_experts(ctypes.byref(shape), n, ctypes.byref(p),
+                                        dst.ctypes.data_as(ctypes.c_void_p)))
+    return dst
+
+
+def moe_workspace_bytes(shape: MoeShape) -> int:
+    n = _lib.load().moe_workspace_bytes(ctypes.byref(shape))
+    if n == 0:
+        raise MoeError(_lib.MOE_ERR_INVALID_ARG, moe_last_error())
+    return int(n)
+
+
+def moe_route(shape, x, router_w, router_b, route_out: dict, ws, norm_w=None, stream=None):
+    import torch
+    rc = _lib.load().moe_route(
+        ctypes.byref(shape), _ptr(x, "x", (torch.float32, torch.bfloat16, torch.int16, torch.uint16)),
+        _ptr(norm_w, "norm_w", torch.float32, optional=True),
+        _ptr(router_w, "router_w", torch.float32), _ptr(router_b, "router_b", torch.float32),
+        _route_out(route_out), _ptr(ws, "ws"), ws.numel() * ws.element_size(), _stream(stream))
+    _check(rc)
+
+
+def _forward(fn, shape, hidden, router_w, router_b, experts, out, ws, norm_w, shared,
+             route_out, stream):
+    import torch
+    rc = fn(ctypes.byref(shape),
+            _ptr(hidden, "hidden", (torch.float32, torch.bfloat16, torch.int16, torch.uint16)),
+            _ptr(norm_w, "norm_w", torch.float32, optional=True),
+            _ptr(router_w, "router_w", torch.float32), _ptr(router_b, "router_b", torch.float32),
+            _ptr(experts, "experts", torch.uint8), _ptr(shared, "shared", torch.uint8, optional=True),
+            _ptr(out, "out", torch.float32), _route_out(route_out), _ptr(ws, "ws"),
+            ws.numel() * ws.element_size(), _stream(stream))
+    _check(rc)
+
+
+def moe_forward_decode(shape, hidden, router_w, router_b, experts, out, ws, norm_w=None,
+                       shared=None, route_out=None, stream=None):
+    _forward(_lib.load().moe_forward_decode, shape, hidden, router_w, router_b, experts, out, ws,
+             norm_w, shared, route_out, stream)
+
+
+def moe_forward_prefill(shape, hidden, router_w, router_b, experts, out, ws, norm_w=None,
+                        shared=None, route_out=None, stream=None):
+    _forward(_lib.load().moe_forward_prefill, shape, hidden, router_w, router_b, experts, out, ws,
+             norm_w, shared, route_out, stream)
+
+
+def moe_dequant_debug(shape, blob, which: int, path: int, out, stream=None):
+    import torch
+    _check(_lib.load().moe_dequant_debug(ctypes.byref(shape), _ptr(blob, "blob", torch.uint8),
+                                         int(which), int(path), _ptr(out, "out", torch.float32),
+                                         _stream(stream)))

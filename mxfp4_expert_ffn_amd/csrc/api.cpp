@@ -1,0 +1,362 @@
+// C ABI of the routed MXFP4 MoE block: host-side validation, workspace
+// carving and the launch sequences. Declarations and contracts are in
+// include/moe_mxfp4.h.
+#include "moe_mxfp4.h"
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "kernels.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    std::vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return code;
+}
+
+int ok() {
+    g_last_error.clear();
+    return MOE_OK;
+}
+
+constexpr uint64_t align_up(uint64_t v, uint64_t a) { return (v + a - 1) / a * a; }
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int check_shape(const moe_shape *s) {
+    if (!s) return fail(MOE_ERR_INVALID_ARG, "shape is NULL");
+    if (s->T < 0 || s->T > (1 << 20)) return fail(MOE_ERR_INVALID_ARG, "T=%d outside [0, 2^20]", s->T);
+    if (s->E < 1 || s->E > moe::kMaxE) return fail(MOE_ERR_INVALID_ARG, "E=%d outside [1, 256]", s->E);
+    if (s->k < 1 || s->k > moe::kMaxK || s->k > s->E)
+        return fail(MOE_ERR_INVALID_ARG, "k=%d outside [1, min(E, 8)]", s->k);
+    if (s->H < 32 || s->H > 16384 || s->H % 32)
+        return fail(MOE_ERR_INVALID_ARG, "H=%d must be a multiple of 32 in [32, 16384]", s->H);
+    if (s->F < 32 || s->F > 16384 || s->F % 32)
+        return fail(MOE_ERR_INVALID_ARG, "F=%d must be a multiple of 32 in [32, 16384]", s->F);
+    if (s->act_dtype != MOE_F32 && s->act_dtype != MOE_BF16)
+        return fail(MOE_ERR_INVALID_ARG, "act_dtype=%d is neither MOE_F32 nor MOE_BF16", s->act_dtype);
+    if (s->n_shared != 0 && s->n_shared != 1)
+        return fail(MOE_ERR_INVALID_ARG, "n_shared=%d must be 0 or 1", s->n_shared);
+    if (!std::isfinite(s->swiglu_alpha)) return fail(MOE_ERR_INVALID_ARG, "swiglu_alpha is not finite");
+    if (!(s->swiglu_limit > 0.f)) return fail(MOE_ERR_INVALID_ARG, "swiglu_limit must be > 0");
+    if (!std::isfinite(s->swiglu_up_offset)) return fail(MOE_ERR_INVALID_ARG, "swiglu_up_offset is not finite");
+    if (!std::isfinite(s->route_scale) || !(s->route_scale > 0.f))
+        return fail(MOE_ERR_INVALID_ARG, "route_scale must be finite and > 0");
+    return MOE_OK;
+}
+
+void layout_of(const moe_shape *s, moe_blob_layout *L) {
+    const uint64_t H = s->H, F = s->F;
+    uint64_t o = 0;
+    auto take = [&](uint64_t bytes) {
+        const uint64_t at = o;
+        o = align_up(o + bytes, 256);
+        return at;
+    };
+    L->gate_q = take(F * H / 2);
+    L->up_q = take(F * H / 2);
+    L->down_q = take(H * F / 2);
+    L->gate_s = take(F * H / 32);
+    L->up_s = take(F * H / 32);
+    L->down_s = take(H * F / 32);
+    L->gate_b = take(F * 4);
+    L->up_b = take(F * 4);
+    const uint64_t db = o;
+    L->down_b = db;
+    L->bytes = db + H * 4;
+    L->stride = align_up(L->bytes, 4096);
+}
+
+struct Workspace {
+    double *xn64;
+    float *xn32;
+    double *logits;
+    int32_t *idx;
+    float *wts;
+    int32_t *counts, *offsets, *mprefix, *perm, *inv, *rank;
+    float *act;
+    uint64_t bytes;
+};
+
+Workspace carve(const moe_shape *s, uint8_t *base) {
+    const uint64_t T = s->T, H = s->H, F = s->F, E = s->E, k = s->k, ns = s->n_shared;
+    const uint64_t R = T * k;
+    Workspace w{};
+    uint64_t o = 0;
+    auto take = [&](uint64_t bytes) {
+        uint8_t *p = base ? base + o : nullptr;
+        o = align_up(o + bytes, 256);
+        return p;
+    };
+    w.xn64 = reinterpret_cast<double *>(take(T * H * 8));
+    w.xn32 = reinterpret_cast<float *>(take(T * H * 4));
+    w.logits = reinterpret_cast<double *>(take(T * E * 8));
+    w.idx = reinterpret_cast<int32_t *>(take(R * 4));
+    w.wts = reinterpret_cast<float *>(take(R * 4));
+    w.counts = reinterpret_cast<int32_t *>(take((E + 1) * 4));
+    w.offsets = reinterpret_cast<int32_t *>(take((E + 2) * 4));
+    w.mprefix = reinterpret_cast<int32_t *>(take((E + 2) * 4));
+    w.perm = reinterpret_cast<int32_t *>(take(R * 4));
+    w.inv = reinterpret_cast<int32_t *>(take(R * 4));
+    w.rank = reinterpret_cast<int32_t *>(take(R * 4));
+    w.act = reinterpret_cast<float *>(take((R + T * ns) * F * 4));
+    w.bytes = o;
+    return w;
+}
+
+int check_ws(const moe_shape *s, void *ws, size_t ws_bytes) {
+    const uint64_t need = carve(s, nullptr).bytes;
+    if (!ws) return fail(MOE_ERR_WORKSPACE, "workspace is NULL");
+    if (!aligned(ws, 256)) return fail(MOE_ERR_WORKSPACE, "workspace is not 256-byte aligned");
+    if (ws_bytes < need)
+        return fail(MOE_ERR_WORKSPACE, "workspace has %zu bytes, needs %llu", ws_bytes,
+                    static_cast<unsigned long long>(need));
+    return MOE_OK;
+}
+
+moe::ExpertPtrs expert_ptrs(const moe_shape *s, const uint8_t *base) {
+    moe_blob_layout L;
+    layout_of(s, &L);
+    moe::ExpertPtrs p;
+    p.base = base;
+    p.stride = L.stride;
+    p.gate_q = L.gate_q;
+    p.up_q = L.up_q;
+    p.down_q = L.down_q;
+    p.gate_s = L.gate_s;
+    p.up_s = L.up_s;
+    p.down_s = L.down_s;
+    p.gate_b = L.gate_b;
+    p.up_b = L.up_b;
+    p.down_b = L.down_b;
+    return p;
+}
+
+int hip_check(hipError_t e, const char *what) {
+    if (e != hipSuccess) return fail(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+    return MOE_OK;
+}
+
+#define MOE_TRY(expr)               \
+    do {                            \
+        const int rc_ = (expr);     \
+        if (rc_ != MOE_OK) return rc_; \
+    } while (0)
+
+// Shared argument checks of the two forward entry points.
+int check_forward(const moe_shape *s, const void *hidden, const float *norm_w,
+                  const float *router_w, const float *router_b, const uint8_t *experts,
+                  const uint8_t *shared, const float *out, void *ws, size_t ws_bytes) {
+    MOE_TRY(check_shape(s));
+    if (s->T == 0) return MOE_OK;  // nothing is read or written
+    if (!hidden || !router_w || !router_b || !experts || !out)
+        return fail(MOE_ERR_INVALID_ARG, "hidden, router_w, router_b, experts and out must be non-NULL");
+    if (s->n_shared && !shared) return fail(MOE_ERR_INVALID_ARG, "n_shared=1 needs a shared expert blob");
+    if (!s->n_shared && shared) return fail(MOE_ERR_INVALID_ARG, "shared blob given with n_shared=0");
+    if (!aligned(hidden, 16) || !aligned(out, 16) || !aligned(router_w, 16))
+        return fail(MOE_ERR_INVALID_ARG, "hidden, out and router_w must be 16-byte aligned");
+    if (!aligned(experts, 256) || (shared && !aligned(shared, 256)))
+        return fail(MOE_ERR_INVALID_ARG, "expert blobs must be 256-byte aligned");
+    if (norm_w && !(s->rms_eps >= 0.f)) return fail(MOE_ERR_INVALID_ARG, "rms_eps must be >= 0");
+    if (s->act_dtype == MOE_BF16 && static_cast<const void *>(out) == hidden)
+        return fail(MOE_ERR_INVALID_ARG, "out may not alias a bfloat16 hidden");
+    return check_ws(s, ws, ws_bytes);
+}
+
+// RMSNorm (optional) and router logits; returns the expert-input pointer.
+int route_front(const moe_shape *s, const void *x, const float *norm_w, const float *router_w,
+                const float *router_b, const Workspace &w, bool small, const void **expert_in,
+                int *expert_in_bf16, hipStream_t st) {
+    const int bf16 = s->act_dtype == MOE_BF16;
+    const void *rin = x;
+    int kind = bf16;
+    *expert_in = x;
+    *expert_in_bf16 = bf16;
+    if (norm_w) {
+        MOE_TRY(hip_check(moe::launch_rmsnorm(x, bf16, norm_w, s->T, s->H, s->rms_eps, w.xn64,
+                                              w.xn32, st), "rmsnorm"));
+        rin = w.xn64;
+        kind = 2;
+        *expert_in = w.xn32;
+        *expert_in_bf16 = 0;
+    }
+    if (small)
+        return hip_check(moe::launch_router_gemv(rin, kind, router_w, router_b, s->T, s->H, s->E,
+                                                 w.logits, st), "router_gemv");
+    return hip_check(moe::launch_router_logits(rin, kind, router_w, router_b, s->T, s->H, s->E,
+                                               w.logits, st), "router_logits");
+}
+
+int max_mtiles(const moe_shape *s) {
+    const long long R = static_cast<long long>(s->T) * s->k;
+    const long long bm = moe::kGemmBM;
+    long long m = (R + bm - 1) / bm + (s->E < R ? s->E : R);
+    if (s->n_shared) m += (s->T + bm - 1) / bm;
+    return static_cast<int>(m);
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_blob_layout_get(const moe_shape *shape, moe_blob_layout *layout) {
+    if (!shape || !layout) return fail(MOE_ERR_INVALID_ARG, "shape and layout must be non-NULL");
+    if (shape->H < 32 || shape->H > 16384 || shape->H % 32 || shape->F < 32 ||
+        shape->F > 16384 || shape->F % 32)
+        return fail(MOE_ERR_INVALID_ARG, "H and F must be multiples of 32 in [32, 16384]");
+    layout_of(shape, layout);
+    return ok();
+}
+
+int moe_pack_experts(const moe_shape *shape, int32_t n, const moe_expert_planes *p, uint8_t *dst) {
+    moe_blob_layout L;
+    MOE_TRY(moe_blob_layout_get(shape, &L));
+    if (n < 0 || !p || !dst) return fail(MOE_ERR_INVALID_ARG, "n >= 0, planes and dst required");
+    if (n > 0 && (!p->gate_q || !p->up_q || !p->down_q || !p->gate_s || !p->up_s || !p->down_s ||
+                  !p->gate_b || !p->up_b || !p->down_b))
+        return fail(MOE_ERR_INVALID_ARG, "every plane pointer must be non-NULL");
+    const uint64_t H = shape->H, F = shape->F;
+    for (int32_t i = 0; i < n; ++i) {
+        uint8_t *b = dst + static_cast<uint64_t>(i) * L.stride;
+        std::memset(b, 0, L.stride);
+        std::memcpy(b + L.gate_q, p->gate_q + i * F * H / 2, F * H / 2);
+        std::memcpy(b + L.up_q, p->up_q + i * F * H / 2, F * H / 2);
+        std::memcpy(b + L.down_q, p->down_q + i * H * F / 2, H * F / 2);
+        std::memcpy(b + L.gate_s, p->gate_s + i * F * H / 32, F * H / 32);
+        std::memcpy(b + L.up_s, p->up_s + i * F * H / 32, F * H / 32);
+        std::memcpy(b + L.down_s, p->down_s + i * H * F / 32, H * F / 32);
+        std::memcpy(b + L.gate_b, p->gate_b + i * F, F * 4);
+        std::memcpy(b + L.up_b, p->up_b + i * F, F * 4);
+        std::memcpy(b + L.down_b, p->down_b + i * H, H * 4);
+    }
+    return ok();
+}
+
+size_t moe_workspace_bytes(const moe_shape *shape) {
+    if (check_shape(shape) != MOE_OK) return 0;
+    return carve(shape, nullptr).bytes;
+}
+
+int moe_route(const moe_shape *s, const void *x, const float *norm_w, const float *router_w,
+              const float *router_b, const moe_route_out *out, void *ws, size_t ws_bytes,
+              hipStream_t st) {
+    MOE_TRY(check_shape(s));
+    if (s->T == 0) return ok();
+    if (!x || !router_w || !router_b || !out)
+        return fail(MOE_ERR_INVALID_ARG, "x, router_w, router_b and out must be non-NULL");
+    if (!aligned(x, 16) || !aligned(router_w, 16))
+        return fail(MOE_ERR_INVALID_ARG, "x and router_w must be 16-byte aligned");
+    if (norm_w && !(s->rms_eps >= 0.f)) return fail(MOE_ERR_INVALID_ARG, "rms_eps must be >= 0");
+    MOE_TRY(check_ws(s, ws, ws_bytes));
+    if (s->T == 0) return ok();
+    const Workspace w = carve(s, static_cast<uint8_t *>(ws));
+    const void *ein;
+    int ein_bf16;
+    MOE_TRY(route_front(s, x, norm_w, router_w, router_b, w, s->T <= 16, &ein, &ein_bf16, st));
+    MOE_TRY(hip_check(moe::launch_topk(w.logits, s->T, s->E, s->k, s->route_scale, w.idx, w.wts,
+                                       out->topk_idx, out->topk_w, nullptr, 0, s->H, nullptr, st),
+                      "topk"));
+    MOE_TRY(hip_check(moe::launch_permute(w.idx, s->T, s->E, s->k, 0, w.counts, w.offsets, w.perm,
+                                          w.inv, w.rank, w.mprefix, out->counts, out->offsets,
+                                          out->perm, out->inv, st),
+                      "permute"));
+    return ok();
+}
+
+int moe_forward_decode(const moe_shape *s, const void *hidden, const float *norm_w,
+                       const float *router_w, const float *router_b, const uint8_t *experts,
+                       const uint8_t *shared, float *out, const moe_route_out *ro, void *ws,
+                       size_t ws_bytes, hipStream_t st) {
+    MOE_TRY(check_forward(s, hidden, norm_w, router_w, router_b, experts, shared, out, ws, ws_bytes));
+    if (s->T > 64) return fail(MOE_ERR_UNSUPPORTED, "decode takes T <= 64 (T=%d); use prefill", s->T);
+    if (s->H > 8192 || s->F > 8192)
+        return fail(MOE_ERR_UNSUPPORTED, "decode takes H, F <= 8192");
+    if (s->T == 0) return ok();
+    const Workspace w = carve(s, static_cast<uint8_t *>(ws));
+    const void *ein;
+    int ein_bf16;
+    MOE_TRY(route_front(s, hidden, norm_w, router_w, router_b, w, true, &ein, &ein_bf16, st));
+    const moe::ExpertPtrs ex = expert_ptrs(s, experts);
+    const moe::ExpertPtrs sh = expert_ptrs(s, shared);
+    const moe::SwigluConsts c{s->swiglu_alpha, s->swiglu_limit, s->swiglu_up_offset};
+    MOE_TRY(hip_check(moe::launch_decode_gate_up(ein, ein_bf16, w.logits, s->T, s->H, s->F, s->E,
+                                                 s->k, s->n_shared, s->route_scale, ex, sh, c,
+                                                 w.idx, w.wts, ro ? ro->topk_idx : nullptr,
+                                                 ro ? ro->topk_w : nullptr, w.act, st),
+                      "decode_gate_up"));
+    MOE_TRY(hip_check(moe::launch_decode_down(hidden, s->act_dtype == MOE_BF16, s->T, s->H, s->F,
+                                              s->k, s->n_shared, ex, sh, w.idx, w.wts, w.act, out,
+                                              st),
+                      "decode_down"));
+    if (ro && (ro->counts || ro->offsets || ro->perm || ro->inv))
+        MOE_TRY(hip_check(moe::launch_permute(w.idx, s->T, s->E, s->k, 0, w.counts, w.offsets,
+                                              w.perm, w.inv, w.rank, w.mprefix, ro->counts,
+                                              ro->offsets, ro->perm, ro->inv, st),
+                          "permute"));
+    return ok();
+}
+
+int moe_forward_prefill(const moe_shape *s, const void *hidden, const float *norm_w,
+                        const float *router_w, const float *router_b, const uint8_t *experts,
+                        const uint8_t *shared, float *out, const moe_route_out *ro, void *ws,
+                        size_t ws_bytes, hipStream_t st) {
+    MOE_TRY(check_forward(s, hidden, norm_w, router_w, router_b, experts, shared, out, ws, ws_bytes));
+    if (s->T == 0) return ok();
+    const Workspace w = carve(s, static_cast<uint8_t *>(ws));
+    const void *ein;
+    int ein_bf16;
+    MOE_TRY(route_front(s, hidden, norm_w, router_w, router_b, w, s->T <= 16, &ein, &ein_bf16, st));
+    MOE_TRY(hip_check(moe::launch_topk(w.logits, s->T, s->E, s->k, s->route_scale, w.idx, w.wts,
+                                       ro ? ro->topk_idx : nullptr, ro ? ro->topk_w : nullptr,
+                                       hidden, s->act_dtype == MOE_BF16, s->H, out, st),
+                      "topk"));
+    MOE_TRY(hip_check(moe::launch_permute(w.idx, s->T, s->E, s->k, s->n_shared, w.counts,
+                                          w.offsets, w.perm, w.inv, w.rank, w.mprefix,
+                                          ro ? ro->counts : nullptr, ro ? ro->offsets : nullptr,
+                                          ro ? ro->perm : nullptr, ro ? ro->inv : nullptr, st),
+                      "permute"));
+    const moe::ExpertPtrs ex = expert_ptrs(s, experts);
+    const moe::ExpertPtrs sh = expert_ptrs(s, shared);
+    const moe::SwigluConsts c{s->swiglu_alpha, s->swiglu_limit, s->swiglu_up_offset};
+    const int mt = max_mtiles(s);
+    MOE_TRY(hip_check(moe::launch_gate_up_gemm(ein, ein_bf16, s->T, s->H, s->F, s->E, s->k,
+                                               s->n_shared, ex, sh, c, w.offsets, w.perm,
+                                               w.mprefix, mt, w.act, st),
+                      "gate_up_gemm"));
+    MOE_TRY(hip_check(moe::launch_down_gemm(s->T, s->H, s->F, s->E, s->k, s->n_shared, ex, sh,
+                                            w.offsets, w.perm, w.wts, w.mprefix, mt, w.act, out,
+                                            st),
+                      "down_gemm"));
+    return ok();
+}
+
+int moe_dequant_debug(const moe_shape *s, const uint8_t *blob, int32_t which, int32_t path,
+                      float *out, hipStream_t st) {
+    moe_blob_layout L;
+    MOE_TRY(moe_blob_layout_get(s, &L));
+    if (!blob || !out) return fail(MOE_ERR_INVALID_ARG, "blob and out must be non-NULL");
+    if (!aligned(blob, 256)) return fail(MOE_ERR_INVALID_ARG, "blob must be 256-byte aligned");
+    if (which < 0 || which > 2) return fail(MOE_ERR_INVALID_ARG, "which must be 0, 1 or 2");
+    if (path < 0 || path > 1) return fail(MOE_ERR_INVALID_ARG, "path must be 0 or 1");
+    const int rows = which == 2 ? s->H : s->F;
+    const int K = which == 2 ? s->F : s->H;
+    const uint8_t *q = blob + (which == 0 ? L.gate_q : which == 1 ? L.up_q : L.down_q);
+    const uint8_t *sc = blob + (which == 0 ? L.gate_s : which == 1 ? L.up_s : L.down_s);
+    MOE_TRY(hip_check(moe::launch_dequant(q, sc, rows, K, path, out, st), "dequant"));
+    return ok();
+}
+
+const char *moe_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

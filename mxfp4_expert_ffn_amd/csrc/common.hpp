@@ -1,0 +1,168 @@
+// Device-side building blocks shared by the MoE kernels (gfx950 / CDNA4).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kernels.hpp"
+
+namespace moe {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------- MXFP4
+// An E8M0 scale byte b stands for 2^(b-127); as float32 bits that is b << 23
+// (exact for b in 1..254).
+__device__ __forceinline__ float e8m0_scale(uint32_t b) { return __uint_as_float(b << 23); }
+
+// Eight E2M1 codes packed in one dword (element 2i in the low nibble of byte i)
+// decoded and scaled to bfloat16 with the gfx950 scaled FP4 converts; any
+// E2M1 value times 2^n is exact in bfloat16.
+__device__ __forceinline__ bf16x8_t fp4x8_to_bf16(uint32_t q, float s) {
+    bf16x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, s, 0);
+    bf16x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, s, 1);
+    bf16x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, s, 2);
+    bf16x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, s, 3);
+    return bf16x8_t{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+}
+
+// Same eight codes decoded to float32 (exact), times s.
+__device__ __forceinline__ void fp4x8_to_f32(uint32_t q, float s, float (&w)[8]) {
+    f32x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q, s, 0);
+    f32x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q, s, 1);
+    f32x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q, s, 2);
+    f32x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q, s, 3);
+    w[0] = p0[0]; w[1] = p0[1]; w[2] = p1[0]; w[3] = p1[1];
+    w[4] = p2[0]; w[5] = p2[1]; w[6] = p3[0]; w[7] = p3[1];
+}
+
+// Dot product of one 32-element MX block (16 code bytes, scale s) with 32
+// float32 activations held in registers.
+__device__ __forceinline__ float mx_block_dot(uint4 q, float s, const float (&x)[32]) {
+    float acc = 0.f;
+    const uint32_t d[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        float w[8];
+        fp4x8_to_f32(d[i], s, w);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc = fmaf(w[j], x[8 * i + j], acc);
+    }
+    return acc;
+}
+
+// ---------------------------------------------------------------- bfloat16
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
+    return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// x = hi + lo with hi = bf16(x) and lo = bf16(x - hi): 16 significant bits,
+// enough that the two-term bf16 products keep float32-level accuracy.
+__device__ __forceinline__ void split_bf16(float x, __bf16 &hi, __bf16 &lo) {
+    hi = static_cast<__bf16>(x);
+    lo = static_cast<__bf16>(x - static_cast<float>(hi));
+}
+
+// ---------------------------------------------------------------- wave sums
+// Sum over the 64 lanes with DPP row operations; the total lands in lane 63
+// and is broadcast with readlane. All lanes must be active.
+__device__ __forceinline__ float wave_sum(float v) {
+    v += __builtin_amdgcn_update_dpp(0.0f, v, 0xB1, 0xf, 0xf, false);   // quad_perm [1,0,3,2]
+    v += __builtin_amdgcn_update_dpp(0.0f, v, 0x4E, 0xf, 0xf, false);   // quad_perm [2,3,0,1]
+    v += __builtin_amdgcn_update_dpp(0.0f, v, 0x141, 0xf, 0xf, false);  // row_half_mirror
+    v += __builtin_amdgcn_update_dpp(0.0f, v, 0x140, 0xf, 0xf, false);  // row_mirror
+    v += __builtin_amdgcn_update_dpp(0.0f, v, 0x142, 0xa, 0xf, false);  // row_bcast:15
+    v += __builtin_amdgcn_update_dpp(0.0f, v, 0x143, 0xc, 0xf, false);  // row_bcast:31
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
+__device__ __forceinline__ double wave_sum_f64(double v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
+    return v;
+}
+
+__device__ __forceinline__ double wave_max_f64(double v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v = fmax(v, __shfl_xor(v, off, kWave));
+    return v;
+}
+
+// ---------------------------------------------------------------- SwiGLU
+// Clamped SwiGLU: gate clamped above at `limit`, up clamped to [-limit, limit],
+// a = g * sigmoid(alpha * g) * (u + up_offset).
+__device__ __forceinline__ float swiglu(float g, float u, float alpha, float limit, float up_off) {
+    g = fminf(g, limit);
+    u = fminf(fmaxf(u, -limit), limit);
+    return g / (1.0f + __expf(-alpha * g)) * (u + up_off);
+}
+
+// ---------------------------------------------------------------- top-k
+// Top-k of one token's fp64 logits (E <= 256) by one wavefront. Lane l holds
+// experts l, l+64, l+128, l+192. Each round takes the wave maximum over the
+// experts still in play, then the lowest expert index holding it (ballot per
+// quarter: lanes are in index order inside a quarter, quarters in index
+// order), and retires it; so the result is by descending value with equal
+// values in ascending index order. A NaN logit counts as -inf, so every
+// returned index is a distinct valid expert whatever the input.
+// sel[j] and val[j] are uniform across the wave on return.
+__device__ __forceinline__ void wave_topk(const double *logits, int E, int k, int *sel,
+                                          double *val) {
+    const int lane = threadIdx.x & (kWave - 1);
+    double v[4];
+    bool alive[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int e = lane + kWave * q;
+        alive[q] = e < E;
+        const double l = alive[q] ? logits[e] : -INFINITY;
+        v[q] = l == l ? l : -INFINITY;
+    }
+    for (int j = 0; j < k; ++j) {
+        double m = -INFINITY;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            if (alive[q]) m = fmax(m, v[q]);
+        m = wave_max_f64(m);
+        int chosen = -1;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const uint64_t hit = __ballot(alive[q] && v[q] == m);
+            if (chosen < 0 && hit) chosen = kWave * q + (__ffsll(static_cast<long long>(hit)) - 1);
+        }
+        sel[j] = chosen;
+        val[j] = m;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            if (lane + kWave * q == chosen) alive[q] = false;
+    }
+}
+
+// Route weights: route_scale * softmax over the k selected logits, in fp64.
+__device__ __forceinline__ void route_softmax(const double *val, int k, float scale, float *w) {
+    double z[kMaxK];
+    double s = 0.0;
+    for (int j = 0; j < k; ++j) {
+        z[j] = exp(val[j] - val[0]);
+        s += z[j];
+    }
+    for (int j = 0; j < k; ++j) w[j] = static_cast<float>(scale * z[j] / s);
+}
+
+// ---------------------------------------------------------------- XCD tiles
+// Logical tile of workgroup `bid` when tiles are dealt so that each XCD (one
+// L2) sweeps a contiguous range of the tile list. Returns false for spare
+// workgroups of an over-sized grid.
+__device__ __forceinline__ bool xcd_tile(int bid, int ntiles, int &tile) {
+    const int xcd = bid % kXcds, slot = bid / kXcds;
+    const int per = (ntiles + kXcds - 1) / kXcds;
+    tile = xcd * per + slot;
+    return slot < per && tile < ntiles;
+}
+
+}  // namespace moe

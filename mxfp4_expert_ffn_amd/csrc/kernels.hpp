@@ -1,0 +1,74 @@
+// Host-side launchers of the MoE kernels (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+constexpr int kXcds = 8;   // MI355X: 8 accelerator dies; workgroups are dealt round-robin
+constexpr int kMaxK = 8;   // experts per token
+constexpr int kMaxE = 256; // routed experts
+
+// Tile geometry of the grouped GEMMs (rows of one expert per tile, weight rows
+// per workgroup), shared by the permutation's tile prefix and the launches.
+constexpr int kGemmBM = 32;
+constexpr int kGateUpBN = 128;   // features per gate/up workgroup (4 waves x 32)
+constexpr int kDownBN = 256;     // hidden rows per down workgroup (4 waves x 2 x 32)
+constexpr int kDecodeRowsGU = 8; // expert rows per decode gate/up workgroup
+constexpr int kDecodeRowsDn = 8; // hidden rows per decode down workgroup
+
+struct ExpertPtrs {
+    const uint8_t *base;     // first packed expert
+    uint64_t stride;         // bytes between experts
+    uint64_t gate_q, up_q, down_q, gate_s, up_s, down_s, gate_b, up_b, down_b;
+};
+
+struct SwigluConsts {
+    float alpha, limit, up_offset;
+};
+
+// routing -----------------------------------------------------------------
+hipError_t launch_rmsnorm(const void *x, int x_bf16, const float *gamma, int T, int H, float eps,
+                          double *xn64, float *xn32, hipStream_t s);
+// in_kind: 0 float32, 1 bf16 bits, 2 float64
+hipError_t launch_router_logits(const void *x, int in_kind, const float *w, const float *b,
+                                int T, int H, int E, double *logits, hipStream_t s);
+hipError_t launch_router_gemv(const void *x, int in_kind, const float *w, const float *b, int T,
+                              int H, int E, double *logits, hipStream_t s);
+hipError_t launch_topk(const double *logits, int T, int E, int k, float route_scale,
+                       int32_t *idx, float *wts, int32_t *out_idx, float *out_w,
+                       const void *resid, int resid_bf16, int H, float *out, hipStream_t s);
+hipError_t launch_permute(const int32_t *idx, int T, int E, int k, int n_shared,
+                          int32_t *counts, int32_t *offsets, int32_t *perm, int32_t *inv,
+                          int32_t *rank, int32_t *mprefix, int32_t *out_counts,
+                          int32_t *out_offsets, int32_t *out_perm, int32_t *out_inv,
+                          hipStream_t s);
+
+// decode ------------------------------------------------------------------
+hipError_t launch_decode_gate_up(const void *x, int x_bf16, const double *logits, int T, int H,
+                                 int F, int E, int k, int n_shared, float route_scale,
+                                 const ExpertPtrs &ex, const ExpertPtrs &sh, SwigluConsts c,
+                                 int32_t *idx, float *wts, int32_t *out_idx, float *out_w,
+                                 float *act, hipStream_t s);
+hipError_t launch_decode_down(const void *resid, int resid_bf16, int T, int H, int F, int k,
+                              int n_shared, const ExpertPtrs &ex, const ExpertPtrs &sh,
+                              const int32_t *idx, const float *wts, const float *act, float *out,
+                              hipStream_t s);
+
+// prefill -----------------------------------------------------------------
+hipError_t launch_gate_up_gemm(const void *x, int x_bf16, int T, int H, int F, int E, int k,
+                               int n_shared, const ExpertPtrs &ex, const ExpertPtrs &sh,
+                               SwigluConsts c, const int32_t *offsets, const int32_t *perm,
+                               const int32_t *mprefix, int max_mtiles, float *act,
+                               hipStream_t s);
+hipError_t launch_down_gemm(int T, int H, int F, int E, int k, int n_shared, const ExpertPtrs &ex,
+                            const ExpertPtrs &sh, const int32_t *offsets, const int32_t *perm,
+                            const float *wts, const int32_t *mprefix, int max_mtiles,
+                            const float *act, float *out, hipStream_t s);
+
+// debug -------------------------------------------------------------------
+hipError_t launch_dequant(const uint8_t *codes, const uint8_t *scales, int rows, int K, int path,
+                          float *out, hipStream_t s);
+
+}  // namespace moe

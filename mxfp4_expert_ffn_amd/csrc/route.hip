@@ -1,0 +1,295 @@
+// Routing kernels: RMSNorm, router logits (fp64), top-k + route weights,
+// per-expert histogram / exclusive scan / stable permutation.
+//
+// Pages: goosedump `gpt_oss.rs` `mixture_of_experts_batch` (router matmul,
+// add_bias_batch, top_experts, softmax, routes_by_expert in token order),
+// `top_experts` (descending value, lower index on ties); antirez `ds4.c`
+// `rms_norm_weight` (sum of squares accumulated in double).
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace moe {
+
+namespace {
+
+template <int KIND>
+__device__ __forceinline__ double load_in(const void *x, size_t i) {
+    if constexpr (KIND == 0) return static_cast<double>(static_cast<const float *>(x)[i]);
+    else if constexpr (KIND == 1) return static_cast<double>(bf16_bits_to_f32(static_cast<const uint16_t *>(x)[i]));
+    else return static_cast<const double *>(x)[i];
+}
+
+// ---------------------------------------------------------------- RMSNorm
+// One workgroup per token: fp64 sum of squares, inv = 1/sqrt(ss/H + eps),
+// xn = x * inv * gamma kept in fp64 (for the router) and float32 (experts).
+template <int KIND>
+__global__ __launch_bounds__(256) void rmsnorm_kernel(const void *x, const float *gamma, int H,
+                                                      float eps, double *xn64, float *xn32) {
+    const int t = blockIdx.x;
+    const size_t row = static_cast<size_t>(t) * H;
+    double ss = 0.0;
+    for (int h = threadIdx.x; h < H; h += blockDim.x) {
+        const double v = load_in<KIND>(x, row + h);
+        ss = fma(v, v, ss);
+    }
+    __shared__ double part[4];
+    ss = wave_sum_f64(ss);
+    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = ss;
+    __syncthreads();
+    const double total = part[0] + part[1] + part[2] + part[3];
+    const double inv = 1.0 / sqrt(total / H + static_cast<double>(eps));
+    for (int h = threadIdx.x; h < H; h += blockDim.x) {
+        const double v = load_in<KIND>(x, row + h) * inv * static_cast<double>(gamma[h]);
+        xn64[row + h] = v;
+        xn32[row + h] = static_cast<float>(v);
+    }
+}
+
+// ---------------------------------------------------------------- router logits
+// Tiled fp64 GEMM for token batches: a workgroup computes a 32-token x
+// 64-expert tile; thread (ti, ei) owns tokens 2ti, 2ti+1 and experts
+// ei + 16q. fp32 x fp32 products are exact in fp64.
+template <int KIND>
+__global__ __launch_bounds__(256) void router_logits_kernel(const void *x, const float *w,
+                                                            const float *b, int T, int H, int E,
+                                                            double *logits) {
+    __shared__ double xs[32][33];
+    __shared__ double wsm[64][33];
+    const int t0 = blockIdx.x * 32, e0 = blockIdx.y * 64;
+    const int ti = threadIdx.x >> 4, ei = threadIdx.x & 15;
+    double acc[2][4] = {};
+    for (int h0 = 0; h0 < H; h0 += 32) {
+        for (int i = threadIdx.x; i < 32 * 32; i += 256) {
+            const int r = i >> 5, c = i & 31, t = t0 + r;
+            xs[r][c] = t < T ? load_in<KIND>(x, static_cast<size_t>(t) * H + h0 + c) : 0.0;
+        }
+        for (int i = threadIdx.x; i < 64 * 32; i += 256) {
+            const int r = i >> 5, c = i & 31, e = e0 + r;
+            wsm[r][c] = e < E ? static_cast<double>(w[static_cast<size_t>(e) * H + h0 + c]) : 0.0;
+        }
+        __syncthreads();
+#pragma unroll 8
+        for (int c = 0; c < 32; ++c) {
+            const double a0 = xs[2 * ti][c], a1 = xs[2 * ti + 1][c];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const double bw = wsm[ei + 16 * q][c];
+                acc[0][q] = fma(a0, bw, acc[0][q]);
+                acc[1][q] = fma(a1, bw, acc[1][q]);
+            }
+        }
+        __syncthreads();
+    }
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+        const int t = t0 + 2 * ti + r;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int e = e0 + ei + 16 * q;
+            if (t < T && e < E)
+                logits[static_cast<size_t>(t) * E + e] = acc[r][q] + static_cast<double>(b[e]);
+        }
+    }
+}
+
+// Router for a handful of tokens: one wavefront per expert streams that
+// expert's router row with 128-bit loads; tokens in groups of 8.
+template <int KIND>
+__global__ __launch_bounds__(256) void router_gemv_kernel(const void *x, const float *w,
+                                                          const float *b, int T, int H, int E,
+                                                          double *logits) {
+    const int lane = threadIdx.x & 63;
+    const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (e >= E) return;  // whole wavefront leaves; no workgroup barrier below
+    const float4 *wr = reinterpret_cast<const float4 *>(w + static_cast<size_t>(e) * H);
+    const int n4 = H / 4;
+    for (int t0 = 0; t0 < T; t0 += 8) {
+        double acc[8] = {};
+        for (int i = lane; i < n4; i += 64) {
+            const float4 wv = wr[i];
+#pragma unroll
+            for (int tt = 0; tt < 8; ++tt) {
+                if (t0 + tt < T) {
+                    const size_t base = static_cast<size_t>(t0 + tt) * H + 4 * i;
+                    acc[tt] = fma(static_cast<double>(wv.x), load_in<KIND>(x, base + 0), acc[tt]);
+                    acc[tt] = fma(static_cast<double>(wv.y), load_in<KIND>(x, base + 1), acc[tt]);
+                    acc[tt] = fma(static_cast<double>(wv.z), load_in<KIND>(x, base + 2), acc[tt]);
+                    acc[tt] = fma(static_cast<double>(wv.w), load_in<KIND>(x, base + 3), acc[tt]);
+                }
+            }
+        }
+#pragma unroll
+        for (int tt = 0; tt < 8; ++tt) {
+            const double s = wave_sum_f64(acc[tt]);
+            if (lane == 0 && t0 + tt < T)
+                logits[static_cast<size_t>(t0 + tt) * E + e] = s + static_cast<double>(b[e]);
+        }
+    }
+}
+
+// ---------------------------------------------------------------- top-k
+// One wavefront per token: top-k, route weights; optionally copies the
+// residual into `out` (the grouped down GEMM then adds into it).
+__global__ __launch_bounds__(256) void topk_kernel(const double *logits, int T, int E, int k,
+                                                   float route_scale, int32_t *idx, float *wts,
+                                                   int32_t *out_idx, float *out_w,
+                                                   const void *resid, int resid_bf16, int H,
+                                                   float *out) {
+    const int lane = threadIdx.x & 63;
+    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t >= T) return;
+    int sel[kMaxK];
+    double val[kMaxK];
+    wave_topk(logits + static_cast<size_t>(t) * E, E, k, sel, val);
+    float w[kMaxK];
+    route_softmax(val, k, route_scale, w);
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j) {
+        if (j < k && lane == j) {
+            idx[t * k + j] = sel[j];
+            wts[t * k + j] = w[j];
+            if (out_idx) out_idx[t * k + j] = sel[j];
+            if (out_w) out_w[t * k + j] = w[j];
+        }
+    }
+    if (out) {
+        float *o = out + static_cast<size_t>(t) * H;
+        if (resid_bf16) {
+            const uint16_t *r = static_cast<const uint16_t *>(resid) + static_cast<size_t>(t) * H;
+            for (int h = lane; h < H; h += 64) o[h] = bf16_bits_to_f32(r[h]);
+        } else {
+            const float4 *r = reinterpret_cast<const float4 *>(static_cast<const float *>(resid) +
+                                                               static_cast<size_t>(t) * H);
+            float4 *o4 = reinterpret_cast<float4 *>(o);
+            if (static_cast<const void *>(r) != static_cast<const void *>(o4))
+                for (int h = lane; h < H / 4; h += 64) o4[h] = r[h];
+        }
+    }
+}
+
+// ---------------------------------------------------------------- permutation
+// One workgroup of 1024 threads. Routes r = t*k + j are taken in chunks of
+// 1024; inside a wavefront the lanes holding the same expert are found with
+// ballots and ranked by lane; per-wave counts are prefix-summed per expert in
+// wave order, so a route's rank counts exactly the earlier routes of its
+// expert: the permutation is stable (ascending token). Then counts, the
+// exclusive scan, the M-tile prefix for the grouped GEMMs, perm and inv.
+// Group E (when n_shared) is the shared expert: T rows, identity order.
+__global__ __launch_bounds__(1024) void permute_kernel(
+    const int32_t *idx, int T, int E, int k, int n_shared, int bm, int32_t *counts,
+    int32_t *offsets, int32_t *perm, int32_t *inv, int32_t *rank, int32_t *mprefix,
+    int32_t *out_counts, int32_t *out_offsets, int32_t *out_perm, int32_t *out_inv) {
+    __shared__ int wcnt[16][kMaxE];
+    __shared__ int base[kMaxE + 1];
+    __shared__ int start[kMaxE + 2];
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+    const int R = T * k;
+    const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    for (int e = tid; e < E; e += 1024) base[e] = 0;
+    __syncthreads();
+    for (int c0 = 0; c0 < R; c0 += 1024) {
+        for (int i = tid; i < 16 * kMaxE; i += 1024) wcnt[i / kMaxE][i % kMaxE] = 0;
+        __syncthreads();
+        const int r = c0 + tid;
+        const bool valid = r < R;
+        const int e = valid ? idx[r] : -1;
+        int myrank = 0;
+        uint64_t todo = __ballot(valid);
+        while (todo) {
+            const int leader = __ffsll(static_cast<long long>(todo)) - 1;
+            const int le = __shfl(e, leader, 64);
+            const uint64_t m = __ballot(e == le);
+            if (e == le) myrank = __popcll(m & lt_mask);
+            if (lane == leader) wcnt[w][le] = __popcll(m);
+            todo &= ~m;
+        }
+        __syncthreads();
+        for (int ee = tid; ee < E; ee += 1024) {
+            int run = base[ee];
+            for (int ww = 0; ww < 16; ++ww) {
+                const int c = wcnt[ww][ee];
+                wcnt[ww][ee] = run;
+                run += c;
+            }
+            base[ee] = run;
+        }
+        __syncthreads();
+        if (valid) rank[r] = wcnt[w][e] + myrank;
+        __syncthreads();
+    }
+    const int G = E + n_shared;
+    if (tid == 0) {
+        int off = 0, mt = 0;
+        for (int g = 0; g < G; ++g) {
+            const int c = g < E ? base[g] : T;
+            start[g] = off;
+            offsets[g] = off;
+            mprefix[g] = mt;
+            counts[g] = c;
+            if (out_counts && g < E) out_counts[g] = c;
+            if (out_offsets && g < E) out_offsets[g] = off;
+            off += c;
+            mt += (c + bm - 1) / bm;
+        }
+        start[G] = off;
+        offsets[G] = off;
+        mprefix[G] = mt;
+        if (out_offsets) out_offsets[E] = R;
+    }
+    __syncthreads();
+    for (int r = tid; r < R; r += 1024) {
+        const int pos = start[idx[r]] + rank[r];
+        perm[pos] = r;
+        inv[r] = pos;
+        if (out_perm) out_perm[pos] = r;
+        if (out_inv) out_inv[r] = pos;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_rmsnorm(const void *x, int x_bf16, const float *gamma, int T, int H, float eps,
+                          double *xn64, float *xn32, hipStream_t s) {
+    if (x_bf16)
+        rmsnorm_kernel<1><<<T, 256, 0, s>>>(x, gamma, H, eps, xn64, xn32);
+    else
+        rmsnorm_kernel<0><<<T, 256, 0, s>>>(x, gamma, H, eps, xn64, xn32);
+    return hipGetLastError();
+}
+
+hipError_t launch_router_logits(const void *x, int in_kind, const float *w, const float *b, int T,
+                                int H, int E, double *logits, hipStream_t s) {
+    dim3 grid((T + 31) / 32, (E + 63) / 64);
+    if (in_kind == 0) router_logits_kernel<0><<<grid, 256, 0, s>>>(x, w, b, T, H, E, logits);
+    else if (in_kind == 1) router_logits_kernel<1><<<grid, 256, 0, s>>>(x, w, b, T, H, E, logits);
+    else router_logits_kernel<2><<<grid, 256, 0, s>>>(x, w, b, T, H, E, logits);
+    return hipGetLastError();
+}
+
+hipError_t launch_router_gemv(const void *x, int in_kind, const float *w, const float *b, int T,
+                              int H, int E, double *logits, hipStream_t s) {
+    const int grid = (E + 3) / 4;
+    if (in_kind == 0) router_gemv_kernel<0><<<grid, 256, 0, s>>>(x, w, b, T, H, E, logits);
+    else if (in_kind == 1) router_gemv_kernel<1><<<grid, 256, 0, s>>>(x, w, b, T, H, E, logits);
+    else router_gemv_kernel<2><<<grid, 256, 0, s>>>(x, w, b, T, H, E, logits);
+    return hipGetLastError();
+}
+
+hipError_t launch_topk(const double *logits, int T, int E, int k, float route_scale, int32_t *idx,
+                       float *wts, int32_t *out_idx, float *out_w, const void *resid,
+                       int resid_bf16, int H, float *out, hipStream_t s) {
+    topk_kernel<<<(T + 3) / 4, 256, 0, s>>>(logits, T, E, k, route_scale, idx, wts, out_idx, out_w,
+                                            resid, resid_bf16, H, out);
+    return hipGetLastError();
+}
+
+hipError_t launch_permute(const int32_t *idx, int T, int E, int k, int n_shared, int32_t *counts,
+                          int32_t *offsets, int32_t *perm, int32_t *inv, int32_t *rank,
+                          int32_t *mprefix, int32_t *out_counts, int32_t *out_offsets,
+                          int32_t *out_perm, int32_t *out_inv, hipStream_t s) {
+    permute_kernel<<<1, 1024, 0, s>>>(idx, T, E, k, n_shared, kGemmBM, counts, offsets, perm, inv,
+                                      rank, mprefix, out_counts, out_offsets, out_perm, out_inv);
+    return hipGetLastError();
+}
+
+}  // namespace moe

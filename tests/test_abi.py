@@ -1,0 +1,161 @@
+"""The C-ABI library: loads, exports what the header declares, packs blobs
+per the documented layout, and rejects bad arguments on the host before
+touching a GPU. No compute calls here (runs without a GPU)."""
+import ctypes
+import glob
+import os
+import re
+
+import numpy as np
+import pytest
+
+import mxfp4_expert_ffn_amd as mx
+from mxfp4_expert_ffn_amd import _lib
+from workloads import config_by_id, make_layer, scaled
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_symbols():
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names |= set(re.findall(r"^\s*(?:int|size_t|const char \*)\s*(moe_\w+)\s*\(", text, re.M))
+    return names
+
+
+def test_header_declares_the_entry_points():
+    names = declared_symbols()
+    for n in ("moe_route", "moe_forward_decode", "moe_forward_prefill", "moe_blob_layout_get",
+              "moe_workspace_bytes", "moe_dequant_debug", "moe_pack_experts", "moe_last_error"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib.load()
+    for n in declared_symbols():
+        assert hasattr(lib, n), n
+        assert n in _lib.SIGNATURES, f"binding lacks {n}"
+
+
+def _shape(**kw):
+    base = dict(T=4, H=256, F=128, E=8, k=2)
+    base.update(kw)
+    return mx.make_shape(**base)
+
+
+def test_blob_layout_offsets_and_sizes():
+    for H, F in ((256, 256), (2880, 2880), (4096, 2048), (320, 96)):
+        L = mx.moe_blob_layout_get(_shape(H=H, F=F))
+        planes = [("gate_q", F * H // 2), ("up_q", F * H // 2), ("down_q", H * F // 2),
+                  ("gate_s", F * H // 32), ("up_s", F * H // 32), ("down_s", H * F // 32),
+                  ("gate_b", 4 * F), ("up_b", 4 * F), ("down_b", 4 * H)]
+        end = 0
+        for name, size in planes:
+            assert L[name] % 256 == 0 and L[name] >= end, name
+            end = L[name] + size
+        assert L["bytes"] == end and L["stride"] % 4096 == 0 and L["stride"] >= end
+        # algorithmic bytes: 17 bytes per 32 weights plus fp32 biases, up to plane padding
+        alg = 3 * F * H * 17 // 32 + 4 * (2 * F + H)
+        assert alg <= L["bytes"] < alg + 9 * 256
+    assert mx.moe_blob_layout_get(_shape(H=2880, F=2880))["bytes"] == 13254144
+    assert mx.moe_blob_layout_get(_shape(H=4096, F=2048))["bytes"] == 13402112
+
+
+def test_pack_places_every_plane():
+    cfg = scaled(config_by_id(1), E=3)
+    layer = make_layer(cfg)
+    shape = mx.make_shape(**cfg.shape_kwargs())
+    L = mx.moe_blob_layout_get(shape)
+    blob = mx.moe_pack_experts(shape, layer.experts)
+    assert blob.size == 3 * L["stride"]
+    H, F = cfg.H, cfg.F
+    for e in range(3):
+        b = blob[e * L["stride"]:(e + 1) * L["stride"]]
+        ex = layer.experts
+
+        def plane(name, n):
+            return b[L[name]:L[name] + n]
+        assert np.array_equal(plane("gate_q", F * H // 2), ex.gate_codes[e].ravel())
+        assert np.array_equal(plane("up_q", F * H // 2), ex.up_codes[e].ravel())
+        assert np.array_equal(plane("down_q", H * F // 2), ex.down_codes[e].ravel())
+        assert np.array_equal(plane("gate_s", F * H // 32), ex.gate_scales[e].ravel())
+        assert np.array_equal(plane("down_s", H * F // 32), ex.down_scales[e].ravel())
+        assert np.array_equal(plane("up_b", 4 * F).view(np.float32), ex.up_bias[e])
+        assert np.array_equal(plane("down_b", 4 * H).view(np.float32), ex.down_bias[e])
+        assert not b[L["bytes"]:].any()
+
+
+def test_workspace_bytes():
+    assert mx.moe_workspace_bytes(_shape()) > 0
+    big = mx.moe_workspace_bytes(_shape(T=2048, H=4096, F=2048, E=256, k=6, n_shared=1))
+    act = (2048 * 6 + 2048) * 2048 * 4
+    assert act < big < act + 2048 * 4096 * 12 + 2048 * 256 * 8 + (1 << 22)
+    with pytest.raises(mx.MoeError):
+        mx.moe_workspace_bytes(_shape(k=9))
+
+
+FAKE = 1 << 20  # a non-NULL, aligned address; validation fails before any use
+
+
+def _call(fn_name, shape, **over):
+    lib = _lib.load()
+    args = dict(hidden=FAKE, norm_w=None, router_w=FAKE, router_b=FAKE, experts=FAKE,
+                shared=None, out=FAKE, ro=None, ws=FAKE, ws_bytes=1 << 40, stream=None)
+    args.update(over)
+    fn = getattr(lib, fn_name)
+    return fn(ctypes.byref(shape), args["hidden"], args["norm_w"], args["router_w"],
+              args["router_b"], args["experts"], args["shared"], args["out"], args["ro"],
+              args["ws"], args["ws_bytes"], args["stream"])
+
+
+@pytest.mark.parametrize("fn", ["moe_forward_decode", "moe_forward_prefill"])
+@pytest.mark.parametrize("case", [
+    ("k > E", dict(k=9, E=8), {}, _lib.MOE_ERR_INVALID_ARG),
+    ("k = 0", dict(k=0), {}, _lib.MOE_ERR_INVALID_ARG),
+    ("E > 256", dict(E=257), {}, _lib.MOE_ERR_INVALID_ARG),
+    ("H % 32", dict(H=100), {}, _lib.MOE_ERR_INVALID_ARG),
+    ("F % 32", dict(F=40), {}, _lib.MOE_ERR_INVALID_ARG),
+    ("null hidden", {}, dict(hidden=None), _lib.MOE_ERR_INVALID_ARG),
+    ("null experts", {}, dict(experts=None), _lib.MOE_ERR_INVALID_ARG),
+    ("misaligned hidden", {}, dict(hidden=FAKE + 4), _lib.MOE_ERR_INVALID_ARG),
+    ("misaligned blob", {}, dict(experts=FAKE + 16), _lib.MOE_ERR_INVALID_ARG),
+    ("shared missing", dict(n_shared=1), {}, _lib.MOE_ERR_INVALID_ARG),
+    ("bad dtype", dict(act_dtype="x"), {}, None),
+    ("small workspace", {}, dict(ws_bytes=1024), _lib.MOE_ERR_WORKSPACE),
+    ("null workspace", {}, dict(ws=None), _lib.MOE_ERR_WORKSPACE),
+    ("misaligned workspace", {}, dict(ws=FAKE + 64), _lib.MOE_ERR_WORKSPACE),
+    ("nonpositive limit", dict(limit=0.0), {}, _lib.MOE_ERR_INVALID_ARG),
+    ("nonpositive scale", dict(route_scale=-1.0), {}, _lib.MOE_ERR_INVALID_ARG),
+], ids=lambda c: c[0] if isinstance(c, tuple) else c)
+def test_host_validation_errors(fn, case):
+    _, skw, over, code = case
+    shape = _shape(**skw)
+    if code is None:  # make_shape maps unknown dtypes to f32; poke an invalid value directly
+        shape.act_dtype = 7
+        code = _lib.MOE_ERR_INVALID_ARG
+    rc = _call(fn, shape, **over)
+    assert rc == code
+    assert mx.moe_last_error()
+
+
+def test_decode_rejects_large_T_and_bf16_alias():
+    assert _call("moe_forward_decode", _shape(T=65)) == _lib.MOE_ERR_UNSUPPORTED
+    assert _call("moe_forward_decode", _shape(H=16384)) == _lib.MOE_ERR_UNSUPPORTED
+    assert _call("moe_forward_prefill", _shape(act_dtype="bf16"), out=FAKE, hidden=FAKE) == \
+        _lib.MOE_ERR_INVALID_ARG
+
+
+def test_zero_tokens_is_ok_without_pointers():
+    shape = _shape(T=0)
+    assert _call("moe_forward_prefill", shape, hidden=None, out=None, ws=None) == 0
+    assert _call("moe_forward_decode", shape, hidden=None, out=None, ws=None) == 0
+
+
+def test_dequant_debug_rejects_bad_arguments():
+    lib = _lib.load()
+    s = _shape()
+    assert lib.moe_dequant_debug(ctypes.byref(s), FAKE, 3, 0, FAKE, None) == _lib.MOE_ERR_INVALID_ARG
+    assert lib.moe_dequant_debug(ctypes.byref(s), FAKE, 0, 2, FAKE, None) == _lib.MOE_ERR_INVALID_ARG
+    assert lib.moe_dequant_debug(ctypes.byref(s), FAKE + 8, 0, 0, FAKE, None) == _lib.MOE_ERR_INVALID_ARG

@@ -46,6 +46,13 @@ class MoeConfig:
     def R(self) -> int:
         return self.T * self.k
 
+    def shape_kwargs(self, T: int | None = None) -> dict:
+        """Keyword arguments describing one block call (T tokens) of this workload."""
+        return dict(T=self.T if T is None else T, H=self.H, F=self.F, E=self.E, k=self.k,
+                    act_dtype=self.act_dtype, n_shared=self.n_shared, alpha=self.alpha,
+                    limit=self.limit, up_offset=self.up_offset, route_scale=self.route_scale,
+                    rms_eps=self.rms_eps or 0.0)
+
 
 CONFIGS = (
     MoeConfig(1, "tiny", T=8, H=256, F=256, E=8, k=2, router_b_std=0.05,
