@@ -1,0 +1,450 @@
+#!/usr/bin/env python3
+"""Throughput of the routed MXFP4 MoE block on one MI355X (gfx950).
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode|prefill|stack|ds4|tiny]
+
+A step is one pass of the whole block over one batch of seeded synthetic
+input (weights and activations resident in HBM before timing):
+  decode  gpt-oss-20b-shaped layer, 1000 tokens as T=1 calls (default)
+  prefill gpt-oss-20b-shaped layer, T=128, Zipf(1.1)-skewed expert loads
+  stack   24 gpt-oss-20b-shaped layers (RMSNorm + MoE), T=512
+  ds4     DeepSeek-V4-Flash-shaped layer, T=2048, 256 experts top-6 + shared
+  tiny    T=8, H=F=256, 8 experts top-2
+Each step's calls are captured once in a HIP graph and replayed; W warm-up
+steps, then exactly K timed steps between two synchronisations. The last
+timed step is launched eagerly with the library's moe_profile_next_launch
+hook armed on every call, so HIP events stamped by the dominant kernel's own
+dispatches give its live average duration for the roofline object. Expert
+weights are held in several device copies, cycled between calls, so that the
+256 MB Infinity Cache cannot serve them from one call to the next.
+
+Prints one JSON line (rank 0, N=1 only).
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MoE block tokens/s (decode T=1, prefill T=128/512) + % HBM/MFMA peak"
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
+
+WORKLOADS = {
+    "decode": dict(config=2, name="gptoss20b_decode_T1_1000tok", kernel="decode_gate_up", copies=8,
+                   steps=100),
+    "prefill": dict(config=3, name="gptoss20b_prefill_T128_zipf", kernel="gate_up_gemm", copies=4,
+                    steps=200),
+    "stack": dict(config=4, name="gptoss20b_stack24_T512", kernel="gate_up_gemm", copies=1,
+                  steps=20),
+    "ds4": dict(config=5, name="ds4flash_T2048_E256_top6_shared", kernel="gate_up_gemm", copies=2,
+                steps=50),
+    "tiny": dict(config=1, name="tiny_T8_H256_E8_top2", kernel="decode_gate_up", copies=1,
+                 steps=200),
+}
+KERNEL_SOURCES = {"decode_gate_up": "decode.hip", "decode_down": "decode.hip",
+                  "gate_up_gemm": "prefill.hip", "down_gemm": "prefill.hip"}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class HipEvents:
+    """Raw hipEvent_t handles from the HIP runtime the process already loaded."""
+
+    def __init__(self):
+        self.lib = ctypes.CDLL("libamdhip64.so.7")
+        self.lib.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.made = []
+
+    def create(self) -> int:
+        e = ctypes.c_void_p()
+        rc = self.lib.hipEventCreateWithFlags(ctypes.byref(e), 0)
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags failed ({rc})")
+        self.made.append(e.value)
+        return e.value
+
+    def record(self, ev: int, stream: int):
+        rc = self.lib.hipEventRecord(ctypes.c_void_p(ev), ctypes.c_void_p(stream))
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed ({rc})")
+
+    def elapsed_ms(self, a: int, b: int) -> float:
+        f = ctypes.c_float()
+        rc = self.lib.hipEventElapsedTime(ctypes.byref(f), ctypes.c_void_p(a), ctypes.c_void_p(b))
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return f.value
+
+    def destroy_all(self):
+        for e in self.made:
+            self.lib.hipEventDestroy(ctypes.c_void_p(e))
+        self.made = []
+
+
+def source_sha(kernel: str) -> str:
+    h = hashlib.sha256()
+    for f in ("common.hpp", "kernels.hpp", KERNEL_SOURCES[kernel]):
+        with open(os.path.join(ROOT, "mxfp4_expert_ffn_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile(kernel: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 --pmc summary, if it
+    was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}__{workload}__pmc.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as f:
+        for ln in f:
+            if ":" in ln and not ln.startswith("#"):
+                k, v = ln.split(":", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("source_sha") != source_sha(kernel):
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+# ---------------------------------------------------------------- workloads
+class Setup:
+    """Device-resident inputs and the per-step call lists of one workload."""
+
+    def __init__(self, wl: str, copies: int | None):
+        import numpy as np
+        import torch
+
+        import mxfp4_expert_ffn_amd as mx
+        from mxfp4_expert_ffn_amd.device import upload_layer, workspace
+        from workloads import config_by_id, make_layer
+        from workloads.gen import make_activations
+
+        spec = WORKLOADS[wl]
+        self.wl, self.spec = wl, spec
+        self.cfg = cfg = config_by_id(spec["config"])
+        self.copies = spec["copies"] if copies is None else copies
+        self.mx = mx
+        t0 = time.time()
+        x, xb = make_activations(cfg)
+        self.x_host = x
+        n_layers = cfg.layers
+        self.host_layers = []
+        self.layers = []
+        self.shape = mx.make_shape(**cfg.shape_kwargs())
+        for l in range(n_layers):
+            layer = make_layer(cfg, l)
+            self.layers.append(upload_layer(self.shape, layer, copies=self.copies))
+            if l == 0:
+                self.host_layers.append(layer)
+            del layer
+        log(f"[bench] {wl}: generated and uploaded {n_layers} layer(s) x {self.copies} "
+            f"cop{'y' if self.copies == 1 else 'ies'} in {time.time() - t0:.1f}s")
+        if cfg.act_dtype == "bf16":
+            self.xd = torch.from_numpy(xb.view(np.int16).copy()).cuda()
+        else:
+            self.xd = torch.from_numpy(x).cuda()
+        self.ws = workspace(self.shape)
+        self.tokens_per_step = cfg.T * cfg.calls
+        if cfg.path == "decode" and cfg.T == 1:
+            # one step = cfg.calls independent T=1 calls
+            self.step_shape = mx.make_shape(**cfg.shape_kwargs(1))
+            self.ws = workspace(self.step_shape)
+            self.out = torch.empty((cfg.calls, cfg.H), dtype=torch.float32, device="cuda")
+            self.xrows = [self.xd[i:i + 1] for i in range(cfg.calls)]
+            self.orows = [self.out[i:i + 1] for i in range(cfg.calls)]
+        else:
+            self.step_shape = self.shape
+            self.out = torch.empty((cfg.T, cfg.H), dtype=torch.float32, device="cuda")
+            self.out2 = torch.empty_like(self.out)
+
+    def step_calls(self, step: int):
+        """Closures making up one step (weights copy chosen per call/step)."""
+        mx, cfg = self.mx, self.cfg
+        calls = []
+        if cfg.path == "decode" and cfg.T == 1:
+            dl = self.layers[0]
+            for i in range(cfg.calls):
+                ex = dl.experts_copy(i)
+                calls.append(lambda i=i, ex=ex: mx.moe_forward_decode(
+                    self.step_shape, self.xrows[i], dl.router_w, dl.router_b, ex, self.orows[i],
+                    self.ws))
+        elif cfg.path == "decode":
+            dl = self.layers[0]
+            calls.append(lambda: mx.moe_forward_decode(
+                self.shape, self.xd, dl.router_w, dl.router_b, dl.experts_copy(step), self.out,
+                self.ws, norm_w=dl.norm_w, shared=dl.shared_copy(step)))
+        else:
+            src = self.xd
+            bufs = (self.out, self.out2)
+            for l, dl in enumerate(self.layers):
+                dst = bufs[l % 2]
+                calls.append(lambda dl=dl, src=src, dst=dst: mx.moe_forward_prefill(
+                    self.shape, src, dl.router_w, dl.router_b, dl.experts_copy(step), dst,
+                    self.ws, norm_w=dl.norm_w, shared=dl.shared_copy(step)))
+                src = dst
+        return calls
+
+    # algorithmic work of the dominant kernel per launch and of the block per step
+    def algorithmic(self, counts_per_call):
+        cfg = self.cfg
+        H, F, k, E = cfg.H, cfg.F, cfg.k, cfg.E
+        mat = F * H * 17 // 32            # codes + scales of one [F,H] matrix
+        xb = 2 if cfg.act_dtype == "bf16" else 4
+        if self.spec["kernel"] == "decode_gate_up":
+            T = 1 if cfg.T == 1 else cfg.T
+            routes = T * k + T * cfg.n_shared
+            byts = routes * 2 * (mat + 4 * F) + T * H * xb + routes * F * 4 + T * E * 8
+            return dict(bytes=byts, flops=routes * 4 * H * F, units=routes,
+                        unit="route (token, selected expert)")
+        # gate/up GEMM: weights of every active expert once, x once, act out
+        T = cfg.T
+        active = [sum(1 for c in counts if c > 0) + cfg.n_shared for counts in counts_per_call]
+        rows = T * k + T * cfg.n_shared
+        per = [a * 2 * (mat + 4 * F) + T * H * xb + rows * F * 4 for a in active]
+        return dict(bytes=sum(per) / len(per), flops=4.0 * rows * H * F, units=rows,
+                    unit="routed row (token, expert) of the grouped GEMM",
+                    active_experts=sum(active) / len(active))
+
+    def block_bytes_per_step(self, counts_per_call):
+        cfg = self.cfg
+        H, F, k = cfg.H, cfg.F, cfg.k
+        expert = 3 * F * H * 17 // 32 + 4 * (2 * F + H)
+        if cfg.path == "decode" and cfg.T == 1:
+            return cfg.calls * k * expert
+        tot = 0
+        for counts in counts_per_call:
+            tot += (sum(1 for c in counts if c > 0) + cfg.n_shared) * expert
+        return tot
+
+
+def route_counts(setup):
+    """Per-call expert histograms of one step (for algorithmic byte counts)."""
+    import torch
+    mx, cfg = setup.mx, setup.cfg
+    res = []
+    if cfg.path == "decode":
+        return res
+    src = setup.xd
+    bufs = (setup.out, setup.out2)
+    for l, dl in enumerate(setup.layers):
+        counts = torch.empty(cfg.E, dtype=torch.int32, device="cuda")
+        dst = bufs[l % 2]
+        mx.moe_forward_prefill(setup.shape, src, dl.router_w, dl.router_b, dl.experts_copy(0), dst,
+                               setup.ws, norm_w=dl.norm_w, shared=dl.shared_copy(0),
+                               route_out={"counts": counts})
+        torch.cuda.synchronize()
+        res.append(counts.cpu().tolist())
+        src = dst
+    return res
+
+
+def capture(calls):
+    """Capture one step's calls into a HIP graph."""
+    import torch
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for c in calls:
+            c()
+    return g
+
+
+def cpu_baseline(setup, budget_s: float):
+    """The oracle, as it stands, on a bounded sample of the same workload."""
+    import numpy as np
+    from oracle import moe as omoe
+    cfg = setup.cfg
+    layer = setup.host_layers[0]
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()
+                     if p.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        cores = 1
+    x = setup.x_host
+    if cfg.path == "decode" and cfg.T == 1:
+        n = 16
+        t0 = time.time()
+        omoe.block_for_config(cfg, layer, x[:n])
+        dt = time.time() - t0
+        return dict(value=n / dt, unit="tokens/s", cores=cores, kind="oracle",
+                    sample=f"first {n} of the {cfg.calls} decode tokens of layer 0, batched in "
+                           f"one fp64 oracle call ({dt:.1f} s)")
+    # prefill-type: all T tokens of the first layer if the budget allows, else a token subset
+    n = cfg.T
+    est_experts = min(cfg.E, cfg.T * cfg.k) + cfg.n_shared
+    if est_experts * 0.35 > budget_s:
+        n = max(1, int(cfg.T * budget_s / (est_experts * 0.35)))
+    toks = np.arange(n)
+    t0 = time.time()
+    omoe.block_for_config(cfg, layer, x[:cfg.T], tokens=toks)
+    dt = time.time() - t0
+    return dict(value=n / dt, unit="tokens/s", cores=cores, kind="oracle",
+                sample=f"{n} of {cfg.T} tokens of layer 0 (routing for all {cfg.T}) in one "
+                       f"fp64 oracle call ({dt:.1f} s)")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None, help="timed steps (default per workload)")
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", choices=sorted(WORKLOADS), default="decode")
+    ap.add_argument("--copies", type=int, default=None, help="device copies of the expert weights")
+    ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of HIP graphs")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds for the oracle sample")
+    ap.add_argument("--calibrate-copy-gib", type=float, default=0.0,
+                    help="also run one device copy of this many GiB (PMC byte calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+    if args.steps is None:
+        args.steps = WORKLOADS[args.workload]["steps"]
+    if args.steps < 1:
+        sys.exit("--steps must be >= 1")
+
+    import torch
+    import mxfp4_expert_ffn_amd as mx
+    if not torch.cuda.is_available():
+        sys.exit("no GPU visible")
+    mx._lib.load()
+    torch.cuda.set_device(0)
+
+    setup = Setup(args.workload, args.copies)
+    spec, cfg = setup.spec, setup.cfg
+    ev = HipEvents()
+    stream = torch.cuda.current_stream().cuda_stream
+
+    counts = route_counts(setup)
+    ncopies_graph = 1 if (cfg.path == "decode" and cfg.T == 1) else setup.copies
+    plain = [setup.step_calls(c) for c in range(ncopies_graph)]
+    for calls in plain:          # eager run once (validates arguments, warms code objects)
+        for c in calls:
+            c()
+    torch.cuda.synchronize()
+
+    kernel = spec["kernel"]
+    last = args.steps - 1
+    last_calls = setup.step_calls(last % ncopies_graph)
+    pairs = [(ev.create(), ev.create()) for _ in last_calls]
+    graphs = None if args.no_graph else [capture(calls) for calls in plain]
+    torch.cuda.synchronize()
+
+    def run_step(s, instrument=False):
+        if instrument:     # eager, timing hook armed on every call of the step
+            for i, c in enumerate(last_calls):
+                mx.moe_profile_next_launch(kernel, pairs[i][0], pairs[i][1])
+                c()
+        elif graphs is None:
+            for c in plain[s % ncopies_graph]:
+                c()
+        else:
+            graphs[s % ncopies_graph].replay()
+
+    for s in range(args.warmup):
+        run_step(s)
+    torch.cuda.synchronize()
+    t_start, t_stop = ev.create(), ev.create()
+    torch.cuda.synchronize()
+    ev.record(t_start, stream)
+    for s in range(args.steps):
+        run_step(s, instrument=(s == last))
+    ev.record(t_stop, stream)
+    torch.cuda.synchronize()
+    total_ms = ev.elapsed_ms(t_start, t_stop)
+    kern_ms = [ev.elapsed_ms(a, b) for a, b in pairs]
+    kern_avg_ms = sum(kern_ms) / len(kern_ms)
+
+    ms_per_step = total_ms / args.steps
+    value = setup.tokens_per_step * args.steps / (total_ms / 1e3)
+    alg = setup.algorithmic(counts)
+    kern_s = kern_avg_ms / 1e3
+    if kernel.startswith("decode"):
+        achieved, peak, unit, bound = alg["bytes"] / kern_s / 1e9, HBM_PEAK_GBPS, "GB/s", "hbm"
+        traffic = traffic_from_profile(kernel, args.workload)
+    else:
+        t_hbm = alg["bytes"] / (HBM_PEAK_GBPS * 1e9)
+        t_mfma = alg["flops"] / (BF16_PEAK_TFLOPS * 1e12)
+        if t_hbm >= t_mfma:
+            achieved, peak, unit, bound = alg["bytes"] / kern_s / 1e9, HBM_PEAK_GBPS, "GB/s", "hbm"
+        else:
+            achieved, peak, unit, bound = alg["flops"] / kern_s / 1e12, BF16_PEAK_TFLOPS, "TFLOP/s", "mfma"
+        traffic = traffic_from_profile(kernel, args.workload)
+    block_bytes = setup.block_bytes_per_step(counts)
+    block_gbps = block_bytes / (ms_per_step / 1e3) / 1e9
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32" if kernel.startswith("decode") else "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": spec["name"], "T": cfg.T, "H": cfg.H, "F": cfg.F, "E": cfg.E,
+            "k": cfg.k, "n_shared": cfg.n_shared, "layers": cfg.layers,
+            "tokens_per_step": setup.tokens_per_step, "weights": "mxfp4 (e2m1 + e8m0/32) + fp32 bias",
+            "activations": cfg.act_dtype, "weight_copies": setup.copies,
+            "launch": "eager" if graphs is None else "hip_graph",
+        },
+        "roofline": {
+            "kernel": kernel, "bound": bound, "achieved": round(achieved, 2), "peak": peak,
+            "unit": unit, "frac": round(achieved / peak, 4),
+            "traffic": traffic,
+            "avg_launch_us": round(kern_avg_ms * 1e3, 3),
+            "algorithmic_bytes_per_launch": int(alg["bytes"]),
+            "algorithmic_flops_per_launch": int(alg["flops"]),
+            "units_per_launch": alg["units"], "unit_of_work": alg["unit"],
+        },
+        "block": {
+            "expert_bytes_per_step": int(block_bytes),
+            "achieved_GBps": round(block_gbps, 1),
+            "frac_of_hbm_peak": round(block_gbps / HBM_PEAK_GBPS, 4),
+        },
+    }
+    if args.calibrate_copy_gib > 0:
+        n = int(args.calibrate_copy_gib * (1 << 30)) // 4
+        a = torch.empty(n, dtype=torch.float32, device="cuda").fill_(1.0)
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        b.copy_(a)
+        torch.cuda.synchronize()
+        result["calibration_copy_bytes"] = 2 * 4 * n
+        del a, b
+    ev.destroy_all()
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle baseline")
+        result["cpu_baseline"] = cpu_baseline(setup, args.cpu_budget)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

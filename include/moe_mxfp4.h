@@ -25,9 +25,9 @@
  *   and moe_last_error() describes the problem.
  * - Row-major layouts; [A,B] means A rows of B contiguous elements.
  * - Shape limits: 1 <= E <= 256, 1 <= k <= min(E, 8), H and F multiples of
- *   32 and at most 16384, 0 <= T, n_shared in {0, 1}. T = 0 is a no-op.
- *   Decode additionally needs T <= 64 and H, F <= 8192. With T = 0 a call
- *   only validates the shape and returns MOE_OK.
+ *   32 and at most 16384, 0 <= T, n_shared in {0, 1}. Decode additionally
+ *   needs T <= 64 and H, F <= 8192. With T = 0 a call only validates the
+ *   shape and returns MOE_OK.
  */
 #ifndef MOE_MXFP4_H
 #define MOE_MXFP4_H
@@ -190,6 +190,28 @@ int moe_forward_prefill(const moe_shape *shape, const void *hidden, const float 
  *   out    float32 [rows, cols], device */
 int moe_dequant_debug(const moe_shape *shape, const uint8_t *blob, int32_t which, int32_t path,
                       float *out, hipStream_t stream);
+
+/* Kernels of the block, as named by moe_profile_next_launch. */
+typedef enum moe_kernel_id {
+    MOE_KERNEL_RMSNORM = 0,
+    MOE_KERNEL_ROUTER = 1,          /* router logits, either form */
+    MOE_KERNEL_TOPK = 2,
+    MOE_KERNEL_PERMUTE = 3,
+    MOE_KERNEL_DECODE_GATE_UP = 4,
+    MOE_KERNEL_DECODE_DOWN = 5,
+    MOE_KERNEL_GATE_UP_GEMM = 6,
+    MOE_KERNEL_DOWN_GEMM = 7
+} moe_kernel_id;
+
+/* Measurement hook (for benchmarks and profilers, not needed to compute):
+ * on the calling thread, the next launch of `kernel` made by any call of
+ * this library carries `start` and `stop`, which the runtime stamps with
+ * that kernel dispatch's own start and end (hipExtLaunchKernel events), so
+ * hipEventElapsedTime(start, stop) is the kernel's duration. The events are
+ * caller-owned and must allow timing; not for use under stream capture.
+ * One-shot: the hook disarms after that launch; kernel < 0 disarms it.
+ * Host only; MOE_OK or MOE_ERR_INVALID_ARG. */
+int moe_profile_next_launch(int32_t kernel, hipEvent_t start, hipEvent_t stop);
 
 /* Message of the last failing call on this thread ("" if none). */
 const char *moe_last_error(void);

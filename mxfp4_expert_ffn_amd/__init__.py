@@ -19,7 +19,7 @@ from ._lib import MOE_BF16, MOE_F32, MoeBlobLayout, MoeExpertPlanes, MoeRouteOut
 __all__ = [
     "MoeError", "MoeShape", "make_shape", "moe_blob_layout_get", "moe_pack_experts",
     "moe_workspace_bytes", "moe_route", "moe_forward_decode", "moe_forward_prefill",
-    "moe_dequant_debug", "moe_last_error", "ROUTE_FIELDS",
+    "moe_dequant_debug", "moe_last_error", "moe_profile_next_launch", "ROUTE_FIELDS",
 ]
 
 ROUTE_FIELDS = ("topk_idx", "topk_w", "counts", "offsets", "perm", "inv")
@@ -154,3 +154,11 @@ def moe_dequant_debug(shape, blob, which: int, path: int, out, stream=None):
     _check(_lib.load().moe_dequant_debug(ctypes.byref(shape), _ptr(blob, "blob", torch.uint8),
                                          int(which), int(path), _ptr(out, "out", torch.float32),
                                          _stream(stream)))
+
+
+def moe_profile_next_launch(kernel, start_event: int, stop_event: int):
+    """Arm the one-shot timing hook: raw hipEvent_t handles (ints) recorded
+    around the next launch of `kernel` (a name of `_lib.KERNELS` or an id)."""
+    kid = _lib.KERNELS[kernel] if isinstance(kernel, str) else int(kernel)
+    _check(_lib.load().moe_profile_next_launch(kid, ctypes.c_void_p(start_event),
+                                               ctypes.c_void_p(stop_event)))

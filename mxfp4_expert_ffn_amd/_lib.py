@@ -14,6 +14,10 @@ MOE_ERR_HIP = -4
 MOE_F32 = 0
 MOE_BF16 = 1
 
+# moe_kernel_id
+KERNELS = {"rmsnorm": 0, "router": 1, "topk": 2, "permute": 3, "decode_gate_up": 4,
+           "decode_down": 5, "gate_up_gemm": 6, "down_gemm": 7}
+
 
 class MoeShape(ctypes.Structure):
     _fields_ = [
@@ -56,6 +60,7 @@ SIGNATURES = {
                                            ctypes.POINTER(MoeRouteOut), _P, ctypes.c_size_t, _P]),
     "moe_dequant_debug": (ctypes.c_int, [ctypes.POINTER(MoeShape), _P, ctypes.c_int32,
                                          ctypes.c_int32, _P, _P]),
+    "moe_profile_next_launch": (ctypes.c_int, [ctypes.c_int32, _P, _P]),
     "moe_last_error": (ctypes.c_char_p, []),
 }
 

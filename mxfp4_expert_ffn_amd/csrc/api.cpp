@@ -15,6 +15,18 @@ namespace {
 
 thread_local std::string g_last_error;
 
+#define MOE_TRY(expr)                  \
+    do {                               \
+        const int rc_ = (expr);        \
+        if (rc_ != MOE_OK) return rc_; \
+    } while (0)
+
+#define MOE_TRY_HIP(expr, what)                                                           \
+    do {                                                                                  \
+        const hipError_t e_ = (expr);                                                     \
+        if (e_ != hipSuccess) return fail(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(e_)); \
+    } while (0)
+
 int fail(int code, const char *fmt, ...) {
     char buf[512];
     va_list ap;
@@ -148,11 +160,28 @@ int hip_check(hipError_t e, const char *what) {
     return MOE_OK;
 }
 
-#define MOE_TRY(expr)               \
-    do {                            \
-        const int rc_ = (expr);     \
-        if (rc_ != MOE_OK) return rc_; \
-    } while (0)
+// One-shot timing hook armed by moe_profile_next_launch.
+struct ProfileHook {
+    int kernel = -1;
+    hipEvent_t start = nullptr, stop = nullptr;
+};
+thread_local ProfileHook g_hook;
+
+// Launch through `fn` (one kernel, returning hipError_t). When the hook is
+// armed for kernel `id`, its events ride on that dispatch (hipExtLaunchKernel
+// stamps the kernel's own start and end into them).
+template <typename Fn>
+int launch(int id, const char *what, hipStream_t st, Fn &&fn) {
+    (void)st;
+    const bool armed = g_hook.kernel == id;
+    if (armed) moe::launch_events() = moe::LaunchEvents{g_hook.start, g_hook.stop};
+    const int rc = hip_check(fn(), what);
+    if (armed) {
+        moe::launch_events() = moe::LaunchEvents{};
+        g_hook.kernel = -1;
+    }
+    return rc;
+}
 
 // Shared argument checks of the two forward entry points.
 int check_forward(const moe_shape *s, const void *hidden, const float *norm_w,
@@ -184,18 +213,20 @@ int route_front(const moe_shape *s, const void *x, const float *norm_w, const fl
     *expert_in = x;
     *expert_in_bf16 = bf16;
     if (norm_w) {
-        MOE_TRY(hip_check(moe::launch_rmsnorm(x, bf16, norm_w, s->T, s->H, s->rms_eps, w.xn64,
-                                              w.xn32, st), "rmsnorm"));
+        MOE_TRY(launch(MOE_KERNEL_RMSNORM, "rmsnorm", st, [&] {
+            return moe::launch_rmsnorm(x, bf16, norm_w, s->T, s->H, s->rms_eps, w.xn64, w.xn32, st);
+        }));
         rin = w.xn64;
         kind = 2;
         *expert_in = w.xn32;
         *expert_in_bf16 = 0;
     }
-    if (small)
-        return hip_check(moe::launch_router_gemv(rin, kind, router_w, router_b, s->T, s->H, s->E,
-                                                 w.logits, st), "router_gemv");
-    return hip_check(moe::launch_router_logits(rin, kind, router_w, router_b, s->T, s->H, s->E,
-                                               w.logits, st), "router_logits");
+    return launch(MOE_KERNEL_ROUTER, "router", st, [&] {
+        return small ? moe::launch_router_gemv(rin, kind, router_w, router_b, s->T, s->H, s->E,
+                                               w.logits, st)
+                     : moe::launch_router_logits(rin, kind, router_w, router_b, s->T, s->H, s->E,
+                                                 w.logits, st);
+    });
 }
 
 int max_mtiles(const moe_shape *s) {
@@ -207,6 +238,13 @@ int max_mtiles(const moe_shape *s) {
 }
 
 }  // namespace
+
+namespace moe {
+LaunchEvents &launch_events() {
+    thread_local LaunchEvents ev;
+    return ev;
+}
+}  // namespace moe
 
 extern "C" {
 
@@ -264,13 +302,11 @@ int moe_route(const moe_shape *s, const void *x, const float *norm_w, const floa
     const void *ein;
     int ein_bf16;
     MOE_TRY(route_front(s, x, norm_w, router_w, router_b, w, s->T <= 16, &ein, &ein_bf16, st));
-    MOE_TRY(hip_check(moe::launch_topk(w.logits, s->T, s->E, s->k, s->route_scale, w.idx, w.wts,
-                                       out->topk_idx, out->topk_w, nullptr, 0, s->H, nullptr, st),
-                      "topk"));
-    MOE_TRY(hip_check(moe::launch_permute(w.idx, s->T, s->E, s->k, 0, w.counts, w.offsets, w.perm,
+    MOE_TRY(launch(MOE_KERNEL_TOPK, "topk", st, [&] { return moe::launch_topk(w.logits, s->T, s->E, s->k, s->route_scale, w.idx, w.wts,
+                                       out->topk_idx, out->topk_w, nullptr, 0, s->H, nullptr, st); }));
+    MOE_TRY(launch(MOE_KERNEL_PERMUTE, "permute", st, [&] { return moe::launch_permute(w.idx, s->T, s->E, s->k, 0, w.counts, w.offsets, w.perm,
                                           w.inv, w.rank, w.mprefix, out->counts, out->offsets,
-                                          out->perm, out->inv, st),
-                      "permute"));
+                                          out->perm, out->inv, st); }));
     return ok();
 }
 
@@ -290,20 +326,17 @@ int moe_forward_decode(const moe_shape *s, const void *hidden, const float *norm
     const moe::ExpertPtrs ex = expert_ptrs(s, experts);
     const moe::ExpertPtrs sh = expert_ptrs(s, shared);
     const moe::SwigluConsts c{s->swiglu_alpha, s->swiglu_limit, s->swiglu_up_offset};
-    MOE_TRY(hip_check(moe::launch_decode_gate_up(ein, ein_bf16, w.logits, s->T, s->H, s->F, s->E,
+    MOE_TRY(launch(MOE_KERNEL_DECODE_GATE_UP, "decode_gate_up", st, [&] { return moe::launch_decode_gate_up(ein, ein_bf16, w.logits, s->T, s->H, s->F, s->E,
                                                  s->k, s->n_shared, s->route_scale, ex, sh, c,
                                                  w.idx, w.wts, ro ? ro->topk_idx : nullptr,
-                                                 ro ? ro->topk_w : nullptr, w.act, st),
-                      "decode_gate_up"));
-    MOE_TRY(hip_check(moe::launch_decode_down(hidden, s->act_dtype == MOE_BF16, s->T, s->H, s->F,
+                                                 ro ? ro->topk_w : nullptr, w.act, st); }));
+    MOE_TRY(launch(MOE_KERNEL_DECODE_DOWN, "decode_down", st, [&] { return moe::launch_decode_down(hidden, s->act_dtype == MOE_BF16, s->T, s->H, s->F,
                                               s->k, s->n_shared, ex, sh, w.idx, w.wts, w.act, out,
-                                              st),
-                      "decode_down"));
+                                              st); }));
     if (ro && (ro->counts || ro->offsets || ro->perm || ro->inv))
-        MOE_TRY(hip_check(moe::launch_permute(w.idx, s->T, s->E, s->k, 0, w.counts, w.offsets,
+        MOE_TRY(launch(MOE_KERNEL_PERMUTE, "permute", st, [&] { return moe::launch_permute(w.idx, s->T, s->E, s->k, 0, w.counts, w.offsets,
                                               w.perm, w.inv, w.rank, w.mprefix, ro->counts,
-                                              ro->offsets, ro->perm, ro->inv, st),
-                          "permute"));
+                                              ro->offsets, ro->perm, ro->inv, st); }));
     return ok();
 }
 
@@ -317,27 +350,23 @@ int moe_forward_prefill(const moe_shape *s, const void *hidden, const float *nor
     const void *ein;
     int ein_bf16;
     MOE_TRY(route_front(s, hidden, norm_w, router_w, router_b, w, s->T <= 16, &ein, &ein_bf16, st));
-    MOE_TRY(hip_check(moe::launch_topk(w.logits, s->T, s->E, s->k, s->route_scale, w.idx, w.wts,
+    MOE_TRY(launch(MOE_KERNEL_TOPK, "topk", st, [&] { return moe::launch_topk(w.logits, s->T, s->E, s->k, s->route_scale, w.idx, w.wts,
                                        ro ? ro->topk_idx : nullptr, ro ? ro->topk_w : nullptr,
-                                       hidden, s->act_dtype == MOE_BF16, s->H, out, st),
-                      "topk"));
-    MOE_TRY(hip_check(moe::launch_permute(w.idx, s->T, s->E, s->k, s->n_shared, w.counts,
+                                       hidden, s->act_dtype == MOE_BF16, s->H, out, st); }));
+    MOE_TRY(launch(MOE_KERNEL_PERMUTE, "permute", st, [&] { return moe::launch_permute(w.idx, s->T, s->E, s->k, s->n_shared, w.counts,
                                           w.offsets, w.perm, w.inv, w.rank, w.mprefix,
                                           ro ? ro->counts : nullptr, ro ? ro->offsets : nullptr,
-                                          ro ? ro->perm : nullptr, ro ? ro->inv : nullptr, st),
-                      "permute"));
+                                          ro ? ro->perm : nullptr, ro ? ro->inv : nullptr, st); }));
     const moe::ExpertPtrs ex = expert_ptrs(s, experts);
     const moe::ExpertPtrs sh = expert_ptrs(s, shared);
     const moe::SwigluConsts c{s->swiglu_alpha, s->swiglu_limit, s->swiglu_up_offset};
     const int mt = max_mtiles(s);
-    MOE_TRY(hip_check(moe::launch_gate_up_gemm(ein, ein_bf16, s->T, s->H, s->F, s->E, s->k,
+    MOE_TRY(launch(MOE_KERNEL_GATE_UP_GEMM, "gate_up_gemm", st, [&] { return moe::launch_gate_up_gemm(ein, ein_bf16, s->T, s->H, s->F, s->E, s->k,
                                                s->n_shared, ex, sh, c, w.offsets, w.perm,
-                                               w.mprefix, mt, w.act, st),
-                      "gate_up_gemm"));
-    MOE_TRY(hip_check(moe::launch_down_gemm(s->T, s->H, s->F, s->E, s->k, s->n_shared, ex, sh,
+                                               w.mprefix, mt, w.act, st); }));
+    MOE_TRY(launch(MOE_KERNEL_DOWN_GEMM, "down_gemm", st, [&] { return moe::launch_down_gemm(s->T, s->H, s->F, s->E, s->k, s->n_shared, ex, sh,
                                             w.offsets, w.perm, w.wts, w.mprefix, mt, w.act, out,
-                                            st),
-                      "down_gemm"));
+                                            st); }));
     return ok();
 }
 
@@ -354,6 +383,19 @@ int moe_dequant_debug(const moe_shape *s, const uint8_t *blob, int32_t which, in
     const uint8_t *q = blob + (which == 0 ? L.gate_q : which == 1 ? L.up_q : L.down_q);
     const uint8_t *sc = blob + (which == 0 ? L.gate_s : which == 1 ? L.up_s : L.down_s);
     MOE_TRY(hip_check(moe::launch_dequant(q, sc, rows, K, path, out, st), "dequant"));
+    return ok();
+}
+
+int moe_profile_next_launch(int32_t kernel, hipEvent_t start, hipEvent_t stop) {
+    if (kernel < 0) {
+        g_hook = ProfileHook{};
+        return ok();
+    }
+    if (kernel > MOE_KERNEL_DOWN_GEMM || !start || !stop)
+        return fail(MOE_ERR_INVALID_ARG, "unknown kernel id %d or NULL event", kernel);
+    g_hook.kernel = kernel;
+    g_hook.start = start;
+    g_hook.stop = stop;
     return ok();
 }
 

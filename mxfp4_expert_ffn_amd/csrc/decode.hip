@@ -223,11 +223,11 @@ hipError_t gate_up_nb(const void *x, int x_bf16, const double *logits, int T, in
                       int32_t *out_idx, float *out_w, float *act, hipStream_t s) {
     dim3 grid(T * k + T * n_shared, (F + kDecodeRowsGU - 1) / kDecodeRowsGU);
     if (x_bf16)
-        decode_gate_up_kernel<NB, true><<<grid, 256, 0, s>>>(x, logits, T, H, F, E, k, route_scale,
-                                                             ex, sh, c, idx, wts, out_idx, out_w, act);
+        launch_kernel(decode_gate_up_kernel<NB, true>, grid, 256, s, x, logits, T, H, F, E, k,
+                      route_scale, ex, sh, c, idx, wts, out_idx, out_w, act);
     else
-        decode_gate_up_kernel<NB, false><<<grid, 256, 0, s>>>(x, logits, T, H, F, E, k, route_scale,
-                                                              ex, sh, c, idx, wts, out_idx, out_w, act);
+        launch_kernel(decode_gate_up_kernel<NB, false>, grid, 256, s, x, logits, T, H, F, E, k,
+                      route_scale, ex, sh, c, idx, wts, out_idx, out_w, act);
     return hipGetLastError();
 }
 
@@ -237,11 +237,11 @@ hipError_t down_nb(const void *resid, int resid_bf16, int T, int H, int F, int k
                    const float *act, float *out, hipStream_t s) {
     dim3 grid(T, (H + kDecodeRowsDn - 1) / kDecodeRowsDn);
     if (resid_bf16)
-        decode_down_kernel<NB, true><<<grid, 256, 0, s>>>(resid, T, H, F, k, n_shared, ex, sh, idx,
-                                                          wts, act, out);
+        launch_kernel(decode_down_kernel<NB, true>, grid, 256, s, resid, T, H, F, k, n_shared, ex,
+                      sh, idx, wts, act, out);
     else
-        decode_down_kernel<NB, false><<<grid, 256, 0, s>>>(resid, T, H, F, k, n_shared, ex, sh, idx,
-                                                           wts, act, out);
+        launch_kernel(decode_down_kernel<NB, false>, grid, 256, s, resid, T, H, F, k, n_shared, ex,
+                      sh, idx, wts, act, out);
     return hipGetLastError();
 }
 

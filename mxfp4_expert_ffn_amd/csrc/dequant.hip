@@ -40,7 +40,7 @@ hipError_t launch_dequant(const uint8_t *codes, const uint8_t *scales, int rows,
     const long long blocks = static_cast<long long>(rows) * (K / 32);
     const int grid = static_cast<int>((blocks + 255) / 256);
     if (grid == 0) return hipSuccess;
-    dequant_kernel<<<grid, 256, 0, s>>>(codes, scales, rows, K, path, out);
+    launch_kernel(dequant_kernel, grid, 256, s, codes, scales, rows, K, path, out);
     return hipGetLastError();
 }
 

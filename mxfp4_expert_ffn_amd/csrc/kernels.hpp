@@ -1,6 +1,7 @@
 // Host-side launchers of the MoE kernels (internal to the library).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -17,6 +18,21 @@ constexpr int kGateUpBN = 128;   // features per gate/up workgroup (4 waves x 32
 constexpr int kDownBN = 256;     // hidden rows per down workgroup (4 waves x 2 x 32)
 constexpr int kDecodeRowsGU = 8; // expert rows per decode gate/up workgroup
 constexpr int kDecodeRowsDn = 8; // hidden rows per decode down workgroup
+
+// Events attached to the next kernel dispatch (the library's timing hook):
+// hipExtLaunchKernel stamps them with that kernel's own start and end. Null
+// events make it a plain launch. Thread-local, set by the C ABI layer.
+struct LaunchEvents {
+    hipEvent_t start = nullptr;
+    hipEvent_t stop = nullptr;
+};
+LaunchEvents &launch_events();
+
+template <typename Kernel, typename... Args>
+inline void launch_kernel(Kernel kernel, dim3 grid, dim3 block, hipStream_t s, Args... args) {
+    const LaunchEvents &ev = launch_events();
+    hipExtLaunchKernelGGL(kernel, grid, block, 0, s, ev.start, ev.stop, 0, args...);
+}
 
 struct ExpertPtrs {
     const uint8_t *base;     // first packed expert

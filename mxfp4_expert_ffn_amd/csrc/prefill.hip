@@ -329,11 +329,11 @@ hipError_t launch_gate_up_gemm(const void *x, int x_bf16, int T, int H, int F, i
     const int grid = static_cast<int>((tiles + kXcds - 1) / kXcds * kXcds);
     if (grid == 0) return hipSuccess;
     if (x_bf16)
-        gate_up_gemm_kernel<true><<<grid, 256, 0, s>>>(x, T, H, F, E, n_shared, k, ex, sh, c,
-                                                       offsets, perm, mprefix, act);
+        launch_kernel(gate_up_gemm_kernel<true>, grid, 256, s, x, T, H, F, E, n_shared, k, ex, sh,
+                      c, offsets, perm, mprefix, act);
     else
-        gate_up_gemm_kernel<false><<<grid, 256, 0, s>>>(x, T, H, F, E, n_shared, k, ex, sh, c,
-                                                        offsets, perm, mprefix, act);
+        launch_kernel(gate_up_gemm_kernel<false>, grid, 256, s, x, T, H, F, E, n_shared, k, ex, sh,
+                      c, offsets, perm, mprefix, act);
     return hipGetLastError();
 }
 
@@ -345,8 +345,8 @@ hipError_t launch_down_gemm(int T, int H, int F, int E, int k, int n_shared, con
     const long long tiles = static_cast<long long>(max_mtiles) * NT;
     const int grid = static_cast<int>((tiles + kXcds - 1) / kXcds * kXcds);
     if (grid == 0) return hipSuccess;
-    down_gemm_kernel<<<grid, 256, 0, s>>>(T, H, F, E, n_shared, k, ex, sh, offsets, perm, wts,
-                                          mprefix, act, out);
+    launch_kernel(down_gemm_kernel, grid, 256, s, T, H, F, E, n_shared, k, ex, sh, offsets, perm,
+                  wts, mprefix, act, out);
     return hipGetLastError();
 }
 

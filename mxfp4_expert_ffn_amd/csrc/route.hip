@@ -251,35 +251,41 @@ __global__ __launch_bounds__(1024) void permute_kernel(
 hipError_t launch_rmsnorm(const void *x, int x_bf16, const float *gamma, int T, int H, float eps,
                           double *xn64, float *xn32, hipStream_t s) {
     if (x_bf16)
-        rmsnorm_kernel<1><<<T, 256, 0, s>>>(x, gamma, H, eps, xn64, xn32);
+        launch_kernel(rmsnorm_kernel<1>, T, 256, s, x, gamma, H, eps, xn64, xn32);
     else
-        rmsnorm_kernel<0><<<T, 256, 0, s>>>(x, gamma, H, eps, xn64, xn32);
+        launch_kernel(rmsnorm_kernel<0>, T, 256, s, x, gamma, H, eps, xn64, xn32);
     return hipGetLastError();
 }
 
 hipError_t launch_router_logits(const void *x, int in_kind, const float *w, const float *b, int T,
                                 int H, int E, double *logits, hipStream_t s) {
-    dim3 grid((T + 31) / 32, (E + 63) / 64);
-    if (in_kind == 0) router_logits_kernel<0><<<grid, 256, 0, s>>>(x, w, b, T, H, E, logits);
-    else if (in_kind == 1) router_logits_kernel<1><<<grid, 256, 0, s>>>(x, w, b, T, H, E, logits);
-    else router_logits_kernel<2><<<grid, 256, 0, s>>>(x, w, b, T, H, E, logits);
+    const dim3 grid((T + 31) / 32, (E + 63) / 64);
+    if (in_kind == 0)
+        launch_kernel(router_logits_kernel<0>, grid, 256, s, x, w, b, T, H, E, logits);
+    else if (in_kind == 1)
+        launch_kernel(router_logits_kernel<1>, grid, 256, s, x, w, b, T, H, E, logits);
+    else
+        launch_kernel(router_logits_kernel<2>, grid, 256, s, x, w, b, T, H, E, logits);
     return hipGetLastError();
 }
 
 hipError_t launch_router_gemv(const void *x, int in_kind, const float *w, const float *b, int T,
                               int H, int E, double *logits, hipStream_t s) {
     const int grid = (E + 3) / 4;
-    if (in_kind == 0) router_gemv_kernel<0><<<grid, 256, 0, s>>>(x, w, b, T, H, E, logits);
-    else if (in_kind == 1) router_gemv_kernel<1><<<grid, 256, 0, s>>>(x, w, b, T, H, E, logits);
-    else router_gemv_kernel<2><<<grid, 256, 0, s>>>(x, w, b, T, H, E, logits);
+    if (in_kind == 0)
+        launch_kernel(router_gemv_kernel<0>, grid, 256, s, x, w, b, T, H, E, logits);
+    else if (in_kind == 1)
+        launch_kernel(router_gemv_kernel<1>, grid, 256, s, x, w, b, T, H, E, logits);
+    else
+        launch_kernel(router_gemv_kernel<2>, grid, 256, s, x, w, b, T, H, E, logits);
     return hipGetLastError();
 }
 
 hipError_t launch_topk(const double *logits, int T, int E, int k, float route_scale, int32_t *idx,
                        float *wts, int32_t *out_idx, float *out_w, const void *resid,
                        int resid_bf16, int H, float *out, hipStream_t s) {
-    topk_kernel<<<(T + 3) / 4, 256, 0, s>>>(logits, T, E, k, route_scale, idx, wts, out_idx, out_w,
-                                            resid, resid_bf16, H, out);
+    launch_kernel(topk_kernel, (T + 3) / 4, 256, s, logits, T, E, k, route_scale, idx, wts,
+                  out_idx, out_w, resid, resid_bf16, H, out);
     return hipGetLastError();
 }
 
@@ -287,8 +293,8 @@ hipError_t launch_permute(const int32_t *idx, int T, int E, int k, int n_shared,
                           int32_t *offsets, int32_t *perm, int32_t *inv, int32_t *rank,
                           int32_t *mprefix, int32_t *out_counts, int32_t *out_offsets,
                           int32_t *out_perm, int32_t *out_inv, hipStream_t s) {
-    permute_kernel<<<1, 1024, 0, s>>>(idx, T, E, k, n_shared, kGemmBM, counts, offsets, perm, inv,
-                                      rank, mprefix, out_counts, out_offsets, out_perm, out_inv);
+    launch_kernel(permute_kernel, 1, 1024, s, idx, T, E, k, n_shared, kGemmBM, counts, offsets,
+                  perm, inv, rank, mprefix, out_counts, out_offsets, out_perm, out_inv);
     return hipGetLastError();
 }
 
