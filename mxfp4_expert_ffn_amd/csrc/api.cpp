@@ -3,6 +3,7 @@
 // include/moe_mxfp4.h.
 #include "moe_mxfp4.h"
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -93,11 +94,15 @@ void layout_of(const moe_shape *s, moe_blob_layout *L) {
 struct Workspace {
     double *xn64;
     float *xn32;
-    double *logits;
+    double *partial;  // router split-K partial logits [splits][T][E]
+    int splits;
     int32_t *idx;
     float *wts;
     int32_t *counts, *offsets, *mprefix, *perm, *inv, *rank;
     float *act;
+    // decode on the block-scaled matrix cores (T <= 64 only): FP8 terms of
+    // the expert input and of the SwiGLU output
+    uint8_t *xq, *xs, *act_q;
     uint64_t bytes;
 };
 
@@ -113,7 +118,9 @@ Workspace carve(const moe_shape *s, uint8_t *base) {
     };
     w.xn64 = reinterpret_cast<double *>(take(T * H * 8));
     w.xn32 = reinterpret_cast<float *>(take(T * H * 4));
-    w.logits = reinterpret_cast<double *>(take(T * E * 8));
+    const moe::RouterPlan rp = moe::router_plan(s->T, s->H, s->E);
+    w.splits = rp.splits;
+    w.partial = reinterpret_cast<double *>(take(static_cast<uint64_t>(rp.splits) * T * E * 8));
     w.idx = reinterpret_cast<int32_t *>(take(R * 4));
     w.wts = reinterpret_cast<float *>(take(R * 4));
     w.counts = reinterpret_cast<int32_t *>(take((E + 1) * 4));
@@ -123,6 +130,14 @@ Workspace carve(const moe_shape *s, uint8_t *base) {
     w.inv = reinterpret_cast<int32_t *>(take(R * 4));
     w.rank = reinterpret_cast<int32_t *>(take(R * 4));
     w.act = reinterpret_cast<float *>(take((R + T * ns) * F * 4));
+    if (T <= 64) {
+        const uint64_t Hp = (H + 127) / 128 * 128, Fp = (F + 127) / 128 * 128;
+        w.xq = take(T * moe::kTerms * Hp);
+        w.xs = take(T * moe::kTerms * Hp / 32);
+        w.act_q = take((R + T * ns) * moe::kTerms * Fp);
+    } else {
+        w.xq = w.xs = w.act_q = nullptr;
+    }
     w.bytes = o;
     return w;
 }
@@ -203,10 +218,12 @@ int check_forward(const moe_shape *s, const void *hidden, const float *norm_w,
     return check_ws(s, ws, ws_bytes);
 }
 
-// RMSNorm (optional) and router logits; returns the expert-input pointer.
+// RMSNorm (optional) and the router's partial logits; returns the
+// expert-input pointer. With `terms`, the router launch also quantises the
+// expert input into FP8 terms (decode on the matrix cores).
 int route_front(const moe_shape *s, const void *x, const float *norm_w, const float *router_w,
-                const float *router_b, const Workspace &w, bool small, const void **expert_in,
-                int *expert_in_bf16, hipStream_t st) {
+                const Workspace &w, bool terms, const void **expert_in, int *expert_in_bf16,
+                hipStream_t st) {
     const int bf16 = s->act_dtype == MOE_BF16;
     const void *rin = x;
     int kind = bf16;
@@ -221,12 +238,25 @@ int route_front(const moe_shape *s, const void *x, const float *norm_w, const fl
         *expert_in = w.xn32;
         *expert_in_bf16 = 0;
     }
+    const moe::TermsOut tq{*expert_in, *expert_in_bf16, w.xq, w.xs};
     return launch(MOE_KERNEL_ROUTER, "router", st, [&] {
-        return small ? moe::launch_router_gemv(rin, kind, router_w, router_b, s->T, s->H, s->E,
-                                               w.logits, st)
-                     : moe::launch_router_logits(rin, kind, router_w, router_b, s->T, s->H, s->E,
-                                                 w.logits, st);
+        return moe::launch_router(rin, kind, router_w, s->T, s->H, s->E, w.partial,
+                                  terms ? &tq : nullptr, st);
     });
+}
+
+// FP8-term exponent for the SwiGLU output: with alpha > 0, |g sigmoid(alpha g)|
+// <= max(L, 0.2785/alpha) for g <= L, and |clamp(u) + o| <= L + |o|, so
+// |a| < 2^(e0 + 8) for e0 = floor(log2(bound)) - 7. False when unbounded.
+bool act_exponent(const moe_shape *s, int *e0) {
+    const double a = s->swiglu_alpha, L = s->swiglu_limit, o = s->swiglu_up_offset;
+    if (!(a > 0.0)) return false;
+    const double bound = std::max(L, 0.2785 / a) * (L + std::fabs(o)) * 1.01;
+    if (!std::isfinite(bound) || !(bound > 0.0)) return false;
+    const int e = static_cast<int>(std::floor(std::log2(bound))) - 7;
+    if (e - 4 * (moe::kTerms - 1) < -126 || e > 120) return false;
+    *e0 = e;
+    return true;
 }
 
 int max_mtiles(const moe_shape *s) {
@@ -301,9 +331,12 @@ int moe_route(const moe_shape *s, const void *x, const float *norm_w, const floa
     const Workspace w = carve(s, static_cast<uint8_t *>(ws));
     const void *ein;
     int ein_bf16;
-    MOE_TRY(route_front(s, x, norm_w, router_w, router_b, w, s->T <= 16, &ein, &ein_bf16, st));
-    MOE_TRY(launch(MOE_KERNEL_TOPK, "topk", st, [&] { return moe::launch_topk(w.logits, s->T, s->E, s->k, s->route_scale, w.idx, w.wts,
-                                       out->topk_idx, out->topk_w, nullptr, 0, s->H, nullptr, st); }));
+    MOE_TRY(route_front(s, x, norm_w, router_w, w, false, &ein, &ein_bf16, st));
+    MOE_TRY(launch(MOE_KERNEL_TOPK, "topk", st, [&] {
+        return moe::launch_topk(w.partial, w.splits, router_b, s->T, s->E, s->k, s->route_scale,
+                                w.idx, w.wts, out->topk_idx, out->topk_w, nullptr, 0, s->H,
+                                nullptr, st);
+    }));
     MOE_TRY(launch(MOE_KERNEL_PERMUTE, "permute", st, [&] { return moe::launch_permute(w.idx, s->T, s->E, s->k, 0, w.counts, w.offsets, w.perm,
                                           w.inv, w.rank, w.mprefix, out->counts, out->offsets,
                                           out->perm, out->inv, st); }));
@@ -322,17 +355,39 @@ int moe_forward_decode(const moe_shape *s, const void *hidden, const float *norm
     const Workspace w = carve(s, static_cast<uint8_t *>(ws));
     const void *ein;
     int ein_bf16;
-    MOE_TRY(route_front(s, hidden, norm_w, router_w, router_b, w, true, &ein, &ein_bf16, st));
+    int act_e0 = 0;
+    const bool mx = moe::mx_steps_per_wave(s->H) > 0 && moe::mx_steps_per_wave(s->F) > 0 &&
+                    act_exponent(s, &act_e0);
+    MOE_TRY(route_front(s, hidden, norm_w, router_w, w, mx, &ein, &ein_bf16, st));
     const moe::ExpertPtrs ex = expert_ptrs(s, experts);
     const moe::ExpertPtrs sh = expert_ptrs(s, shared);
     const moe::SwigluConsts c{s->swiglu_alpha, s->swiglu_limit, s->swiglu_up_offset};
-    MOE_TRY(launch(MOE_KERNEL_DECODE_GATE_UP, "decode_gate_up", st, [&] { return moe::launch_decode_gate_up(ein, ein_bf16, w.logits, s->T, s->H, s->F, s->E,
-                                                 s->k, s->n_shared, s->route_scale, ex, sh, c,
-                                                 w.idx, w.wts, ro ? ro->topk_idx : nullptr,
-                                                 ro ? ro->topk_w : nullptr, w.act, st); }));
-    MOE_TRY(launch(MOE_KERNEL_DECODE_DOWN, "decode_down", st, [&] { return moe::launch_decode_down(hidden, s->act_dtype == MOE_BF16, s->T, s->H, s->F,
-                                              s->k, s->n_shared, ex, sh, w.idx, w.wts, w.act, out,
-                                              st); }));
+    const int rbf = s->act_dtype == MOE_BF16;
+    int32_t *oidx = ro ? ro->topk_idx : nullptr;
+    float *ow = ro ? ro->topk_w : nullptr;
+    if (mx) {
+        MOE_TRY(launch(MOE_KERNEL_DECODE_GATE_UP, "decode_gate_up", st, [&] {
+            return moe::launch_decode_gate_up_mx(w.xq, w.xs, w.partial, w.splits, router_b, s->T,
+                                                 s->H, s->F, s->E, s->k, s->n_shared,
+                                                 s->route_scale, ex, sh, c, act_e0, w.idx, w.wts,
+                                                 oidx, ow, hidden, rbf, out, w.act_q, st);
+        }));
+        MOE_TRY(launch(MOE_KERNEL_DECODE_DOWN, "decode_down", st, [&] {
+            return moe::launch_decode_down_mx(w.act_q, act_e0, s->T, s->H, s->F, s->k,
+                                              s->n_shared, ex, sh, w.idx, w.wts, out, st);
+        }));
+    } else {
+        MOE_TRY(launch(MOE_KERNEL_DECODE_GATE_UP, "decode_gate_up", st, [&] {
+            return moe::launch_decode_gate_up(ein, ein_bf16, w.partial, w.splits, router_b, s->T,
+                                              s->H, s->F, s->E, s->k, s->n_shared, s->route_scale,
+                                              ex, sh, c, w.idx, w.wts, oidx, ow, hidden, rbf, out,
+                                              w.act, st);
+        }));
+        MOE_TRY(launch(MOE_KERNEL_DECODE_DOWN, "decode_down", st, [&] {
+            return moe::launch_decode_down(s->T, s->H, s->F, s->k, s->n_shared, ex, sh, w.idx,
+                                           w.wts, w.act, out, st);
+        }));
+    }
     if (ro && (ro->counts || ro->offsets || ro->perm || ro->inv))
         MOE_TRY(launch(MOE_KERNEL_PERMUTE, "permute", st, [&] { return moe::launch_permute(w.idx, s->T, s->E, s->k, 0, w.counts, w.offsets,
                                               w.perm, w.inv, w.rank, w.mprefix, ro->counts,
@@ -349,10 +404,13 @@ int moe_forward_prefill(const moe_shape *s, const void *hidden, const float *nor
     const Workspace w = carve(s, static_cast<uint8_t *>(ws));
     const void *ein;
     int ein_bf16;
-    MOE_TRY(route_front(s, hidden, norm_w, router_w, router_b, w, s->T <= 16, &ein, &ein_bf16, st));
-    MOE_TRY(launch(MOE_KERNEL_TOPK, "topk", st, [&] { return moe::launch_topk(w.logits, s->T, s->E, s->k, s->route_scale, w.idx, w.wts,
-                                       ro ? ro->topk_idx : nullptr, ro ? ro->topk_w : nullptr,
-                                       hidden, s->act_dtype == MOE_BF16, s->H, out, st); }));
+    MOE_TRY(route_front(s, hidden, norm_w, router_w, w, false, &ein, &ein_bf16, st));
+    MOE_TRY(launch(MOE_KERNEL_TOPK, "topk", st, [&] {
+        return moe::launch_topk(w.partial, w.splits, router_b, s->T, s->E, s->k, s->route_scale,
+                                w.idx, w.wts, ro ? ro->topk_idx : nullptr,
+                                ro ? ro->topk_w : nullptr, hidden, s->act_dtype == MOE_BF16,
+                                s->H, out, st);
+    }));
     MOE_TRY(launch(MOE_KERNEL_PERMUTE, "permute", st, [&] { return moe::launch_permute(w.idx, s->T, s->E, s->k, s->n_shared, w.counts,
                                           w.offsets, w.perm, w.inv, w.rank, w.mprefix,
                                           ro ? ro->counts : nullptr, ro ? ro->offsets : nullptr,

@@ -103,25 +103,58 @@ __device__ __forceinline__ float swiglu(float g, float u, float alpha, float lim
 }
 
 // ---------------------------------------------------------------- top-k
-// Top-k of one token's fp64 logits (E <= 256) by one wavefront. Lane l holds
-// experts l, l+64, l+128, l+192. Each round takes the wave maximum over the
-// experts still in play, then the lowest expert index holding it (ballot per
-// quarter: lanes are in index order inside a quarter, quarters in index
+// Logits of one token for the lane's experts e = lane + 64q (q < NQ, so
+// E <= 64 NQ): the router's split-K partial sums (partial[s][t][e], fp64)
+// added in split order, plus the bias; experts >= E get -inf. The loads of
+// each group of kGatherUnroll splits are issued together (indices clamped,
+// extra values masked) so the gather costs one memory round trip per group.
+constexpr int kGatherUnroll = 8;
+template <int NQ>
+__device__ __forceinline__ void gather_logits(const double *partial, int S, int T, int t, int E,
+                                              const float *bias, double (&v)[4]) {
+    const int lane = threadIdx.x & (kWave - 1);
+    double acc[NQ];
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) acc[q] = 0.0;
+    for (int s0 = 0; s0 < S; s0 += kGatherUnroll) {
+        double part[kGatherUnroll][NQ];
+#pragma unroll
+        for (int i = 0; i < kGatherUnroll; ++i) {
+            const double *row = partial + (static_cast<size_t>(min(s0 + i, S - 1)) * T + t) * E;
+#pragma unroll
+            for (int q = 0; q < NQ; ++q) part[i][q] = row[min(lane + kWave * q, E - 1)];
+        }
+#pragma unroll
+        for (int i = 0; i < kGatherUnroll; ++i)
+#pragma unroll
+            for (int q = 0; q < NQ; ++q)
+                if (s0 + i < S) acc[q] += part[i][q];
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int e = lane + kWave * q;
+        v[q] = (q < NQ && e < E) ? acc[q < NQ ? q : 0] + static_cast<double>(bias[min(e, E - 1)])
+                                 : -INFINITY;
+    }
+}
+
+// Top-k of one token's fp64 logits (E <= 256) by one wavefront; v holds the
+// lane's experts l, l+64, l+128, l+192. Each round takes the wave maximum over
+// the experts still in play, then the lowest expert index holding it (ballot
+// per quarter: lanes are in index order inside a quarter, quarters in index
 // order), and retires it; so the result is by descending value with equal
 // values in ascending index order. A NaN logit counts as -inf, so every
 // returned index is a distinct valid expert whatever the input.
 // sel[j] and val[j] are uniform across the wave on return.
-__device__ __forceinline__ void wave_topk(const double *logits, int E, int k, int *sel,
+__device__ __forceinline__ void wave_topk(const double (&vin)[4], int E, int k, int *sel,
                                           double *val) {
     const int lane = threadIdx.x & (kWave - 1);
     double v[4];
     bool alive[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-        const int e = lane + kWave * q;
-        alive[q] = e < E;
-        const double l = alive[q] ? logits[e] : -INFINITY;
-        v[q] = l == l ? l : -INFINITY;
+        alive[q] = lane + kWave * q < E;
+        v[q] = vin[q] == vin[q] ? vin[q] : -INFINITY;
     }
     for (int j = 0; j < k; ++j) {
         double m = -INFINITY;
@@ -163,6 +196,79 @@ __device__ __forceinline__ bool xcd_tile(int bid, int ntiles, int &tile) {
     const int per = (ntiles + kXcds - 1) / kXcds;
     tile = xcd * per + slot;
     return slot < per && tile < ntiles;
+}
+
+}  // namespace moe
+
+namespace moe {
+
+// ---------------------------------------------------------------- FP8 terms
+// Activations meet MXFP4 weights on the block-scaled matrix cores as a sum of
+// kTerms FP8 (OCP E4M3) vectors, each with its own E8M0 scales: term n holds
+// what terms 0..n-1 left over, so every extra term adds about four
+// significant bits (kTerms = 4: ~16 bits, float32-level products).
+
+// OCP E4M3 code of x, |x| < 448, rounded to nearest (ties to even).
+__device__ __forceinline__ uint32_t e4m3_encode(float x) {
+    const uint32_t sign = (__float_as_uint(x) >> 24) & 0x80u;
+    const float ax = fabsf(x);
+    uint32_t code;
+    if (ax < 0.015625f) {  // below 2^-6: subnormals, steps of 2^-9 (8 * 2^-9 is the first normal)
+        code = static_cast<uint32_t>(__float2int_rn(ax * 512.0f));
+    } else {
+        const uint32_t ab = __float_as_uint(ax);
+        const uint32_t r = ab + 0x7FFFFu + ((ab >> 20) & 1u);  // round the mantissa to 3 bits
+        code = ((((r >> 23) & 0xffu) - 120u) << 3) | ((r >> 20) & 7u);
+        code = code > 0x7Eu ? 0x7Eu : code;
+    }
+    return sign | code;
+}
+
+__device__ __forceinline__ float e4m3_decode(uint32_t c) {
+    const uint32_t e = (c >> 3) & 15u, m = c & 7u;
+    const float v = e == 0 ? static_cast<float>(m) * 0.001953125f
+                           : __uint_as_float(((e + 120u) << 23) | (m << 20));
+    return (c & 0x80u) ? -v : v;
+}
+
+// 2^e as float32 for e in [-126, 127].
+__device__ __forceinline__ float pow2f(int e) { return __uint_as_float(static_cast<uint32_t>(e + 127) << 23); }
+
+// Split the 32 values held by the 32 lanes of a half-wavefront into kTerms
+// E4M3 codes with one E8M0 scale byte per term (scale 2^(floor(log2 amax)-7)
+// of what is left, so codes stay below 256). Returns the codes packed in one
+// dword (term n in byte n) and the scale bytes likewise.
+__device__ __forceinline__ void fp8_terms_group(float v, uint32_t &codes, uint32_t &scales) {
+    codes = 0;
+    scales = 0;
+    float r = v;
+#pragma unroll
+    for (int n = 0; n < kTerms; ++n) {
+        float amax = fabsf(r);
+#pragma unroll
+        for (int off = 16; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 32));
+        int e = static_cast<int>((__float_as_uint(amax) >> 23) & 0xffu) - 127 - 7;
+        e = e < -126 ? -126 : (e > 127 ? 127 : e);
+        const uint32_t q = e4m3_encode(r * pow2f(-e));
+        r -= e4m3_decode(q) * pow2f(e);
+        codes |= q << (8 * n);
+        scales |= static_cast<uint32_t>(e + 127) << (8 * n);
+    }
+}
+
+// Same split with fixed per-term exponents e0 - 4n (a value range known in
+// advance, |v| < 2^(e0 + 8)); codes only.
+__device__ __forceinline__ uint32_t fp8_terms_fixed(float v, int e0) {
+    uint32_t codes = 0;
+    float r = v;
+#pragma unroll
+    for (int n = 0; n < kTerms; ++n) {
+        const int e = e0 - 4 * n;
+        const uint32_t q = e4m3_encode(r * pow2f(-e));
+        r -= e4m3_decode(q) * pow2f(e);
+        codes |= q << (8 * n);
+    }
+    return codes;
 }
 
 }  // namespace moe

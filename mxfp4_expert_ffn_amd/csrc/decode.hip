@@ -8,8 +8,9 @@
 //
 // Lane mapping: in a row of K weights (K/32 MX blocks of 16 code bytes and
 // one scale byte), lane l always takes blocks l, l+64, l+128, ... so the 32
-// activations of each of its blocks are loaded once into registers and reused
-// for every row the wavefront streams. A row sum is then one DPP reduction.
+// activations of each of its blocks are read once (from the workgroup's LDS
+// copy) into registers and reused for every row the wavefront streams. A row
+// sum is then one DPP reduction.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -17,92 +18,102 @@ namespace moe {
 
 namespace {
 
-template <int NB, bool BF16>
-__device__ __forceinline__ void load_vec_blocks(const void *src, int K, float (&v)[NB][32]) {
+constexpr int kMaxBlocks = 8192 / 32;  // MX blocks per row (K <= 8192)
+
+// Stage a length-K vector (fp32 or bf16 bits) in LDS as float32, transposed
+// to [32][K/32 + 1] so that lane l reading element i of block l hits
+// consecutive addresses.
+template <bool BF16>
+__device__ __forceinline__ void stage_vec(const void *src, int K, float (*sv)[kMaxBlocks + 1]) {
+    for (int i4 = threadIdx.x; i4 < K / 4; i4 += blockDim.x) {
+        float v[4];
+        if constexpr (BF16) {
+            const uint2 u = reinterpret_cast<const uint2 *>(src)[i4];
+            v[0] = __uint_as_float(u.x << 16); v[1] = __uint_as_float(u.x & 0xffff0000u);
+            v[2] = __uint_as_float(u.y << 16); v[3] = __uint_as_float(u.y & 0xffff0000u);
+        } else {
+            const float4 f = reinterpret_cast<const float4 *>(src)[i4];
+            v[0] = f.x; v[1] = f.y; v[2] = f.z; v[3] = f.w;
+        }
+        const int h = 4 * i4, b = h >> 5, i = h & 31;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) sv[i + j][b] = v[j];
+    }
+}
+
+// Lane l's blocks l, l+64, ... of the staged vector into registers.
+template <int NB>
+__device__ __forceinline__ void lane_blocks(const float (*sv)[kMaxBlocks + 1], int K, float (&v)[NB][32]) {
     const int lane = threadIdx.x & 63;
-    const int nblk = K / 32;
 #pragma unroll
     for (int c = 0; c < NB; ++c) {
         const int b = lane + 64 * c;
-        if (b < nblk) {
-            if constexpr (BF16) {
-                const uint4 *p = reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(src) + 32 * b);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const uint4 u = p[i];
-                    const uint32_t d[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        v[c][8 * i + 2 * j] = __uint_as_float(d[j] << 16);
-                        v[c][8 * i + 2 * j + 1] = __uint_as_float(d[j] & 0xffff0000u);
-                    }
-                }
-            } else {
-                const float4 *p = reinterpret_cast<const float4 *>(static_cast<const float *>(src) + 32 * b);
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const float4 f = p[i];
-                    v[c][4 * i] = f.x; v[c][4 * i + 1] = f.y; v[c][4 * i + 2] = f.z; v[c][4 * i + 3] = f.w;
-                }
-            }
-        } else {
-#pragma unroll
-            for (int i = 0; i < 32; ++i) v[c][i] = 0.f;
-        }
+        for (int i = 0; i < 32; ++i) v[c][i] = b < K / 32 ? sv[i][b] : 0.f;
     }
 }
 
 // gate/up GEMV + biases + clamped SwiGLU. grid.x = routes (T*k routed, then
 // T*n_shared shared rows), grid.y = blocks of kDecodeRowsGU expert rows.
+// Wavefront 0 recomputes the token's top-k from the router partials (every
+// workgroup of a route agrees: same inputs, same order) while the others
+// stage the activation row in LDS. Workgroups of slot 0 also seed out[t]
+// with the residual, which the down kernel then accumulates into.
 template <int NB, bool BF16>
 __global__ __launch_bounds__(256) void decode_gate_up_kernel(
-    const void *x, const double *logits, int T, int H, int F, int E, int k, float route_scale,
-    ExpertPtrs ex, ExpertPtrs sh, SwigluConsts sc, int32_t *idx, float *wts, int32_t *out_idx,
-    float *out_w, float *act) {
+    const void *x, const double *partial, int S, const float *router_b, int T, int H, int F,
+    int E, int k, float route_scale, ExpertPtrs ex, ExpertPtrs sh, SwigluConsts sc, int32_t *idx,
+    float *wts, int32_t *out_idx, float *out_w, const void *resid, int resid_bf16, float *out,
+    float *act) {
     constexpr int RPW = kDecodeRowsGU / 4;  // rows per wavefront
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int r = blockIdx.x, R = T * k;
     __shared__ int s_expert;
-    const uint8_t *blob;
-    int t;
-    if (r < R) {
-        t = r / k;
-        const int j = r - t * k;
-        if (w == 0) {
-            int sel[kMaxK];
-            double val[kMaxK];
-            wave_topk(logits + static_cast<size_t>(t) * E, E, k, sel, val);
-            int mine = sel[0];
+    __shared__ float s_x[32][kMaxBlocks + 1];
+    const int t = r < R ? r / k : r - R;
+    const int j = r < R ? r - t * k : -1;
+    const void *xt = BF16 ? static_cast<const void *>(static_cast<const uint16_t *>(x) + static_cast<size_t>(t) * H)
+                          : static_cast<const void *>(static_cast<const float *>(x) + static_cast<size_t>(t) * H);
+    if (r < R && w == 0) {
+        double v[4];
+        if (E <= 64) gather_logits<1>(partial, S, T, t, E, router_b, v);
+        else if (E <= 128) gather_logits<2>(partial, S, T, t, E, router_b, v);
+        else gather_logits<4>(partial, S, T, t, E, router_b, v);
+        int sel[kMaxK];
+        double val[kMaxK];
+        wave_topk(v, E, k, sel, val);
+        int mine = sel[0];
 #pragma unroll
-            for (int jj = 1; jj < kMaxK; ++jj)
-                if (jj == j) mine = sel[jj];
-            if (lane == 0) s_expert = mine;
-            if (j == 0 && blockIdx.y == 0) {
-                float wv[kMaxK];
-                route_softmax(val, k, route_scale, wv);
+        for (int jj = 1; jj < kMaxK; ++jj)
+            if (jj == j) mine = sel[jj];
+        if (lane == 0) s_expert = mine;
+        if (j == 0 && blockIdx.y == 0) {
+            float wv[kMaxK];
+            route_softmax(val, k, route_scale, wv);
 #pragma unroll
-                for (int jj = 0; jj < kMaxK; ++jj) {
-                    if (jj < k && lane == jj) {
-                        idx[t * k + jj] = sel[jj];
-                        wts[t * k + jj] = wv[jj];
-                        if (out_idx) out_idx[t * k + jj] = sel[jj];
-                        if (out_w) out_w[t * k + jj] = wv[jj];
-                    }
+            for (int jj = 0; jj < kMaxK; ++jj) {
+                if (jj < k && lane == jj) {
+                    idx[t * k + jj] = sel[jj];
+                    wts[t * k + jj] = wv[jj];
+                    if (out_idx) out_idx[t * k + jj] = sel[jj];
+                    if (out_w) out_w[t * k + jj] = wv[jj];
                 }
             }
         }
-        __syncthreads();
-        blob = ex.base + static_cast<size_t>(s_expert) * ex.stride;
-    } else {
-        t = r - R;
-        blob = sh.base;
     }
-
-    float xv[NB][32];
-    if constexpr (BF16)
-        load_vec_blocks<NB, true>(static_cast<const uint16_t *>(x) + static_cast<size_t>(t) * H, H, xv);
-    else
-        load_vec_blocks<NB, false>(static_cast<const float *>(x) + static_cast<size_t>(t) * H, H, xv);
+    stage_vec<BF16>(xt, H, s_x);
+    float *o = out + static_cast<size_t>(t) * H;
+    const float *rf = static_cast<const float *>(resid) + static_cast<size_t>(t) * H;
+    if (j == 0 && (resid_bf16 || o != rf)) {
+        // residual seed: this workgroup's share of out[t]
+        const uint16_t *rb = static_cast<const uint16_t *>(resid) + static_cast<size_t>(t) * H;
+        const int share = (H + gridDim.y - 1) / gridDim.y;
+        const int h0 = blockIdx.y * share;
+        for (int h = h0 + threadIdx.x; h < min(H, h0 + share); h += blockDim.x)
+            o[h] = resid_bf16 ? bf16_bits_to_f32(rb[h]) : rf[h];
+    }
+    __syncthreads();
+    const uint8_t *blob = r < R ? ex.base + static_cast<size_t>(s_expert) * ex.stride : sh.base;
 
     const int nblk = H / 32;
     const int f0 = blockIdx.y * kDecodeRowsGU + w * RPW;
@@ -111,27 +122,27 @@ __global__ __launch_bounds__(256) void decode_gate_up_kernel(
     const float *gb = reinterpret_cast<const float *>(blob + ex.gate_b);
     const float *ub = reinterpret_cast<const float *>(blob + ex.up_b);
 
+    // Every load is unconditional (clamped to a valid row/block) so that all of
+    // them are in flight together; out-of-range rows are never stored and
+    // out-of-range blocks meet zero activations.
     uint4 qg[RPW][NB], qu[RPW][NB];
     uint32_t sg[RPW][NB], su[RPW][NB];
 #pragma unroll
     for (int i = 0; i < RPW; ++i) {
-        const int f = f0 + i;
+        const int f = min(f0 + i, F - 1);
 #pragma unroll
         for (int c = 0; c < NB; ++c) {
-            const int b = lane + 64 * c;
-            if (f < F && b < nblk) {
-                const size_t qo = static_cast<size_t>(f) * (H / 2) + 16 * b;
-                const size_t so = static_cast<size_t>(f) * nblk + b;
-                qg[i][c] = *reinterpret_cast<const uint4 *>(gq + qo);
-                qu[i][c] = *reinterpret_cast<const uint4 *>(uq + qo);
-                sg[i][c] = gs[so];
-                su[i][c] = us[so];
-            } else {
-                qg[i][c] = qu[i][c] = make_uint4(0, 0, 0, 0);
-                sg[i][c] = su[i][c] = 127;
-            }
+            const int b = min(lane + 64 * c, nblk - 1);
+            const size_t qo = static_cast<size_t>(f) * (H / 2) + 16 * b;
+            const size_t so = static_cast<size_t>(f) * nblk + b;
+            qg[i][c] = *reinterpret_cast<const uint4 *>(gq + qo);
+            qu[i][c] = *reinterpret_cast<const uint4 *>(uq + qo);
+            sg[i][c] = gs[so];
+            su[i][c] = us[so];
         }
     }
+    float xv[NB][32];
+    lane_blocks<NB>(s_x, H, xv);
 #pragma unroll
     for (int i = 0; i < RPW; ++i) {
         const int f = f0 + i;
@@ -149,129 +160,115 @@ __global__ __launch_bounds__(256) void decode_gate_up_kernel(
     }
 }
 
-// down GEMV + bias + route-weighted, slot-ordered combine with the residual.
-// grid.x = tokens, grid.y = blocks of kDecodeRowsDn hidden rows; wavefront w
-// takes slots w, w+4, ... (routed slots, then the shared expert).
-template <int NB, bool RBF16>
+// down GEMV + bias, times the route weight, added into out[t] (seeded with
+// the residual by the gate/up kernel). grid.x = (token, slot) pairs with the
+// shared expert as the last slot, grid.y = blocks of kDecodeRowsDn rows.
+template <int NB>
 __global__ __launch_bounds__(256) void decode_down_kernel(
-    const void *resid, int T, int H, int F, int k, int n_shared, ExpertPtrs ex, ExpertPtrs sh,
-    const int32_t *idx, const float *wts, const float *act, float *out) {
-    constexpr int ROWS = kDecodeRowsDn;
+    int T, int H, int F, int k, int n_shared, ExpertPtrs ex, ExpertPtrs sh, const int32_t *idx,
+    const float *wts, const float *act, float *out) {
+    constexpr int RPW = kDecodeRowsDn / 4;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const int t = blockIdx.x, h0 = blockIdx.y * ROWS;
-    const int nslots = k + n_shared, nblk = F / 32;
-    __shared__ float ys[kMaxK + 1][ROWS];
-    for (int slot = w; slot < nslots; slot += 4) {
-        const uint8_t *blob;
-        size_t r;
-        if (slot < k) {
-            blob = ex.base + static_cast<size_t>(idx[t * k + slot]) * ex.stride;
-            r = static_cast<size_t>(t) * k + slot;
-        } else {
-            blob = sh.base;
-            r = static_cast<size_t>(T) * k + t;
-        }
-        float av[NB][32];
-        load_vec_blocks<NB, false>(act + r * F, F, av);
-        const uint8_t *dq = blob + ex.down_q, *ds = blob + ex.down_s;
-        const float *db = reinterpret_cast<const float *>(blob + ex.down_b);
-        uint4 q[ROWS][NB];
-        uint32_t s[ROWS][NB];
+    const int nslots = k + n_shared;
+    const int t = blockIdx.x / nslots, slot = blockIdx.x - t * nslots;
+    const uint8_t *blob;
+    size_t r;
+    float wt;
+    if (slot < k) {
+        blob = ex.base + static_cast<size_t>(idx[t * k + slot]) * ex.stride;
+        r = static_cast<size_t>(t) * k + slot;
+        wt = wts[t * k + slot];
+    } else {
+        blob = sh.base;
+        r = static_cast<size_t>(T) * k + t;
+        wt = 1.0f;
+    }
+    __shared__ float s_a[32][kMaxBlocks + 1];
+    stage_vec<false>(act + r * F, F, s_a);
+    const int nblk = F / 32;
+    const int h0 = blockIdx.y * kDecodeRowsDn + w * RPW;
+    const uint8_t *dq = blob + ex.down_q, *ds = blob + ex.down_s;
+    const float *db = reinterpret_cast<const float *>(blob + ex.down_b);
+    uint4 q[RPW][NB];
+    uint32_t sq[RPW][NB];
 #pragma unroll
-        for (int i = 0; i < ROWS; ++i) {
-            const int h = h0 + i;
+    for (int i = 0; i < RPW; ++i) {
+        const int h = min(h0 + i, H - 1);
 #pragma unroll
-            for (int c = 0; c < NB; ++c) {
-                const int b = lane + 64 * c;
-                if (h < H && b < nblk) {
-                    q[i][c] = *reinterpret_cast<const uint4 *>(dq + static_cast<size_t>(h) * (F / 2) + 16 * b);
-                    s[i][c] = ds[static_cast<size_t>(h) * nblk + b];
-                } else {
-                    q[i][c] = make_uint4(0, 0, 0, 0);
-                    s[i][c] = 127;
-                }
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < ROWS; ++i) {
-            float a = 0.f;
-#pragma unroll
-            for (int c = 0; c < NB; ++c) a += mx_block_dot(q[i][c], e8m0_scale(s[i][c]), av[c]);
-            a = wave_sum(a);
-            const int h = h0 + i;
-            if (lane == 0 && h < H) ys[slot][i] = a + db[h];
+        for (int c = 0; c < NB; ++c) {
+            const int b = min(lane + 64 * c, nblk - 1);  // clamped: see the gate/up kernel
+            q[i][c] = *reinterpret_cast<const uint4 *>(dq + static_cast<size_t>(h) * (F / 2) + 16 * b);
+            sq[i][c] = ds[static_cast<size_t>(h) * nblk + b];
         }
     }
     __syncthreads();
-    if (threadIdx.x < ROWS) {
-        const int i = threadIdx.x, h = h0 + i;
-        if (h < H) {
-            const size_t o = static_cast<size_t>(t) * H + h;
-            float acc = RBF16 ? bf16_bits_to_f32(static_cast<const uint16_t *>(resid)[o])
-                              : static_cast<const float *>(resid)[o];
-            for (int j = 0; j < k; ++j) acc = fmaf(wts[t * k + j], ys[j][i], acc);
-            if (n_shared) acc += ys[k][i];
-            out[o] = acc;
-        }
+    float av[NB][32];
+    lane_blocks<NB>(s_a, F, av);
+#pragma unroll
+    for (int i = 0; i < RPW; ++i) {
+        float a = 0.f;
+#pragma unroll
+        for (int c = 0; c < NB; ++c) a += mx_block_dot(q[i][c], e8m0_scale(sq[i][c]), av[c]);
+        a = wave_sum(a);
+        const int h = h0 + i;
+        if (lane == 0 && h < H)
+            unsafeAtomicAdd(out + static_cast<size_t>(t) * H + h, wt * (a + db[h]));
     }
 }
 
 template <int NB>
-hipError_t gate_up_nb(const void *x, int x_bf16, const double *logits, int T, int H, int F, int E,
-                      int k, int n_shared, float route_scale, const ExpertPtrs &ex,
-                      const ExpertPtrs &sh, SwigluConsts c, int32_t *idx, float *wts,
-                      int32_t *out_idx, float *out_w, float *act, hipStream_t s) {
-    dim3 grid(T * k + T * n_shared, (F + kDecodeRowsGU - 1) / kDecodeRowsGU);
+hipError_t gate_up_nb(const void *x, int x_bf16, const double *partial, int S, const float *router_b,
+                      int T, int H, int F, int E, int k, int n_shared, float route_scale,
+                      const ExpertPtrs &ex, const ExpertPtrs &sh, SwigluConsts c, int32_t *idx,
+                      float *wts, int32_t *out_idx, float *out_w, const void *resid,
+                      int resid_bf16, float *out, float *act, hipStream_t s) {
+    const dim3 grid(T * k + T * n_shared, (F + kDecodeRowsGU - 1) / kDecodeRowsGU);
     if (x_bf16)
-        launch_kernel(decode_gate_up_kernel<NB, true>, grid, 256, s, x, logits, T, H, F, E, k,
-                      route_scale, ex, sh, c, idx, wts, out_idx, out_w, act);
+        launch_kernel(decode_gate_up_kernel<NB, true>, grid, 256, s, x, partial, S, router_b, T, H,
+                      F, E, k, route_scale, ex, sh, c, idx, wts, out_idx, out_w, resid,
+                      resid_bf16, out, act);
     else
-        launch_kernel(decode_gate_up_kernel<NB, false>, grid, 256, s, x, logits, T, H, F, E, k,
-                      route_scale, ex, sh, c, idx, wts, out_idx, out_w, act);
+        launch_kernel(decode_gate_up_kernel<NB, false>, grid, 256, s, x, partial, S, router_b, T,
+                      H, F, E, k, route_scale, ex, sh, c, idx, wts, out_idx, out_w, resid,
+                      resid_bf16, out, act);
     return hipGetLastError();
 }
 
 template <int NB>
-hipError_t down_nb(const void *resid, int resid_bf16, int T, int H, int F, int k, int n_shared,
-                   const ExpertPtrs &ex, const ExpertPtrs &sh, const int32_t *idx, const float *wts,
-                   const float *act, float *out, hipStream_t s) {
-    dim3 grid(T, (H + kDecodeRowsDn - 1) / kDecodeRowsDn);
-    if (resid_bf16)
-        launch_kernel(decode_down_kernel<NB, true>, grid, 256, s, resid, T, H, F, k, n_shared, ex,
-                      sh, idx, wts, act, out);
-    else
-        launch_kernel(decode_down_kernel<NB, false>, grid, 256, s, resid, T, H, F, k, n_shared, ex,
-                      sh, idx, wts, act, out);
+hipError_t down_nb(int T, int H, int F, int k, int n_shared, const ExpertPtrs &ex,
+                   const ExpertPtrs &sh, const int32_t *idx, const float *wts, const float *act,
+                   float *out, hipStream_t s) {
+    const dim3 grid(T * (k + n_shared), (H + kDecodeRowsDn - 1) / kDecodeRowsDn);
+    launch_kernel(decode_down_kernel<NB>, grid, 256, s, T, H, F, k, n_shared, ex, sh, idx, wts,
+                  act, out);
     return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_decode_gate_up(const void *x, int x_bf16, const double *logits, int T, int H,
-                                 int F, int E, int k, int n_shared, float route_scale,
-                                 const ExpertPtrs &ex, const ExpertPtrs &sh, SwigluConsts c,
-                                 int32_t *idx, float *wts, int32_t *out_idx, float *out_w,
-                                 float *act, hipStream_t s) {
-    const int nb = (H / 32 + 63) / 64;
-    switch (nb) {
-    case 1: return gate_up_nb<1>(x, x_bf16, logits, T, H, F, E, k, n_shared, route_scale, ex, sh, c, idx, wts, out_idx, out_w, act, s);
-    case 2: return gate_up_nb<2>(x, x_bf16, logits, T, H, F, E, k, n_shared, route_scale, ex, sh, c, idx, wts, out_idx, out_w, act, s);
-    case 3: return gate_up_nb<3>(x, x_bf16, logits, T, H, F, E, k, n_shared, route_scale, ex, sh, c, idx, wts, out_idx, out_w, act, s);
-    case 4: return gate_up_nb<4>(x, x_bf16, logits, T, H, F, E, k, n_shared, route_scale, ex, sh, c, idx, wts, out_idx, out_w, act, s);
+hipError_t launch_decode_gate_up(const void *x, int x_bf16, const double *partial, int S,
+                                 const float *router_b, int T, int H, int F, int E, int k,
+                                 int n_shared, float route_scale, const ExpertPtrs &ex,
+                                 const ExpertPtrs &sh, SwigluConsts c, int32_t *idx, float *wts,
+                                 int32_t *out_idx, float *out_w, const void *resid,
+                                 int resid_bf16, float *out, float *act, hipStream_t s) {
+    switch ((H / 32 + 63) / 64) {
+    case 1: return gate_up_nb<1>(x, x_bf16, partial, S, router_b, T, H, F, E, k, n_shared, route_scale, ex, sh, c, idx, wts, out_idx, out_w, resid, resid_bf16, out, act, s);
+    case 2: return gate_up_nb<2>(x, x_bf16, partial, S, router_b, T, H, F, E, k, n_shared, route_scale, ex, sh, c, idx, wts, out_idx, out_w, resid, resid_bf16, out, act, s);
+    case 3: return gate_up_nb<3>(x, x_bf16, partial, S, router_b, T, H, F, E, k, n_shared, route_scale, ex, sh, c, idx, wts, out_idx, out_w, resid, resid_bf16, out, act, s);
+    case 4: return gate_up_nb<4>(x, x_bf16, partial, S, router_b, T, H, F, E, k, n_shared, route_scale, ex, sh, c, idx, wts, out_idx, out_w, resid, resid_bf16, out, act, s);
     default: return hipErrorInvalidValue;
     }
 }
 
-hipError_t launch_decode_down(const void *resid, int resid_bf16, int T, int H, int F, int k,
-                              int n_shared, const ExpertPtrs &ex, const ExpertPtrs &sh,
-                              const int32_t *idx, const float *wts, const float *act, float *out,
-                              hipStream_t s) {
-    const int nb = (F / 32 + 63) / 64;
-    switch (nb) {
-    case 1: return down_nb<1>(resid, resid_bf16, T, H, F, k, n_shared, ex, sh, idx, wts, act, out, s);
-    case 2: return down_nb<2>(resid, resid_bf16, T, H, F, k, n_shared, ex, sh, idx, wts, act, out, s);
-    case 3: return down_nb<3>(resid, resid_bf16, T, H, F, k, n_shared, ex, sh, idx, wts, act, out, s);
-    case 4: return down_nb<4>(resid, resid_bf16, T, H, F, k, n_shared, ex, sh, idx, wts, act, out, s);
+hipError_t launch_decode_down(int T, int H, int F, int k, int n_shared, const ExpertPtrs &ex,
+                              const ExpertPtrs &sh, const int32_t *idx, const float *wts,
+                              const float *act, float *out, hipStream_t s) {
+    switch ((F / 32 + 63) / 64) {
+    case 1: return down_nb<1>(T, H, F, k, n_shared, ex, sh, idx, wts, act, out, s);
+    case 2: return down_nb<2>(T, H, F, k, n_shared, ex, sh, idx, wts, act, out, s);
+    case 3: return down_nb<3>(T, H, F, k, n_shared, ex, sh, idx, wts, act, out, s);
+    case 4: return down_nb<4>(T, H, F, k, n_shared, ex, sh, idx, wts, act, out, s);
     default: return hipErrorInvalidValue;
     }
 }

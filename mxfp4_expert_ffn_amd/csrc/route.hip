@@ -46,19 +46,130 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const void *x, const float
 }
 
 // ---------------------------------------------------------------- router logits
-// Tiled fp64 GEMM for token batches: a workgroup computes a 32-token x
-// 64-expert tile; thread (ti, ei) owns tokens 2ti, 2ti+1 and experts
-// ei + 16q. fp32 x fp32 products are exact in fp64.
+// Both router kernels write split-K partial sums partial[s][t][e] (fp64) over
+// hidden-dimension slices; consumers add the S partials in split order and
+// the bias (gather_logits), so the logits are deterministic. fp32 x fp32
+// products are exact in fp64.
+
+// Few tokens: one wavefront per (expert, hidden slice of kRouterGemvSlice
+// units); lane l holds the router weights of units 4(l + 64i) .. +3 of the
+// slice in registers (all loads issued at once), then each token's
+// activations are loaded the same way and reduced with a wave sum.
 template <int KIND>
-__global__ __launch_bounds__(256) void router_logits_kernel(const void *x, const float *w,
-                                                            const float *b, int T, int H, int E,
-                                                            double *logits) {
+__device__ __forceinline__ void load4(const void *x, size_t i, double (&v)[4]) {
+    if constexpr (KIND == 0) {
+        const float4 f = *reinterpret_cast<const float4 *>(static_cast<const float *>(x) + i);
+        v[0] = f.x; v[1] = f.y; v[2] = f.z; v[3] = f.w;
+    } else if constexpr (KIND == 1) {
+        const uint2 u = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(x) + i);
+        v[0] = __uint_as_float(u.x << 16); v[1] = __uint_as_float(u.x & 0xffff0000u);
+        v[2] = __uint_as_float(u.y << 16); v[3] = __uint_as_float(u.y & 0xffff0000u);
+    } else {
+        const double *d = static_cast<const double *>(x) + i;
+        v[0] = d[0]; v[1] = d[1]; v[2] = d[2]; v[3] = d[3];
+    }
+}
+
+// Workgroups past the router's own quantise the expert input into FP8 terms
+// for the block-scaled decode kernels: one half-wavefront per 32-value block
+// of k (the unit an E8M0 scale of the matrix core's operand B covers); codes
+// go to xq[t][n][k] (zero past H), scales to xs[t][n][k / 32].
+__device__ __forceinline__ void quantize_terms_group(const void *q_in, int q_bf16, int T, int H,
+                                                     int Kp, uint8_t *xq, uint8_t *xs, int gidx) {
+    const int lane = threadIdx.x & 63, i = lane & 31;
+    const int nb = Kp / 32;  // blocks per token
+    const bool on = gidx < T * nb;
+    const int g = on ? gidx : 0;
+    const int t = g / nb, blk = g - t * nb;
+    const int kk = 32 * blk + i;
+    float v = 0.f;
+    if (on && kk < H) {
+        const size_t at = static_cast<size_t>(t) * H + kk;
+        v = q_bf16 ? bf16_bits_to_f32(static_cast<const uint16_t *>(q_in)[at])
+                   : static_cast<const float *>(q_in)[at];
+    }
+    uint32_t codes, scales;
+    fp8_terms_group(v, codes, scales);
+    if (on) {
+#pragma unroll
+        for (int n = 0; n < kTerms; ++n) {
+            xq[(static_cast<size_t>(t) * kTerms + n) * Kp + kk] = static_cast<uint8_t>(codes >> (8 * n));
+            if (i == 0)
+                xs[(static_cast<size_t>(t) * kTerms + n) * nb + blk] = static_cast<uint8_t>(scales >> (8 * n));
+        }
+    }
+}
+
+// Stand-alone form of the FP8-term quantisation, for batches the tiled router
+// takes: 8 blocks of 32 values per workgroup.
+__global__ __launch_bounds__(256) void quantize_terms_kernel(const void *q_in, int q_bf16, int T,
+                                                             int H, int Kp, uint8_t *xq,
+                                                             uint8_t *xs) {
+    quantize_terms_group(q_in, q_bf16, T, H, Kp, xq, xs, blockIdx.x * 8 + (threadIdx.x >> 5));
+}
+
+template <int KIND>
+__global__ __launch_bounds__(256) void router_gemv_kernel(const void *x, const float *w, int T,
+                                                          int H, int E, double *partial,
+                                                          int router_wgs, const void *q_in,
+                                                          int q_bf16, int Kp, uint8_t *xq,
+                                                          uint8_t *xs) {
+    constexpr int NV = kRouterGemvSlice / 256;  // float4 per lane
+    const int lane = threadIdx.x & 63;
+    if (static_cast<int>(blockIdx.x) >= router_wgs) {
+        const int gidx = (blockIdx.x - router_wgs) * 8 + (threadIdx.x >> 5);
+        quantize_terms_group(q_in, q_bf16, T, H, Kp, xq, xs, gidx);
+        return;
+    }
+    const int item = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int S = (H + kRouterGemvSlice - 1) / kRouterGemvSlice;
+    if (item >= E * S) return;  // whole wavefront; no workgroup barrier below
+    const int e = item / S, s = item - e * S;
+    const int hbase = s * kRouterGemvSlice;
+    float4 wr[NV];
+    bool on[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        const int h = hbase + 4 * (lane + 64 * i);
+        on[i] = h < H;
+        wr[i] = *reinterpret_cast<const float4 *>(w + static_cast<size_t>(e) * H + (on[i] ? h : 0));
+    }
+    for (int t = 0; t < T; ++t) {
+        double xv[NV][4];
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            const int h = hbase + 4 * (lane + 64 * i);
+            load4<KIND>(x, static_cast<size_t>(t) * H + (on[i] ? h : 0), xv[i]);
+        }
+        double acc = 0.0;
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            if (on[i]) {
+                acc = fma(static_cast<double>(wr[i].x), xv[i][0], acc);
+                acc = fma(static_cast<double>(wr[i].y), xv[i][1], acc);
+                acc = fma(static_cast<double>(wr[i].z), xv[i][2], acc);
+                acc = fma(static_cast<double>(wr[i].w), xv[i][3], acc);
+            }
+        }
+        acc = wave_sum_f64(acc);
+        if (lane == 0) partial[(static_cast<size_t>(s) * T + t) * E + e] = acc;
+    }
+}
+
+// Token batches: workgroup = 32 tokens x 64 experts over one hidden slice of
+// `slice` units (a multiple of 32); thread (ti, ei) owns tokens 2ti, 2ti+1 and
+// experts ei + 16q. Tiles of x and the router rows are staged in LDS as fp64.
+template <int KIND>
+__global__ __launch_bounds__(256) void router_tiled_kernel(const void *x, const float *w, int T,
+                                                           int H, int E, int slice,
+                                                           double *partial) {
     __shared__ double xs[32][33];
     __shared__ double wsm[64][33];
-    const int t0 = blockIdx.x * 32, e0 = blockIdx.y * 64;
+    const int t0 = blockIdx.x * 32, e0 = blockIdx.y * 64, s = blockIdx.z;
     const int ti = threadIdx.x >> 4, ei = threadIdx.x & 15;
+    const int hbeg = s * slice, hend = min(H, hbeg + slice);
     double acc[2][4] = {};
-    for (int h0 = 0; h0 < H; h0 += 32) {
+    for (int h0 = hbeg; h0 < hend; h0 += 32) {
         for (int i = threadIdx.x; i < 32 * 32; i += 256) {
             const int r = i >> 5, c = i & 31, t = t0 + r;
             xs[r][c] = t < T ? load_in<KIND>(x, static_cast<size_t>(t) * H + h0 + c) : 0.0;
@@ -86,61 +197,30 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const void *x, const
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const int e = e0 + ei + 16 * q;
-            if (t < T && e < E)
-                logits[static_cast<size_t>(t) * E + e] = acc[r][q] + static_cast<double>(b[e]);
-        }
-    }
-}
-
-// Router for a handful of tokens: one wavefront per expert streams that
-// expert's router row with 128-bit loads; tokens in groups of 8.
-template <int KIND>
-__global__ __launch_bounds__(256) void router_gemv_kernel(const void *x, const float *w,
-                                                          const float *b, int T, int H, int E,
-                                                          double *logits) {
-    const int lane = threadIdx.x & 63;
-    const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (e >= E) return;  // whole wavefront leaves; no workgroup barrier below
-    const float4 *wr = reinterpret_cast<const float4 *>(w + static_cast<size_t>(e) * H);
-    const int n4 = H / 4;
-    for (int t0 = 0; t0 < T; t0 += 8) {
-        double acc[8] = {};
-        for (int i = lane; i < n4; i += 64) {
-            const float4 wv = wr[i];
-#pragma unroll
-            for (int tt = 0; tt < 8; ++tt) {
-                if (t0 + tt < T) {
-                    const size_t base = static_cast<size_t>(t0 + tt) * H + 4 * i;
-                    acc[tt] = fma(static_cast<double>(wv.x), load_in<KIND>(x, base + 0), acc[tt]);
-                    acc[tt] = fma(static_cast<double>(wv.y), load_in<KIND>(x, base + 1), acc[tt]);
-                    acc[tt] = fma(static_cast<double>(wv.z), load_in<KIND>(x, base + 2), acc[tt]);
-                    acc[tt] = fma(static_cast<double>(wv.w), load_in<KIND>(x, base + 3), acc[tt]);
-                }
-            }
-        }
-#pragma unroll
-        for (int tt = 0; tt < 8; ++tt) {
-            const double s = wave_sum_f64(acc[tt]);
-            if (lane == 0 && t0 + tt < T)
-                logits[static_cast<size_t>(t0 + tt) * E + e] = s + static_cast<double>(b[e]);
+            if (t < T && e < E) partial[(static_cast<size_t>(s) * T + t) * E + e] = acc[r][q];
         }
     }
 }
 
 // ---------------------------------------------------------------- top-k
-// One wavefront per token: top-k, route weights; optionally copies the
-// residual into `out` (the grouped down GEMM then adds into it).
-__global__ __launch_bounds__(256) void topk_kernel(const double *logits, int T, int E, int k,
-                                                   float route_scale, int32_t *idx, float *wts,
-                                                   int32_t *out_idx, float *out_w,
-                                                   const void *resid, int resid_bf16, int H,
-                                                   float *out) {
+// One wavefront per token: logits from the router partials, top-k, route
+// weights; optionally copies the residual into `out` (the grouped down GEMM
+// then adds into it).
+__global__ __launch_bounds__(256) void topk_kernel(const double *partial, int S, const float *bias,
+                                                   int T, int E, int k, float route_scale,
+                                                   int32_t *idx, float *wts, int32_t *out_idx,
+                                                   float *out_w, const void *resid,
+                                                   int resid_bf16, int H, float *out) {
     const int lane = threadIdx.x & 63;
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= T) return;
+    double v[4];
+    if (E <= 64) gather_logits<1>(partial, S, T, t, E, bias, v);
+    else if (E <= 128) gather_logits<2>(partial, S, T, t, E, bias, v);
+    else gather_logits<4>(partial, S, T, t, E, bias, v);
     int sel[kMaxK];
     double val[kMaxK];
-    wave_topk(logits + static_cast<size_t>(t) * E, E, k, sel, val);
+    wave_topk(v, E, k, sel, val);
     float w[kMaxK];
     route_softmax(val, k, route_scale, w);
 #pragma unroll
@@ -257,35 +337,71 @@ hipError_t launch_rmsnorm(const void *x, int x_bf16, const float *gamma, int T, 
     return hipGetLastError();
 }
 
-hipError_t launch_router_logits(const void *x, int in_kind, const float *w, const float *b, int T,
-                                int H, int E, double *logits, hipStream_t s) {
-    const dim3 grid((T + 31) / 32, (E + 63) / 64);
-    if (in_kind == 0)
-        launch_kernel(router_logits_kernel<0>, grid, 256, s, x, w, b, T, H, E, logits);
-    else if (in_kind == 1)
-        launch_kernel(router_logits_kernel<1>, grid, 256, s, x, w, b, T, H, E, logits);
-    else
-        launch_kernel(router_logits_kernel<2>, grid, 256, s, x, w, b, T, H, E, logits);
+RouterPlan router_plan(int T, int H, int E) {
+    RouterPlan p;
+    if (T <= kRouterGemvMaxT) {
+        p.gemv = true;
+        p.slice = kRouterGemvSlice;
+        p.splits = (H + kRouterGemvSlice - 1) / kRouterGemvSlice;
+        return p;
+    }
+    const int tiles = ((T + 31) / 32) * ((E + 63) / 64);
+    int want = (512 + tiles - 1) / tiles;
+    want = want < 1 ? 1 : (want > 16 ? 16 : want);
+    const int units = H / 32;
+    if (want > units) want = units;
+    p.gemv = false;
+    p.slice = 32 * ((units + want - 1) / want);
+    p.splits = (H + p.slice - 1) / p.slice;
+    return p;
+}
+
+hipError_t launch_router(const void *x, int in_kind, const float *w, int T, int H, int E,
+                         double *partial, const TermsOut *terms, hipStream_t s) {
+    const RouterPlan p = router_plan(T, H, E);
+    if (p.gemv) {
+        const int rwgs = (E * p.splits + 3) / 4;
+        int qwgs = 0, Kp = 0;
+        if (terms) {
+            Kp = 128 * ((H + 127) / 128);
+            qwgs = (T * (Kp / 32) + 7) / 8;
+        }
+        const void *qin = terms ? terms->in : nullptr;
+        const int qbf = terms ? terms->in_bf16 : 0;
+        uint8_t *xq = terms ? terms->q : nullptr;
+        uint8_t *xs = terms ? terms->scales : nullptr;
+        const int grid = rwgs + qwgs;
+        if (in_kind == 0)
+            launch_kernel(router_gemv_kernel<0>, grid, 256, s, x, w, T, H, E, partial, rwgs, qin,
+                          qbf, Kp, xq, xs);
+        else if (in_kind == 1)
+            launch_kernel(router_gemv_kernel<1>, grid, 256, s, x, w, T, H, E, partial, rwgs, qin,
+                          qbf, Kp, xq, xs);
+        else
+            launch_kernel(router_gemv_kernel<2>, grid, 256, s, x, w, T, H, E, partial, rwgs, qin,
+                          qbf, Kp, xq, xs);
+    } else {
+        if (terms) {
+            const int Kp = 128 * ((H + 127) / 128);
+            launch_kernel(quantize_terms_kernel, (T * (Kp / 32) + 7) / 8, 256, s, terms->in,
+                          terms->in_bf16, T, H, Kp, terms->q, terms->scales);
+        }
+        const dim3 grid((T + 31) / 32, (E + 63) / 64, p.splits);
+        if (in_kind == 0)
+            launch_kernel(router_tiled_kernel<0>, grid, 256, s, x, w, T, H, E, p.slice, partial);
+        else if (in_kind == 1)
+            launch_kernel(router_tiled_kernel<1>, grid, 256, s, x, w, T, H, E, p.slice, partial);
+        else
+            launch_kernel(router_tiled_kernel<2>, grid, 256, s, x, w, T, H, E, p.slice, partial);
+    }
     return hipGetLastError();
 }
 
-hipError_t launch_router_gemv(const void *x, int in_kind, const float *w, const float *b, int T,
-                              int H, int E, double *logits, hipStream_t s) {
-    const int grid = (E + 3) / 4;
-    if (in_kind == 0)
-        launch_kernel(router_gemv_kernel<0>, grid, 256, s, x, w, b, T, H, E, logits);
-    else if (in_kind == 1)
-        launch_kernel(router_gemv_kernel<1>, grid, 256, s, x, w, b, T, H, E, logits);
-    else
-        launch_kernel(router_gemv_kernel<2>, grid, 256, s, x, w, b, T, H, E, logits);
-    return hipGetLastError();
-}
-
-hipError_t launch_topk(const double *logits, int T, int E, int k, float route_scale, int32_t *idx,
-                       float *wts, int32_t *out_idx, float *out_w, const void *resid,
-                       int resid_bf16, int H, float *out, hipStream_t s) {
-    launch_kernel(topk_kernel, (T + 3) / 4, 256, s, logits, T, E, k, route_scale, idx, wts,
-                  out_idx, out_w, resid, resid_bf16, H, out);
+hipError_t launch_topk(const double *partial, int S, const float *bias, int T, int E, int k,
+                       float route_scale, int32_t *idx, float *wts, int32_t *out_idx, float *out_w,
+                       const void *resid, int resid_bf16, int H, float *out, hipStream_t s) {
+    launch_kernel(topk_kernel, (T + 3) / 4, 256, s, partial, S, bias, T, E, k, route_scale, idx,
+                  wts, out_idx, out_w, resid, resid_bf16, H, out);
     return hipGetLastError();
 }
 
