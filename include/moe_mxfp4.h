@@ -24,6 +24,11 @@
  *   invalid argument nothing is enqueued, a negative moe_status is returned
  *   and moe_last_error() describes the problem.
  * - Row-major layouts; [A,B] means A rows of B contiguous elements.
+ * - Numerics: weights are used exactly as stored. Activations meet them on
+ *   the gfx950 block-scaled matrix cores as a sum of 4 FP8 (E4M3) terms per
+ *   value with one E8M0 scale per 32 values and term (each value is carried
+ *   to within about 2^-16 of its block's largest magnitude); products
+ *   accumulate in float32. Router logits are accumulated in float64.
  * - Shape limits: 1 <= E <= 256, 1 <= k <= min(E, 8), H and F multiples of
  *   32 and at most 16384, 0 <= T, n_shared in {0, 1}. Decode additionally
  *   needs T <= 64 and H, F <= 8192. With T = 0 a call only validates the
@@ -79,17 +84,25 @@ typedef struct moe_shape {
 /* Byte layout of one packed expert blob. Offsets are from the blob start;
  * every plane is 256-byte aligned. Expert e of a packed set starts at
  * base + e * stride.
- *   gate_q [F, H/2]  up_q [F, H/2]  down_q [H, F/2]   E2M1 codes, element 2i
- *                                                     in the low nibble of byte i
- *   gate_s [F, H/32] up_s [F, H/32] down_s [H, F/32]  E8M0 scale bytes,
- *                                                     value 2^(b-127)
- *   gate_b [F]       up_b [F]       down_b [H]        float32 biases
- * The weight of gate row f, column h is E2M1(code) * 2^(gate_s[f][h/32]-127)
- * (MXFP4: blocks of 32 sharing one power-of-two scale; pages: ds4.c
- * `dsv4_e2m1fn_value_cpu`, `dsv4_fp4_act_quantize_row_inplace_cpu`;
+ *   gate_q, up_q (F x H weights), down_q (H x F)   E2M1 codes, 16 bytes per
+ *       32-value MX block, element 2i in the low nibble of byte i
+ *   gate_s, up_s, down_s                            one E8M0 scale byte per
+ *       block, value 2^(b-127)
+ *   gate_b [F], up_b [F], down_b [H]                float32 biases
+ * A code plane of R x K weights (R rows, K columns, both multiples of 32;
+ * nb = K / 32 blocks per row) is tiled for the matrix cores: block c of row
+ * r sits at byte
+ *     (r / 16) * 256 * nb + (c / 4) * 1024 + ((c % 4) * 16 + r % 16) * 16
+ * i.e. rows in tiles of 16, each tile in steps of four blocks (128 columns),
+ * a step storing its blocks one after the other, 16 rows each. Its scale
+ * byte sits at
+ *     (r / 16) * 16 * nb + (c / 4) * 64 + (c % 4) * 16 + r % 16.
+ * The weight of gate row f, column h is E2M1(code) * 2^(scale - 127) of block
+ * h / 32 of row f (MXFP4: blocks of 32 sharing one power-of-two scale;
+ * pages: ds4.c `dsv4_e2m1fn_value_cpu`, `dsv4_fp4_act_quantize_row_inplace_cpu`;
  * goosedump `validate_tensors`, Mxfp4 expert tensors with F32 biases).
- * Supported scale bytes: 2..252 (every E2M1 product is then a normal,
- * finite float32/bfloat16; outside that range results are unspecified). */
+ * Supported scale bytes: 2..252 (outside that range results are
+ * unspecified). moe_pack_experts writes this layout from row-major planes. */
 typedef struct moe_blob_layout {
     uint64_t gate_q, up_q, down_q;
     uint64_t gate_s, up_s, down_s;
@@ -98,9 +111,10 @@ typedef struct moe_blob_layout {
     uint64_t stride;  /* bytes rounded up to 4096 */
 } moe_blob_layout;
 
-/* Host-side planar MXFP4 weights of n experts, as produced by a quantiser:
- * gate_q/up_q [n, F, H/2], down_q [n, H, F/2]; gate_s/up_s [n, F, H/32],
- * down_s [n, H, F/32]; gate_b/up_b [n, F], down_b [n, H]. All host. */
+/* Host-side row-major MXFP4 weights of n experts, as produced by a
+ * quantiser: gate_q/up_q [n, F, H/2], down_q [n, H, F/2] (element 2i of a
+ * row in the low nibble of byte i); gate_s/up_s [n, F, H/32], down_s
+ * [n, H, F/32]; gate_b/up_b [n, F], down_b [n, H]. All host. */
 typedef struct moe_expert_planes {
     const uint8_t *gate_q, *up_q, *down_q;
     const uint8_t *gate_s, *up_s, *down_s;
@@ -132,8 +146,9 @@ typedef struct moe_route_out {
  * Returns MOE_OK or MOE_ERR_INVALID_ARG. */
 int moe_blob_layout_get(const moe_shape *shape, moe_blob_layout *layout);
 
-/* Pack n experts from planes into dst (host, n * layout.stride bytes,
- * padding zeroed). Host only; MOE_OK or MOE_ERR_INVALID_ARG. */
+/* Pack n experts from row-major planes into dst in the tiled blob layout
+ * (host, n * layout.stride bytes, padding zeroed). Host only; MOE_OK or
+ * MOE_ERR_INVALID_ARG. */
 int moe_pack_experts(const moe_shape *shape, int32_t n, const moe_expert_planes *planes,
                      uint8_t *dst);
 
@@ -156,7 +171,7 @@ int moe_route(const moe_shape *shape, const void *x, const float *norm_w,
               void *ws, size_t ws_bytes, hipStream_t stream);
 
 /* The whole block for a few tokens (T <= 64): streams only the k selected
- * experts' bytes per token with GEMV kernels.
+ * experts' bytes per token with GEMV kernels on the matrix cores.
  *   hidden   [T, H] float32 or bfloat16, device; it is also the residual
  *   experts  E packed blobs, layout.stride bytes apart, device
  *   shared   n_shared packed blobs (same layout) or NULL when n_shared == 0
@@ -184,10 +199,11 @@ int moe_forward_prefill(const moe_shape *shape, const void *hidden, const float 
 /* Export the weights the kernels compute with, for bit-exact checks.
  *   blob   one packed expert, device
  *   which  0 gate [F, H], 1 up [F, H], 2 down [H, F]
- *   path   0: the float32 decoding the GEMV (decode) kernels use;
- *          1: the bfloat16 decoding the matrix-core (prefill) kernels use,
- *             widened to float32
- *   out    float32 [rows, cols], device */
+ *   path   0: decoded with the gfx950 scaled FP4-to-float32 converts;
+ *          1: decoded with the scaled FP4-to-bfloat16 converts, widened;
+ *          2: decoded by the block-scaled matrix core, as every forward
+ *             kernel uses the weights (B operand one-hot 1.0)
+ *   out    float32 [rows, cols] row-major, device */
 int moe_dequant_debug(const moe_shape *shape, const uint8_t *blob, int32_t which, int32_t path,
                       float *out, hipStream_t stream);
 
@@ -200,7 +216,9 @@ typedef enum moe_kernel_id {
     MOE_KERNEL_DECODE_GATE_UP = 4,
     MOE_KERNEL_DECODE_DOWN = 5,
     MOE_KERNEL_GATE_UP_GEMM = 6,
-    MOE_KERNEL_DOWN_GEMM = 7
+    MOE_KERNEL_DOWN_GEMM = 7,
+    MOE_KERNEL_QUANTIZE = 8         /* FP8 terms of the expert input, when it is
+                                       its own kernel (T > 16) */
 } moe_kernel_id;
 
 /* Measurement hook (for benchmarks and profilers, not needed to compute):

@@ -99,16 +99,17 @@ struct Workspace {
     int32_t *idx;
     float *wts;
     int32_t *counts, *offsets, *mprefix, *perm, *inv, *rank;
-    float *act;
-    // decode on the block-scaled matrix cores (T <= 64 only): FP8 terms of
-    // the expert input and of the SwiGLU output
-    uint8_t *xq, *xs, *act_q;
+    // FP8 terms (codes, E8M0 scales) of the expert input [T] and of the
+    // SwiGLU output [T*k + T*n_shared] (route order in decode, position
+    // order in prefill)
+    uint8_t *xq, *xs, *act_q, *act_s;
     uint64_t bytes;
 };
 
 Workspace carve(const moe_shape *s, uint8_t *base) {
-    const uint64_t T = s->T, H = s->H, F = s->F, E = s->E, k = s->k, ns = s->n_shared;
+    const uint64_t T = s->T, H = s->H, E = s->E, k = s->k, ns = s->n_shared;
     const uint64_t R = T * k;
+    const uint64_t Hp = moe::pad128(s->H), Fp = moe::pad128(s->F);
     Workspace w{};
     uint64_t o = 0;
     auto take = [&](uint64_t bytes) {
@@ -129,15 +130,10 @@ Workspace carve(const moe_shape *s, uint8_t *base) {
     w.perm = reinterpret_cast<int32_t *>(take(R * 4));
     w.inv = reinterpret_cast<int32_t *>(take(R * 4));
     w.rank = reinterpret_cast<int32_t *>(take(R * 4));
-    w.act = reinterpret_cast<float *>(take((R + T * ns) * F * 4));
-    if (T <= 64) {
-        const uint64_t Hp = (H + 127) / 128 * 128, Fp = (F + 127) / 128 * 128;
-        w.xq = take(T * moe::kTerms * Hp);
-        w.xs = take(T * moe::kTerms * Hp / 32);
-        w.act_q = take((R + T * ns) * moe::kTerms * Fp);
-    } else {
-        w.xq = w.xs = w.act_q = nullptr;
-    }
+    w.xq = take(T * moe::kTerms * Hp);
+    w.xs = take(T * moe::kTerms * Hp / 32);
+    w.act_q = take((R + T * ns) * moe::kTerms * Fp);
+    w.act_s = take((R + T * ns) * moe::kTerms * Fp / 32);
     w.bytes = o;
     return w;
 }
@@ -218,48 +214,39 @@ int check_forward(const moe_shape *s, const void *hidden, const float *norm_w,
     return check_ws(s, ws, ws_bytes);
 }
 
-// RMSNorm (optional) and the router's partial logits; returns the
-// expert-input pointer. With `terms`, the router launch also quantises the
-// expert input into FP8 terms (decode on the matrix cores).
+// RMSNorm (optional), the router's partial logits and, with `terms`, the FP8
+// terms of the expert input (in the router's grid for small T, else their own
+// kernel).
 int route_front(const moe_shape *s, const void *x, const float *norm_w, const float *router_w,
-                const Workspace &w, bool terms, const void **expert_in, int *expert_in_bf16,
-                hipStream_t st) {
+                const Workspace &w, bool terms, hipStream_t st) {
     const int bf16 = s->act_dtype == MOE_BF16;
     const void *rin = x;
     int kind = bf16;
-    *expert_in = x;
-    *expert_in_bf16 = bf16;
+    const void *ein = x;
+    int ein_bf16 = bf16;
     if (norm_w) {
         MOE_TRY(launch(MOE_KERNEL_RMSNORM, "rmsnorm", st, [&] {
             return moe::launch_rmsnorm(x, bf16, norm_w, s->T, s->H, s->rms_eps, w.xn64, w.xn32, st);
         }));
         rin = w.xn64;
         kind = 2;
-        *expert_in = w.xn32;
-        *expert_in_bf16 = 0;
+        ein = w.xn32;
+        ein_bf16 = 0;
     }
-    const moe::TermsOut tq{*expert_in, *expert_in_bf16, w.xq, w.xs};
-    return launch(MOE_KERNEL_ROUTER, "router", st, [&] {
+    const moe::TermsOut tq{ein, ein_bf16, w.xq, w.xs};
+    const bool fused = terms && moe::router_quantizes(s->T);
+    MOE_TRY(launch(MOE_KERNEL_ROUTER, "router", st, [&] {
         return moe::launch_router(rin, kind, router_w, s->T, s->H, s->E, w.partial,
-                                  terms ? &tq : nullptr, st);
-    });
+                                  fused ? &tq : nullptr, st);
+    }));
+    if (terms && !fused)
+        MOE_TRY(launch(MOE_KERNEL_QUANTIZE, "quantize", st,
+                       [&] { return moe::launch_quantize(tq, s->T, s->H, st); }));
+    return MOE_OK;
 }
 
-// FP8-term exponent for the SwiGLU output: with alpha > 0, |g sigmoid(alpha g)|
-// <= max(L, 0.2785/alpha) for g <= L, and |clamp(u) + o| <= L + |o|, so
-// |a| < 2^(e0 + 8) for e0 = floor(log2(bound)) - 7. False when unbounded.
-bool act_exponent(const moe_shape *s, int *e0) {
-    const double a = s->swiglu_alpha, L = s->swiglu_limit, o = s->swiglu_up_offset;
-    if (!(a > 0.0)) return false;
-    const double bound = std::max(L, 0.2785 / a) * (L + std::fabs(o)) * 1.01;
-    if (!std::isfinite(bound) || !(bound > 0.0)) return false;
-    const int e = static_cast<int>(std::floor(std::log2(bound))) - 7;
-    if (e - 4 * (moe::kTerms - 1) < -126 || e > 120) return false;
-    *e0 = e;
-    return true;
-}
-
-int max_mtiles(const moe_shape *s) {
+// Upper bound on the grouped GEMMs' row tiles (the grid is sized by it).
+int max_tiles(const moe_shape *s) {
     const long long R = static_cast<long long>(s->T) * s->k;
     const long long bm = moe::kGemmBM;
     long long m = (R + bm - 1) / bm + (s->E < R ? s->E : R);
@@ -294,19 +281,28 @@ int moe_pack_experts(const moe_shape *shape, int32_t n, const moe_expert_planes 
     if (n > 0 && (!p->gate_q || !p->up_q || !p->down_q || !p->gate_s || !p->up_s || !p->down_s ||
                   !p->gate_b || !p->up_b || !p->down_b))
         return fail(MOE_ERR_INVALID_ARG, "every plane pointer must be non-NULL");
-    const uint64_t H = shape->H, F = shape->F;
+    const uint32_t H = shape->H, F = shape->F;
+    // one row-major code/scale plane (rows x K) into the tiled order
+    auto tile_plane = [](uint8_t *q_dst, uint8_t *s_dst, const uint8_t *q_src, const uint8_t *s_src,
+                         uint32_t rows, uint32_t K) {
+        const uint32_t nb = K / 32;
+        for (uint32_t r = 0; r < rows; ++r)
+            for (uint32_t c = 0; c < nb; ++c) {
+                std::memcpy(q_dst + moe::mx_code_offset(r, c, nb),
+                            q_src + static_cast<uint64_t>(r) * (K / 2) + 16ull * c, 16);
+                s_dst[moe::mx_scale_offset(r, c, nb)] = s_src[static_cast<uint64_t>(r) * nb + c];
+            }
+    };
+    const uint64_t fh = static_cast<uint64_t>(F) * H;
     for (int32_t i = 0; i < n; ++i) {
         uint8_t *b = dst + static_cast<uint64_t>(i) * L.stride;
         std::memset(b, 0, L.stride);
-        std::memcpy(b + L.gate_q, p->gate_q + i * F * H / 2, F * H / 2);
-        std::memcpy(b + L.up_q, p->up_q + i * F * H / 2, F * H / 2);
-        std::memcpy(b + L.down_q, p->down_q + i * H * F / 2, H * F / 2);
-        std::memcpy(b + L.gate_s, p->gate_s + i * F * H / 32, F * H / 32);
-        std::memcpy(b + L.up_s, p->up_s + i * F * H / 32, F * H / 32);
-        std::memcpy(b + L.down_s, p->down_s + i * H * F / 32, H * F / 32);
-        std::memcpy(b + L.gate_b, p->gate_b + i * F, F * 4);
-        std::memcpy(b + L.up_b, p->up_b + i * F, F * 4);
-        std::memcpy(b + L.down_b, p->down_b + i * H, H * 4);
+        tile_plane(b + L.gate_q, b + L.gate_s, p->gate_q + i * fh / 2, p->gate_s + i * fh / 32, F, H);
+        tile_plane(b + L.up_q, b + L.up_s, p->up_q + i * fh / 2, p->up_s + i * fh / 32, F, H);
+        tile_plane(b + L.down_q, b + L.down_s, p->down_q + i * fh / 2, p->down_s + i * fh / 32, H, F);
+        std::memcpy(b + L.gate_b, p->gate_b + static_cast<uint64_t>(i) * F, F * 4ull);
+        std::memcpy(b + L.up_b, p->up_b + static_cast<uint64_t>(i) * F, F * 4ull);
+        std::memcpy(b + L.down_b, p->down_b + static_cast<uint64_t>(i) * H, H * 4ull);
     }
     return ok();
 }
@@ -329,9 +325,7 @@ int moe_route(const moe_shape *s, const void *x, const float *norm_w, const floa
     MOE_TRY(check_ws(s, ws, ws_bytes));
     if (s->T == 0) return ok();
     const Workspace w = carve(s, static_cast<uint8_t *>(ws));
-    const void *ein;
-    int ein_bf16;
-    MOE_TRY(route_front(s, x, norm_w, router_w, w, false, &ein, &ein_bf16, st));
+    MOE_TRY(route_front(s, x, norm_w, router_w, w, false, st));
     MOE_TRY(launch(MOE_KERNEL_TOPK, "topk", st, [&] {
         return moe::launch_topk(w.partial, w.splits, router_b, s->T, s->E, s->k, s->route_scale,
                                 w.idx, w.wts, out->topk_idx, out->topk_w, nullptr, 0, s->H,
@@ -353,45 +347,27 @@ int moe_forward_decode(const moe_shape *s, const void *hidden, const float *norm
         return fail(MOE_ERR_UNSUPPORTED, "decode takes H, F <= 8192");
     if (s->T == 0) return ok();
     const Workspace w = carve(s, static_cast<uint8_t *>(ws));
-    const void *ein;
-    int ein_bf16;
-    int act_e0 = 0;
-    const bool mx = moe::mx_steps_per_wave(s->H) > 0 && moe::mx_steps_per_wave(s->F) > 0 &&
-                    act_exponent(s, &act_e0);
-    MOE_TRY(route_front(s, hidden, norm_w, router_w, w, mx, &ein, &ein_bf16, st));
+    MOE_TRY(route_front(s, hidden, norm_w, router_w, w, true, st));
     const moe::ExpertPtrs ex = expert_ptrs(s, experts);
     const moe::ExpertPtrs sh = expert_ptrs(s, shared);
     const moe::SwigluConsts c{s->swiglu_alpha, s->swiglu_limit, s->swiglu_up_offset};
-    const int rbf = s->act_dtype == MOE_BF16;
-    int32_t *oidx = ro ? ro->topk_idx : nullptr;
-    float *ow = ro ? ro->topk_w : nullptr;
-    if (mx) {
-        MOE_TRY(launch(MOE_KERNEL_DECODE_GATE_UP, "decode_gate_up", st, [&] {
-            return moe::launch_decode_gate_up_mx(w.xq, w.xs, w.partial, w.splits, router_b, s->T,
-                                                 s->H, s->F, s->E, s->k, s->n_shared,
-                                                 s->route_scale, ex, sh, c, act_e0, w.idx, w.wts,
-                                                 oidx, ow, hidden, rbf, out, w.act_q, st);
-        }));
-        MOE_TRY(launch(MOE_KERNEL_DECODE_DOWN, "decode_down", st, [&] {
-            return moe::launch_decode_down_mx(w.act_q, act_e0, s->T, s->H, s->F, s->k,
-                                              s->n_shared, ex, sh, w.idx, w.wts, out, st);
-        }));
-    } else {
-        MOE_TRY(launch(MOE_KERNEL_DECODE_GATE_UP, "decode_gate_up", st, [&] {
-            return moe::launch_decode_gate_up(ein, ein_bf16, w.partial, w.splits, router_b, s->T,
-                                              s->H, s->F, s->E, s->k, s->n_shared, s->route_scale,
-                                              ex, sh, c, w.idx, w.wts, oidx, ow, hidden, rbf, out,
-                                              w.act, st);
-        }));
-        MOE_TRY(launch(MOE_KERNEL_DECODE_DOWN, "decode_down", st, [&] {
-            return moe::launch_decode_down(s->T, s->H, s->F, s->k, s->n_shared, ex, sh, w.idx,
-                                           w.wts, w.act, out, st);
-        }));
-    }
+    MOE_TRY(launch(MOE_KERNEL_DECODE_GATE_UP, "decode_gate_up", st, [&] {
+        return moe::launch_decode_gate_up(w.xq, w.xs, w.partial, w.splits, router_b, s->T, s->H,
+                                          s->F, s->E, s->k, s->n_shared, s->route_scale, ex, sh, c,
+                                          w.idx, w.wts, ro ? ro->topk_idx : nullptr,
+                                          ro ? ro->topk_w : nullptr, hidden,
+                                          s->act_dtype == MOE_BF16, out, w.act_q, w.act_s, st);
+    }));
+    MOE_TRY(launch(MOE_KERNEL_DECODE_DOWN, "decode_down", st, [&] {
+        return moe::launch_decode_down(w.act_q, w.act_s, s->T, s->H, s->F, s->k, s->n_shared,
+                                       w.idx, w.wts, ex, sh, out, st);
+    }));
     if (ro && (ro->counts || ro->offsets || ro->perm || ro->inv))
-        MOE_TRY(launch(MOE_KERNEL_PERMUTE, "permute", st, [&] { return moe::launch_permute(w.idx, s->T, s->E, s->k, 0, w.counts, w.offsets,
-                                              w.perm, w.inv, w.rank, w.mprefix, ro->counts,
-                                              ro->offsets, ro->perm, ro->inv, st); }));
+        MOE_TRY(launch(MOE_KERNEL_PERMUTE, "permute", st, [&] {
+            return moe::launch_permute(w.idx, s->T, s->E, s->k, 0, w.counts, w.offsets, w.perm,
+                                       w.inv, w.rank, w.mprefix, ro->counts, ro->offsets,
+                                       ro->perm, ro->inv, st);
+        }));
     return ok();
 }
 
@@ -402,29 +378,32 @@ int moe_forward_prefill(const moe_shape *s, const void *hidden, const float *nor
     MOE_TRY(check_forward(s, hidden, norm_w, router_w, router_b, experts, shared, out, ws, ws_bytes));
     if (s->T == 0) return ok();
     const Workspace w = carve(s, static_cast<uint8_t *>(ws));
-    const void *ein;
-    int ein_bf16;
-    MOE_TRY(route_front(s, hidden, norm_w, router_w, w, false, &ein, &ein_bf16, st));
+    MOE_TRY(route_front(s, hidden, norm_w, router_w, w, true, st));
     MOE_TRY(launch(MOE_KERNEL_TOPK, "topk", st, [&] {
         return moe::launch_topk(w.partial, w.splits, router_b, s->T, s->E, s->k, s->route_scale,
                                 w.idx, w.wts, ro ? ro->topk_idx : nullptr,
                                 ro ? ro->topk_w : nullptr, hidden, s->act_dtype == MOE_BF16,
                                 s->H, out, st);
     }));
-    MOE_TRY(launch(MOE_KERNEL_PERMUTE, "permute", st, [&] { return moe::launch_permute(w.idx, s->T, s->E, s->k, s->n_shared, w.counts,
-                                          w.offsets, w.perm, w.inv, w.rank, w.mprefix,
-                                          ro ? ro->counts : nullptr, ro ? ro->offsets : nullptr,
-                                          ro ? ro->perm : nullptr, ro ? ro->inv : nullptr, st); }));
+    MOE_TRY(launch(MOE_KERNEL_PERMUTE, "permute", st, [&] {
+        return moe::launch_permute(w.idx, s->T, s->E, s->k, s->n_shared, w.counts, w.offsets,
+                                   w.perm, w.inv, w.rank, w.mprefix, ro ? ro->counts : nullptr,
+                                   ro ? ro->offsets : nullptr, ro ? ro->perm : nullptr,
+                                   ro ? ro->inv : nullptr, st);
+    }));
     const moe::ExpertPtrs ex = expert_ptrs(s, experts);
     const moe::ExpertPtrs sh = expert_ptrs(s, shared);
     const moe::SwigluConsts c{s->swiglu_alpha, s->swiglu_limit, s->swiglu_up_offset};
-    const int mt = max_mtiles(s);
-    MOE_TRY(launch(MOE_KERNEL_GATE_UP_GEMM, "gate_up_gemm", st, [&] { return moe::launch_gate_up_gemm(ein, ein_bf16, s->T, s->H, s->F, s->E, s->k,
-                                               s->n_shared, ex, sh, c, w.offsets, w.perm,
-                                               w.mprefix, mt, w.act, st); }));
-    MOE_TRY(launch(MOE_KERNEL_DOWN_GEMM, "down_gemm", st, [&] { return moe::launch_down_gemm(s->T, s->H, s->F, s->E, s->k, s->n_shared, ex, sh,
-                                            w.offsets, w.perm, w.wts, w.mprefix, mt, w.act, out,
-                                            st); }));
+    const int mt = max_tiles(s);
+    MOE_TRY(launch(MOE_KERNEL_GATE_UP_GEMM, "gate_up_gemm", st, [&] {
+        return moe::launch_gate_up_gemm(w.xq, w.xs, s->T, s->H, s->F, s->E, s->k, s->n_shared, ex,
+                                        sh, c, w.offsets, w.perm, w.mprefix, mt, w.act_q, w.act_s,
+                                        st);
+    }));
+    MOE_TRY(launch(MOE_KERNEL_DOWN_GEMM, "down_gemm", st, [&] {
+        return moe::launch_down_gemm(w.act_q, w.act_s, s->T, s->H, s->F, s->E, s->k, s->n_shared,
+                                     ex, sh, w.offsets, w.perm, w.wts, w.mprefix, mt, out, st);
+    }));
     return ok();
 }
 
@@ -435,7 +414,7 @@ int moe_dequant_debug(const moe_shape *s, const uint8_t *blob, int32_t which, in
     if (!blob || !out) return fail(MOE_ERR_INVALID_ARG, "blob and out must be non-NULL");
     if (!aligned(blob, 256)) return fail(MOE_ERR_INVALID_ARG, "blob must be 256-byte aligned");
     if (which < 0 || which > 2) return fail(MOE_ERR_INVALID_ARG, "which must be 0, 1 or 2");
-    if (path < 0 || path > 1) return fail(MOE_ERR_INVALID_ARG, "path must be 0 or 1");
+    if (path < 0 || path > 2) return fail(MOE_ERR_INVALID_ARG, "path must be 0, 1 or 2");
     const int rows = which == 2 ? s->H : s->F;
     const int K = which == 2 ? s->F : s->H;
     const uint8_t *q = blob + (which == 0 ? L.gate_q : which == 1 ? L.up_q : L.down_q);
@@ -449,7 +428,7 @@ int moe_profile_next_launch(int32_t kernel, hipEvent_t start, hipEvent_t stop) {
         g_hook = ProfileHook{};
         return ok();
     }
-    if (kernel > MOE_KERNEL_DOWN_GEMM || !start || !stop)
+    if (kernel > MOE_KERNEL_QUANTIZE || !start || !stop)
         return fail(MOE_ERR_INVALID_ARG, "unknown kernel id %d or NULL event", kernel);
     g_hook.kernel = kernel;
     g_hook.start = start;

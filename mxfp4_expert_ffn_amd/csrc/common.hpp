@@ -81,16 +81,38 @@ __device__ __forceinline__ float wave_sum(float v) {
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
+// float64 through the 32-bit DPP / readlane paths, one half at a time.
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v) {
+    const uint64_t b = static_cast<uint64_t>(__double_as_longlong(v));
+    const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(b), CTRL, 0xf, 0xf, false));
+    const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(b >> 32), CTRL, 0xf, 0xf, false));
+    return __longlong_as_double(static_cast<long long>((static_cast<uint64_t>(hi) << 32) | lo));
+}
+
+__device__ __forceinline__ double readlane_f64(double v, int lane) {
+    const uint64_t b = static_cast<uint64_t>(__double_as_longlong(v));
+    const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(b), lane));
+    const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(b >> 32), lane));
+    return __longlong_as_double(static_cast<long long>((static_cast<uint64_t>(hi) << 32) | lo));
+}
+
+// Sum over the 64 lanes in a fixed order (rows of 16 by DPP, then the four
+// row sums), the same in every lane. All lanes must be active.
 __device__ __forceinline__ double wave_sum_f64(double v) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
-    return v;
+    v += dpp_f64<0xB1>(v);   // quad_perm [1,0,3,2]
+    v += dpp_f64<0x4E>(v);   // quad_perm [2,3,0,1]
+    v += dpp_f64<0x141>(v);  // row_half_mirror
+    v += dpp_f64<0x140>(v);  // row_mirror
+    return (readlane_f64(v, 0) + readlane_f64(v, 16)) + (readlane_f64(v, 32) + readlane_f64(v, 48));
 }
 
 __device__ __forceinline__ double wave_max_f64(double v) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v = fmax(v, __shfl_xor(v, off, kWave));
-    return v;
+    v = fmax(v, dpp_f64<0xB1>(v));
+    v = fmax(v, dpp_f64<0x4E>(v));
+    v = fmax(v, dpp_f64<0x141>(v));
+    v = fmax(v, dpp_f64<0x140>(v));
+    return fmax(fmax(readlane_f64(v, 0), readlane_f64(v, 16)), fmax(readlane_f64(v, 32), readlane_f64(v, 48)));
 }
 
 // ---------------------------------------------------------------- SwiGLU
@@ -234,19 +256,34 @@ __device__ __forceinline__ float e4m3_decode(uint32_t c) {
 // 2^e as float32 for e in [-126, 127].
 __device__ __forceinline__ float pow2f(int e) { return __uint_as_float(static_cast<uint32_t>(e + 127) << 23); }
 
+// Maximum over each half-wavefront (lanes 0..31 and 32..63) of a value that
+// is >= 0, returned to every lane of that half: DPP within rows of 16 lanes,
+// then the two rows of a half combined through readlanes.
+__device__ __forceinline__ float half_wave_max(float v) {
+    v = fmaxf(v, __builtin_amdgcn_update_dpp(0.0f, v, 0xB1, 0xf, 0xf, false));   // quad_perm [1,0,3,2]
+    v = fmaxf(v, __builtin_amdgcn_update_dpp(0.0f, v, 0x4E, 0xf, 0xf, false));   // quad_perm [2,3,0,1]
+    v = fmaxf(v, __builtin_amdgcn_update_dpp(0.0f, v, 0x141, 0xf, 0xf, false));  // row_half_mirror
+    v = fmaxf(v, __builtin_amdgcn_update_dpp(0.0f, v, 0x140, 0xf, 0xf, false));  // row_mirror
+    const int b = __float_as_int(v);
+    const float r0 = __int_as_float(__builtin_amdgcn_readlane(b, 0));
+    const float r1 = __int_as_float(__builtin_amdgcn_readlane(b, 16));
+    const float r2 = __int_as_float(__builtin_amdgcn_readlane(b, 32));
+    const float r3 = __int_as_float(__builtin_amdgcn_readlane(b, 48));
+    return (threadIdx.x & 32) ? fmaxf(r2, r3) : fmaxf(r0, r1);
+}
+
 // Split the 32 values held by the 32 lanes of a half-wavefront into kTerms
 // E4M3 codes with one E8M0 scale byte per term (scale 2^(floor(log2 amax)-7)
 // of what is left, so codes stay below 256). Returns the codes packed in one
-// dword (term n in byte n) and the scale bytes likewise.
+// dword (term n in byte n) and the scale bytes likewise. Every lane of the
+// wavefront must take part.
 __device__ __forceinline__ void fp8_terms_group(float v, uint32_t &codes, uint32_t &scales) {
     codes = 0;
     scales = 0;
     float r = v;
 #pragma unroll
     for (int n = 0; n < kTerms; ++n) {
-        float amax = fabsf(r);
-#pragma unroll
-        for (int off = 16; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 32));
+        const float amax = half_wave_max(fabsf(r));
         int e = static_cast<int>((__float_as_uint(amax) >> 23) & 0xffu) - 127 - 7;
         e = e < -126 ? -126 : (e > 127 ? 127 : e);
         const uint32_t q = e4m3_encode(r * pow2f(-e));
@@ -254,21 +291,6 @@ __device__ __forceinline__ void fp8_terms_group(float v, uint32_t &codes, uint32
         codes |= q << (8 * n);
         scales |= static_cast<uint32_t>(e + 127) << (8 * n);
     }
-}
-
-// Same split with fixed per-term exponents e0 - 4n (a value range known in
-// advance, |v| < 2^(e0 + 8)); codes only.
-__device__ __forceinline__ uint32_t fp8_terms_fixed(float v, int e0) {
-    uint32_t codes = 0;
-    float r = v;
-#pragma unroll
-    for (int n = 0; n < kTerms; ++n) {
-        const int e = e0 - 4 * n;
-        const uint32_t q = e4m3_encode(r * pow2f(-e));
-        r -= e4m3_decode(q) * pow2f(e);
-        codes |= q << (8 * n);
-    }
-    return codes;
 }
 
 }  // namespace moe

@@ -12,13 +12,35 @@ constexpr int kMaxK = 8;   // experts per token
 constexpr int kMaxE = 256; // routed experts
 constexpr int kTerms = 4;  // FP8 terms per activation on the block-scaled matrix cores
 
-// Tile geometry of the grouped GEMMs (rows of one expert per tile, weight rows
-// per workgroup), shared by the permutation's tile prefix and the launches.
+// Grouped GEMMs: routed rows of one expert per tile (4 groups of 4 rows, one
+// group per matrix-core B operand of 4 rows x kTerms terms), 4 wavefronts per
+// workgroup; the permutation's tile prefix uses the same row count.
 constexpr int kGemmBM = 32;
-constexpr int kGateUpBN = 256;   // features per gate/up workgroup (4 waves x 2 x 32)
-constexpr int kDownBN = 512;     // hidden rows per down workgroup (4 waves x 4 x 32)
-constexpr int kDecodeRowsGU = 16; // expert rows per decode gate/up workgroup
-constexpr int kDecodeRowsDn = 16; // hidden rows per decode down workgroup
+constexpr int kGemmWaves = 4;
+constexpr int kGateUpRowsWG = 128;  // gate/up: 32 feature rows (gate and up) per wavefront
+constexpr int kDownRowsWG = 256;    // down: 64 hidden rows per wavefront
+// Decode GEMVs: 32 weight rows per workgroup, K split over 8 wavefronts.
+constexpr int kDecodeRows = 32;
+constexpr int kDecodeWaves = 8;
+
+// Packed MXFP4 plane of `rows` x K weights (rows and K multiples of 32), as
+// laid out in an expert blob: rows in tiles of 16, K in steps of 128 (four
+// 32-value MX blocks); inside a (tile, step) the 16-byte code blocks run
+// block-major then row, so the 64 lanes of a wavefront, lane = 16 * block +
+// row, read one contiguous kilobyte, which is also the A operand of the
+// block-scaled 16x16x128 matrix-core instruction. Scale bytes follow the same
+// order, one byte per code block. A ragged last step holds only its blocks.
+__host__ __device__ constexpr uint64_t mx_code_offset(uint32_t row, uint32_t blk, uint32_t nblk) {
+    return static_cast<uint64_t>(row >> 4) * (256ull * nblk) + static_cast<uint64_t>(blk >> 2) * 1024ull +
+           static_cast<uint64_t>(((blk & 3u) << 4) | (row & 15u)) * 16ull;
+}
+__host__ __device__ constexpr uint64_t mx_scale_offset(uint32_t row, uint32_t blk, uint32_t nblk) {
+    return static_cast<uint64_t>(row >> 4) * (16ull * nblk) + static_cast<uint64_t>(blk >> 2) * 64ull +
+           (((blk & 3u) << 4) | (row & 15u));
+}
+
+// K padded to whole 128-wide steps (the FP8-term rows of activations).
+__host__ __device__ constexpr int pad128(int k) { return (k + 127) / 128 * 128; }
 
 // Events attached to the next kernel dispatch (the library's timing hook):
 // hipExtLaunchKernel stamps them with that kernel's own start and end. Null
@@ -60,8 +82,10 @@ struct RouterPlan {
     int splits;  // S
 };
 RouterPlan router_plan(int T, int H, int E);
-// FP8-term quantisation of the expert input riding with the GEMV router:
-// q [T][kTerms][Kp] codes, scales [T][kTerms][Kp/32], Kp = H rounded up to 128.
+// FP8-term quantisation of the expert input (every forward): q
+// [T][kTerms][Kp] E4M3 codes, scales [T][kTerms][Kp/32] E8M0 bytes, Kp =
+// pad128(H), zero codes past H. It rides in the GEMV router's grid, or runs as
+// its own kernel beside the tiled router.
 struct TermsOut {
     const void *in;
     int in_bf16;
@@ -69,8 +93,12 @@ struct TermsOut {
     uint8_t *scales;
 };
 // in_kind: 0 float32, 1 bf16 bits, 2 float64
+// `terms` is honoured only where router_quantizes(T); otherwise it must be
+// NULL and launch_quantize does that work.
 hipError_t launch_router(const void *x, int in_kind, const float *w, int T, int H, int E,
                          double *partial, const TermsOut *terms, hipStream_t s);
+bool router_quantizes(int T);  // true when launch_router's grid also quantises
+hipError_t launch_quantize(const TermsOut &terms, int T, int H, hipStream_t s);
 hipError_t launch_topk(const double *partial, int S, const float *bias, int T, int E, int k,
                        float route_scale, int32_t *idx, float *wts, int32_t *out_idx, float *out_w,
                        const void *resid, int resid_bf16, int H, float *out, hipStream_t s);
@@ -80,43 +108,41 @@ hipError_t launch_permute(const int32_t *idx, int T, int E, int k, int n_shared,
                           int32_t *out_offsets, int32_t *out_perm, int32_t *out_inv,
                           hipStream_t s);
 
-// decode ------------------------------------------------------------------
-hipError_t launch_decode_gate_up(const void *x, int x_bf16, const double *partial, int S,
+// decode (T <= 64) -----------------------------------------------------------
+// Route r < T*k is slot r % k of token r / k; r >= T*k is the shared expert of
+// token r - T*k. act_q / act_s: FP8 terms of the SwiGLU output per route,
+// [routes][kTerms][pad128(F)] codes and [routes][kTerms][pad128(F)/32] scales.
+// gate/up also selects each token's experts (top-k of the router's partial
+// logits, written to idx / wts and the optional exports) and seeds out with
+// the residual.
+hipError_t launch_decode_gate_up(const uint8_t *xq, const uint8_t *xs, const double *partial, int S,
                                  const float *router_b, int T, int H, int F, int E, int k,
                                  int n_shared, float route_scale, const ExpertPtrs &ex,
                                  const ExpertPtrs &sh, SwigluConsts c, int32_t *idx, float *wts,
-                                 int32_t *out_idx, float *out_w, const void *resid,
-                                 int resid_bf16, float *out, float *act, hipStream_t s);
-hipError_t launch_decode_down(int T, int H, int F, int k, int n_shared, const ExpertPtrs &ex,
-                              const ExpertPtrs &sh, const int32_t *idx, const float *wts,
-                              const float *act, float *out, hipStream_t s);
+                                 int32_t *out_idx, float *out_w, const void *resid, int resid_bf16,
+                                 float *out, uint8_t *act_q, uint8_t *act_s, hipStream_t s);
+hipError_t launch_decode_down(const uint8_t *act_q, const uint8_t *act_s, int T, int H, int F,
+                              int k, int n_shared, const int32_t *idx, const float *wts,
+                              const ExpertPtrs &ex, const ExpertPtrs &sh, float *out,
+                              hipStream_t s);
 
-// decode on the block-scaled matrix cores: K-steps per wavefront for a
-// K-wide GEMV (0 when K is too large for this form)
-int mx_steps_per_wave(int K);
-hipError_t launch_decode_gate_up_mx(const uint8_t *xq, const uint8_t *xs, const double *partial,
-                                    int S, const float *router_b, int T, int H, int F, int E, int k,
-                                    int n_shared, float route_scale, const ExpertPtrs &ex,
-                                    const ExpertPtrs &sh, SwigluConsts c, int act_e0,
-                                    int32_t *idx, float *wts, int32_t *out_idx, float *out_w,
-                                    const void *resid, int resid_bf16, float *out, uint8_t *act_q,
-                                    hipStream_t s);
-hipError_t launch_decode_down_mx(const uint8_t *act_q, int act_e0, int T, int H, int F, int k,
-                                 int n_shared, const ExpertPtrs &ex, const ExpertPtrs &sh,
-                                 const int32_t *idx, const float *wts, float *out, hipStream_t s);
-
-// prefill -----------------------------------------------------------------
-hipError_t launch_gate_up_gemm(const void *x, int x_bf16, int T, int H, int F, int E, int k,
-                               int n_shared, const ExpertPtrs &ex, const ExpertPtrs &sh,
+// prefill (any T) -------------------------------------------------------------
+// Rows in expert order: position p < T*k is route perm[p]; p >= T*k is the
+// shared expert of token p - T*k. act_q / act_s are indexed by p.
+hipError_t launch_gate_up_gemm(const uint8_t *xq, const uint8_t *xs, int T, int H, int F, int E,
+                               int k, int n_shared, const ExpertPtrs &ex, const ExpertPtrs &sh,
                                SwigluConsts c, const int32_t *offsets, const int32_t *perm,
-                               const int32_t *mprefix, int max_mtiles, float *act,
-                               hipStream_t s);
-hipError_t launch_down_gemm(int T, int H, int F, int E, int k, int n_shared, const ExpertPtrs &ex,
-                            const ExpertPtrs &sh, const int32_t *offsets, const int32_t *perm,
-                            const float *wts, const int32_t *mprefix, int max_mtiles,
-                            const float *act, float *out, hipStream_t s);
+                               const int32_t *mprefix, int max_tiles, uint8_t *act_q,
+                               uint8_t *act_s, hipStream_t s);
+hipError_t launch_down_gemm(const uint8_t *act_q, const uint8_t *act_s, int T, int H, int F, int E,
+                            int k, int n_shared, const ExpertPtrs &ex, const ExpertPtrs &sh,
+                            const int32_t *offsets, const int32_t *perm, const float *wts,
+                            const int32_t *mprefix, int max_tiles, float *out, hipStream_t s);
 
 // debug -------------------------------------------------------------------
+// Decoded weights of one packed plane as float32 [rows][K]: path 0 through
+// the scaled FP4 converts, path 1 through the bfloat16 converts, path 2
+// through the block-scaled matrix core (one-hot FP8 operand B).
 hipError_t launch_dequant(const uint8_t *codes, const uint8_t *scales, int rows, int K, int path,
                           float *out, hipStream_t s);
 

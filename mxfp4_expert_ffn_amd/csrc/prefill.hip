@@ -1,375 +1,300 @@
-// Prefill path: grouped GEMMs over the expert-sorted rows on the CDNA4 matrix
-// cores (v_mfma_f32_32x32x16_bf16).
+// Prefill: grouped GEMMs over the routed rows in expert order, on the
+// block-scaled matrix cores (MXFP4 weights as operand A, FP8-term activations
+// as operand B).
 //
-// Page: goosedump `gpt_oss.rs` `expert_batch_output`: per active expert, the
-// routed rows are gathered, multiplied by the gate/up pair, biased, passed
-// through the clamped SwiGLU, multiplied by down, biased, and scaled by the
-// route weight; `mix_expert_outputs` sums each token's routes.
+// A work item is (weight-row block, tile of up to 32 rows of one expert). Its
+// workgroup of 4 wavefronts streams the weight rows once per tile, each
+// wavefront its own rows (4 A fragments per 128-wide step, read as contiguous
+// kilobytes from the tiled plane), while the tile's 32 rows x kTerms terms
+// are staged per step through LDS (double-buffered) and shared by the 4
+// wavefronts: 8 B fragments, 32 matrix-core instructions per wavefront per
+// step. Items are dealt so that the tiles of one expert and row block run
+// back to back on one accelerator die and share its L2.
 //
-// Operands. MXFP4 weights are exact in bfloat16. Float32 activations are split
-// as x = hi + lo (two bfloat16), so each product takes two MFMAs sharing the
-// decoded weight tile and keeps float32-level accuracy; bfloat16 inputs need
-// only the hi term.
+// gate/up: 32 features per wavefront for both matrices, epilogue adds the
+// biases, applies the clamped SwiGLU and writes the FP8 terms of each
+// 32-feature block per row (the down GEMM's operand). down: 64 hidden rows per
+// wavefront, epilogue adds the bias and scatter-adds route weight x result
+// into out[token] (which holds the residual).
 //
-// K order. A 32x32x16 MFMA has lane l supply 8 consecutive k values for row
-// (or column) l%32 from k-group l/32. Any permutation of k applied to both
-// operands leaves the sum unchanged, so in a 64-wide k step lane group g takes
-// MX block (2s + g) and the four MFMAs j = 0..3 walk its 32 elements 8 at a
-// time. One 128-bit load per lane is then exactly one MX block (16 code bytes
-// and one scale), decoded in registers: no LDS round trip for the weights.
-// The activation tile (32 rows x 64 k) is staged in LDS as bfloat16 hi/lo and
-// read back in the same permuted order.
-//
-// Tiles. The permutation kernel leaves mprefix[g] = number of 32-row tiles of
-// groups < g. Tiles are numbered group-major, then by weight tile, then by row
-// tile, and dealt so that each XCD sweeps a contiguous range: consecutive
-// workgroups on one L2 share an expert's weight tile and its rows.
-#include "common.hpp"
-#include "kernels.hpp"
+// Page: goosedump `gpt_oss.rs`, `mixture_of_experts` and its grouped form over
+// expert-sorted rows; DeepSeek-V4 shared expert (ungated, weight 1).
+#include "mx_mfma.hpp"
 
 namespace moe {
 
 namespace {
 
-constexpr int kBM = kGemmBM;
-constexpr int kTiles = 4;  // B tiles (32 weight rows each) per wavefront
-constexpr int kDepth = 2;  // K steps (64 wide) of loads kept in flight per thread
+constexpr int kRowGroups = kGemmBM / 4;         // B operands per step (4 rows each)
+constexpr int kBRowBytes = 128 + 16;            // one (row, term) step in LDS, padded
+constexpr int kBBufBytes = kGemmBM * kTerms * kBRowBytes;
+constexpr int kThreads = kGemmWaves * 64;
+static_assert(kGemmBM * kTerms * 128 / 16 == 4 * kThreads, "B staging: 4 x 16 bytes per thread");
+static_assert(kGemmBM * kTerms == 128, "B scale staging: one dword per thread of the first 128");
 
-struct TileInfo {
-    int g, nt, row0, rows;
+struct Tile {
+    int g;   // group: expert, or E for the shared expert
+    int p0;  // first row position
+    int n;   // rows in the tile (1..32)
 };
 
-// Tile -> (group, weight tile, row range). The M-tile prefix is first copied
-// to LDS (one round of loads), then binary-searched there.
-__device__ __forceinline__ TileInfo find_tile(int tile, int NT, int G, const int32_t *mprefix,
-                                              const int32_t *offsets, int *s_pre) {
-    for (int i = threadIdx.x; i <= G; i += blockDim.x) s_pre[i] = mprefix[i];
-    __syncthreads();
-    int lo = 0, hi = G - 1;  // largest g with s_pre[g] * NT <= tile
+// Work item of this workgroup, dealt XCD-major (items i and i+1 run back to
+// back on one die); false when it is past the real tiles.
+__device__ __forceinline__ bool find_item(int max_tiles, int nrb, const int32_t *offsets,
+                                          const int *s_pre, int G, int &rb, Tile &tl) {
+    const int per = gridDim.x / kXcds;
+    const int item = (blockIdx.x % kXcds) * per + blockIdx.x / kXcds;
+    rb = item / max_tiles;
+    const int tile = item - rb * max_tiles;
+    if (rb >= nrb || tile >= s_pre[G]) return false;
+    int lo = 0, hi = G - 1;  // last group whose first tile is <= tile
     while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
-        if (s_pre[mid] * NT <= tile) lo = mid;
+        if (s_pre[mid] <= tile) lo = mid;
         else hi = mid - 1;
     }
-    TileInfo ti;
-    ti.g = lo;
-    const int mt_g = s_pre[lo + 1] - s_pre[lo];
-    const int local = tile - s_pre[lo] * NT;
-    ti.nt = local / mt_g;
-    const int mt = local - ti.nt * mt_g;
-    ti.row0 = offsets[lo] + mt * kBM;
-    ti.rows = min(kBM, offsets[lo + 1] - ti.row0);
-    return ti;
+    tl.g = lo;
+    tl.p0 = offsets[lo] + (tile - s_pre[lo]) * kGemmBM;
+    tl.n = min(kGemmBM, offsets[lo + 1] - tl.p0);
+    return true;
 }
 
-// Staged activation tile: [buffer][hi, lo][32 rows][64 bf16]. Each 128-byte
-// row holds eight 16-byte chunks stored at chunk ^ (row & 7), so the MFMA
-// operand reads (32 rows at one logical chunk) and the staging writes (one
-// row, eight chunks) both touch every LDS bank once per 8 lanes.
-typedef __bf16 ATile[2][2][kBM][64];
+// Main loop: acc[j][rg] += A fragment j x B row group rg over all K-steps.
+// brow: per tile row, the FP8-term row index in bq / bs (row stride kTerms).
+template <int NA>
+__device__ __forceinline__ void gemm_mainloop(const uint8_t *const (&aq)[NA],
+                                              const uint8_t *const (&as)[NA], const int (&atile)[NA],
+                                              int nblk, int NS, const uint8_t *bq, const uint8_t *bs,
+                                              int Kb, const int *s_brow, uint8_t *sB, uint32_t *sBs,
+                                              f32x4_t (&acc)[NA][kRowGroups]) {
+    const int tid = threadIdx.x, lane = tid & 63;
+    // this thread's staging sources: 4 x 16 bytes of codes, one scale dword
+    const uint8_t *src[4];
+    int dst[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int q = tid + kThreads * i;
+        const int row = q >> 5, term = (q >> 3) & 3, chunk = q & 7;
+        src[i] = bq + (static_cast<size_t>(s_brow[row]) * kTerms + term) * Kb + 16 * chunk;
+        dst[i] = (row * kTerms + term) * kBRowBytes + 16 * chunk;
+    }
+    const bool sc_on = tid < kGemmBM * kTerms;
+    const int srow = sc_on ? tid >> 2 : 0, sterm = tid & 3;
+    const uint32_t *ssrc = reinterpret_cast<const uint32_t *>(
+        bs + (static_cast<size_t>(s_brow[srow]) * kTerms + sterm) * (Kb / 32));
 
-__device__ __forceinline__ int swz(int row, int chunk) { return ((chunk ^ (row & 7)) << 3); }
+    uint4 st[4];
+    uint32_t sts = 0;
+    AFrag an[NA];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) st[i] = *reinterpret_cast<const uint4 *>(src[i]);
+    if (sc_on) sts = ssrc[0];
+#pragma unroll
+    for (int j = 0; j < NA; ++j) an[j] = load_afrag(aq[j], as[j], atile[j], 0, nblk, lane);
 
-// Activation staging: 256 threads, thread -> row tid/8, 16-byte chunk tid%8
-// (8 consecutive k). Loads are unconditional (invalid rows or k read row 0,
-// column 0) and validity is applied when the registers are written to LDS,
-// so loads stay in flight.
-template <bool BF16>
-struct AStage {
-    float4 f[2];
-    uint4 b;
-    bool ok;
-    __device__ __forceinline__ void load(const void *src, int ld, int srow, int col, int K) {
-        ok = srow >= 0 && col < K;
-        const size_t off = ok ? static_cast<size_t>(srow) * ld + col : 0;
-        if constexpr (BF16) {
-            b = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(src) + off);
-        } else {
-            const float4 *p = reinterpret_cast<const float4 *>(static_cast<const float *>(src) + off);
-            f[0] = p[0];
-            f[1] = p[1];
+    const int bn = lane & 15, bh = lane >> 4;
+    const int brd = ((4 * 0 + (bn >> 2)) * kTerms + (bn & 3)) * kBRowBytes + 16 * bh;  // + group offset
+    for (int s = 0; s < NS; ++s) {
+        uint8_t *buf = sB + (s & 1) * kBBufBytes;
+        uint32_t *sbuf = sBs + (s & 1) * (kGemmBM * kTerms);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4 *>(buf + dst[i]) = st[i];
+        if (sc_on) sbuf[tid] = sts;
+        AFrag a[NA];
+#pragma unroll
+        for (int j = 0; j < NA; ++j) a[j] = an[j];
+        if (s + 1 < NS) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                st[i] = *reinterpret_cast<const uint4 *>(src[i] + 128 * (s + 1));
+            if (sc_on) sts = ssrc[s + 1];
+#pragma unroll
+            for (int j = 0; j < NA; ++j) an[j] = load_afrag(aq[j], as[j], atile[j], s + 1, nblk, lane);
         }
-    }
-    __device__ __forceinline__ void store(ATile &sa, int buf, int row, int chunk) const {
-        __bf16 *hi = &sa[buf][0][row][swz(row, chunk)];
-        __bf16 *lo = &sa[buf][1][row][swz(row, chunk)];
-        if constexpr (BF16) {
-            *reinterpret_cast<uint4 *>(hi) = ok ? b : make_uint4(0, 0, 0, 0);
-        } else {
-            const float v[8] = {f[0].x, f[0].y, f[0].z, f[0].w, f[1].x, f[1].y, f[1].z, f[1].w};
-            bf16x8_t h, l;
+        __syncthreads();
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                __bf16 a, c;
-                split_bf16(ok ? v[i] : 0.f, a, c);
-                h[i] = a;
-                l[i] = c;
-            }
-            *reinterpret_cast<bf16x8_t *>(hi) = h;
-            *reinterpret_cast<bf16x8_t *>(lo) = l;
-        }
-    }
-};
-
-// One MX block (16 code bytes + scale) of a K-wide row. Unconditional: a
-// block past the end of K reads the row's last block (finite weights), which
-// meets zero activations.
-__device__ __forceinline__ void load_mx(const uint8_t *q, const uint8_t *sc, int row, int K, int kb,
-                                        uint4 &code, uint32_t &scale) {
-    const int b = min(kb, K / 32 - 1);
-    code = *reinterpret_cast<const uint4 *>(q + static_cast<size_t>(row) * (K / 2) + 16 * b);
-    scale = sc[static_cast<size_t>(row) * (K / 32) + b];
-}
-
-__device__ __forceinline__ uint32_t dword(const uint4 &q, int j) {
-    return j == 0 ? q.x : j == 1 ? q.y : j == 2 ? q.z : q.w;
-}
-
-// B tiles of one wavefront: tile i is the 32 weight rows row[i] (one per lane
-// l%32) of the MXFP4 plane (q[i], sc[i]) with K-wide rows; on[i] is uniform.
-struct BTiles {
-    const uint8_t *q[kTiles];
-    const uint8_t *sc[kTiles];
-    int row[kTiles];
-    bool on[kTiles];
-};
-
-// Shared main loop: 32 activation rows (staged from `src`, rows s_src[m], a
-// row-major [*, K] matrix of float32 or bfloat16) times kTiles MXFP4 weight
-// tiles per wavefront. Global loads run kDepth steps ahead through a register
-// ring; the activation tile is double-buffered in LDS, one barrier per step.
-template <bool BF16>
-__device__ __forceinline__ void mx_gemm_mainloop(const void *src, int K, const int *s_src,
-                                                 ATile &sa, BTiles bt, f32x16_t (&acc)[kTiles]) {
-    const int lane = threadIdx.x & 63;
-    const int gsel = lane >> 5, l32 = lane & 31;
-    const int arow = threadIdx.x >> 3, achunk = threadIdx.x & 7;
-    const int asrc = s_src[arow];
-    const int nsteps = (K + 63) / 64;
+        for (int rg = 0; rg < kRowGroups; ++rg) {
+            const int off = brd + rg * 4 * kTerms * kBRowBytes;
+            const uint4 blo = *reinterpret_cast<const uint4 *>(buf + off);
+            const uint4 bhi = *reinterpret_cast<const uint4 *>(buf + off + 64);
+            const uint32_t bsc = (sbuf[(4 * rg + (bn >> 2)) * kTerms + (bn & 3)] >> (8 * bh)) & 0xffu;
 #pragma unroll
-    for (int i = 0; i < kTiles; ++i)
-        if (!bt.on[i]) bt.row[i] = 0;  // disabled tiles load row 0: loads stay unconditional
-    AStage<BF16> ast[kDepth];
-    uint4 bq[kDepth][kTiles];
-    uint32_t bs[kDepth][kTiles];
-#pragma unroll
-    for (int d = 0; d < kDepth; ++d) {
-        const int sd = min(d, nsteps - 1);
-        ast[d].load(src, K, asrc, 64 * sd + 8 * achunk, K);
-#pragma unroll
-        for (int i = 0; i < kTiles; ++i) load_mx(bt.q[i], bt.sc[i], bt.row[i], K, 2 * sd + gsel, bq[d][i], bs[d][i]);
-    }
-    for (int s0 = 0; s0 < nsteps; s0 += kDepth) {
-#pragma unroll
-        for (int d = 0; d < kDepth; ++d) {
-            const int s = s0 + d;
-            if (s < nsteps) {
-                const int buf = s & 1;
-                ast[d].store(sa, buf, arow, achunk);
-                uint4 w[kTiles];
-                float f[kTiles];
-#pragma unroll
-                for (int i = 0; i < kTiles; ++i) {
-                    w[i] = bq[d][i];
-                    f[i] = e8m0_scale(bs[d][i]);
-                }
-                __syncthreads();
-                {
-                    // refill the slot unconditionally (the last kDepth steps
-                    // reload step nsteps-1; those values are never used)
-                    const int sn = min(s + kDepth, nsteps - 1);
-                    ast[d].load(src, K, asrc, 64 * sn + 8 * achunk, K);
-#pragma unroll
-                    for (int i = 0; i < kTiles; ++i)
-                        load_mx(bt.q[i], bt.sc[i], bt.row[i], K, 2 * sn + gsel, bq[d][i], bs[d][i]);
-                }
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int off = swz(l32, gsel * 4 + j);
-                    const bf16x8_t ah = *reinterpret_cast<const bf16x8_t *>(&sa[buf][0][l32][off]);
-                    bf16x8_t al;
-                    if constexpr (!BF16) al = *reinterpret_cast<const bf16x8_t *>(&sa[buf][1][l32][off]);
-#pragma unroll
-                    for (int i = 0; i < kTiles; ++i) {
-                        if (bt.on[i]) {
-                            const bf16x8_t bw = fp4x8_to_bf16(dword(w[i], j), f[i]);
-                            acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bw, acc[i], 0, 0, 0);
-                            if constexpr (!BF16)
-                                acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, bw, acc[i], 0, 0, 0);
-                        }
-                    }
-                }
-            }
+            for (int j = 0; j < NA; ++j) acc[j][rg] = mx_mfma(a[j], blo, bhi, bsc, acc[j][rg]);
         }
     }
 }
 
-// ---------------------------------------------------------------- gate/up
-// Workgroup tile: 32 rows of one expert x kGateUpBN = 256 features (4 waves x
-// 2 subtiles of 32), gate and up each; epilogue adds the biases, applies the
-// clamped SwiGLU and stores the float32 activation row of each route.
-template <bool BF16>
-__global__ __launch_bounds__(256) void gate_up_gemm_kernel(
-    const void *x, int T, int H, int F, int E, int n_shared, int k, ExpertPtrs ex,
-    ExpertPtrs sh, SwigluConsts sc, const int32_t *offsets, const int32_t *perm,
-    const int32_t *mprefix, float *act) {
-    static_assert(kGateUpBN == 4 * 2 * 32, "gate/up tile: 4 waves x 2 subtiles x 32 features");
-    const int G = E + n_shared;
-    const int NT = (F + kGateUpBN - 1) / kGateUpBN;
-    int tile;
-    if (!xcd_tile(blockIdx.x, mprefix[G] * NT, tile)) return;
+__device__ __forceinline__ void load_pre(const int32_t *mprefix, int G, int *s_pre) {
+    for (int i = threadIdx.x; i <= G; i += blockDim.x) s_pre[i] = mprefix[i];
+    __syncthreads();
+}
+
+// gate/up: grid = kXcds-rounded (pad128(F) / 128) x max_tiles items.
+__global__ __launch_bounds__(kThreads) void gate_up_gemm_kernel(
+    const uint8_t *xq, const uint8_t *xs, int T, int H, int F, int E, int k, int n_shared,
+    ExpertPtrs ex, ExpertPtrs sh, SwigluConsts sc, const int32_t *offsets, const int32_t *perm,
+    const int32_t *mprefix, int max_tiles, uint8_t *act_q, uint8_t *act_s) {
     __shared__ int s_pre[kMaxE + 2];
-    const TileInfo ti = find_tile(tile, NT, G, mprefix, offsets, s_pre);
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const int gsel = lane >> 5, l32 = lane & 31;
-    const uint8_t *blob = ti.g < E ? ex.base + static_cast<size_t>(ti.g) * ex.stride : sh.base;
-
-    __shared__ int s_src[kBM];
-    __shared__ __align__(16) ATile s_a;
-    if (threadIdx.x < kBM) {
-        const int m = threadIdx.x;
-        int src = -1;
-        if (m < ti.rows) {
-            const int p = ti.row0 + m;
-            src = ti.g < E ? perm[p] / k : p - offsets[E];
-        }
-        s_src[m] = src;
+    __shared__ int s_brow[kGemmBM];
+    __shared__ __align__(16) uint8_t sB[2 * kBBufBytes];
+    __shared__ uint32_t sBs[2 * kGemmBM * kTerms];
+    __shared__ float sAct[kGemmWaves][kGemmBM][33];
+    const int G = E + n_shared, R = T * k;
+    load_pre(mprefix, G, s_pre);
+    const int Fp = pad128(F), nrb = Fp / kGateUpRowsWG;
+    int rb;
+    Tile tl;
+    if (!find_item(max_tiles, nrb, offsets, s_pre, G, rb, tl)) return;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    if (tid < kGemmBM) {
+        const int p = tl.p0 + min(tid, tl.n - 1);
+        s_brow[tid] = p < R ? perm[p] / k : p - R;  // the token (x row)
     }
     __syncthreads();
+    const uint8_t *blob = tl.g < E ? ex.base + static_cast<size_t>(tl.g) * ex.stride : sh.base;
+    const int f0 = rb * kGateUpRowsWG + 32 * w;  // this wavefront's 32 features
+    const int last_tile = F / 16 - 1;
+    const uint8_t *const aq[4] = {blob + ex.gate_q, blob + ex.gate_q, blob + ex.up_q, blob + ex.up_q};
+    const uint8_t *const as[4] = {blob + ex.gate_s, blob + ex.gate_s, blob + ex.up_s, blob + ex.up_s};
+    const int t0 = min(f0 / 16, last_tile), t1 = min(f0 / 16 + 1, last_tile);
+    const int atile[4] = {t0, t1, t0, t1};
+    f32x4_t acc[4][kRowGroups];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int rg = 0; rg < kRowGroups; ++rg) acc[j][rg] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    const int Kp = pad128(H);
+    gemm_mainloop<4>(aq, as, atile, H / 32, Kp / 128, xq, xs, Kp, s_brow, sB, sBs, acc);
 
-    const int base = ti.nt * kGateUpBN + 64 * w;
-    const int n0 = base + l32, n1 = base + 32 + l32;  // features of the two subtiles
-    BTiles bt;
-    bt.q[0] = blob + ex.gate_q; bt.sc[0] = blob + ex.gate_s; bt.row[0] = n0; bt.on[0] = base < F;
-    bt.q[1] = blob + ex.up_q;   bt.sc[1] = blob + ex.up_s;   bt.row[1] = n0; bt.on[1] = base < F;
-    bt.q[2] = blob + ex.gate_q; bt.sc[2] = blob + ex.gate_s; bt.row[2] = n1; bt.on[2] = base + 32 < F;
-    bt.q[3] = blob + ex.up_q;   bt.sc[3] = blob + ex.up_s;   bt.row[3] = n1; bt.on[3] = base + 32 < F;
-    f32x16_t acc[kTiles];
+    // epilogue: SwiGLU into LDS, then one 32-feature block per row to FP8 terms
+    const bool live = f0 < F;  // F % 32 == 0: a wavefront is all features or all padding
+    if (live) {
+        const float *gb = reinterpret_cast<const float *>(blob + ex.gate_b);
+        const float *ub = reinterpret_cast<const float *>(blob + ex.up_b);
+        const int rq = (lane & 15) >> 2;
 #pragma unroll
-    for (int i = 0; i < kTiles; ++i) acc[i] = f32x16_t{};
-    mx_gemm_mainloop<BF16>(x, H, s_src, s_a, bt, acc);
-    const float *gb = reinterpret_cast<const float *>(blob + ex.gate_b);
-    const float *ub = reinterpret_cast<const float *>(blob + ex.up_b);
+        for (int j = 0; j < 2; ++j)
 #pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
-        if (!bt.on[2 * sub]) continue;
-        const int n = sub == 0 ? n0 : n1;
-        const float bgate = gb[n], bup = ub[n];
+            for (int v = 0; v < 4; ++v) {
+                const int fl = 16 * j + 4 * (lane >> 4) + v;
+                const float bg = gb[f0 + fl], bu = ub[f0 + fl];
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            const int m = 8 * (v >> 2) + 4 * gsel + (v & 3);
-            if (m < ti.rows)
-                act[static_cast<size_t>(ti.row0 + m) * F + n] =
-                    swiglu(acc[2 * sub][v] + bgate, acc[2 * sub + 1][v] + bup, sc.alpha, sc.limit,
-                           sc.up_offset);
+                for (int rg = 0; rg < kRowGroups; ++rg) {
+                    // the quad sums run on every lane (DPP reads its neighbours)
+                    const float g = quad_sum(acc[j][rg][v]), u = quad_sum(acc[2 + j][rg][v]);
+                    if ((lane & 3) == 0)
+                        sAct[w][4 * rg + rq][fl] = swiglu(g + bg, u + bu, sc.alpha, sc.limit, sc.up_offset);
+                }
+            }
+    }
+    __syncthreads();
+    const int half = lane >> 5, i = lane & 31, nbp = Fp / 32;
+    for (int r0 = 0; r0 < kGemmBM; r0 += 2) {
+        const int row = r0 + half;
+        uint32_t codes = 0, scales = 0x7f7f7f7fu;
+        if (live) fp8_terms_group(sAct[w][row][i], codes, scales);
+        if (row < tl.n) {
+            const size_t p = static_cast<size_t>(tl.p0 + row);
+#pragma unroll
+            for (int n = 0; n < kTerms; ++n) {
+                act_q[(p * kTerms + n) * Fp + f0 + i] = static_cast<uint8_t>(codes >> (8 * n));
+                if (i == 0) act_s[(p * kTerms + n) * nbp + f0 / 32] = static_cast<uint8_t>(scales >> (8 * n));
+            }
         }
     }
 }
 
-// ---------------------------------------------------------------- down
-// Workgroup tile: 32 rows of one expert x kDownBN = 512 hidden units (4 waves
-// x 4 subtiles of 32); epilogue adds the down bias, multiplies by the route
-// weight and adds into the token's output row (which holds the residual).
-__global__ __launch_bounds__(256) void down_gemm_kernel(
-    int T, int H, int F, int E, int n_shared, int k, ExpertPtrs ex, ExpertPtrs sh,
-    const int32_t *offsets, const int32_t *perm, const float *wts, const int32_t *mprefix,
-    const float *act, float *out) {
-    static_assert(kDownBN == 4 * kTiles * 32, "down tile: 4 waves x kTiles subtiles x 32 rows");
-    const int G = E + n_shared;
-    const int NT = (H + kDownBN - 1) / kDownBN;
-    int tile;
-    if (!xcd_tile(blockIdx.x, mprefix[G] * NT, tile)) return;
+// down: grid = kXcds-rounded ceil(H / 256) x max_tiles items.
+__global__ __launch_bounds__(kThreads) void down_gemm_kernel(
+    const uint8_t *act_q, const uint8_t *act_s, int T, int H, int F, int E, int k, int n_shared,
+    ExpertPtrs ex, ExpertPtrs sh, const int32_t *offsets, const int32_t *perm, const float *wts,
+    const int32_t *mprefix, int max_tiles, float *out) {
     __shared__ int s_pre[kMaxE + 2];
-    const TileInfo ti = find_tile(tile, NT, G, mprefix, offsets, s_pre);
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const int gsel = lane >> 5, l32 = lane & 31;
-    const uint8_t *blob = ti.g < E ? ex.base + static_cast<size_t>(ti.g) * ex.stride : sh.base;
-
-    __shared__ int s_src[kBM];
-    __shared__ int s_tok[kBM];
-    __shared__ float s_wt[kBM];
-    __shared__ __align__(16) ATile s_a;
-    if (threadIdx.x < kBM) {
-        const int m = threadIdx.x;
-        int src = -1, tok = 0;
-        float wt = 0.f;
-        if (m < ti.rows) {
-            const int p = ti.row0 + m;
-            src = p;
-            if (ti.g < E) {
-                const int r = perm[p];
-                tok = r / k;
-                wt = wts[r];
-            } else {
-                tok = p - offsets[E];
-                wt = 1.0f;
-            }
+    __shared__ int s_brow[kGemmBM];
+    __shared__ int s_tok[kGemmBM];
+    __shared__ float s_wt[kGemmBM];
+    __shared__ __align__(16) uint8_t sB[2 * kBBufBytes];
+    __shared__ uint32_t sBs[2 * kGemmBM * kTerms];
+    const int G = E + n_shared, R = T * k;
+    load_pre(mprefix, G, s_pre);
+    const int nrb = (H + kDownRowsWG - 1) / kDownRowsWG;
+    int rb;
+    Tile tl;
+    if (!find_item(max_tiles, nrb, offsets, s_pre, G, rb, tl)) return;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    if (tid < kGemmBM) {
+        const int p = tl.p0 + min(tid, tl.n - 1);
+        s_brow[tid] = p;  // activation rows are in position order
+        if (p < R) {
+            const int route = perm[p];
+            s_tok[tid] = route / k;
+            s_wt[tid] = wts[route];
+        } else {
+            s_tok[tid] = p - R;
+            s_wt[tid] = 1.0f;
         }
-        s_src[m] = src;
-        s_tok[m] = tok;
-        s_wt[m] = wt;
     }
     __syncthreads();
+    const uint8_t *blob = tl.g < E ? ex.base + static_cast<size_t>(tl.g) * ex.stride : sh.base;
+    const int h0 = rb * kDownRowsWG + 64 * w;  // this wavefront's 64 hidden rows
+    const int last_tile = H / 16 - 1;
+    const uint8_t *const aq[4] = {blob + ex.down_q, blob + ex.down_q, blob + ex.down_q, blob + ex.down_q};
+    const uint8_t *const as[4] = {blob + ex.down_s, blob + ex.down_s, blob + ex.down_s, blob + ex.down_s};
+    const int atile[4] = {min(h0 / 16, last_tile), min(h0 / 16 + 1, last_tile),
+                          min(h0 / 16 + 2, last_tile), min(h0 / 16 + 3, last_tile)};
+    f32x4_t acc[4][kRowGroups];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int rg = 0; rg < kRowGroups; ++rg) acc[j][rg] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    const int Fp = pad128(F);
+    gemm_mainloop<4>(aq, as, atile, F / 32, Fp / 128, act_q, act_s, Fp, s_brow, sB, sBs, acc);
 
-    BTiles bt;
-#pragma unroll
-    for (int i = 0; i < kTiles; ++i) {
-        const int base = ti.nt * kDownBN + (w * kTiles + i) * 32;
-        bt.q[i] = blob + ex.down_q;
-        bt.sc[i] = blob + ex.down_s;
-        bt.row[i] = base + l32;
-        bt.on[i] = base < H;
-    }
-    f32x16_t acc[kTiles];
-#pragma unroll
-    for (int i = 0; i < kTiles; ++i) acc[i] = f32x16_t{};
-    mx_gemm_mainloop<false>(act, F, s_src, s_a, bt, acc);
     const float *db = reinterpret_cast<const float *>(blob + ex.down_b);
+    const int rq = (lane & 15) >> 2;
 #pragma unroll
-    for (int i = 0; i < kTiles; ++i) {
-        if (!bt.on[i]) continue;
-        const int hr = ti.nt * kDownBN + (w * kTiles + i) * 32 + l32;
-        const float bias = db[hr];
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            const int m = 8 * (v >> 2) + 4 * gsel + (v & 3);
-            if (m < ti.rows)
-                unsafeAtomicAdd(out + static_cast<size_t>(s_tok[m]) * H + hr,
-                                s_wt[m] * (acc[i][v] + bias));
+        for (int v = 0; v < 4; ++v) {
+            const int h = h0 + 16 * j + 4 * (lane >> 4) + v;
+            const float bias = h < H ? db[h] : 0.f;
+#pragma unroll
+            for (int rg = 0; rg < kRowGroups; ++rg) {
+                const float y = quad_sum(acc[j][rg][v]);
+                const int row = 4 * rg + rq;
+                if ((lane & 3) == 0 && h < H && row < tl.n)
+                    unsafeAtomicAdd(out + static_cast<size_t>(s_tok[row]) * H + h, s_wt[row] * (y + bias));
+            }
         }
-    }
+}
+
+int items(int nrb, int max_tiles) {
+    const long long n = static_cast<long long>(nrb) * max_tiles;
+    return static_cast<int>((n + kXcds - 1) / kXcds * kXcds);
 }
 
 }  // namespace
 
-hipError_t launch_gate_up_gemm(const void *x, int x_bf16, int T, int H, int F, int E, int k,
-                               int n_shared, const ExpertPtrs &ex, const ExpertPtrs &sh,
+hipError_t launch_gate_up_gemm(const uint8_t *xq, const uint8_t *xs, int T, int H, int F, int E,
+                               int k, int n_shared, const ExpertPtrs &ex, const ExpertPtrs &sh,
                                SwigluConsts c, const int32_t *offsets, const int32_t *perm,
-                               const int32_t *mprefix, int max_mtiles, float *act,
-                               hipStream_t s) {
-    const int NT = (F + kGateUpBN - 1) / kGateUpBN;
-    const long long tiles = static_cast<long long>(max_mtiles) * NT;
-    const int grid = static_cast<int>((tiles + kXcds - 1) / kXcds * kXcds);
+                               const int32_t *mprefix, int max_tiles, uint8_t *act_q,
+                               uint8_t *act_s, hipStream_t s) {
+    const int grid = items(pad128(F) / kGateUpRowsWG, max_tiles);
     if (grid == 0) return hipSuccess;
-    if (x_bf16)
-        launch_kernel(gate_up_gemm_kernel<true>, grid, 256, s, x, T, H, F, E, n_shared, k, ex, sh,
-                      c, offsets, perm, mprefix, act);
-    else
-        launch_kernel(gate_up_gemm_kernel<false>, grid, 256, s, x, T, H, F, E, n_shared, k, ex, sh,
-                      c, offsets, perm, mprefix, act);
+    launch_kernel(gate_up_gemm_kernel, grid, kThreads, s, xq, xs, T, H, F, E, k, n_shared, ex, sh,
+                  c, offsets, perm, mprefix, max_tiles, act_q, act_s);
     return hipGetLastError();
 }
 
-hipError_t launch_down_gemm(int T, int H, int F, int E, int k, int n_shared, const ExpertPtrs &ex,
-                            const ExpertPtrs &sh, const int32_t *offsets, const int32_t *perm,
-                            const float *wts, const int32_t *mprefix, int max_mtiles,
-                            const float *act, float *out, hipStream_t s) {
-    const int NT = (H + kDownBN - 1) / kDownBN;
-    const long long tiles = static_cast<long long>(max_mtiles) * NT;
-    const int grid = static_cast<int>((tiles + kXcds - 1) / kXcds * kXcds);
+hipError_t launch_down_gemm(const uint8_t *act_q, const uint8_t *act_s, int T, int H, int F, int E,
+                            int k, int n_shared, const ExpertPtrs &ex, const ExpertPtrs &sh,
+                            const int32_t *offsets, const int32_t *perm, const float *wts,
+                            const int32_t *mprefix, int max_tiles, float *out, hipStream_t s) {
+    const int grid = items((H + kDownRowsWG - 1) / kDownRowsWG, max_tiles);
     if (grid == 0) return hipSuccess;
-    launch_kernel(down_gemm_kernel, grid, 256, s, T, H, F, E, n_shared, k, ex, sh, offsets, perm,
-                  wts, mprefix, act, out);
+    launch_kernel(down_gemm_kernel, grid, kThreads, s, act_q, act_s, T, H, F, E, k, n_shared, ex, sh,
+                  offsets, perm, wts, mprefix, max_tiles, out);
     return hipGetLastError();
 }
 

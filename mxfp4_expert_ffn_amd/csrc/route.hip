@@ -381,11 +381,7 @@ hipError_t launch_router(const void *x, int in_kind, const float *w, int T, int 
             launch_kernel(router_gemv_kernel<2>, grid, 256, s, x, w, T, H, E, partial, rwgs, qin,
                           qbf, Kp, xq, xs);
     } else {
-        if (terms) {
-            const int Kp = 128 * ((H + 127) / 128);
-            launch_kernel(quantize_terms_kernel, (T * (Kp / 32) + 7) / 8, 256, s, terms->in,
-                          terms->in_bf16, T, H, Kp, terms->q, terms->scales);
-        }
+        if (terms) return hipErrorInvalidValue;  // see router_quantizes
         const dim3 grid((T + 31) / 32, (E + 63) / 64, p.splits);
         if (in_kind == 0)
             launch_kernel(router_tiled_kernel<0>, grid, 256, s, x, w, T, H, E, p.slice, partial);
@@ -394,6 +390,15 @@ hipError_t launch_router(const void *x, int in_kind, const float *w, int T, int 
         else
             launch_kernel(router_tiled_kernel<2>, grid, 256, s, x, w, T, H, E, p.slice, partial);
     }
+    return hipGetLastError();
+}
+
+bool router_quantizes(int T) { return T <= kRouterGemvMaxT; }
+
+hipError_t launch_quantize(const TermsOut &terms, int T, int H, hipStream_t s) {
+    const int Kp = pad128(H);
+    launch_kernel(quantize_terms_kernel, (T * (Kp / 32) + 7) / 8, 256, s, terms.in, terms.in_bf16,
+                  T, H, Kp, terms.q, terms.scales);
     return hipGetLastError();
 }
 

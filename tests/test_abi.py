@@ -63,6 +63,35 @@ def test_blob_layout_offsets_and_sizes():
     assert mx.moe_blob_layout_get(_shape(H=4096, F=2048))["bytes"] == 13402112
 
 
+def _tiled(codes, scales):
+    """Row-major codes [rows, K/2] and scales [rows, K/32] laid out in the
+    blob's tiled order, written from the header's offset formulas."""
+    rows, nb = scales.shape
+    q = np.zeros(rows * nb * 16, np.uint8)
+    s = np.zeros(rows * nb, np.uint8)
+    for r in range(rows):
+        for c in range(nb):
+            qo = (r // 16) * 256 * nb + (c // 4) * 1024 + ((c % 4) * 16 + r % 16) * 16
+            q[qo:qo + 16] = codes[r, 16 * c:16 * c + 16]
+            s[(r // 16) * 16 * nb + (c // 4) * 64 + (c % 4) * 16 + r % 16] = scales[r, c]
+    return q, s
+
+
+def test_tiled_order_puts_a_wavefront_load_in_one_kilobyte():
+    # the 64 lanes (block g = lane // 16, row = lane % 16) of a 128-wide step
+    # read 64 distinct 16-byte blocks covering one contiguous kilobyte
+    codes = np.arange(32 * 256 // 2, dtype=np.int64).reshape(32, 128).astype(np.uint8)
+    scales = np.arange(32 * 8, dtype=np.int64).reshape(32, 8).astype(np.uint8)
+    q, s = _tiled(codes, scales)
+    for tile in range(2):
+        for step in range(2):
+            base = tile * 256 * 8 + step * 1024
+            for lane in range(64):
+                r, c = 16 * tile + lane % 16, 4 * step + lane // 16
+                assert np.array_equal(q[base + 16 * lane:base + 16 * lane + 16], codes[r, 16 * c:16 * c + 16])
+                assert s[tile * 16 * 8 + step * 64 + lane] == scales[r, c]
+
+
 def test_pack_places_every_plane():
     cfg = scaled(config_by_id(1), E=3)
     layer = make_layer(cfg)
@@ -77,11 +106,10 @@ def test_pack_places_every_plane():
 
         def plane(name, n):
             return b[L[name]:L[name] + n]
-        assert np.array_equal(plane("gate_q", F * H // 2), ex.gate_codes[e].ravel())
-        assert np.array_equal(plane("up_q", F * H // 2), ex.up_codes[e].ravel())
-        assert np.array_equal(plane("down_q", H * F // 2), ex.down_codes[e].ravel())
-        assert np.array_equal(plane("gate_s", F * H // 32), ex.gate_scales[e].ravel())
-        assert np.array_equal(plane("down_s", H * F // 32), ex.down_scales[e].ravel())
+        for m in ("gate", "up", "down"):
+            q, sc = _tiled(getattr(ex, f"{m}_codes")[e], getattr(ex, f"{m}_scales")[e])
+            assert np.array_equal(plane(f"{m}_q", F * H // 2), q), m
+            assert np.array_equal(plane(f"{m}_s", F * H // 32), sc), m
         assert np.array_equal(plane("up_b", 4 * F).view(np.float32), ex.up_bias[e])
         assert np.array_equal(plane("down_b", 4 * H).view(np.float32), ex.down_bias[e])
         assert not b[L["bytes"]:].any()
@@ -90,8 +118,9 @@ def test_pack_places_every_plane():
 def test_workspace_bytes():
     assert mx.moe_workspace_bytes(_shape()) > 0
     big = mx.moe_workspace_bytes(_shape(T=2048, H=4096, F=2048, E=256, k=6, n_shared=1))
-    act = (2048 * 6 + 2048) * 2048 * 4
-    assert act < big < act + 2048 * 4096 * 12 + 16 * 2048 * 256 * 8 + (1 << 22)
+    # FP8 terms of the SwiGLU output (4 codes + scales per value) dominate
+    act = (2048 * 6 + 2048) * 2048 * 4 * 33 // 32
+    assert act < big < act + 2048 * 4096 * (12 + 5) + 16 * 2048 * 256 * 8 + (1 << 22)
     with pytest.raises(mx.MoeError):
         mx.moe_workspace_bytes(_shape(k=9))
 
@@ -157,5 +186,5 @@ def test_dequant_debug_rejects_bad_arguments():
     lib = _lib.load()
     s = _shape()
     assert lib.moe_dequant_debug(ctypes.byref(s), FAKE, 3, 0, FAKE, None) == _lib.MOE_ERR_INVALID_ARG
-    assert lib.moe_dequant_debug(ctypes.byref(s), FAKE, 0, 2, FAKE, None) == _lib.MOE_ERR_INVALID_ARG
+    assert lib.moe_dequant_debug(ctypes.byref(s), FAKE, 0, 3, FAKE, None) == _lib.MOE_ERR_INVALID_ARG
     assert lib.moe_dequant_debug(ctypes.byref(s), FAKE + 8, 0, 0, FAKE, None) == _lib.MOE_ERR_INVALID_ARG
