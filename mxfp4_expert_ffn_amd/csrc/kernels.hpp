@@ -12,10 +12,10 @@ constexpr int kMaxK = 8;   // experts per token
 constexpr int kMaxE = 256; // routed experts
 constexpr int kTerms = 4;  // FP8 terms per activation on the block-scaled matrix cores
 
-// Grouped GEMMs: routed rows of one expert per tile (4 groups of 4 rows, one
+// Grouped GEMMs: routed rows of one expert per tile (groups of 4 rows, one
 // group per matrix-core B operand of 4 rows x kTerms terms), 4 wavefronts per
 // workgroup; the permutation's tile prefix uses the same row count.
-constexpr int kGemmBM = 32;
+constexpr int kGemmBM = 16;
 constexpr int kGemmWaves = 4;
 constexpr int kGateUpRowsWG = 128;  // gate/up: 32 feature rows (gate and up) per wavefront
 constexpr int kDownRowsWG = 256;    // down: 64 hidden rows per wavefront

@@ -51,6 +51,39 @@ __device__ __forceinline__ AFrag load_afrag(const uint8_t *codes, const uint8_t 
     return a;
 }
 
+// Per-lane byte offsets of A fragments inside a 16-row tile: step s of a
+// tile starting at (uniform) code base cb and scale base sb reads cb +
+// code(s) and sb + scale(s). Only the last step can be ragged; there the lanes
+// past the plane's blocks re-read its last block (their B operand is zero).
+struct ALane {
+    uint32_t q, sc;          // step 0
+    uint32_t q_last, s_last;  // step ns - 1
+    int ns;
+    __device__ __forceinline__ ALane(int nblk, int lane) {
+        ns = (nblk + 3) >> 2;
+        const int g = lane >> 4, r = lane & 15;
+        q = static_cast<uint32_t>((16 * g + r) * 16);
+        sc = static_cast<uint32_t>(16 * g + r);
+        const int gl = min(g, nblk - 1 - 4 * (ns - 1));
+        q_last = static_cast<uint32_t>((ns - 1) * 1024 + (16 * gl + r) * 16);
+        s_last = static_cast<uint32_t>((ns - 1) * 64 + 16 * gl + r);
+    }
+    __device__ __forceinline__ uint32_t code(int s) const { return s >= ns - 1 ? q_last : q + 1024u * s; }
+    __device__ __forceinline__ uint32_t scale(int s) const { return s >= ns - 1 ? s_last : sc + 64u * s; }
+};
+
+// Byte offset of 16-row tile `tile` in a code / scale plane with nblk blocks per row.
+__device__ __forceinline__ uint64_t tile_code_base(int tile, int nblk) { return static_cast<uint64_t>(tile) * 256u * nblk; }
+__device__ __forceinline__ uint64_t tile_scale_base(int tile, int nblk) { return static_cast<uint64_t>(tile) * 16u * nblk; }
+
+// A fragment of step s (clamped to the last step) of the tile at cb / sb.
+__device__ __forceinline__ AFrag load_afrag(const uint8_t *cb, const uint8_t *sb, const ALane &al, int s) {
+    AFrag a;
+    a.q = *reinterpret_cast<const uint4 *>(cb + al.code(s));
+    a.s = sb[al.scale(s)];
+    return a;
+}
+
 // B operand from one FP8-term row (codes `q`, scales `sc`, natural k order,
 // zero past the true K) for lane k-group h.
 __device__ __forceinline__ BFrag load_bfrag(const uint8_t *q, const uint8_t *sc, int step, int h) {

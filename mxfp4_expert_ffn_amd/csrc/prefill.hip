@@ -2,13 +2,13 @@
 // block-scaled matrix cores (MXFP4 weights as operand A, FP8-term activations
 // as operand B).
 //
-// A work item is (weight-row block, tile of up to 32 rows of one expert). Its
+// A work item is (weight-row block, tile of up to kGemmBM rows of one expert). Its
 // workgroup of 4 wavefronts streams the weight rows once per tile, each
 // wavefront its own rows (4 A fragments per 128-wide step, read as contiguous
-// kilobytes from the tiled plane), while the tile's 32 rows x kTerms terms
-// are staged per step through LDS (double-buffered) and shared by the 4
-// wavefronts: 8 B fragments, 32 matrix-core instructions per wavefront per
-// step. Items are dealt so that the tiles of one expert and row block run
+// kilobytes from the tiled plane, kRing steps ahead), while the tile's rows x
+// kTerms terms are staged per step through LDS (double-buffered) and shared
+// by the 4 wavefronts: up to 4 B fragments, 16 matrix-core instructions per
+// wavefront per step. Items are dealt so that the tiles of one expert and row block run
 // back to back on one accelerator die and share its L2.
 //
 // gate/up: 32 features per wavefront for both matrices, epilogue adds the
@@ -19,6 +19,8 @@
 //
 // Page: goosedump `gpt_oss.rs`, `mixture_of_experts` and its grouped form over
 // expert-sorted rows; DeepSeek-V4 shared expert (ungated, weight 1).
+#include <type_traits>
+
 #include "mx_mfma.hpp"
 
 namespace moe {
@@ -29,13 +31,16 @@ constexpr int kRowGroups = kGemmBM / 4;         // B operands per step (4 rows e
 constexpr int kBRowBytes = 128 + 16;            // one (row, term) step in LDS, padded
 constexpr int kBBufBytes = kGemmBM * kTerms * kBRowBytes;
 constexpr int kThreads = kGemmWaves * 64;
-static_assert(kGemmBM * kTerms * 128 / 16 == 4 * kThreads, "B staging: 4 x 16 bytes per thread");
-static_assert(kGemmBM * kTerms == 128, "B scale staging: one dword per thread of the first 128");
+constexpr int kStage = kGemmBM * kTerms * 128 / 16 / kThreads;  // 16-byte B pieces per thread per step
+constexpr int kRing = 3;                        // K-steps of A fragments in flight per wavefront
+static_assert(kStage * kThreads * 16 == kGemmBM * kTerms * 128, "B staging covers the tile");
+static_assert(kGemmBM * kTerms <= kThreads, "B scale staging: one dword per thread");
+static_assert(kStage == 2, "the main loop stages B in two named registers");
 
 struct Tile {
     int g;   // group: expert, or E for the shared expert
     int p0;  // first row position
-    int n;   // rows in the tile (1..32)
+    int n;   // rows in the tile (1..kGemmBM)
 };
 
 // Work item of this workgroup, dealt XCD-major (items i and i+1 run back to
@@ -59,68 +64,102 @@ __device__ __forceinline__ bool find_item(int max_tiles, int nrb, const int32_t 
     return true;
 }
 
-// Main loop: acc[j][rg] += A fragment j x B row group rg over all K-steps.
-// brow: per tile row, the FP8-term row index in bq / bs (row stride kTerms).
+// Main loop: acc[j][rg] += A fragment j x B row group rg over all K-steps
+// (aq[j] / as[j]: the tile bases of A fragment j),
+// for the row groups that hold tile rows (n of them). A fragments stream
+// through a register ring kRing steps deep (unrolled, so a slot is always the
+// same registers and its refill waits on nothing); B pieces run 2 steps ahead
+// and go through double-buffered LDS to be shared by the wavefronts (one
+// barrier per step); every load is issued unconditionally with its step clamped into
+// range.
 template <int NA>
 __device__ __forceinline__ void gemm_mainloop(const uint8_t *const (&aq)[NA],
-                                              const uint8_t *const (&as)[NA], const int (&atile)[NA],
-                                              int nblk, int NS, const uint8_t *bq, const uint8_t *bs,
-                                              int Kb, const int *s_brow, uint8_t *sB, uint32_t *sBs,
-                                              f32x4_t (&acc)[NA][kRowGroups]) {
+                                              const uint8_t *const (&as)[NA], const ALane &al,
+                                              int NS, const uint8_t *bq, const uint8_t *bs,
+                                              int Kb, const int *s_brow, int n, uint8_t *sB,
+                                              uint32_t *sBs, f32x4_t (&acc)[NA][kRowGroups]) {
     const int tid = threadIdx.x, lane = tid & 63;
-    // this thread's staging sources: 4 x 16 bytes of codes, one scale dword
-    const uint8_t *src[4];
-    int dst[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int q = tid + kThreads * i;
-        const int row = q >> 5, term = (q >> 3) & 3, chunk = q & 7;
-        src[i] = bq + (static_cast<size_t>(s_brow[row]) * kTerms + term) * Kb + 16 * chunk;
-        dst[i] = (row * kTerms + term) * kBRowBytes + 16 * chunk;
-    }
+    // staging pieces q = tid and tid + kThreads: (row, term, 16-byte chunk)
+    const int q0 = tid, q1 = tid + kThreads;
+    const uint8_t *src0 = bq + (static_cast<size_t>(s_brow[q0 >> 5]) * kTerms + ((q0 >> 3) & 3)) * Kb + 16 * (q0 & 7);
+    const uint8_t *src1 = bq + (static_cast<size_t>(s_brow[q1 >> 5]) * kTerms + ((q1 >> 3) & 3)) * Kb + 16 * (q1 & 7);
+    const int dst0 = ((q0 >> 5) * kTerms + ((q0 >> 3) & 3)) * kBRowBytes + 16 * (q0 & 7);
+    const int dst1 = ((q1 >> 5) * kTerms + ((q1 >> 3) & 3)) * kBRowBytes + 16 * (q1 & 7);
     const bool sc_on = tid < kGemmBM * kTerms;
     const int srow = sc_on ? tid >> 2 : 0, sterm = tid & 3;
     const uint32_t *ssrc = reinterpret_cast<const uint32_t *>(
         bs + (static_cast<size_t>(s_brow[srow]) * kTerms + sterm) * (Kb / 32));
+    const int ngroups = (n + 3) >> 2;  // row groups holding tile rows
 
-    uint4 st[4];
-    uint32_t sts = 0;
-    AFrag an[NA];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) st[i] = *reinterpret_cast<const uint4 *>(src[i]);
-    if (sc_on) sts = ssrc[0];
-#pragma unroll
-    for (int j = 0; j < NA; ++j) an[j] = load_afrag(aq[j], as[j], atile[j], 0, nblk, lane);
-
-    const int bn = lane & 15, bh = lane >> 4;
-    const int brd = ((4 * 0 + (bn >> 2)) * kTerms + (bn & 3)) * kBRowBytes + 16 * bh;  // + group offset
-    for (int s = 0; s < NS; ++s) {
-        uint8_t *buf = sB + (s & 1) * kBBufBytes;
-        uint32_t *sbuf = sBs + (s & 1) * (kGemmBM * kTerms);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4 *>(buf + dst[i]) = st[i];
-        if (sc_on) sbuf[tid] = sts;
+    // Loads run ahead of use: A fragments kRing = 3 steps, B pieces 2 steps.
+    // Vector loads complete in issue order, so within a step B(s+2) is issued
+    // before A(s+3): waiting for B(s) then leaves A(s+1), A(s+2) in flight.
+    // Slots are named (A slot s % 3, B slot and LDS buffer s % 2; the pattern
+    // repeats every 6 steps) so that no slot is ever indexed at run time. All
+    // loads are unconditional with their step clamped into range; the steps
+    // past NS in the last round skip their matrix-core work.
+    typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+    struct BSlot {
+        u32x4_t b0, b1;  // this thread's two B pieces
+        uint32_t bs;     // B scale dword (threads < kGemmBM * kTerms)
+    };
+    struct ASlot {
         AFrag a[NA];
+    };
+    auto fill_b = [&](BSlot &sl, int step) __attribute__((always_inline)) {
+        const int sd = min(step, NS - 1);
+        sl.b0 = *reinterpret_cast<const u32x4_t *>(src0 + 128 * sd);
+        sl.b1 = *reinterpret_cast<const u32x4_t *>(src1 + 128 * sd);
+        sl.bs = ssrc[sd];
+    };
+    auto fill_a = [&](ASlot &sl, int step) __attribute__((always_inline)) {
+        const int sd = min(step, NS - 1);
 #pragma unroll
-        for (int j = 0; j < NA; ++j) a[j] = an[j];
-        if (s + 1 < NS) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                st[i] = *reinterpret_cast<const uint4 *>(src[i] + 128 * (s + 1));
-            if (sc_on) sts = ssrc[s + 1];
-#pragma unroll
-            for (int j = 0; j < NA; ++j) an[j] = load_afrag(aq[j], as[j], atile[j], s + 1, nblk, lane);
-        }
+        for (int j = 0; j < NA; ++j) sl.a[j] = load_afrag(aq[j], as[j], al, sd);
+    };
+    const int bn = lane & 15, bh = lane >> 4;
+    const int brd = ((bn >> 2) * kTerms + (bn & 3)) * kBRowBytes + 16 * bh;
+    auto step = [&](auto lbuf, BSlot &bsl, ASlot &asl, int s) __attribute__((always_inline)) {
+        constexpr int L = decltype(lbuf)::value;
+        uint8_t *buf = sB + L * kBBufBytes;
+        uint32_t *sbuf = sBs + L * (kGemmBM * kTerms);
+        *reinterpret_cast<u32x4_t *>(buf + dst0) = bsl.b0;
+        *reinterpret_cast<u32x4_t *>(buf + dst1) = bsl.b1;
+        if (sc_on) sbuf[tid] = bsl.bs;
+        fill_b(bsl, s + 2);
         __syncthreads();
+        if (s < NS) {  // uniform; no loads inside
 #pragma unroll
-        for (int rg = 0; rg < kRowGroups; ++rg) {
-            const int off = brd + rg * 4 * kTerms * kBRowBytes;
-            const uint4 blo = *reinterpret_cast<const uint4 *>(buf + off);
-            const uint4 bhi = *reinterpret_cast<const uint4 *>(buf + off + 64);
-            const uint32_t bsc = (sbuf[(4 * rg + (bn >> 2)) * kTerms + (bn & 3)] >> (8 * bh)) & 0xffu;
+            for (int rg = 0; rg < kRowGroups; ++rg) {
+                if (rg < ngroups) {
+                    const int off = brd + rg * 4 * kTerms * kBRowBytes;
+                    const uint4 blo = *reinterpret_cast<const uint4 *>(buf + off);
+                    const uint4 bhi = *reinterpret_cast<const uint4 *>(buf + off + 64);
+                    const uint32_t bsc = (sbuf[(4 * rg + (bn >> 2)) * kTerms + (bn & 3)] >> (8 * bh)) & 0xffu;
 #pragma unroll
-            for (int j = 0; j < NA; ++j) acc[j][rg] = mx_mfma(a[j], blo, bhi, bsc, acc[j][rg]);
+                    for (int j = 0; j < NA; ++j) acc[j][rg] = mx_mfma(asl.a[j], blo, bhi, bsc, acc[j][rg]);
+                }
+            }
         }
+        fill_a(asl, s + kRing);
+    };
+    static_assert(kRing == 3, "three named A slots");
+    ASlot a0, a1, a2;
+    BSlot b0, b1;
+    fill_a(a0, 0);
+    fill_b(b0, 0);
+    fill_a(a1, 1);
+    fill_b(b1, 1);
+    fill_a(a2, 2);
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    for (int s0 = 0; s0 < NS; s0 += 6) {
+        step(I0{}, b0, a0, s0);
+        step(I1{}, b1, a1, s0 + 1);
+        step(I0{}, b0, a2, s0 + 2);
+        step(I1{}, b1, a0, s0 + 3);
+        step(I0{}, b0, a1, s0 + 4);
+        step(I1{}, b1, a2, s0 + 5);
     }
 }
 
@@ -153,18 +192,20 @@ __global__ __launch_bounds__(kThreads) void gate_up_gemm_kernel(
     __syncthreads();
     const uint8_t *blob = tl.g < E ? ex.base + static_cast<size_t>(tl.g) * ex.stride : sh.base;
     const int f0 = rb * kGateUpRowsWG + 32 * w;  // this wavefront's 32 features
-    const int last_tile = F / 16 - 1;
-    const uint8_t *const aq[4] = {blob + ex.gate_q, blob + ex.gate_q, blob + ex.up_q, blob + ex.up_q};
-    const uint8_t *const as[4] = {blob + ex.gate_s, blob + ex.gate_s, blob + ex.up_s, blob + ex.up_s};
+    const int last_tile = F / 16 - 1, nblk = H / 32;
     const int t0 = min(f0 / 16, last_tile), t1 = min(f0 / 16 + 1, last_tile);
-    const int atile[4] = {t0, t1, t0, t1};
+    const uint8_t *const aq[4] = {blob + ex.gate_q + tile_code_base(t0, nblk), blob + ex.gate_q + tile_code_base(t1, nblk),
+                                  blob + ex.up_q + tile_code_base(t0, nblk), blob + ex.up_q + tile_code_base(t1, nblk)};
+    const uint8_t *const as[4] = {blob + ex.gate_s + tile_scale_base(t0, nblk), blob + ex.gate_s + tile_scale_base(t1, nblk),
+                                  blob + ex.up_s + tile_scale_base(t0, nblk), blob + ex.up_s + tile_scale_base(t1, nblk)};
+    const ALane al(nblk, lane);
     f32x4_t acc[4][kRowGroups];
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int rg = 0; rg < kRowGroups; ++rg) acc[j][rg] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     const int Kp = pad128(H);
-    gemm_mainloop<4>(aq, as, atile, H / 32, Kp / 128, xq, xs, Kp, s_brow, sB, sBs, acc);
+    gemm_mainloop<4>(aq, as, al, Kp / 128, xq, xs, Kp, s_brow, tl.n, sB, sBs, acc);
 
     // epilogue: SwiGLU into LDS, then one 32-feature block per row to FP8 terms
     const bool live = f0 < F;  // F % 32 == 0: a wavefront is all features or all padding
@@ -189,7 +230,7 @@ __global__ __launch_bounds__(kThreads) void gate_up_gemm_kernel(
     }
     __syncthreads();
     const int half = lane >> 5, i = lane & 31, nbp = Fp / 32;
-    for (int r0 = 0; r0 < kGemmBM; r0 += 2) {
+    for (int r0 = 0; r0 < tl.n; r0 += 2) {
         const int row = r0 + half;
         uint32_t codes = 0, scales = 0x7f7f7f7fu;
         if (live) fp8_terms_group(sAct[w][row][i], codes, scales);
@@ -237,18 +278,22 @@ __global__ __launch_bounds__(kThreads) void down_gemm_kernel(
     __syncthreads();
     const uint8_t *blob = tl.g < E ? ex.base + static_cast<size_t>(tl.g) * ex.stride : sh.base;
     const int h0 = rb * kDownRowsWG + 64 * w;  // this wavefront's 64 hidden rows
-    const int last_tile = H / 16 - 1;
-    const uint8_t *const aq[4] = {blob + ex.down_q, blob + ex.down_q, blob + ex.down_q, blob + ex.down_q};
-    const uint8_t *const as[4] = {blob + ex.down_s, blob + ex.down_s, blob + ex.down_s, blob + ex.down_s};
-    const int atile[4] = {min(h0 / 16, last_tile), min(h0 / 16 + 1, last_tile),
-                          min(h0 / 16 + 2, last_tile), min(h0 / 16 + 3, last_tile)};
+    const int last_tile = H / 16 - 1, nblk = F / 32;
+    const uint8_t *aq[4], *as[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int tj = min(h0 / 16 + j, last_tile);
+        aq[j] = blob + ex.down_q + tile_code_base(tj, nblk);
+        as[j] = blob + ex.down_s + tile_scale_base(tj, nblk);
+    }
+    const ALane al(nblk, lane);
     f32x4_t acc[4][kRowGroups];
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int rg = 0; rg < kRowGroups; ++rg) acc[j][rg] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     const int Fp = pad128(F);
-    gemm_mainloop<4>(aq, as, atile, F / 32, Fp / 128, act_q, act_s, Fp, s_brow, sB, sBs, acc);
+    gemm_mainloop<4>(aq, as, al, Fp / 128, act_q, act_s, Fp, s_brow, tl.n, sB, sBs, acc);
 
     const float *db = reinterpret_cast<const float *>(blob + ex.down_b);
     const int rq = (lane & 15) >> 2;
