@@ -36,7 +36,8 @@ if ROOT not in sys.path:
 
 METRIC = "MoE block tokens/s (decode T=1, prefill T=128/512) + % HBM/MFMA peak"
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
-BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
+FP8_PEAK_TFLOPS = 5000.0        # MI355X dense FP8 MFMA: the rate of the FP4 x FP8 scaled MFMA used
+DTYPE = "fp4xfp8"               # MXFP4 weights x FP8-term activations, float32 accumulation
 
 WORKLOADS = {
     "decode": dict(config=2, name="gptoss20b_decode_T1_1000tok", kernel="decode_gate_up", copies=8,
@@ -98,7 +99,7 @@ class HipEvents:
 
 def source_sha(kernel: str) -> str:
     h = hashlib.sha256()
-    for f in ("common.hpp", "kernels.hpp", KERNEL_SOURCES[kernel]):
+    for f in ("common.hpp", "kernels.hpp", "mx_mfma.hpp", KERNEL_SOURCES[kernel]):
         with open(os.path.join(ROOT, "mxfp4_expert_ffn_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -202,23 +203,28 @@ class Setup:
                 src = dst
         return calls
 
-    # algorithmic work of the dominant kernel per launch and of the block per step
+    # algorithmic work of the dominant kernel per launch and of the block per step:
+    # the expert weights it must read (codes + scales + biases) plus its
+    # activation operands in and out in the formats it uses (FP8 terms:
+    # 4 codes + 4 scale bytes per 32 values)
     def algorithmic(self, counts_per_call):
         cfg = self.cfg
         H, F, k, E = cfg.H, cfg.F, cfg.k, cfg.E
         mat = F * H * 17 // 32            # codes + scales of one [F,H] matrix
-        xb = 2 if cfg.act_dtype == "bf16" else 4
+        pad = lambda n: (n + 127) // 128 * 128
+        terms = lambda n: 4 * pad(n) + 4 * pad(n) // 32
         if self.spec["kernel"] == "decode_gate_up":
             T = 1 if cfg.T == 1 else cfg.T
             routes = T * k + T * cfg.n_shared
-            byts = routes * 2 * (mat + 4 * F) + T * H * xb + routes * F * 4 + T * E * 8
+            splits = (H + 2047) // 2048
+            byts = routes * 2 * (mat + 4 * F) + T * terms(H) + routes * terms(F) + T * splits * E * 8
             return dict(bytes=byts, flops=routes * 4 * H * F, units=routes,
                         unit="route (token, selected expert)")
-        # gate/up GEMM: weights of every active expert once, x once, act out
+        # gate/up GEMM: weights of every active expert once, x terms once, act terms out
         T = cfg.T
         active = [sum(1 for c in counts if c > 0) + cfg.n_shared for counts in counts_per_call]
         rows = T * k + T * cfg.n_shared
-        per = [a * 2 * (mat + 4 * F) + T * H * xb + rows * F * 4 for a in active]
+        per = [a * 2 * (mat + 4 * F) + T * terms(H) + rows * terms(F) for a in active]
         return dict(bytes=sum(per) / len(per), flops=4.0 * rows * H * F, units=rows,
                     unit="routed row (token, expert) of the grouped GEMM",
                     active_experts=sum(active) / len(active))
@@ -280,7 +286,7 @@ def cpu_baseline(setup, budget_s: float):
         cores = 1
     x = setup.x_host
     if cfg.path == "decode" and cfg.T == 1:
-        n = 16
+        n = 96
         t0 = time.time()
         omoe.block_for_config(cfg, layer, x[:n])
         dt = time.time() - t0
@@ -384,11 +390,11 @@ def main():
         traffic = traffic_from_profile(kernel, args.workload)
     else:
         t_hbm = alg["bytes"] / (HBM_PEAK_GBPS * 1e9)
-        t_mfma = alg["flops"] / (BF16_PEAK_TFLOPS * 1e12)
+        t_mfma = alg["flops"] / (FP8_PEAK_TFLOPS * 1e12)
         if t_hbm >= t_mfma:
             achieved, peak, unit, bound = alg["bytes"] / kern_s / 1e9, HBM_PEAK_GBPS, "GB/s", "hbm"
         else:
-            achieved, peak, unit, bound = alg["flops"] / kern_s / 1e12, BF16_PEAK_TFLOPS, "TFLOP/s", "mfma"
+            achieved, peak, unit, bound = alg["flops"] / kern_s / 1e12, FP8_PEAK_TFLOPS, "TFLOP/s", "mfma"
         traffic = traffic_from_profile(kernel, args.workload)
     block_bytes = setup.block_bytes_per_step(counts)
     block_gbps = block_bytes / (ms_per_step / 1e3) / 1e9
@@ -404,7 +410,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32" if kernel.startswith("decode") else "bf16",
+        "dtype": DTYPE,
         "data": "synthetic",
         "config": {
             "workload": spec["name"], "T": cfg.T, "H": cfg.H, "F": cfg.F, "E": cfg.E,
