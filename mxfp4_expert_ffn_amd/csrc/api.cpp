@@ -246,9 +246,8 @@ int route_front(const moe_shape *s, const void *x, const float *norm_w, const fl
 }
 
 // Upper bound on the grouped GEMMs' row tiles (the grid is sized by it).
-int max_tiles(const moe_shape *s) {
+int max_tiles(const moe_shape *s, int bm) {
     const long long R = static_cast<long long>(s->T) * s->k;
-    const long long bm = moe::kGemmBM;
     long long m = (R + bm - 1) / bm + (s->E < R ? s->E : R);
     if (s->n_shared) m += (s->T + bm - 1) / bm;
     return static_cast<int>(m);
@@ -331,7 +330,7 @@ int moe_route(const moe_shape *s, const void *x, const float *norm_w, const floa
                                 w.idx, w.wts, out->topk_idx, out->topk_w, nullptr, 0, s->H,
                                 nullptr, st);
     }));
-    MOE_TRY(launch(MOE_KERNEL_PERMUTE, "permute", st, [&] { return moe::launch_permute(w.idx, s->T, s->E, s->k, 0, w.counts, w.offsets, w.perm,
+    MOE_TRY(launch(MOE_KERNEL_PERMUTE, "permute", st, [&] { return moe::launch_permute(w.idx, s->T, s->E, s->k, 0, 16, w.counts, w.offsets, w.perm,
                                           w.inv, w.rank, w.mprefix, out->counts, out->offsets,
                                           out->perm, out->inv, st); }));
     return ok();
@@ -364,7 +363,7 @@ int moe_forward_decode(const moe_shape *s, const void *hidden, const float *norm
     }));
     if (ro && (ro->counts || ro->offsets || ro->perm || ro->inv))
         MOE_TRY(launch(MOE_KERNEL_PERMUTE, "permute", st, [&] {
-            return moe::launch_permute(w.idx, s->T, s->E, s->k, 0, w.counts, w.offsets, w.perm,
+            return moe::launch_permute(w.idx, s->T, s->E, s->k, 0, 16, w.counts, w.offsets, w.perm,
                                        w.inv, w.rank, w.mprefix, ro->counts, ro->offsets,
                                        ro->perm, ro->inv, st);
         }));
@@ -377,6 +376,12 @@ int moe_forward_prefill(const moe_shape *s, const void *hidden, const float *nor
                         size_t ws_bytes, hipStream_t st) {
     MOE_TRY(check_forward(s, hidden, norm_w, router_w, router_b, experts, shared, out, ws, ws_bytes));
     if (s->T == 0) return ok();
+    {  // the grouped GEMMs address FP8-term rows with 32-bit byte offsets
+        const uint64_t rows = static_cast<uint64_t>(s->T) * (s->k + s->n_shared);
+        if (static_cast<uint64_t>(s->T) * moe::kTerms * moe::pad128(s->H) >= (1ull << 32) ||
+            rows * moe::kTerms * moe::pad128(s->F) >= (1ull << 32))
+            return fail(MOE_ERR_UNSUPPORTED, "prefill needs T*(k+n_shared)*4*pad128(F) and T*4*pad128(H) below 2^32");
+    }
     const Workspace w = carve(s, static_cast<uint8_t *>(ws));
     MOE_TRY(route_front(s, hidden, norm_w, router_w, w, true, st));
     MOE_TRY(launch(MOE_KERNEL_TOPK, "topk", st, [&] {
@@ -385,8 +390,9 @@ int moe_forward_prefill(const moe_shape *s, const void *hidden, const float *nor
                                 ro ? ro->topk_w : nullptr, hidden, s->act_dtype == MOE_BF16,
                                 s->H, out, st);
     }));
+    const int bm = moe::gemm_tile_rows(s->T, s->k, s->E, s->n_shared);
     MOE_TRY(launch(MOE_KERNEL_PERMUTE, "permute", st, [&] {
-        return moe::launch_permute(w.idx, s->T, s->E, s->k, s->n_shared, w.counts, w.offsets,
+        return moe::launch_permute(w.idx, s->T, s->E, s->k, s->n_shared, bm, w.counts, w.offsets,
                                    w.perm, w.inv, w.rank, w.mprefix, ro ? ro->counts : nullptr,
                                    ro ? ro->offsets : nullptr, ro ? ro->perm : nullptr,
                                    ro ? ro->inv : nullptr, st);
@@ -394,15 +400,15 @@ int moe_forward_prefill(const moe_shape *s, const void *hidden, const float *nor
     const moe::ExpertPtrs ex = expert_ptrs(s, experts);
     const moe::ExpertPtrs sh = expert_ptrs(s, shared);
     const moe::SwigluConsts c{s->swiglu_alpha, s->swiglu_limit, s->swiglu_up_offset};
-    const int mt = max_tiles(s);
+    const int mt = max_tiles(s, bm);
     MOE_TRY(launch(MOE_KERNEL_GATE_UP_GEMM, "gate_up_gemm", st, [&] {
         return moe::launch_gate_up_gemm(w.xq, w.xs, s->T, s->H, s->F, s->E, s->k, s->n_shared, ex,
-                                        sh, c, w.offsets, w.perm, w.mprefix, mt, w.act_q, w.act_s,
-                                        st);
+                                        sh, c, w.offsets, w.perm, w.mprefix, bm, mt, w.act_q,
+                                        w.act_s, st);
     }));
     MOE_TRY(launch(MOE_KERNEL_DOWN_GEMM, "down_gemm", st, [&] {
         return moe::launch_down_gemm(w.act_q, w.act_s, s->T, s->H, s->F, s->E, s->k, s->n_shared,
-                                     ex, sh, w.offsets, w.perm, w.wts, w.mprefix, mt, out, st);
+                                     ex, sh, w.offsets, w.perm, w.wts, w.mprefix, bm, mt, out, st);
     }));
     return ok();
 }

@@ -12,13 +12,8 @@ constexpr int kMaxK = 8;   // experts per token
 constexpr int kMaxE = 256; // routed experts
 constexpr int kTerms = 4;  // FP8 terms per activation on the block-scaled matrix cores
 
-// Grouped GEMMs: routed rows of one expert per tile (groups of 4 rows, one
-// group per matrix-core B operand of 4 rows x kTerms terms), 4 wavefronts per
-// workgroup; the permutation's tile prefix uses the same row count.
-constexpr int kGemmBM = 16;
-constexpr int kGemmWaves = 4;
-constexpr int kGateUpRowsWG = 128;  // gate/up: 32 feature rows (gate and up) per wavefront
-constexpr int kDownRowsWG = 256;    // down: 64 hidden rows per wavefront
+// Grouped GEMMs: tiles of 16, 32 or 64 routed rows of one expert
+// (gemm_tile_rows), which the permutation's tile prefix also uses.
 // Decode GEMVs: 32 weight rows per workgroup, K split over 8 wavefronts.
 constexpr int kDecodeRows = 32;
 constexpr int kDecodeWaves = 8;
@@ -102,7 +97,9 @@ hipError_t launch_quantize(const TermsOut &terms, int T, int H, hipStream_t s);
 hipError_t launch_topk(const double *partial, int S, const float *bias, int T, int E, int k,
                        float route_scale, int32_t *idx, float *wts, int32_t *out_idx, float *out_w,
                        const void *resid, int resid_bf16, int H, float *out, hipStream_t s);
-hipError_t launch_permute(const int32_t *idx, int T, int E, int k, int n_shared,
+// mprefix[g] = tiles of tile_rows rows before group g (groups: E experts,
+// then the shared expert's T rows when n_shared).
+hipError_t launch_permute(const int32_t *idx, int T, int E, int k, int n_shared, int tile_rows,
                           int32_t *counts, int32_t *offsets, int32_t *perm, int32_t *inv,
                           int32_t *rank, int32_t *mprefix, int32_t *out_counts,
                           int32_t *out_offsets, int32_t *out_perm, int32_t *out_inv,
@@ -128,16 +125,19 @@ hipError_t launch_decode_down(const uint8_t *act_q, const uint8_t *act_s, int T,
 
 // prefill (any T) -------------------------------------------------------------
 // Rows in expert order: position p < T*k is route perm[p]; p >= T*k is the
-// shared expert of token p - T*k. act_q / act_s are indexed by p.
+// shared expert of token p - T*k. act_q / act_s are indexed by p. tile_rows
+// (16, 32 or 64) comes from gemm_tile_rows, max_tiles bounds the tile count.
+int gemm_tile_rows(int T, int k, int E, int n_shared);
 hipError_t launch_gate_up_gemm(const uint8_t *xq, const uint8_t *xs, int T, int H, int F, int E,
                                int k, int n_shared, const ExpertPtrs &ex, const ExpertPtrs &sh,
                                SwigluConsts c, const int32_t *offsets, const int32_t *perm,
-                               const int32_t *mprefix, int max_tiles, uint8_t *act_q,
+                               const int32_t *mprefix, int tile_rows, int max_tiles, uint8_t *act_q,
                                uint8_t *act_s, hipStream_t s);
 hipError_t launch_down_gemm(const uint8_t *act_q, const uint8_t *act_s, int T, int H, int F, int E,
                             int k, int n_shared, const ExpertPtrs &ex, const ExpertPtrs &sh,
                             const int32_t *offsets, const int32_t *perm, const float *wts,
-                            const int32_t *mprefix, int max_tiles, float *out, hipStream_t s);
+                            const int32_t *mprefix, int tile_rows, int max_tiles, float *out,
+                            hipStream_t s);
 
 // debug -------------------------------------------------------------------
 // Decoded weights of one packed plane as float32 [rows][K]: path 0 through

@@ -2,23 +2,30 @@
 // block-scaled matrix cores (MXFP4 weights as operand A, FP8-term activations
 // as operand B).
 //
-// A work item is (weight-row block, tile of up to kGemmBM rows of one expert). Its
-// workgroup of 4 wavefronts streams the weight rows once per tile, each
-// wavefront its own rows (4 A fragments per 128-wide step, read as contiguous
-// kilobytes from the tiled plane, kRing steps ahead), while the tile's rows x
-// kTerms terms are staged per step through LDS (double-buffered) and shared
-// by the 4 wavefronts: up to 4 B fragments, 16 matrix-core instructions per
-// wavefront per step. Items are dealt so that the tiles of one expert and row block run
-// back to back on one accelerator die and share its L2.
+// The kTerms FP8 terms of an activation row are laid along K: for each
+// 128-wide step, term n of 16 rows is one B operand (column c = row c of the
+// group), and the kTerms instructions accumulate into the same result. So a
+// 16x16 result tile holds 16 weight rows x 16 activation rows outright.
 //
-// gate/up: 32 features per wavefront for both matrices, epilogue adds the
-// biases, applies the clamped SwiGLU and writes the FP8 terms of each
-// 32-feature block per row (the down GEMM's operand). down: 64 hidden rows per
-// wavefront, epilogue adds the bias and scatter-adds route weight x result
-// into out[token] (which holds the residual).
+// A work item is (tile of up to 16*NG rows of one expert, weight-row block).
+// Its workgroup of W wavefronts streams the block's weight rows once per tile:
+// each wavefront has its own rows and NA A fragments per step, read as
+// contiguous kilobytes from the tiled plane 2-3 steps ahead. The tile's rows x
+// terms are staged 2 steps ahead through double-buffered LDS and shared by the
+// W wavefronts. Per step a wavefront issues NA x NG x kTerms matrix-core
+// instructions, less for row groups of 16 the tile does not fill. Items are
+// dealt so that the row blocks of one tile run back to back on one
+// accelerator die and share its activation rows in L2.
+//
+// gate/up: NA/2 16-row tiles of each matrix per wavefront. The epilogue adds
+// the biases, applies the clamped SwiGLU and writes the FP8 terms of each
+// 32-feature block per row (the down GEMM's operand). down: NA 16-row tiles
+// per wavefront. The epilogue adds the bias and scatter-adds route weight x
+// result into out[token] (which holds the residual).
 //
 // Page: goosedump `gpt_oss.rs`, `mixture_of_experts` and its grouped form over
-// expert-sorted rows; DeepSeek-V4 shared expert (ungated, weight 1).
+// expert-sorted rows (`mixture_of_experts_batch`); DeepSeek-V4 shared expert
+// (ungated, weight 1).
 #include <type_traits>
 
 #include "mx_mfma.hpp"
@@ -27,31 +34,46 @@ namespace moe {
 
 namespace {
 
-constexpr int kRowGroups = kGemmBM / 4;         // B operands per step (4 rows each)
-constexpr int kBRowBytes = 128 + 16;            // one (row, term) step in LDS, padded
-constexpr int kBBufBytes = kGemmBM * kTerms * kBRowBytes;
-constexpr int kThreads = kGemmWaves * 64;
-constexpr int kStage = kGemmBM * kTerms * 128 / 16 / kThreads;  // 16-byte B pieces per thread per step
-constexpr int kRing = 3;                        // K-steps of A fragments in flight per wavefront
-static_assert(kStage * kThreads * 16 == kGemmBM * kTerms * 128, "B staging covers the tile");
-static_assert(kGemmBM * kTerms <= kThreads, "B scale staging: one dword per thread");
-static_assert(kStage == 2, "the main loop stages B in two named registers");
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// Tile geometry: NG row groups of 16 per tile, W wavefronts per workgroup,
+// NA A fragments (16-row weight tiles) per wavefront.
+template <int NG, int W, int NA>
+struct Geo {
+    static constexpr int kThreads = 64 * W;
+    static constexpr int kRows = 16 * NG;                  // activation rows per tile
+    static constexpr int kPieces = kTerms * NG * 8 * 16;   // 16-byte B pieces per step
+    static constexpr int kPerThread = kPieces / kThreads;  // pieces staged per thread
+    static constexpr int kBufBytes = kPieces * 16;
+    static constexpr int kScales = kRows * kTerms;         // B scale dwords per step
+    static constexpr int kGURowsWave = 8 * NA;             // gate/up features per wavefront
+    static constexpr int kGateUpRows = W * kGURowsWave;    // features per gate/up workgroup
+    static constexpr int kDownRows = W * 16 * NA;          // hidden rows per down workgroup
+    // K-steps of A fragments in flight: 3, or 2 where a step's matrix-core
+    // work is long (64-row tiles) and registers are short
+    static constexpr int kASlots = NG >= 4 ? 2 : 3;
+    static_assert(kPieces % kThreads == 0, "B staging divides evenly");
+    static_assert(kScales <= kThreads, "one scale dword per thread at most");
+    static_assert(kGateUpRows % 32 == 0, "gate/up blocks hold whole 32-feature MX blocks");
+};
 
 struct Tile {
     int g;   // group: expert, or E for the shared expert
     int p0;  // first row position
-    int n;   // rows in the tile (1..kGemmBM)
+    int n;   // rows in the tile (1..16*NG)
 };
 
-// Work item of this workgroup, dealt XCD-major (items i and i+1 run back to
-// back on one die); false when it is past the real tiles.
-__device__ __forceinline__ bool find_item(int max_tiles, int nrb, const int32_t *offsets,
+// Work item of this workgroup: item = tile * nrb + row block, dealt XCD-major
+// (items i and i+1 run back to back on one die), so the row blocks of one
+// tile share its activation rows in that die's L2 and consecutive tiles of an
+// expert follow each other; false when it is past the real tiles.
+__device__ __forceinline__ bool find_item(int nrb, int bm, const int32_t *offsets,
                                           const int *s_pre, int G, int &rb, Tile &tl) {
     const int per = gridDim.x / kXcds;
     const int item = (blockIdx.x % kXcds) * per + blockIdx.x / kXcds;
-    rb = item / max_tiles;
-    const int tile = item - rb * max_tiles;
-    if (rb >= nrb || tile >= s_pre[G]) return false;
+    const int tile = item / nrb;
+    rb = item - tile * nrb;
+    if (tile >= s_pre[G]) return false;
     int lo = 0, hi = G - 1;  // last group whose first tile is <= tile
     while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
@@ -59,107 +81,134 @@ __device__ __forceinline__ bool find_item(int max_tiles, int nrb, const int32_t 
         else hi = mid - 1;
     }
     tl.g = lo;
-    tl.p0 = offsets[lo] + (tile - s_pre[lo]) * kGemmBM;
-    tl.n = min(kGemmBM, offsets[lo + 1] - tl.p0);
+    tl.p0 = offsets[lo] + (tile - s_pre[lo]) * bm;
+    tl.n = min(bm, offsets[lo + 1] - tl.p0);
     return true;
 }
 
-// Main loop: acc[j][rg] += A fragment j x B row group rg over all K-steps
-// (aq[j] / as[j]: the tile bases of A fragment j),
-// for the row groups that hold tile rows (n of them). A fragments stream
-// through a register ring kRing steps deep (unrolled, so a slot is always the
-// same registers and its refill waits on nothing); B pieces run 2 steps ahead
-// and go through double-buffered LDS to be shared by the wavefronts (one
-// barrier per step); every load is issued unconditionally with its step clamped into
-// range.
-template <int NA>
+// Main loop: acc[j][g] += A fragment j x (row group g, all terms) over all
+// K-steps (aq[j] / as[j]: the tile bases of A fragment j; brow: per tile row,
+// the FP8-term row index in bq / bs, row stride kTerms).
+//
+// Loads run ahead of use: A fragments kASlots (3 or 2) steps, B pieces 2
+// steps. Vector loads complete in issue order, so within a step B(s+2) is
+// issued before A(s+kASlots): waiting for B(s) leaves the later A fragments
+// in flight. Slots are named (A slot s % kASlots, B slot and LDS buffer s % 2;
+// the pattern repeats every 6 or 2 steps) so that no slot is indexed at run
+// time. All loads are unconditional with their step clamped into range; the
+// steps past NS in the last round skip their matrix-core work.
+//
+// LDS holds a step's B pieces in fragment order: piece p = ((term * NG +
+// group) * 8 + chunk) * 16 + column, so the 16 lanes of one k-group read 256
+// contiguous bytes; the B scale bytes sit in lane order, [term][k-group][row].
+template <int NG, int W, int NA>
 __device__ __forceinline__ void gemm_mainloop(const uint8_t *const (&aq)[NA],
                                               const uint8_t *const (&as)[NA], const ALane &al,
-                                              int NS, const uint8_t *bq, const uint8_t *bs,
-                                              int Kb, const int *s_brow, int n, uint8_t *sB,
-                                              uint32_t *sBs, f32x4_t (&acc)[NA][kRowGroups]) {
+                                              int NS, const uint8_t *bq, const uint8_t *bs, int Kb,
+                                              const int *s_brow, int n, uint8_t *sB, uint8_t *sBs,
+                                              f32x4_t (&acc)[NA][NG]) {
+    using Gm = Geo<NG, W, NA>;
+    constexpr int kThreads = Gm::kThreads;
     const int tid = threadIdx.x, lane = tid & 63;
-    // staging pieces q = tid and tid + kThreads: (row, term, 16-byte chunk)
-    const int q0 = tid, q1 = tid + kThreads;
-    const uint8_t *src0 = bq + (static_cast<size_t>(s_brow[q0 >> 5]) * kTerms + ((q0 >> 3) & 3)) * Kb + 16 * (q0 & 7);
-    const uint8_t *src1 = bq + (static_cast<size_t>(s_brow[q1 >> 5]) * kTerms + ((q1 >> 3) & 3)) * Kb + 16 * (q1 & 7);
-    const int dst0 = ((q0 >> 5) * kTerms + ((q0 >> 3) & 3)) * kBRowBytes + 16 * (q0 & 7);
-    const int dst1 = ((q1 >> 5) * kTerms + ((q1 >> 3) & 3)) * kBRowBytes + 16 * (q1 & 7);
-    const bool sc_on = tid < kGemmBM * kTerms;
-    const int srow = sc_on ? tid >> 2 : 0, sterm = tid & 3;
+    // this thread's B pieces: byte offsets from bq at step 0
+    uint32_t soff[Gm::kPerThread];
+#pragma unroll
+    for (int i = 0; i < Gm::kPerThread; ++i) {
+        const int p = tid + kThreads * i;
+        const int col = p & 15, chunk = (p >> 4) & 7, grp = (p >> 7) % NG, term = (p >> 7) / NG;
+        soff[i] = static_cast<uint32_t>((s_brow[16 * grp + col] * kTerms + term) * Kb + 16 * chunk);
+    }
+    // threads < kScales stage the scale dword (blocks 4s..4s+3) of one (row, term)
+    const bool sc_on = tid < Gm::kScales;
+    const int stok = sc_on ? tid >> 2 : 0, sterm = tid & 3;
     const uint32_t *ssrc = reinterpret_cast<const uint32_t *>(
-        bs + (static_cast<size_t>(s_brow[srow]) * kTerms + sterm) * (Kb / 32));
-    const int ngroups = (n + 3) >> 2;  // row groups holding tile rows
+        bs + (static_cast<size_t>(s_brow[stok]) * kTerms + sterm) * (Kb / 32));
+    const int sdst = sterm * 4 * Gm::kRows + stok;  // byte of k-group h at sdst + h * kRows
+    const int ngroups = (n + 15) >> 4;               // row groups holding tile rows
 
-    // Loads run ahead of use: A fragments kRing = 3 steps, B pieces 2 steps.
-    // Vector loads complete in issue order, so within a step B(s+2) is issued
-    // before A(s+3): waiting for B(s) then leaves A(s+1), A(s+2) in flight.
-    // Slots are named (A slot s % 3, B slot and LDS buffer s % 2; the pattern
-    // repeats every 6 steps) so that no slot is ever indexed at run time. All
-    // loads are unconditional with their step clamped into range; the steps
-    // past NS in the last round skip their matrix-core work.
-    typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
     struct BSlot {
-        u32x4_t b0, b1;  // this thread's two B pieces
-        uint32_t bs;     // B scale dword (threads < kGemmBM * kTerms)
+        u32x4_t b[Gm::kPerThread];
+        uint32_t s;
     };
     struct ASlot {
         AFrag a[NA];
     };
     auto fill_b = [&](BSlot &sl, int step) __attribute__((always_inline)) {
         const int sd = min(step, NS - 1);
-        sl.b0 = *reinterpret_cast<const u32x4_t *>(src0 + 128 * sd);
-        sl.b1 = *reinterpret_cast<const u32x4_t *>(src1 + 128 * sd);
-        sl.bs = ssrc[sd];
+#pragma unroll
+        for (int i = 0; i < Gm::kPerThread; ++i)
+            sl.b[i] = *reinterpret_cast<const u32x4_t *>(bq + soff[i] + 128 * sd);
+        sl.s = ssrc[sd];
     };
     auto fill_a = [&](ASlot &sl, int step) __attribute__((always_inline)) {
         const int sd = min(step, NS - 1);
 #pragma unroll
         for (int j = 0; j < NA; ++j) sl.a[j] = load_afrag(aq[j], as[j], al, sd);
     };
-    const int bn = lane & 15, bh = lane >> 4;
-    const int brd = ((bn >> 2) * kTerms + (bn & 3)) * kBRowBytes + 16 * bh;
+    const int col = lane & 15, kh = lane >> 4;
     auto step = [&](auto lbuf, BSlot &bsl, ASlot &asl, int s) __attribute__((always_inline)) {
         constexpr int L = decltype(lbuf)::value;
-        uint8_t *buf = sB + L * kBBufBytes;
-        uint32_t *sbuf = sBs + L * (kGemmBM * kTerms);
-        *reinterpret_cast<u32x4_t *>(buf + dst0) = bsl.b0;
-        *reinterpret_cast<u32x4_t *>(buf + dst1) = bsl.b1;
-        if (sc_on) sbuf[tid] = bsl.bs;
+        uint8_t *buf = sB + L * Gm::kBufBytes;
+        uint8_t *sbuf = sBs + L * 4 * Gm::kScales;
+#pragma unroll
+        for (int i = 0; i < Gm::kPerThread; ++i)
+            *reinterpret_cast<u32x4_t *>(buf + 16 * (tid + kThreads * i)) = bsl.b[i];
+        if (sc_on) {
+#pragma unroll
+            for (int h = 0; h < 4; ++h) sbuf[sdst + h * Gm::kRows] = static_cast<uint8_t>(bsl.s >> (8 * h));
+        }
         fill_b(bsl, s + 2);
         __syncthreads();
         if (s < NS) {  // uniform; no loads inside
 #pragma unroll
-            for (int rg = 0; rg < kRowGroups; ++rg) {
-                if (rg < ngroups) {
-                    const int off = brd + rg * 4 * kTerms * kBRowBytes;
-                    const uint4 blo = *reinterpret_cast<const uint4 *>(buf + off);
-                    const uint4 bhi = *reinterpret_cast<const uint4 *>(buf + off + 64);
-                    const uint32_t bsc = (sbuf[(4 * rg + (bn >> 2)) * kTerms + (bn & 3)] >> (8 * bh)) & 0xffu;
+            for (int g = 0; g < NG; ++g) {
+                if (g < ngroups) {  // uniform: row groups the tile fills
 #pragma unroll
-                    for (int j = 0; j < NA; ++j) acc[j][rg] = mx_mfma(asl.a[j], blo, bhi, bsc, acc[j][rg]);
+                    for (int t = 0; t < kTerms; ++t) {
+                        const int pc = ((t * NG + g) * 8 + kh) * 16 + col;
+                        const uint4 blo = *reinterpret_cast<const uint4 *>(buf + 16 * pc);
+                        const uint4 bhi = *reinterpret_cast<const uint4 *>(buf + 16 * (pc + 64));
+                        const uint32_t bsc = sbuf[(t * 4 + kh) * Gm::kRows + 16 * g + col];
+#pragma unroll
+                        for (int j = 0; j < NA; ++j) acc[j][g] = mx_mfma(asl.a[j], blo, bhi, bsc, acc[j][g]);
+                        // one term's B operand live at a time: keeps the scheduler from
+                        // hoisting every term's reads into registers the tile needs
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
                 }
             }
         }
-        fill_a(asl, s + kRing);
+        fill_a(asl, s + Gm::kASlots);
     };
-    static_assert(kRing == 3, "three named A slots");
-    ASlot a0, a1, a2;
-    BSlot b0, b1;
-    fill_a(a0, 0);
-    fill_b(b0, 0);
-    fill_a(a1, 1);
-    fill_b(b1, 1);
-    fill_a(a2, 2);
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
-    for (int s0 = 0; s0 < NS; s0 += 6) {
-        step(I0{}, b0, a0, s0);
-        step(I1{}, b1, a1, s0 + 1);
-        step(I0{}, b0, a2, s0 + 2);
-        step(I1{}, b1, a0, s0 + 3);
-        step(I0{}, b0, a1, s0 + 4);
-        step(I1{}, b1, a2, s0 + 5);
+    if constexpr (Gm::kASlots == 3) {
+        ASlot a0, a1, a2;
+        BSlot b0, b1;
+        fill_a(a0, 0);
+        fill_b(b0, 0);
+        fill_a(a1, 1);
+        fill_b(b1, 1);
+        fill_a(a2, 2);
+        for (int s0 = 0; s0 < NS; s0 += 6) {
+            step(I0{}, b0, a0, s0);
+            step(I1{}, b1, a1, s0 + 1);
+            step(I0{}, b0, a2, s0 + 2);
+            step(I1{}, b1, a0, s0 + 3);
+            step(I0{}, b0, a1, s0 + 4);
+            step(I1{}, b1, a2, s0 + 5);
+        }
+    } else {
+        ASlot a0, a1;
+        BSlot b0, b1;
+        fill_a(a0, 0);
+        fill_b(b0, 0);
+        fill_a(a1, 1);
+        fill_b(b1, 1);
+        for (int s0 = 0; s0 < NS; s0 += 2) {
+            step(I0{}, b0, a0, s0);
+            step(I1{}, b1, a1, s0 + 1);
+        }
     }
 }
 
@@ -168,102 +217,125 @@ __device__ __forceinline__ void load_pre(const int32_t *mprefix, int G, int *s_p
     __syncthreads();
 }
 
-// gate/up: grid = kXcds-rounded (pad128(F) / 128) x max_tiles items.
-__global__ __launch_bounds__(kThreads) void gate_up_gemm_kernel(
+// gate/up: grid = kXcds-rounded max_tiles x ceil(pad128(F) / kGateUpRows) items.
+template <int NG, int W, int NA>
+__global__ __launch_bounds__(64 * W) void gate_up_gemm_kernel(
     const uint8_t *xq, const uint8_t *xs, int T, int H, int F, int E, int k, int n_shared,
     ExpertPtrs ex, ExpertPtrs sh, SwigluConsts sc, const int32_t *offsets, const int32_t *perm,
-    const int32_t *mprefix, int max_tiles, uint8_t *act_q, uint8_t *act_s) {
+    const int32_t *mprefix, uint8_t *act_q, uint8_t *act_s) {
+    using Gm = Geo<NG, W, NA>;
+    constexpr int kTilesPerMat = NA / 2;   // 16-row tiles of gate (and of up) per wavefront
+    constexpr int kActStride = Gm::kGateUpRows + 1;
     __shared__ int s_pre[kMaxE + 2];
-    __shared__ int s_brow[kGemmBM];
-    __shared__ __align__(16) uint8_t sB[2 * kBBufBytes];
-    __shared__ uint32_t sBs[2 * kGemmBM * kTerms];
-    __shared__ float sAct[kGemmWaves][kGemmBM][33];
+    __shared__ int s_brow[Gm::kRows];
+    // B staging buffers; after the main loop the workgroup's SwiGLU outputs
+    // ([rows][kGateUpRows + 1] floats) reuse them
+    constexpr int kActBytes = Gm::kRows * kActStride * 4;
+    constexpr int kStageBytes = 2 * Gm::kBufBytes;
+    __shared__ __align__(16) uint8_t sB[kStageBytes > kActBytes ? kStageBytes : kActBytes];
+    __shared__ uint8_t sBs[2 * 4 * Gm::kScales];
     const int G = E + n_shared, R = T * k;
     load_pre(mprefix, G, s_pre);
-    const int Fp = pad128(F), nrb = Fp / kGateUpRowsWG;
+    const int Fp = pad128(F), nrb = (Fp + Gm::kGateUpRows - 1) / Gm::kGateUpRows;
     int rb;
     Tile tl;
-    if (!find_item(max_tiles, nrb, offsets, s_pre, G, rb, tl)) return;
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    if (tid < kGemmBM) {
+    if (!find_item(nrb, Gm::kRows, offsets, s_pre, G, rb, tl)) return;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    if (tid < Gm::kRows) {
         const int p = tl.p0 + min(tid, tl.n - 1);
         s_brow[tid] = p < R ? perm[p] / k : p - R;  // the token (x row)
     }
     __syncthreads();
     const uint8_t *blob = tl.g < E ? ex.base + static_cast<size_t>(tl.g) * ex.stride : sh.base;
-    const int f0 = rb * kGateUpRowsWG + 32 * w;  // this wavefront's 32 features
+    const int fw = rb * Gm::kGateUpRows;          // the workgroup's first feature
+    const int f0 = fw + Gm::kGURowsWave * w;     // this wavefront's first feature
     const int last_tile = F / 16 - 1, nblk = H / 32;
-    const int t0 = min(f0 / 16, last_tile), t1 = min(f0 / 16 + 1, last_tile);
-    const uint8_t *const aq[4] = {blob + ex.gate_q + tile_code_base(t0, nblk), blob + ex.gate_q + tile_code_base(t1, nblk),
-                                  blob + ex.up_q + tile_code_base(t0, nblk), blob + ex.up_q + tile_code_base(t1, nblk)};
-    const uint8_t *const as[4] = {blob + ex.gate_s + tile_scale_base(t0, nblk), blob + ex.gate_s + tile_scale_base(t1, nblk),
-                                  blob + ex.up_s + tile_scale_base(t0, nblk), blob + ex.up_s + tile_scale_base(t1, nblk)};
+    const uint8_t *aq[NA], *as[NA];
+#pragma unroll
+    for (int j = 0; j < kTilesPerMat; ++j) {
+        const int tj = min(f0 / 16 + j, last_tile);
+        aq[j] = blob + ex.gate_q + tile_code_base(tj, nblk);
+        as[j] = blob + ex.gate_s + tile_scale_base(tj, nblk);
+        aq[kTilesPerMat + j] = blob + ex.up_q + tile_code_base(tj, nblk);
+        as[kTilesPerMat + j] = blob + ex.up_s + tile_scale_base(tj, nblk);
+    }
     const ALane al(nblk, lane);
-    f32x4_t acc[4][kRowGroups];
+    f32x4_t acc[NA][NG];
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < NA; ++j)
 #pragma unroll
-        for (int rg = 0; rg < kRowGroups; ++rg) acc[j][rg] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int g = 0; g < NG; ++g) acc[j][g] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     const int Kp = pad128(H);
-    gemm_mainloop<4>(aq, as, al, Kp / 128, xq, xs, Kp, s_brow, tl.n, sB, sBs, acc);
+    gemm_mainloop<NG, W, NA>(aq, as, al, Kp / 128, xq, xs, Kp, s_brow, tl.n, sB, sBs, acc);
 
-    // epilogue: SwiGLU into LDS, then one 32-feature block per row to FP8 terms
-    const bool live = f0 < F;  // F % 32 == 0: a wavefront is all features or all padding
-    if (live) {
+    // epilogue: SwiGLU of the workgroup's features into LDS, then one
+    // 32-feature block per (row, block) to FP8 terms
+    __syncthreads();  // the staging buffers become the SwiGLU outputs
+    float *sAct = reinterpret_cast<float *>(sB);
+    const int col = lane & 15, kh = lane >> 4;
+    if (f0 < F) {  // F % 16 == 0: a wavefront's features are all real or all padding
         const float *gb = reinterpret_cast<const float *>(blob + ex.gate_b);
         const float *ub = reinterpret_cast<const float *>(blob + ex.up_b);
-        const int rq = (lane & 15) >> 2;
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < kTilesPerMat; ++j)
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
-                const int fl = 16 * j + 4 * (lane >> 4) + v;
-                const float bg = gb[f0 + fl], bu = ub[f0 + fl];
+                const int fl = Gm::kGURowsWave * w + 16 * j + 4 * kh + v;  // feature - fw
+                const float bg = gb[fw + fl], bu = ub[fw + fl];
 #pragma unroll
-                for (int rg = 0; rg < kRowGroups; ++rg) {
-                    // the quad sums run on every lane (DPP reads its neighbours)
-                    const float g = quad_sum(acc[j][rg][v]), u = quad_sum(acc[2 + j][rg][v]);
-                    if ((lane & 3) == 0)
-                        sAct[w][4 * rg + rq][fl] = swiglu(g + bg, u + bu, sc.alpha, sc.limit, sc.up_offset);
-                }
+                for (int g = 0; g < NG; ++g)
+                    sAct[(16 * g + col) * kActStride + fl] =
+                        swiglu(acc[j][g][v] + bg, acc[kTilesPerMat + j][g][v] + bu, sc.alpha, sc.limit,
+                               sc.up_offset);
             }
     }
     __syncthreads();
+    // (row, block) tasks, one per half-wavefront; blocks at or past F are the
+    // K padding of the down GEMM's operand (zero codes), blocks past Fp skipped
+    constexpr int kBlocks = Gm::kGateUpRows / 32;
     const int half = lane >> 5, i = lane & 31, nbp = Fp / 32;
-    for (int r0 = 0; r0 < tl.n; r0 += 2) {
-        const int row = r0 + half;
+    const int ntask = tl.n * kBlocks;
+    for (int task0 = 2 * w; task0 < ntask; task0 += 2 * W) {
+        const int task = task0 + half;
+        const bool on = task < ntask;
+        const int row = on ? task / kBlocks : 0, blk = on ? task - row * kBlocks : 0;
+        const int fb = fw + 32 * blk;  // first feature of the block
         uint32_t codes = 0, scales = 0x7f7f7f7fu;
-        if (live) fp8_terms_group(sAct[w][row][i], codes, scales);
-        if (row < tl.n) {
+        if (fb < F) fp8_terms_group(sAct[row * kActStride + 32 * blk + i], codes, scales);
+        if (on && fb < Fp) {
             const size_t p = static_cast<size_t>(tl.p0 + row);
 #pragma unroll
             for (int n = 0; n < kTerms; ++n) {
-                act_q[(p * kTerms + n) * Fp + f0 + i] = static_cast<uint8_t>(codes >> (8 * n));
-                if (i == 0) act_s[(p * kTerms + n) * nbp + f0 / 32] = static_cast<uint8_t>(scales >> (8 * n));
+                act_q[(p * kTerms + n) * Fp + fb + i] = static_cast<uint8_t>(codes >> (8 * n));
+                if (i == 0) act_s[(p * kTerms + n) * nbp + fb / 32] = static_cast<uint8_t>(scales >> (8 * n));
             }
         }
     }
 }
 
-// down: grid = kXcds-rounded ceil(H / 256) x max_tiles items.
-__global__ __launch_bounds__(kThreads) void down_gemm_kernel(
+// down: grid = kXcds-rounded max_tiles x ceil(H / kDownRows) items.
+template <int NG, int W, int NA>
+__global__ __launch_bounds__(64 * W) void down_gemm_kernel(
     const uint8_t *act_q, const uint8_t *act_s, int T, int H, int F, int E, int k, int n_shared,
     ExpertPtrs ex, ExpertPtrs sh, const int32_t *offsets, const int32_t *perm, const float *wts,
-    const int32_t *mprefix, int max_tiles, float *out) {
+    const int32_t *mprefix, float *out) {
+    using Gm = Geo<NG, W, NA>;
     __shared__ int s_pre[kMaxE + 2];
-    __shared__ int s_brow[kGemmBM];
-    __shared__ int s_tok[kGemmBM];
-    __shared__ float s_wt[kGemmBM];
-    __shared__ __align__(16) uint8_t sB[2 * kBBufBytes];
-    __shared__ uint32_t sBs[2 * kGemmBM * kTerms];
+    __shared__ int s_brow[Gm::kRows];
+    __shared__ int s_tok[Gm::kRows];
+    __shared__ float s_wt[Gm::kRows];
+    __shared__ __align__(16) uint8_t sB[2 * Gm::kBufBytes];
+    __shared__ uint8_t sBs[2 * 4 * Gm::kScales];
     const int G = E + n_shared, R = T * k;
     load_pre(mprefix, G, s_pre);
-    const int nrb = (H + kDownRowsWG - 1) / kDownRowsWG;
+    const int nrb = (H + Gm::kDownRows - 1) / Gm::kDownRows;
     int rb;
     Tile tl;
-    if (!find_item(max_tiles, nrb, offsets, s_pre, G, rb, tl)) return;
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    if (tid < kGemmBM) {
+    if (!find_item(nrb, Gm::kRows, offsets, s_pre, G, rb, tl)) return;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    if (tid < Gm::kRows) {
         const int p = tl.p0 + min(tid, tl.n - 1);
         s_brow[tid] = p;  // activation rows are in position order
         if (p < R) {
@@ -277,38 +349,40 @@ __global__ __launch_bounds__(kThreads) void down_gemm_kernel(
     }
     __syncthreads();
     const uint8_t *blob = tl.g < E ? ex.base + static_cast<size_t>(tl.g) * ex.stride : sh.base;
-    const int h0 = rb * kDownRowsWG + 64 * w;  // this wavefront's 64 hidden rows
+    const int h0 = rb * Gm::kDownRows + 16 * NA * w;  // this wavefront's hidden rows
     const int last_tile = H / 16 - 1, nblk = F / 32;
-    const uint8_t *aq[4], *as[4];
+    const uint8_t *aq[NA], *as[NA];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < NA; ++j) {
         const int tj = min(h0 / 16 + j, last_tile);
         aq[j] = blob + ex.down_q + tile_code_base(tj, nblk);
         as[j] = blob + ex.down_s + tile_scale_base(tj, nblk);
     }
     const ALane al(nblk, lane);
-    f32x4_t acc[4][kRowGroups];
+    f32x4_t acc[NA][NG];
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < NA; ++j)
 #pragma unroll
-        for (int rg = 0; rg < kRowGroups; ++rg) acc[j][rg] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int g = 0; g < NG; ++g) acc[j][g] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     const int Fp = pad128(F);
-    gemm_mainloop<4>(aq, as, al, Fp / 128, act_q, act_s, Fp, s_brow, tl.n, sB, sBs, acc);
+    gemm_mainloop<NG, W, NA>(aq, as, al, Fp / 128, act_q, act_s, Fp, s_brow, tl.n, sB, sBs, acc);
 
     const float *db = reinterpret_cast<const float *>(blob + ex.down_b);
-    const int rq = (lane & 15) >> 2;
+    const int col = lane & 15, kh = lane >> 4;
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < NA; ++j)
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-            const int h = h0 + 16 * j + 4 * (lane >> 4) + v;
-            const float bias = h < H ? db[h] : 0.f;
+            const int h = h0 + 16 * j + 4 * kh + v;
+            if (h < H) {
+                const float bias = db[h];
 #pragma unroll
-            for (int rg = 0; rg < kRowGroups; ++rg) {
-                const float y = quad_sum(acc[j][rg][v]);
-                const int row = 4 * rg + rq;
-                if ((lane & 3) == 0 && h < H && row < tl.n)
-                    unsafeAtomicAdd(out + static_cast<size_t>(s_tok[row]) * H + h, s_wt[row] * (y + bias));
+                for (int g = 0; g < NG; ++g) {
+                    const int row = 16 * g + col;
+                    if (row < tl.n)
+                        unsafeAtomicAdd(out + static_cast<size_t>(s_tok[row]) * H + h,
+                                        s_wt[row] * (acc[j][g][v] + bias));
+                }
             }
         }
 }
@@ -320,26 +394,61 @@ int items(int nrb, int max_tiles) {
 
 }  // namespace
 
+// 16-row tiles for experts of about 16 rows, 32 above. 64-row tiles (8
+// wavefronts x 2 A fragments) are built but not chosen: at 2 A fragments per
+// B operand their LDS reads run at the LDS limit (measured slower on the
+// 24-layer stack and the DS4-shaped layer).
+int gemm_tile_rows(int T, int k, int E, int n_shared) {
+    const double avg = static_cast<double>(T) * (k + n_shared) / (E + n_shared);
+    return avg >= 20.0 ? 32 : 16;
+}
+
+// Tiles of 16 and 32 rows: 4 wavefronts with 4 A fragments each; 64-row
+// tiles: 8 wavefronts with 2 (the accumulators and B staging of a 64-row tile
+// leave no room for 4).
 hipError_t launch_gate_up_gemm(const uint8_t *xq, const uint8_t *xs, int T, int H, int F, int E,
                                int k, int n_shared, const ExpertPtrs &ex, const ExpertPtrs &sh,
                                SwigluConsts c, const int32_t *offsets, const int32_t *perm,
-                               const int32_t *mprefix, int max_tiles, uint8_t *act_q,
+                               const int32_t *mprefix, int tile_rows, int max_tiles, uint8_t *act_q,
                                uint8_t *act_s, hipStream_t s) {
-    const int grid = items(pad128(F) / kGateUpRowsWG, max_tiles);
-    if (grid == 0) return hipSuccess;
-    launch_kernel(gate_up_gemm_kernel, grid, kThreads, s, xq, xs, T, H, F, E, k, n_shared, ex, sh,
-                  c, offsets, perm, mprefix, max_tiles, act_q, act_s);
+#define MOE_GU(NG, W, NA)                                                                           \
+    do {                                                                                            \
+        using Gm = Geo<NG, W, NA>;                                                                  \
+        const int grid = items((pad128(F) + Gm::kGateUpRows - 1) / Gm::kGateUpRows, max_tiles);    \
+        if (grid == 0) return hipSuccess;                                                           \
+        launch_kernel(gate_up_gemm_kernel<NG, W, NA>, grid, 64 * (W), s, xq, xs, T, H, F, E, k,     \
+                      n_shared, ex, sh, c, offsets, perm, mprefix, act_q, act_s);                   \
+    } while (0)
+    switch (tile_rows) {
+    case 16: MOE_GU(1, 4, 4); break;
+    case 32: MOE_GU(2, 4, 4); break;
+    case 64: MOE_GU(4, 8, 2); break;
+    default: return hipErrorInvalidValue;
+    }
+#undef MOE_GU
     return hipGetLastError();
 }
 
 hipError_t launch_down_gemm(const uint8_t *act_q, const uint8_t *act_s, int T, int H, int F, int E,
                             int k, int n_shared, const ExpertPtrs &ex, const ExpertPtrs &sh,
                             const int32_t *offsets, const int32_t *perm, const float *wts,
-                            const int32_t *mprefix, int max_tiles, float *out, hipStream_t s) {
-    const int grid = items((H + kDownRowsWG - 1) / kDownRowsWG, max_tiles);
-    if (grid == 0) return hipSuccess;
-    launch_kernel(down_gemm_kernel, grid, kThreads, s, act_q, act_s, T, H, F, E, k, n_shared, ex, sh,
-                  offsets, perm, wts, mprefix, max_tiles, out);
+                            const int32_t *mprefix, int tile_rows, int max_tiles, float *out,
+                            hipStream_t s) {
+#define MOE_DN(NG, W, NA)                                                                           \
+    do {                                                                                            \
+        using Gm = Geo<NG, W, NA>;                                                                  \
+        const int grid = items((H + Gm::kDownRows - 1) / Gm::kDownRows, max_tiles);                 \
+        if (grid == 0) return hipSuccess;                                                           \
+        launch_kernel(down_gemm_kernel<NG, W, NA>, grid, 64 * (W), s, act_q, act_s, T, H, F, E, k,  \
+                      n_shared, ex, sh, offsets, perm, wts, mprefix, out);                          \
+    } while (0)
+    switch (tile_rows) {
+    case 16: MOE_DN(1, 4, 4); break;
+    case 32: MOE_DN(2, 4, 4); break;
+    case 64: MOE_DN(4, 8, 2); break;
+    default: return hipErrorInvalidValue;
+    }
+#undef MOE_DN
     return hipGetLastError();
 }
 

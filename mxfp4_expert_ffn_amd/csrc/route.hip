@@ -410,11 +410,12 @@ hipError_t launch_topk(const double *partial, int S, const float *bias, int T, i
     return hipGetLastError();
 }
 
-hipError_t launch_permute(const int32_t *idx, int T, int E, int k, int n_shared, int32_t *counts,
+hipError_t launch_permute(const int32_t *idx, int T, int E, int k, int n_shared, int tile_rows,
+                          int32_t *counts,
                           int32_t *offsets, int32_t *perm, int32_t *inv, int32_t *rank,
                           int32_t *mprefix, int32_t *out_counts, int32_t *out_offsets,
                           int32_t *out_perm, int32_t *out_inv, hipStream_t s) {
-    launch_kernel(permute_kernel, 1, 1024, s, idx, T, E, k, n_shared, kGemmBM, counts, offsets,
+    launch_kernel(permute_kernel, 1, 1024, s, idx, T, E, k, n_shared, tile_rows, counts, offsets,
                   perm, inv, rank, mprefix, out_counts, out_offsets, out_perm, out_inv);
     return hipGetLastError();
 }
