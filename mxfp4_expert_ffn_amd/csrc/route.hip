@@ -5,6 +5,8 @@
 // add_bias_batch, top_experts, softmax, routes_by_expert in token order),
 // `top_experts` (descending value, lower index on ties); antirez `ds4.c`
 // `rms_norm_weight` (sum of squares accumulated in double).
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -156,48 +158,77 @@ __global__ __launch_bounds__(256) void router_gemv_kernel(const void *x, const f
     }
 }
 
-// Token batches: workgroup = 32 tokens x 64 experts over one hidden slice of
-// `slice` units (a multiple of 32); thread (ti, ei) owns tokens 2ti, 2ti+1 and
-// experts ei + 16q. Tiles of x and the router rows are staged in LDS as fp64.
+// Tiled router for larger batches: a workgroup computes the fp64 partial
+// logits of 64 tokens x 64 experts over one K slice, each of its 256 threads
+// 4 tokens x 4 experts. K advances 32 at a time through double-buffered LDS
+// tiles kept in the inputs' own precision (widened exactly to fp64 when
+// read); the next chunk's loads are in flight during the current chunk's
+// FMAs. Tokens and experts past T and E are clamped on load and not written.
 template <int KIND>
 __global__ __launch_bounds__(256) void router_tiled_kernel(const void *x, const float *w, int T,
                                                            int H, int E, int slice,
                                                            double *partial) {
-    __shared__ double xs[32][33];
-    __shared__ double wsm[64][33];
-    const int t0 = blockIdx.x * 32, e0 = blockIdx.y * 64, s = blockIdx.z;
-    const int ti = threadIdx.x >> 4, ei = threadIdx.x & 15;
+    typedef typename std::conditional<KIND == 2, double, float>::type XT;
+    constexpr int kPad = 4;
+    __shared__ __align__(16) XT xs[2][32][64 + kPad];     // [k][token]
+    __shared__ __align__(16) float wsm[2][32][64 + kPad];  // [k][expert]
+    const int tid = threadIdx.x;
+    const int t0 = blockIdx.x * 64, e0 = blockIdx.y * 64, s = blockIdx.z;
     const int hbeg = s * slice, hend = min(H, hbeg + slice);
-    double acc[2][4] = {};
+    // loads: thread -> (row tid / 4, k part 8 * (tid % 4)) of the 64 x 32 chunk
+    const int lr = tid >> 2, lk = 8 * (tid & 3);
+    const size_t xrow = static_cast<size_t>(min(t0 + lr, T - 1)) * H;
+    const float *wrow = w + static_cast<size_t>(min(e0 + lr, E - 1)) * H;
+    XT xv[8];
+    float wv[8];
+    auto load = [&](int h0) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            if (KIND == 1) xv[i] = bf16_bits_to_f32(static_cast<const uint16_t *>(x)[xrow + h0 + lk + i]);
+            else xv[i] = static_cast<const XT *>(x)[xrow + h0 + lk + i];
+        }
+        const float4 a = *reinterpret_cast<const float4 *>(wrow + h0 + lk);
+        const float4 b = *reinterpret_cast<const float4 *>(wrow + h0 + lk + 4);
+        wv[0] = a.x; wv[1] = a.y; wv[2] = a.z; wv[3] = a.w;
+        wv[4] = b.x; wv[5] = b.y; wv[6] = b.z; wv[7] = b.w;
+    };
+    auto store = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            xs[buf][lk + i][lr] = xv[i];
+            wsm[buf][lk + i][lr] = wv[i];
+        }
+    };
+    const int ti = tid >> 4, ei = tid & 15;  // 4 tokens 4*ti.., 4 experts 4*ei..
+    double acc[4][4] = {};
+    load(hbeg);
+    int buf = 0;
     for (int h0 = hbeg; h0 < hend; h0 += 32) {
-        for (int i = threadIdx.x; i < 32 * 32; i += 256) {
-            const int r = i >> 5, c = i & 31, t = t0 + r;
-            xs[r][c] = t < T ? load_in<KIND>(x, static_cast<size_t>(t) * H + h0 + c) : 0.0;
-        }
-        for (int i = threadIdx.x; i < 64 * 32; i += 256) {
-            const int r = i >> 5, c = i & 31, e = e0 + r;
-            wsm[r][c] = e < E ? static_cast<double>(w[static_cast<size_t>(e) * H + h0 + c]) : 0.0;
-        }
+        store(buf);
         __syncthreads();
+        if (h0 + 32 < hend) load(h0 + 32);
 #pragma unroll 8
         for (int c = 0; c < 32; ++c) {
-            const double a0 = xs[2 * ti][c], a1 = xs[2 * ti + 1][c];
+            double a[4], b[4];
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const double bw = wsm[ei + 16 * q][c];
-                acc[0][q] = fma(a0, bw, acc[0][q]);
-                acc[1][q] = fma(a1, bw, acc[1][q]);
+                a[q] = static_cast<double>(xs[buf][c][4 * ti + q]);
+                b[q] = static_cast<double>(wsm[buf][c][4 * ei + q]);
             }
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[i][j] = fma(a[i], b[j], acc[i][j]);
         }
-        __syncthreads();
+        buf ^= 1;
     }
 #pragma unroll
-    for (int r = 0; r < 2; ++r) {
-        const int t = t0 + 2 * ti + r;
+    for (int i = 0; i < 4; ++i) {
+        const int t = t0 + 4 * ti + i;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int e = e0 + ei + 16 * q;
-            if (t < T && e < E) partial[(static_cast<size_t>(s) * T + t) * E + e] = acc[r][q];
+        for (int j = 0; j < 4; ++j) {
+            const int e = e0 + 4 * ei + j;
+            if (t < T && e < E) partial[(static_cast<size_t>(s) * T + t) * E + e] = acc[i][j];
         }
     }
 }
@@ -250,7 +281,7 @@ __global__ __launch_bounds__(256) void topk_kernel(const double *partial, int S,
 // ---------------------------------------------------------------- permutation
 // One workgroup of 1024 threads. Routes r = t*k + j are taken in chunks of
 // 1024; inside a wavefront the lanes holding the same expert are found with
-// ballots and ranked by lane; per-wave counts are prefix-summed per expert in
+// eight bit-plane ballots and ranked by lane; per-wave counts are prefix-summed per expert in
 // wave order, so a route's rank counts exactly the earlier routes of its
 // expert: the permutation is stable (ascending token). Then counts, the
 // exclusive scan, the M-tile prefix for the grouped GEMMs, perm and inv.
@@ -272,17 +303,19 @@ __global__ __launch_bounds__(1024) void permute_kernel(
         __syncthreads();
         const int r = c0 + tid;
         const bool valid = r < R;
-        const int e = valid ? idx[r] : -1;
-        int myrank = 0;
-        uint64_t todo = __ballot(valid);
-        while (todo) {
-            const int leader = __ffsll(static_cast<long long>(todo)) - 1;
-            const int le = __shfl(e, leader, 64);
-            const uint64_t m = __ballot(e == le);
-            if (e == le) myrank = __popcll(m & lt_mask);
-            if (lane == leader) wcnt[w][le] = __popcll(m);
-            todo &= ~m;
+        const int e = valid ? idx[r] : 0;
+        // lanes holding the same expert: the intersection of the 8 bit-plane
+        // ballots of the expert index
+        static_assert(kMaxE <= 256, "expert indices fit 8 bit planes");
+        uint64_t eq = __ballot(valid);
+#pragma unroll
+        for (int b = 0; b < 8; ++b) {
+            const bool bit = (e >> b) & 1;
+            const uint64_t plane = __ballot(bit);
+            eq &= bit ? plane : ~plane;
         }
+        const int myrank = __popcll(eq & lt_mask);
+        if (valid && myrank == 0) wcnt[w][e] = __popcll(eq);  // the first lane of its expert
         __syncthreads();
         for (int ee = tid; ee < E; ee += 1024) {
             int run = base[ee];
@@ -345,7 +378,7 @@ RouterPlan router_plan(int T, int H, int E) {
         p.splits = (H + kRouterGemvSlice - 1) / kRouterGemvSlice;
         return p;
     }
-    const int tiles = ((T + 31) / 32) * ((E + 63) / 64);
+    const int tiles = ((T + 63) / 64) * ((E + 63) / 64);
     int want = (512 + tiles - 1) / tiles;
     want = want < 1 ? 1 : (want > 16 ? 16 : want);
     const int units = H / 32;
@@ -382,7 +415,7 @@ hipError_t launch_router(const void *x, int in_kind, const float *w, int T, int 
                           qbf, Kp, xq, xs);
     } else {
         if (terms) return hipErrorInvalidValue;  // see router_quantizes
-        const dim3 grid((T + 31) / 32, (E + 63) / 64, p.splits);
+        const dim3 grid((T + 63) / 64, (E + 63) / 64, p.splits);
         if (in_kind == 0)
             launch_kernel(router_tiled_kernel<0>, grid, 256, s, x, w, T, H, E, p.slice, partial);
         else if (in_kind == 1)
