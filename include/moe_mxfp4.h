@@ -187,8 +187,10 @@ int moe_forward_decode(const moe_shape *shape, const void *hidden, const float *
 
 /* The whole block for a token batch: routing, permutation, grouped GEMMs on
  * the matrix cores (gate/up with bias and clamped SwiGLU fused; down with
- * bias, route weight and scatter-add into out fused). Same arguments as
- * moe_forward_decode; any T. out may alias a float32 hidden.
+ * bias and route weight fused), then a combine that adds each token's routes
+ * to its residual in a fixed order (deterministic). Same arguments as
+ * moe_forward_decode; any T up to the workspace and 2^32-byte FP8-term limits
+ * (MOE_ERR_UNSUPPORTED past them). out may alias a float32 hidden.
  * Pages: goosedump `mixture_of_experts_batch`, `expert_batch_output`,
  * `mix_expert_outputs`. */
 int moe_forward_prefill(const moe_shape *shape, const void *hidden, const float *norm_w,
@@ -217,8 +219,9 @@ typedef enum moe_kernel_id {
     MOE_KERNEL_DECODE_DOWN = 5,
     MOE_KERNEL_GATE_UP_GEMM = 6,
     MOE_KERNEL_DOWN_GEMM = 7,
-    MOE_KERNEL_QUANTIZE = 8         /* FP8 terms of the expert input, when it is
+    MOE_KERNEL_QUANTIZE = 8,        /* FP8 terms of the expert input, when it is
                                        its own kernel (T > 16) */
+    MOE_KERNEL_COMBINE = 9          /* prefill: residual + sum of the routes' outputs */
 } moe_kernel_id;
 
 /* Measurement hook (for benchmarks and profilers, not needed to compute):

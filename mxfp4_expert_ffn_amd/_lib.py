@@ -16,7 +16,7 @@ MOE_BF16 = 1
 
 # moe_kernel_id
 KERNELS = {"rmsnorm": 0, "router": 1, "topk": 2, "permute": 3, "decode_gate_up": 4,
-           "decode_down": 5, "gate_up_gemm": 6, "down_gemm": 7, "quantize": 8}
+           "decode_down": 5, "gate_up_gemm": 6, "down_gemm": 7, "quantize": 8, "combine": 9}
 
 
 class MoeShape(ctypes.Structure):

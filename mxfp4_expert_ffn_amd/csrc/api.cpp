@@ -103,6 +103,7 @@ struct Workspace {
     // SwiGLU output [T*k + T*n_shared] (route order in decode, position
     // order in prefill)
     uint8_t *xq, *xs, *act_q, *act_s;
+    float *y;  // prefill: weighted down output per row position [T*k + T*n_shared][H]
     uint64_t bytes;
 };
 
@@ -134,6 +135,7 @@ Workspace carve(const moe_shape *s, uint8_t *base) {
     w.xs = take(T * moe::kTerms * Hp / 32);
     w.act_q = take((R + T * ns) * moe::kTerms * Fp);
     w.act_s = take((R + T * ns) * moe::kTerms * Fp / 32);
+    w.y = reinterpret_cast<float *>(take((R + T * ns) * H * 4));
     w.bytes = o;
     return w;
 }
@@ -387,8 +389,7 @@ int moe_forward_prefill(const moe_shape *s, const void *hidden, const float *nor
     MOE_TRY(launch(MOE_KERNEL_TOPK, "topk", st, [&] {
         return moe::launch_topk(w.partial, w.splits, router_b, s->T, s->E, s->k, s->route_scale,
                                 w.idx, w.wts, ro ? ro->topk_idx : nullptr,
-                                ro ? ro->topk_w : nullptr, hidden, s->act_dtype == MOE_BF16,
-                                s->H, out, st);
+                                ro ? ro->topk_w : nullptr, nullptr, 0, s->H, nullptr, st);
     }));
     const int bm = moe::gemm_tile_rows(s->T, s->k, s->E, s->n_shared);
     MOE_TRY(launch(MOE_KERNEL_PERMUTE, "permute", st, [&] {
@@ -408,7 +409,11 @@ int moe_forward_prefill(const moe_shape *s, const void *hidden, const float *nor
     }));
     MOE_TRY(launch(MOE_KERNEL_DOWN_GEMM, "down_gemm", st, [&] {
         return moe::launch_down_gemm(w.act_q, w.act_s, s->T, s->H, s->F, s->E, s->k, s->n_shared,
-                                     ex, sh, w.offsets, w.perm, w.wts, w.mprefix, bm, mt, out, st);
+                                     ex, sh, w.offsets, w.perm, w.wts, w.mprefix, bm, mt, w.y, st);
+    }));
+    MOE_TRY(launch(MOE_KERNEL_COMBINE, "combine", st, [&] {
+        return moe::launch_combine(w.y, w.inv, s->T, s->H, s->k, s->n_shared, hidden,
+                                   s->act_dtype == MOE_BF16, out, st);
     }));
     return ok();
 }
@@ -434,7 +439,7 @@ int moe_profile_next_launch(int32_t kernel, hipEvent_t start, hipEvent_t stop) {
         g_hook = ProfileHook{};
         return ok();
     }
-    if (kernel > MOE_KERNEL_QUANTIZE || !start || !stop)
+    if (kernel > MOE_KERNEL_COMBINE || !start || !stop)
         return fail(MOE_ERR_INVALID_ARG, "unknown kernel id %d or NULL event", kernel);
     g_hook.kernel = kernel;
     g_hook.start = start;

@@ -121,7 +121,7 @@ __device__ __forceinline__ double wave_max_f64(double v) {
 __device__ __forceinline__ float swiglu(float g, float u, float alpha, float limit, float up_off) {
     g = fminf(g, limit);
     u = fminf(fmaxf(u, -limit), limit);
-    return g / (1.0f + __expf(-alpha * g)) * (u + up_off);
+    return g * __frcp_rn(1.0f + __expf(-alpha * g)) * (u + up_off);
 }
 
 // ---------------------------------------------------------------- top-k
@@ -273,18 +273,23 @@ __device__ __forceinline__ float half_wave_max(float v) {
 }
 
 // Split the 32 values held by the 32 lanes of a half-wavefront into kTerms
-// E4M3 codes with one E8M0 scale byte per term (scale 2^(floor(log2 amax)-7)
-// of what is left, so codes stay below 256). Returns the codes packed in one
+// E4M3 codes, term n with the E8M0 scale 2^(e0 - 4n), e0 = floor(log2 amax) - 7
+// (so the first term's codes lie in [128, 256) x 2^e0 at the block maximum).
+// After term n every value is within half an E4M3 step of that term, at most
+// 8 x 2^(e0 - 4n), so term n + 1 sees at most 128 x its own scale and never
+// saturates; after kTerms terms the error is at most 2^(e0 - 4 kTerms + 7),
+// i.e. about 2^-4kTerms of the block maximum. Returns the codes packed in one
 // dword (term n in byte n) and the scale bytes likewise. Every lane of the
-// wavefront must take part.
+// wavefront must take part (one half-wavefront maximum).
 __device__ __forceinline__ void fp8_terms_group(float v, uint32_t &codes, uint32_t &scales) {
+    const float amax = half_wave_max(fabsf(v));
+    const int e0 = static_cast<int>((__float_as_uint(amax) >> 23) & 0xffu) - 127 - 7;
     codes = 0;
     scales = 0;
     float r = v;
 #pragma unroll
     for (int n = 0; n < kTerms; ++n) {
-        const float amax = half_wave_max(fabsf(r));
-        int e = static_cast<int>((__float_as_uint(amax) >> 23) & 0xffu) - 127 - 7;
+        int e = e0 - 4 * n;
         e = e < -126 ? -126 : (e > 127 ? 127 : e);
         const uint32_t q = e4m3_encode(r * pow2f(-e));
         r -= e4m3_decode(q) * pow2f(e);

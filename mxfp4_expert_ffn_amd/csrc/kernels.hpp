@@ -133,11 +133,15 @@ hipError_t launch_gate_up_gemm(const uint8_t *xq, const uint8_t *xs, int T, int 
                                SwigluConsts c, const int32_t *offsets, const int32_t *perm,
                                const int32_t *mprefix, int tile_rows, int max_tiles, uint8_t *act_q,
                                uint8_t *act_s, hipStream_t s);
+// y [T*k + T*n_shared][H] fp32: route weight x (down + bias) per row position
 hipError_t launch_down_gemm(const uint8_t *act_q, const uint8_t *act_s, int T, int H, int F, int E,
                             int k, int n_shared, const ExpertPtrs &ex, const ExpertPtrs &sh,
                             const int32_t *offsets, const int32_t *perm, const float *wts,
-                            const int32_t *mprefix, int tile_rows, int max_tiles, float *out,
+                            const int32_t *mprefix, int tile_rows, int max_tiles, float *y,
                             hipStream_t s);
+// out[t] = resid[t] + sum_j y[inv[t*k + j]] (+ y[T*k + t]); out may alias a float32 resid
+hipError_t launch_combine(const float *y, const int32_t *inv, int T, int H, int k, int n_shared,
+                          const void *resid, int resid_bf16, float *out, hipStream_t s);
 
 // debug -------------------------------------------------------------------
 // Decoded weights of one packed plane as float32 [rows][K]: path 0 through

@@ -20,8 +20,9 @@
 // gate/up: NA/2 16-row tiles of each matrix per wavefront. The epilogue adds
 // the biases, applies the clamped SwiGLU and writes the FP8 terms of each
 // 32-feature block per row (the down GEMM's operand). down: NA 16-row tiles
-// per wavefront. The epilogue adds the bias and scatter-adds route weight x
-// result into out[token] (which holds the residual).
+// per wavefront. The epilogue adds the bias and writes route weight x result
+// as the row's fp32 output y[p]; the combine kernel then adds each token's
+// rows to its residual in a fixed order (no atomics, deterministic).
 //
 // Page: goosedump `gpt_oss.rs`, `mixture_of_experts` and its grouped form over
 // expert-sorted rows (`mixture_of_experts_batch`); DeepSeek-V4 shared expert
@@ -63,25 +64,29 @@ struct Tile {
     int n;   // rows in the tile (1..16*NG)
 };
 
-// Work item of this workgroup: item = tile * nrb + row block, dealt XCD-major
-// (items i and i+1 run back to back on one die), so the row blocks of one
-// tile share its activation rows in that die's L2 and consecutive tiles of an
-// expert follow each other; false when it is past the real tiles.
+// Work item of this workgroup, dealt XCD-major (items i and i+1 run back to
+// back on one die). Items run group by group; inside a group (an expert's
+// tiles x the row blocks) row block by row block, and inside a row block tile
+// by tile: all tiles of an expert that need the same weight rows run side by
+// side and share them in L2, and a tile's row blocks follow each other (its
+// activation rows stay in L2 too). False when past the real tiles.
 __device__ __forceinline__ bool find_item(int nrb, int bm, const int32_t *offsets,
                                           const int *s_pre, int G, int &rb, Tile &tl) {
     const int per = gridDim.x / kXcds;
     const int item = (blockIdx.x % kXcds) * per + blockIdx.x / kXcds;
-    const int tile = item / nrb;
-    rb = item - tile * nrb;
-    if (tile >= s_pre[G]) return false;
-    int lo = 0, hi = G - 1;  // last group whose first tile is <= tile
+    if (item >= s_pre[G] * nrb) return false;
+    int lo = 0, hi = G - 1;  // last group whose first item is <= item
     while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
-        if (s_pre[mid] <= tile) lo = mid;
+        if (s_pre[mid] * nrb <= item) lo = mid;
         else hi = mid - 1;
     }
+    const int nt = s_pre[lo + 1] - s_pre[lo];  // >= 1: a group with no tiles owns no items
+    const int local = item - s_pre[lo] * nrb;
+    rb = local / nt;
+    const int tile = local - rb * nt;
     tl.g = lo;
-    tl.p0 = offsets[lo] + (tile - s_pre[lo]) * bm;
+    tl.p0 = offsets[lo] + tile * bm;
     tl.n = min(bm, offsets[lo + 1] - tl.p0);
     return true;
 }
@@ -319,11 +324,10 @@ template <int NG, int W, int NA>
 __global__ __launch_bounds__(64 * W) void down_gemm_kernel(
     const uint8_t *act_q, const uint8_t *act_s, int T, int H, int F, int E, int k, int n_shared,
     ExpertPtrs ex, ExpertPtrs sh, const int32_t *offsets, const int32_t *perm, const float *wts,
-    const int32_t *mprefix, float *out) {
+    const int32_t *mprefix, float *y) {
     using Gm = Geo<NG, W, NA>;
     __shared__ int s_pre[kMaxE + 2];
     __shared__ int s_brow[Gm::kRows];
-    __shared__ int s_tok[Gm::kRows];
     __shared__ float s_wt[Gm::kRows];
     __shared__ __align__(16) uint8_t sB[2 * Gm::kBufBytes];
     __shared__ uint8_t sBs[2 * 4 * Gm::kScales];
@@ -338,14 +342,7 @@ __global__ __launch_bounds__(64 * W) void down_gemm_kernel(
     if (tid < Gm::kRows) {
         const int p = tl.p0 + min(tid, tl.n - 1);
         s_brow[tid] = p;  // activation rows are in position order
-        if (p < R) {
-            const int route = perm[p];
-            s_tok[tid] = route / k;
-            s_wt[tid] = wts[route];
-        } else {
-            s_tok[tid] = p - R;
-            s_wt[tid] = 1.0f;
-        }
+        s_wt[tid] = p < R ? wts[perm[p]] : 1.0f;
     }
     __syncthreads();
     const uint8_t *blob = tl.g < E ? ex.base + static_cast<size_t>(tl.g) * ex.stride : sh.base;
@@ -367,24 +364,56 @@ __global__ __launch_bounds__(64 * W) void down_gemm_kernel(
     const int Fp = pad128(F);
     gemm_mainloop<NG, W, NA>(aq, as, al, Fp / 128, act_q, act_s, Fp, s_brow, tl.n, sB, sBs, acc);
 
+    // y[p][h] = route weight x (down + bias), four consecutive h per lane
     const float *db = reinterpret_cast<const float *>(blob + ex.down_b);
     const int col = lane & 15, kh = lane >> 4;
 #pragma unroll
-    for (int j = 0; j < NA; ++j)
+    for (int j = 0; j < NA; ++j) {
+        const int h = h0 + 16 * j + 4 * kh;
+        if (h < H) {  // H % 16 == 0: the lane's four rows are all in or all out
+            const float4 bias = *reinterpret_cast<const float4 *>(db + h);
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            const int h = h0 + 16 * j + 4 * kh + v;
-            if (h < H) {
-                const float bias = db[h];
-#pragma unroll
-                for (int g = 0; g < NG; ++g) {
-                    const int row = 16 * g + col;
-                    if (row < tl.n)
-                        unsafeAtomicAdd(out + static_cast<size_t>(s_tok[row]) * H + h,
-                                        s_wt[row] * (acc[j][g][v] + bias));
+            for (int g = 0; g < NG; ++g) {
+                const int row = 16 * g + col;
+                if (row < tl.n) {
+                    const float wt = s_wt[row];
+                    const float4 yv = make_float4(wt * (acc[j][g][0] + bias.x), wt * (acc[j][g][1] + bias.y),
+                                                  wt * (acc[j][g][2] + bias.z), wt * (acc[j][g][3] + bias.w));
+                    *reinterpret_cast<float4 *>(y + static_cast<size_t>(tl.p0 + row) * H + h) = yv;
                 }
             }
         }
+    }
+}
+
+// out[t] = resid[t] + sum over slots j of y[inv[t*k + j]] (+ y[T*k + t] for the
+// shared expert), added in that fixed order; four hidden units per thread.
+__global__ __launch_bounds__(256) void combine_kernel(const float *y, const int32_t *inv, int T,
+                                                      int H, int k, int n_shared,
+                                                      const void *resid, int resid_bf16,
+                                                      float *out) {
+    const int H4 = H / 4;
+    const long long i = static_cast<long long>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (i >= static_cast<long long>(T) * H4) return;
+    const int t = static_cast<int>(i / H4), h = 4 * static_cast<int>(i - static_cast<long long>(t) * H4);
+    float4 a;
+    if (resid_bf16) {
+        const uint2 rb = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(resid) +
+                                                          static_cast<size_t>(t) * H + h);
+        a = make_float4(bf16_bits_to_f32(rb.x & 0xffffu), bf16_bits_to_f32(rb.x >> 16),
+                        bf16_bits_to_f32(rb.y & 0xffffu), bf16_bits_to_f32(rb.y >> 16));
+    } else {
+        a = *reinterpret_cast<const float4 *>(static_cast<const float *>(resid) + static_cast<size_t>(t) * H + h);
+    }
+    for (int j = 0; j < k; ++j) {
+        const float4 v = *reinterpret_cast<const float4 *>(y + static_cast<size_t>(inv[t * k + j]) * H + h);
+        a.x += v.x; a.y += v.y; a.z += v.z; a.w += v.w;
+    }
+    if (n_shared) {
+        const float4 v = *reinterpret_cast<const float4 *>(y + (static_cast<size_t>(T) * k + t) * H + h);
+        a.x += v.x; a.y += v.y; a.z += v.z; a.w += v.w;
+    }
+    *reinterpret_cast<float4 *>(out + static_cast<size_t>(t) * H + h) = a;
 }
 
 int items(int nrb, int max_tiles) {
@@ -432,7 +461,7 @@ hipError_t launch_gate_up_gemm(const uint8_t *xq, const uint8_t *xs, int T, int 
 hipError_t launch_down_gemm(const uint8_t *act_q, const uint8_t *act_s, int T, int H, int F, int E,
                             int k, int n_shared, const ExpertPtrs &ex, const ExpertPtrs &sh,
                             const int32_t *offsets, const int32_t *perm, const float *wts,
-                            const int32_t *mprefix, int tile_rows, int max_tiles, float *out,
+                            const int32_t *mprefix, int tile_rows, int max_tiles, float *y,
                             hipStream_t s) {
 #define MOE_DN(NG, W, NA)                                                                           \
     do {                                                                                            \
@@ -440,7 +469,7 @@ hipError_t launch_down_gemm(const uint8_t *act_q, const uint8_t *act_s, int T, i
         const int grid = items((H + Gm::kDownRows - 1) / Gm::kDownRows, max_tiles);                 \
         if (grid == 0) return hipSuccess;                                                           \
         launch_kernel(down_gemm_kernel<NG, W, NA>, grid, 64 * (W), s, act_q, act_s, T, H, F, E, k,  \
-                      n_shared, ex, sh, offsets, perm, wts, mprefix, out);                          \
+                      n_shared, ex, sh, offsets, perm, wts, mprefix, y);                            \
     } while (0)
     switch (tile_rows) {
     case 16: MOE_DN(1, 4, 4); break;
@@ -449,6 +478,15 @@ hipError_t launch_down_gemm(const uint8_t *act_q, const uint8_t *act_s, int T, i
     default: return hipErrorInvalidValue;
     }
 #undef MOE_DN
+    return hipGetLastError();
+}
+
+hipError_t launch_combine(const float *y, const int32_t *inv, int T, int H, int k, int n_shared,
+                          const void *resid, int resid_bf16, float *out, hipStream_t s) {
+    const long long n = static_cast<long long>(T) * (H / 4);
+    const int grid = static_cast<int>((n + 255) / 256);
+    if (grid == 0) return hipSuccess;
+    launch_kernel(combine_kernel, grid, 256, s, y, inv, T, H, k, n_shared, resid, resid_bf16, out);
     return hipGetLastError();
 }
 

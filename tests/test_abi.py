@@ -118,8 +118,10 @@ def test_pack_places_every_plane():
 def test_workspace_bytes():
     assert mx.moe_workspace_bytes(_shape()) > 0
     big = mx.moe_workspace_bytes(_shape(T=2048, H=4096, F=2048, E=256, k=6, n_shared=1))
-    # FP8 terms of the SwiGLU output (4 codes + scales per value) dominate
-    act = (2048 * 6 + 2048) * 2048 * 4 * 33 // 32
+    # FP8 terms of the SwiGLU output (4 codes + scales per value) and the
+    # fp32 down output per routed row dominate
+    rows = 2048 * 6 + 2048
+    act = rows * 2048 * 4 * 33 // 32 + rows * 4096 * 4
     assert act < big < act + 2048 * 4096 * (12 + 5) + 16 * 2048 * 256 * 8 + (1 << 22)
     with pytest.raises(mx.MoeError):
         mx.moe_workspace_bytes(_shape(k=9))
