@@ -3,7 +3,6 @@
 // include/moe_mxfp4.h.
 #include "moe_mxfp4.h"
 
-#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -349,20 +348,35 @@ int moe_forward_decode(const moe_shape *s, const void *hidden, const float *norm
     if (s->T == 0) return ok();
     const Workspace w = carve(s, static_cast<uint8_t *>(ws));
     MOE_TRY(route_front(s, hidden, norm_w, router_w, w, true, st));
-    const moe::ExpertPtrs ex = expert_ptrs(s, experts);
-    const moe::ExpertPtrs sh = expert_ptrs(s, shared);
-    const moe::SwigluConsts c{s->swiglu_alpha, s->swiglu_limit, s->swiglu_up_offset};
-    MOE_TRY(launch(MOE_KERNEL_DECODE_GATE_UP, "decode_gate_up", st, [&] {
-        return moe::launch_decode_gate_up(w.xq, w.xs, w.partial, w.splits, router_b, s->T, s->H,
-                                          s->F, s->E, s->k, s->n_shared, s->route_scale, ex, sh, c,
-                                          w.idx, w.wts, ro ? ro->topk_idx : nullptr,
-                                          ro ? ro->topk_w : nullptr, hidden,
-                                          s->act_dtype == MOE_BF16, out, w.act_q, w.act_s, st);
-    }));
-    MOE_TRY(launch(MOE_KERNEL_DECODE_DOWN, "decode_down", st, [&] {
-        return moe::launch_decode_down(w.act_q, w.act_s, s->T, s->H, s->F, s->k, s->n_shared,
-                                       w.idx, w.wts, ex, sh, out, st);
-    }));
+    moe::DecodeArgs a{};
+    a.xq = w.xq;
+    a.xs = w.xs;
+    a.partial = w.partial;
+    a.S = w.splits;
+    a.router_b = router_b;
+    a.T = s->T;
+    a.H = s->H;
+    a.F = s->F;
+    a.E = s->E;
+    a.k = s->k;
+    a.n_shared = s->n_shared;
+    a.route_scale = s->route_scale;
+    a.ex = expert_ptrs(s, experts);
+    a.sh = expert_ptrs(s, shared);
+    a.sc = moe::SwigluConsts{s->swiglu_alpha, s->swiglu_limit, s->swiglu_up_offset};
+    a.idx = w.idx;
+    a.wts = w.wts;
+    a.out_idx = ro ? ro->topk_idx : nullptr;
+    a.out_w = ro ? ro->topk_w : nullptr;
+    a.resid = hidden;
+    a.resid_bf16 = s->act_dtype == MOE_BF16;
+    a.out = out;
+    a.act_q = w.act_q;
+    a.act_s = w.act_s;
+    MOE_TRY(launch(MOE_KERNEL_DECODE_GATE_UP, "decode_gate_up", st,
+                   [&] { return moe::launch_decode_gate_up(a, st); }));
+    MOE_TRY(launch(MOE_KERNEL_DECODE_DOWN, "decode_down", st,
+                   [&] { return moe::launch_decode_down(a, st); }));
     if (ro && (ro->counts || ro->offsets || ro->perm || ro->inv))
         MOE_TRY(launch(MOE_KERNEL_PERMUTE, "permute", st, [&] {
             return moe::launch_permute(w.idx, s->T, s->E, s->k, 0, 16, w.counts, w.offsets, w.perm,

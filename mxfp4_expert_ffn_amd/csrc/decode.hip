@@ -1,9 +1,12 @@
 // Decode (T <= 64): per route, GEMVs over the selected expert's MXFP4 planes
-// on the block-scaled matrix cores.
+// on the block-scaled matrix cores, after the router launch: gate/up over
+// (route, feature block), then down over (route, 32-row block of H).
 //
-// A workgroup takes 32 weight rows (two 16-row tiles) of one route; its 8
-// wavefronts split K into 128-wide steps, and each issues every load of its
-// steps before its first matrix-core instruction. Weight tiles are read as
+// A work item is 32 weight rows (two 16-row tiles) of one route, for one
+// workgroup; its 8 wavefronts split K into 128-wide steps. Every wavefront
+// issues all of its loads (B first, then the weight tiles from a scalar base)
+// before its first matrix-core instruction, with no branch in between, so
+// each instruction waits only for its own operands. Weight tiles are read as
 // whole contiguous kilobytes (the blob's tiled plane layout). The expert input
 // arrives as FP8 terms in B columns 0..kTerms-1; the other 12 columns are
 // zero, which costs nothing here: the GEMV is bound by weight bytes.
@@ -29,110 +32,125 @@ __device__ __forceinline__ void route_token(const double *partial, int S, const 
     wave_topk(v, E, k, sel, val);
 }
 
-// gate/up + biases + clamped SwiGLU for 32 features of one route; writes the
-// activation block's FP8 terms and scales. grid.x = routes, grid.y = 32-wide
-// feature blocks of pad128(F) (blocks past F write the zero padding).
-// Every wavefront selects the route's expert itself (top-k of the token's
-// logits), so its weight loads wait on no barrier. Workgroups of slot 0 also
-// seed out[t] with the residual (a share each) and, in feature block 0,
-// publish the token's experts and route weights.
-template <int SPW>
-__global__ __launch_bounds__(kDecodeWaves * 64) void decode_gate_up_kernel(
-    const uint8_t *xq, const uint8_t *xs, const double *partial, int S, const float *router_b,
-    int T, int H, int F, int E, int k, float route_scale, ExpertPtrs ex, ExpertPtrs sh,
-    SwigluConsts sc, int32_t *idx, float *wts, int32_t *out_idx, float *out_w,
-    const void *resid, int resid_bf16, float *out, uint8_t *act_q, uint8_t *act_s) {
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const int r = blockIdx.x, R = T * k;
-    const int t = r < R ? r / k : r - R;
-    const int j = r < R ? r - t * k : -1;
-    const int fb = blockIdx.y;
-    const int Kp = pad128(H), Fp = pad128(F), nbp = Fp / 32;
-    if (j == 0) {  // residual seed, unless out already is the float32 residual
-        float *o = out + static_cast<size_t>(t) * H;
-        const float *rf = static_cast<const float *>(resid) + static_cast<size_t>(t) * H;
-        if (resid_bf16 || o != rf) {
-            const uint16_t *rb = static_cast<const uint16_t *>(resid) + static_cast<size_t>(t) * H;
-            const int share = (H + gridDim.y - 1) / gridDim.y;
-            const int end = min(H, (fb + 1) * share);
-            for (int h = fb * share + threadIdx.x; h < end; h += blockDim.x)
-                o[h] = resid_bf16 ? bf16_bits_to_f32(rb[h]) : rf[h];
-        }
-    }
-    uint8_t *aq = act_q + static_cast<size_t>(r) * kTerms * Fp;
-    uint8_t *as = act_s + static_cast<size_t>(r) * kTerms * nbp;
-    if (32 * fb >= F) {  // K padding of the down GEMV's operand: zero codes
-        if (threadIdx.x < 32 * kTerms) {
-            const int n = threadIdx.x >> 5, i = threadIdx.x & 31;
-            aq[n * Fp + 32 * fb + i] = 0;
-            if (i == 0) as[n * nbp + fb] = 127;
-        }
-        return;
-    }
-    const uint8_t *blob = sh.base;
-    if (r < R) {
-        int sel[kMaxK];
-        double val[kMaxK];
-        route_token(partial, S, router_b, T, t, E, k, sel, val);
-        int mine = sel[0];
+// Expert blob of route r, selected by the calling wavefront itself (top-k of
+// the token's logits). `publish` (wave-uniform) writes the token's experts
+// and route weights to idx / wts and the exports.
+__device__ __forceinline__ const uint8_t *route_blob(const DecodeArgs &a, int r, bool publish) {
+    const int R = a.T * a.k;
+    if (r >= R) return a.sh.base;
+    const int lane = threadIdx.x & 63;
+    const int t = r / a.k, j = r - t * a.k;
+    int sel[kMaxK];
+    double val[kMaxK];
+    route_token(a.partial, a.S, a.router_b, a.T, t, a.E, a.k, sel, val);
+    int mine = sel[0];
 #pragma unroll
-        for (int jj = 1; jj < kMaxK; ++jj)
-            if (jj == j) mine = sel[jj];
-        blob = ex.base + static_cast<size_t>(mine) * ex.stride;
-        if (j == 0 && fb == 0 && w == 0) {
-            float wv[kMaxK];
-            route_softmax(val, k, route_scale, wv);
+    for (int jj = 1; jj < kMaxK; ++jj)
+        if (jj == j) mine = sel[jj];
+    mine = __builtin_amdgcn_readfirstlane(mine);  // equal in every lane; lets loads take a scalar base
+    if (publish) {
+        float wv[kMaxK];
+        route_softmax(val, a.k, a.route_scale, wv);
 #pragma unroll
-            for (int jj = 0; jj < kMaxK; ++jj) {
-                if (jj < k && lane == jj) {
-                    idx[t * k + jj] = sel[jj];
-                    wts[t * k + jj] = wv[jj];
-                    if (out_idx) out_idx[t * k + jj] = sel[jj];
-                    if (out_w) out_w[t * k + jj] = wv[jj];
-                }
+        for (int jj = 0; jj < kMaxK; ++jj) {
+            if (jj < a.k && lane == jj) {
+                a.idx[t * a.k + jj] = sel[jj];
+                a.wts[t * a.k + jj] = wv[jj];
+                if (a.out_idx) a.out_idx[t * a.k + jj] = sel[jj];
+                if (a.out_w) a.out_w[t * a.k + jj] = wv[jj];
             }
         }
     }
+    return a.ex.base + static_cast<size_t>(mine) * a.ex.stride;
+}
+
+// gate/up + biases + clamped SwiGLU for 32 features (block fb) of route r;
+// writes the activation block's FP8 terms and scales (blocks past F write the
+// zero padding of the down GEMV's operand). Workgroups of slot 0 also seed
+// out[t] with the residual, a share each. s_part: kDecodeWaves * 4 * 16
+// floats of LDS.
+template <int SPW>
+__device__ __forceinline__ void gate_up_item(const DecodeArgs &a, int r, int fb, float *s_part) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int R = a.T * a.k;
+    const int t = r < R ? r / a.k : r - R;
+    const int j = r < R ? r - t * a.k : -1;
+    const int H = a.H, F = a.F;
+    const int Kp = pad128(H), Fp = pad128(F), nbp = Fp / 32;
+    if (j == 0) {  // residual seed, unless out already is the float32 residual
+        float *o = a.out + static_cast<size_t>(t) * H;
+        const float *rf = static_cast<const float *>(a.resid) + static_cast<size_t>(t) * H;
+        if (a.resid_bf16 || o != rf) {
+            const uint16_t *rb = static_cast<const uint16_t *>(a.resid) + static_cast<size_t>(t) * H;
+            const int share = (H + nbp - 1) / nbp;
+            const int end = min(H, (fb + 1) * share);
+            for (int h = fb * share + threadIdx.x; h < end; h += blockDim.x)
+                o[h] = a.resid_bf16 ? bf16_bits_to_f32(rb[h]) : rf[h];
+        }
+    }
+    uint8_t *aq = a.act_q + static_cast<size_t>(r) * kTerms * Fp;
+    uint8_t *as = a.act_s + static_cast<size_t>(r) * kTerms * nbp;
+    if (32 * fb >= F) {  // K padding of the down GEMV's operand: zero codes, by wavefront 0
+        if (w == 0) {
+            for (int e = lane; e < 32 * kTerms; e += 64) {
+                const int n = e >> 5, i = e & 31;
+                aq[n * Fp + 32 * fb + i] = 0;
+                if (i == 0) as[n * nbp + fb] = 127;
+            }
+        }
+        return;
+    }
+    const uint8_t *blob = route_blob(a, r, j == 0 && fb == 0 && w == 0);
     // the epilogue's biases, loaded with the weights
     const int fe = 32 * fb + (lane & 31);
-    const float bias_g = reinterpret_cast<const float *>(blob + ex.gate_b)[fe];
-    const float bias_u = reinterpret_cast<const float *>(blob + ex.up_b)[fe];
-    const uint8_t *gq = blob + ex.gate_q, *uq = blob + ex.up_q;
-    const uint8_t *gs = blob + ex.gate_s, *us = blob + ex.up_s;
+    const float bias_g = reinterpret_cast<const float *>(blob + a.ex.gate_b)[fe];
+    const float bias_u = reinterpret_cast<const float *>(blob + a.ex.up_b)[fe];
     const int NS = Kp / 128, nblk = H / 32;
+    // the four 16-row tiles: gate rows 32 fb.., 32 fb + 16.., then up
+    const uint8_t *tq[4], *ts[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        const int tile = 2 * fb + (m & 1);
+        tq[m] = blob + (m < 2 ? a.ex.gate_q : a.ex.up_q) + tile_code_base(tile, nblk);
+        ts[m] = blob + (m < 2 ? a.ex.gate_s : a.ex.up_s) + tile_scale_base(tile, nblk);
+    }
+    const ALane al(nblk, lane);
     const int bn = lane & 15, bh = lane >> 4;
     const int nn = min(bn, kTerms - 1);
     const bool bon = bn < kTerms;
-    const uint8_t *xrow = xq + (static_cast<size_t>(t) * kTerms + nn) * Kp;
-    const uint8_t *srow = xs + (static_cast<size_t>(t) * kTerms + nn) * (Kp / 32);
+    const uint8_t *xrow = a.xq + (static_cast<size_t>(t) * kTerms + nn) * Kp;
+    const uint8_t *srow = a.xs + (static_cast<size_t>(t) * kTerms + nn) * (Kp / 32);
     const uint4 zero = make_uint4(0u, 0u, 0u, 0u);
+    const int wu = __builtin_amdgcn_readfirstlane(w);
 
     f32x4_t acc[4];  // gate tile 0, gate tile 1, up tile 0, up tile 1
 #pragma unroll
     for (int m = 0; m < 4; ++m) acc[m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    for (int s0 = w * SPW; s0 < NS; s0 += kDecodeWaves * SPW) {  // one round unless K > 4096
-        AFrag a[SPW][4];
+    for (int s0 = wu * SPW; s0 < NS; s0 += kDecodeWaves * SPW) {  // one round unless K > 4096
+        AFrag af[SPW][4];
         BFrag b[SPW];
+        // B (small, cached) first, then every weight load: the memory counter
+        // retires in order, so the first instruction waits only for its own data
+#pragma unroll
+        for (int i = 0; i < SPW; ++i) b[i] = load_bfrag(xrow, srow, min(s0 + i, NS - 1), bh);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < SPW; ++i)
+#pragma unroll
+            for (int m = 0; m < 4; ++m) af[i][m] = load_afrag(tq[m], ts[m], al, min(s0 + i, NS - 1));
+        __builtin_amdgcn_sched_barrier(0);
+        // no branch between the loads and the matrix-core instructions (a
+        // branch there makes the compiler drain the loads step by step): a
+        // step past K runs with a zero B operand
 #pragma unroll
         for (int i = 0; i < SPW; ++i) {
-            const int s = min(s0 + i, NS - 1);
-            a[i][0] = load_afrag(gq, gs, 2 * fb, s, nblk, lane);
-            a[i][1] = load_afrag(gq, gs, 2 * fb + 1, s, nblk, lane);
-            a[i][2] = load_afrag(uq, us, 2 * fb, s, nblk, lane);
-            a[i][3] = load_afrag(uq, us, 2 * fb + 1, s, nblk, lane);
-            b[i] = load_bfrag(xrow, srow, s, bh);
-        }
+            const bool on = bon && s0 + i < NS;
+            const uint4 blo = on ? b[i].lo : zero, bhi = on ? b[i].hi : zero;
 #pragma unroll
-        for (int i = 0; i < SPW; ++i) {
-            if (s0 + i < NS) {
-                const uint4 blo = bon ? b[i].lo : zero, bhi = bon ? b[i].hi : zero;
-#pragma unroll
-                for (int m = 0; m < 4; ++m) acc[m] = mx_mfma(a[i][m], blo, bhi, b[i].s, acc[m]);
-            }
+            for (int m = 0; m < 4; ++m) acc[m] = mx_mfma(af[i][m], blo, bhi, b[i].s, acc[m]);
         }
     }
 
-    __shared__ float s_part[kDecodeWaves][4][16];
 #pragma unroll
     for (int m = 0; m < 4; ++m)
 #pragma unroll
@@ -141,7 +159,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_gate_up_kernel(
 #pragma unroll
         for (int m = 0; m < 4; ++m)
 #pragma unroll
-            for (int v = 0; v < 4; ++v) s_part[w][m][4 * bh + v] = acc[m][v];
+            for (int v = 0; v < 4; ++v) s_part[(w * 4 + m) * 16 + 4 * bh + v] = acc[m][v];
     }
     __syncthreads();
     if (w == 0) {  // both half-waves hold the block; lanes 0..31 store it
@@ -150,12 +168,12 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_gate_up_kernel(
         float g = 0.f, u = 0.f;
 #pragma unroll
         for (int ww = 0; ww < kDecodeWaves; ++ww) {
-            g += s_part[ww][tile][row];
-            u += s_part[ww][2 + tile][row];
+            g += s_part[(ww * 4 + tile) * 16 + row];
+            u += s_part[(ww * 4 + 2 + tile) * 16 + row];
         }
-        const float a = swiglu(g + bias_g, u + bias_u, sc.alpha, sc.limit, sc.up_offset);
+        const float act = swiglu(g + bias_g, u + bias_u, a.sc.alpha, a.sc.limit, a.sc.up_offset);
         uint32_t codes, scales;
-        fp8_terms_group(a, codes, scales);
+        fp8_terms_group(act, codes, scales);
         if (lane < 32) {
 #pragma unroll
             for (int n = 0; n < kTerms; ++n) {
@@ -167,49 +185,57 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_gate_up_kernel(
 }
 
 // down + bias, times the route weight, added into out[t] (which already holds
-// the residual). grid.x = routes, grid.y = 32-row blocks of H.
+// the residual) for rows 32 hb .. 32 hb + 31 of route r; the expert and the
+// weight come from idx / wts. s_part: kDecodeWaves * 2 * 16 floats of LDS.
 template <int SPW>
-__global__ __launch_bounds__(kDecodeWaves * 64) void decode_down_kernel(
-    const uint8_t *act_q, const uint8_t *act_s, int T, int H, int F, int k, const int32_t *idx,
-    const float *wts, ExpertPtrs ex, ExpertPtrs sh, float *out) {
+__device__ __forceinline__ void down_item(const DecodeArgs &a, int r, int hb, float *s_part) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const int r = blockIdx.x, R = T * k;
-    const int t = r < R ? r / k : r - R;
-    const int hb = blockIdx.y;
-    const uint8_t *blob = r < R ? ex.base + static_cast<size_t>(idx[r]) * ex.stride : sh.base;
-    const uint8_t *dq = blob + ex.down_q, *ds = blob + ex.down_s;
-    const float wt = r < R ? wts[r] : 1.0f;
-    const float bias = reinterpret_cast<const float *>(blob + ex.down_b)[32 * hb + (lane & 31)];
+    const int R = a.T * a.k;
+    const int t = r < R ? r / a.k : r - R;
+    const int H = a.H, F = a.F;
+    const uint8_t *blob = r < R ? a.ex.base + static_cast<size_t>(a.idx[r]) * a.ex.stride : a.sh.base;
+    const float wt = r < R ? a.wts[r] : 1.0f;
+    const float bias = reinterpret_cast<const float *>(blob + a.ex.down_b)[32 * hb + (lane & 31)];
     const int Fp = pad128(F), NS = Fp / 128, nblk = F / 32;
+    const uint8_t *tq[2], *ts[2];
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+        tq[m] = blob + a.ex.down_q + tile_code_base(2 * hb + m, nblk);
+        ts[m] = blob + a.ex.down_s + tile_scale_base(2 * hb + m, nblk);
+    }
+    const ALane al(nblk, lane);
+    const int wu = __builtin_amdgcn_readfirstlane(w);
     const int bn = lane & 15, bh = lane >> 4;
     const int nn = min(bn, kTerms - 1);
     const bool bon = bn < kTerms;
-    const uint8_t *xrow = act_q + (static_cast<size_t>(r) * kTerms + nn) * Fp;
-    const uint8_t *srow = act_s + (static_cast<size_t>(r) * kTerms + nn) * (Fp / 32);
+    const uint8_t *xrow = a.act_q + (static_cast<size_t>(r) * kTerms + nn) * Fp;
+    const uint8_t *srow = a.act_s + (static_cast<size_t>(r) * kTerms + nn) * (Fp / 32);
     const uint4 zero = make_uint4(0u, 0u, 0u, 0u);
 
     f32x4_t acc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
-    for (int s0 = w * SPW; s0 < NS; s0 += kDecodeWaves * SPW) {
-        AFrag a[SPW][2];
+    for (int s0 = wu * SPW; s0 < NS; s0 += kDecodeWaves * SPW) {  // one round unless K > 4096
+        AFrag af[SPW][2];
         BFrag b[SPW];
+        // B (small, cached) first, then every weight load
+#pragma unroll
+        for (int i = 0; i < SPW; ++i) b[i] = load_bfrag(xrow, srow, min(s0 + i, NS - 1), bh);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int i = 0; i < SPW; ++i) {
-            const int s = min(s0 + i, NS - 1);
-            a[i][0] = load_afrag(dq, ds, 2 * hb, s, nblk, lane);
-            a[i][1] = load_afrag(dq, ds, 2 * hb + 1, s, nblk, lane);
-            b[i] = load_bfrag(xrow, srow, s, bh);
+            af[i][0] = load_afrag(tq[0], ts[0], al, min(s0 + i, NS - 1));
+            af[i][1] = load_afrag(tq[1], ts[1], al, min(s0 + i, NS - 1));
         }
+        __builtin_amdgcn_sched_barrier(0);
+        // branch-free as in gate/up: a step past K runs with a zero B operand
 #pragma unroll
         for (int i = 0; i < SPW; ++i) {
-            if (s0 + i < NS) {
-                const uint4 blo = bon ? b[i].lo : zero, bhi = bon ? b[i].hi : zero;
-                acc[0] = mx_mfma(a[i][0], blo, bhi, b[i].s, acc[0]);
-                acc[1] = mx_mfma(a[i][1], blo, bhi, b[i].s, acc[1]);
-            }
+            const bool on = bon && s0 + i < NS;
+            const uint4 blo = on ? b[i].lo : zero, bhi = on ? b[i].hi : zero;
+            acc[0] = mx_mfma(af[i][0], blo, bhi, b[i].s, acc[0]);
+            acc[1] = mx_mfma(af[i][1], blo, bhi, b[i].s, acc[1]);
         }
     }
 
-    __shared__ float s_part[kDecodeWaves][2][16];
 #pragma unroll
     for (int m = 0; m < 2; ++m)
 #pragma unroll
@@ -218,16 +244,30 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_down_kernel(
 #pragma unroll
         for (int m = 0; m < 2; ++m)
 #pragma unroll
-            for (int v = 0; v < 4; ++v) s_part[w][m][4 * bh + v] = acc[m][v];
+            for (int v = 0; v < 4; ++v) s_part[(w * 2 + m) * 16 + 4 * bh + v] = acc[m][v];
     }
     __syncthreads();
     if (threadIdx.x < 32) {
         const int i = threadIdx.x, h = 32 * hb + i;
         float y = 0.f;
 #pragma unroll
-        for (int ww = 0; ww < kDecodeWaves; ++ww) y += s_part[ww][i >> 4][i & 15];
-        unsafeAtomicAdd(out + static_cast<size_t>(t) * H + h, wt * (y + bias));
+        for (int ww = 0; ww < kDecodeWaves; ++ww) y += s_part[(ww * 2 + (i >> 4)) * 16 + (i & 15)];
+        unsafeAtomicAdd(a.out + static_cast<size_t>(t) * H + h, wt * (y + bias));
     }
+}
+
+// grid.x = routes, grid.y = 32-wide feature blocks of pad128(F).
+template <int SPW>
+__global__ __launch_bounds__(kDecodeWaves * 64) void decode_gate_up_kernel(DecodeArgs a) {
+    __shared__ float s_part[kDecodeWaves * 4 * 16];
+    gate_up_item<SPW>(a, blockIdx.x, blockIdx.y, s_part);
+}
+
+// grid.x = routes, grid.y = 32-row blocks of H.
+template <int SPW>
+__global__ __launch_bounds__(kDecodeWaves * 64) void decode_down_kernel(DecodeArgs a) {
+    __shared__ float s_part[kDecodeWaves * 2 * 16];
+    down_item<SPW>(a, blockIdx.x, blockIdx.y, s_part);
 }
 
 // K-steps per wavefront per round (rounds repeat past 8 * 4 steps, K > 4096).
@@ -239,44 +279,27 @@ int decode_spw(int K) {
 
 }  // namespace
 
-hipError_t launch_decode_gate_up(const uint8_t *xq, const uint8_t *xs, const double *partial, int S,
-                                 const float *router_b, int T, int H, int F, int E, int k,
-                                 int n_shared, float route_scale, const ExpertPtrs &ex,
-                                 const ExpertPtrs &sh, SwigluConsts c, int32_t *idx, float *wts,
-                                 int32_t *out_idx, float *out_w, const void *resid, int resid_bf16,
-                                 float *out, uint8_t *act_q, uint8_t *act_s, hipStream_t s) {
-    const dim3 grid(T * (k + n_shared), pad128(F) / 32);
+hipError_t launch_decode_gate_up(const DecodeArgs &a, hipStream_t s) {
+    const dim3 grid(a.T * (a.k + a.n_shared), pad128(a.F) / 32);
     const dim3 block(kDecodeWaves * 64);
-#define MOE_GU(SPW)                                                                              \
-    launch_kernel(decode_gate_up_kernel<SPW>, grid, block, s, xq, xs, partial, S, router_b, T, H, \
-                  F, E, k, route_scale, ex, sh, c, idx, wts, out_idx, out_w, resid, resid_bf16,   \
-                  out, act_q, act_s)
-    switch (decode_spw(H)) {
-    case 1: MOE_GU(1); break;
-    case 2: MOE_GU(2); break;
-    case 3: MOE_GU(3); break;
-    default: MOE_GU(4); break;
+    switch (decode_spw(a.H)) {
+    case 1: launch_kernel(decode_gate_up_kernel<1>, grid, block, s, a); break;
+    case 2: launch_kernel(decode_gate_up_kernel<2>, grid, block, s, a); break;
+    case 3: launch_kernel(decode_gate_up_kernel<3>, grid, block, s, a); break;
+    default: launch_kernel(decode_gate_up_kernel<4>, grid, block, s, a); break;
     }
-#undef MOE_GU
     return hipGetLastError();
 }
 
-hipError_t launch_decode_down(const uint8_t *act_q, const uint8_t *act_s, int T, int H, int F,
-                              int k, int n_shared, const int32_t *idx, const float *wts,
-                              const ExpertPtrs &ex, const ExpertPtrs &sh, float *out,
-                              hipStream_t s) {
-    const dim3 grid(T * (k + n_shared), H / 32);
+hipError_t launch_decode_down(const DecodeArgs &a, hipStream_t s) {
+    const dim3 grid(a.T * (a.k + a.n_shared), a.H / 32);
     const dim3 block(kDecodeWaves * 64);
-#define MOE_DN(SPW)                                                                           \
-    launch_kernel(decode_down_kernel<SPW>, grid, block, s, act_q, act_s, T, H, F, k, idx, wts, \
-                  ex, sh, out)
-    switch (decode_spw(F)) {
-    case 1: MOE_DN(1); break;
-    case 2: MOE_DN(2); break;
-    case 3: MOE_DN(3); break;
-    default: MOE_DN(4); break;
+    switch (decode_spw(a.F)) {
+    case 1: launch_kernel(decode_down_kernel<1>, grid, block, s, a); break;
+    case 2: launch_kernel(decode_down_kernel<2>, grid, block, s, a); break;
+    case 3: launch_kernel(decode_down_kernel<3>, grid, block, s, a); break;
+    default: launch_kernel(decode_down_kernel<4>, grid, block, s, a); break;
     }
-#undef MOE_DN
     return hipGetLastError();
 }
 

@@ -109,19 +109,31 @@ hipError_t launch_permute(const int32_t *idx, int T, int E, int k, int n_shared,
 // Route r < T*k is slot r % k of token r / k; r >= T*k is the shared expert of
 // token r - T*k. act_q / act_s: FP8 terms of the SwiGLU output per route,
 // [routes][kTerms][pad128(F)] codes and [routes][kTerms][pad128(F)/32] scales.
-// gate/up also selects each token's experts (top-k of the router's partial
-// logits, written to idx / wts and the optional exports) and seeds out with
-// the residual.
-hipError_t launch_decode_gate_up(const uint8_t *xq, const uint8_t *xs, const double *partial, int S,
-                                 const float *router_b, int T, int H, int F, int E, int k,
-                                 int n_shared, float route_scale, const ExpertPtrs &ex,
-                                 const ExpertPtrs &sh, SwigluConsts c, int32_t *idx, float *wts,
-                                 int32_t *out_idx, float *out_w, const void *resid, int resid_bf16,
-                                 float *out, uint8_t *act_q, uint8_t *act_s, hipStream_t s);
-hipError_t launch_decode_down(const uint8_t *act_q, const uint8_t *act_s, int T, int H, int F,
-                              int k, int n_shared, const int32_t *idx, const float *wts,
-                              const ExpertPtrs &ex, const ExpertPtrs &sh, float *out,
-                              hipStream_t s);
+// Every gate/up workgroup selects its token's experts itself (top-k of the
+// router's partial logits); slot 0's first feature block writes idx / wts and
+// the optional exports.
+struct DecodeArgs {
+    const uint8_t *xq, *xs;  // FP8 terms of the expert input
+    const double *partial;   // router partial logits [S][T][E]
+    int S;
+    const float *router_b;
+    int T, H, F, E, k, n_shared;
+    float route_scale;
+    ExpertPtrs ex, sh;
+    SwigluConsts sc;
+    int32_t *idx;
+    float *wts;
+    int32_t *out_idx;  // optional exports (NULL: not written)
+    float *out_w;
+    const void *resid;
+    int resid_bf16;
+    float *out;
+    uint8_t *act_q, *act_s;
+};
+// gate/up (which also selects the experts and seeds out with the residual),
+// then down; both after launch_router (+ launch_quantize).
+hipError_t launch_decode_gate_up(const DecodeArgs &a, hipStream_t s);
+hipError_t launch_decode_down(const DecodeArgs &a, hipStream_t s);
 
 // prefill (any T) -------------------------------------------------------------
 // Rows in expert order: position p < T*k is route perm[p]; p >= T*k is the
