@@ -72,9 +72,14 @@ struct Tile {
 // activation rows stay in L2 too). False when past the real tiles.
 __device__ __forceinline__ bool find_item(int nrb, int bm, const int32_t *offsets,
                                           const int *s_pre, int G, int &rb, Tile &tl) {
-    const int per = gridDim.x / kXcds;
-    const int item = (blockIdx.x % kXcds) * per + blockIdx.x / kXcds;
-    if (item >= s_pre[G] * nrb) return false;
+    // the real item count splits evenly over the dies (the grid is an upper
+    // bound; dealing by grid size would leave the last dies without work)
+    const int total = s_pre[G] * nrb;
+    const int per = (total + kXcds - 1) / kXcds;
+    const int xi = blockIdx.x / kXcds;  // this workgroup's turn on its die
+    if (xi >= per) return false;
+    const int item = (blockIdx.x % kXcds) * per + xi;
+    if (item >= total) return false;
     int lo = 0, hi = G - 1;  // last group whose first item is <= item
     while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
@@ -239,6 +244,7 @@ __global__ __launch_bounds__(64 * W) void gate_up_gemm_kernel(
     constexpr int kStageBytes = 2 * Gm::kBufBytes;
     __shared__ __align__(16) uint8_t sB[kStageBytes > kActBytes ? kStageBytes : kActBytes];
     __shared__ uint8_t sBs[2 * 4 * Gm::kScales];
+    __shared__ float s_bias[2][Gm::kGateUpRows];  // gate, up biases of the workgroup's features
     const int G = E + n_shared, R = T * k;
     load_pre(mprefix, G, s_pre);
     const int Fp = pad128(F), nrb = (Fp + Gm::kGateUpRows - 1) / Gm::kGateUpRows;
@@ -247,13 +253,19 @@ __global__ __launch_bounds__(64 * W) void gate_up_gemm_kernel(
     if (!find_item(nrb, Gm::kRows, offsets, s_pre, G, rb, tl)) return;
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const uint8_t *blob = tl.g < E ? ex.base + static_cast<size_t>(tl.g) * ex.stride : sh.base;
+    const int fw = rb * Gm::kGateUpRows;          // the workgroup's first feature
     if (tid < Gm::kRows) {
         const int p = tl.p0 + min(tid, tl.n - 1);
         s_brow[tid] = p < R ? perm[p] / k : p - R;  // the token (x row)
     }
+    // the epilogue's biases, fetched now rather than after the main loop
+    for (int i = tid; i < 2 * Gm::kGateUpRows; i += Gm::kThreads) {
+        const int m = i / Gm::kGateUpRows, fl = i - m * Gm::kGateUpRows;
+        const float *bp = reinterpret_cast<const float *>(blob + (m ? ex.up_b : ex.gate_b));
+        s_bias[m][fl] = fw + fl < F ? bp[fw + fl] : 0.f;
+    }
     __syncthreads();
-    const uint8_t *blob = tl.g < E ? ex.base + static_cast<size_t>(tl.g) * ex.stride : sh.base;
-    const int fw = rb * Gm::kGateUpRows;          // the workgroup's first feature
     const int f0 = fw + Gm::kGURowsWave * w;     // this wavefront's first feature
     const int last_tile = F / 16 - 1, nblk = H / 32;
     const uint8_t *aq[NA], *as[NA];
@@ -280,14 +292,12 @@ __global__ __launch_bounds__(64 * W) void gate_up_gemm_kernel(
     float *sAct = reinterpret_cast<float *>(sB);
     const int col = lane & 15, kh = lane >> 4;
     if (f0 < F) {  // F % 16 == 0: a wavefront's features are all real or all padding
-        const float *gb = reinterpret_cast<const float *>(blob + ex.gate_b);
-        const float *ub = reinterpret_cast<const float *>(blob + ex.up_b);
 #pragma unroll
         for (int j = 0; j < kTilesPerMat; ++j)
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
                 const int fl = Gm::kGURowsWave * w + 16 * j + 4 * kh + v;  // feature - fw
-                const float bg = gb[fw + fl], bu = ub[fw + fl];
+                const float bg = s_bias[0][fl], bu = s_bias[1][fl];
 #pragma unroll
                 for (int g = 0; g < NG; ++g)
                     sAct[(16 * g + col) * kActStride + fl] =
@@ -296,24 +306,40 @@ __global__ __launch_bounds__(64 * W) void gate_up_gemm_kernel(
             }
     }
     __syncthreads();
-    // (row, block) tasks, one per half-wavefront; blocks at or past F are the
-    // K padding of the down GEMM's operand (zero codes), blocks past Fp skipped
+    // (row, block) tasks, two per half-wavefront at a time (their reduction
+    // chains interleave); blocks at or past F are the K padding of the down
+    // GEMM's operand (zero codes), blocks past Fp skipped
     constexpr int kBlocks = Gm::kGateUpRows / 32;
     const int half = lane >> 5, i = lane & 31, nbp = Fp / 32;
     const int ntask = tl.n * kBlocks;
-    for (int task0 = 2 * w; task0 < ntask; task0 += 2 * W) {
-        const int task = task0 + half;
-        const bool on = task < ntask;
-        const int row = on ? task / kBlocks : 0, blk = on ? task - row * kBlocks : 0;
-        const int fb = fw + 32 * blk;  // first feature of the block
-        uint32_t codes = 0, scales = 0x7f7f7f7fu;
-        if (fb < F) fp8_terms_group(sAct[row * kActStride + 32 * blk + i], codes, scales);
-        if (on && fb < Fp) {
-            const size_t p = static_cast<size_t>(tl.p0 + row);
+    for (int task0 = 4 * w; task0 < ntask; task0 += 4 * W) {
+        int row[2], fb[2];
+        bool on[2];
+        uint32_t codes[2], scales[2];
 #pragma unroll
-            for (int n = 0; n < kTerms; ++n) {
-                act_q[(p * kTerms + n) * Fp + fb + i] = static_cast<uint8_t>(codes >> (8 * n));
-                if (i == 0) act_s[(p * kTerms + n) * nbp + fb / 32] = static_cast<uint8_t>(scales >> (8 * n));
+        for (int u = 0; u < 2; ++u) {
+            const int task = task0 + 2 * u + half;
+            on[u] = task < ntask;
+            row[u] = on[u] ? task / kBlocks : 0;
+            const int blk = on[u] ? task - row[u] * kBlocks : 0;
+            fb[u] = fw + 32 * blk;  // first feature of the block
+            const float v = fb[u] < F ? sAct[row[u] * kActStride + 32 * blk + i] : 0.f;
+            fp8_terms_group(v, codes[u], scales[u]);  // every lane takes part
+            if (fb[u] >= F) {
+                codes[u] = 0;
+                scales[u] = 0x7f7f7f7fu;
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            if (on[u] && fb[u] < Fp) {
+                const size_t p = static_cast<size_t>(tl.p0 + row[u]);
+#pragma unroll
+                for (int n = 0; n < kTerms; ++n) {
+                    act_q[(p * kTerms + n) * Fp + fb[u] + i] = static_cast<uint8_t>(codes[u] >> (8 * n));
+                    if (i == 0)
+                        act_s[(p * kTerms + n) * nbp + fb[u] / 32] = static_cast<uint8_t>(scales[u] >> (8 * n));
+                }
             }
         }
     }
@@ -331,6 +357,7 @@ __global__ __launch_bounds__(64 * W) void down_gemm_kernel(
     __shared__ float s_wt[Gm::kRows];
     __shared__ __align__(16) uint8_t sB[2 * Gm::kBufBytes];
     __shared__ uint8_t sBs[2 * 4 * Gm::kScales];
+    __shared__ __align__(16) float s_bias[Gm::kDownRows];  // biases of the workgroup's hidden rows
     const int G = E + n_shared, R = T * k;
     load_pre(mprefix, G, s_pre);
     const int nrb = (H + Gm::kDownRows - 1) / Gm::kDownRows;
@@ -339,13 +366,18 @@ __global__ __launch_bounds__(64 * W) void down_gemm_kernel(
     if (!find_item(nrb, Gm::kRows, offsets, s_pre, G, rb, tl)) return;
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const uint8_t *blob = tl.g < E ? ex.base + static_cast<size_t>(tl.g) * ex.stride : sh.base;
     if (tid < Gm::kRows) {
         const int p = tl.p0 + min(tid, tl.n - 1);
         s_brow[tid] = p;  // activation rows are in position order
         s_wt[tid] = p < R ? wts[perm[p]] : 1.0f;
     }
+    // the epilogue's biases, fetched now rather than after the main loop
+    for (int i = tid; i < Gm::kDownRows; i += Gm::kThreads) {
+        const int h = rb * Gm::kDownRows + i;
+        s_bias[i] = h < H ? reinterpret_cast<const float *>(blob + ex.down_b)[h] : 0.f;
+    }
     __syncthreads();
-    const uint8_t *blob = tl.g < E ? ex.base + static_cast<size_t>(tl.g) * ex.stride : sh.base;
     const int h0 = rb * Gm::kDownRows + 16 * NA * w;  // this wavefront's hidden rows
     const int last_tile = H / 16 - 1, nblk = F / 32;
     const uint8_t *aq[NA], *as[NA];
@@ -365,13 +397,12 @@ __global__ __launch_bounds__(64 * W) void down_gemm_kernel(
     gemm_mainloop<NG, W, NA>(aq, as, al, Fp / 128, act_q, act_s, Fp, s_brow, tl.n, sB, sBs, acc);
 
     // y[p][h] = route weight x (down + bias), four consecutive h per lane
-    const float *db = reinterpret_cast<const float *>(blob + ex.down_b);
     const int col = lane & 15, kh = lane >> 4;
 #pragma unroll
     for (int j = 0; j < NA; ++j) {
         const int h = h0 + 16 * j + 4 * kh;
         if (h < H) {  // H % 16 == 0: the lane's four rows are all in or all out
-            const float4 bias = *reinterpret_cast<const float4 *>(db + h);
+            const float4 bias = *reinterpret_cast<const float4 *>(s_bias + (h - rb * Gm::kDownRows));
 #pragma unroll
             for (int g = 0; g < NG; ++g) {
                 const int row = 16 * g + col;
