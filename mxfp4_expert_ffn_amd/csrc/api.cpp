@@ -417,9 +417,11 @@ int moe_forward_prefill(const moe_shape *s, const void *hidden, const float *nor
     const moe::SwigluConsts c{s->swiglu_alpha, s->swiglu_limit, s->swiglu_up_offset};
     const int mt = max_tiles(s, bm);
     MOE_TRY(launch(MOE_KERNEL_GATE_UP_GEMM, "gate_up_gemm", st, [&] {
+        // a bfloat16 input (no RMSNorm in between) needs only three FP8 terms
+        const int x_terms = s->act_dtype == MOE_BF16 && !norm_w ? 3 : moe::kTerms;
         return moe::launch_gate_up_gemm(w.xq, w.xs, s->T, s->H, s->F, s->E, s->k, s->n_shared, ex,
-                                        sh, c, w.offsets, w.perm, w.mprefix, bm, mt, w.act_q,
-                                        w.act_s, st);
+                                        sh, c, w.offsets, w.perm, w.mprefix, bm, mt, x_terms,
+                                        w.act_q, w.act_s, st);
     }));
     MOE_TRY(launch(MOE_KERNEL_DOWN_GEMM, "down_gemm", st, [&] {
         return moe::launch_down_gemm(w.act_q, w.act_s, s->T, s->H, s->F, s->E, s->k, s->n_shared,

@@ -140,11 +140,17 @@ hipError_t launch_decode_down(const DecodeArgs &a, hipStream_t s);
 // shared expert of token p - T*k. act_q / act_s are indexed by p. tile_rows
 // (16, 32 or 64) comes from gemm_tile_rows, max_tiles bounds the tile count.
 int gemm_tile_rows(int T, int k, int E, int n_shared);
+// x_terms: FP8 terms of the expert input that take part, 3 or kTerms (three
+// carry a bfloat16 input as closely as four; a float32 one needs four).
 hipError_t launch_gate_up_gemm(const uint8_t *xq, const uint8_t *xs, int T, int H, int F, int E,
                                int k, int n_shared, const ExpertPtrs &ex, const ExpertPtrs &sh,
                                SwigluConsts c, const int32_t *offsets, const int32_t *perm,
-                               const int32_t *mprefix, int tile_rows, int max_tiles, uint8_t *act_q,
-                               uint8_t *act_s, hipStream_t s);
+                               const int32_t *mprefix, int tile_rows, int max_tiles, int x_terms,
+                               uint8_t *act_q, uint8_t *act_s, hipStream_t s);
+// FP8 terms of the SwiGLU output that take part in the grouped down GEMM:
+// the fourth moves the block output by under 3e-5 of its RMS on every
+// configuration (the down GEMM averages the third term's rounding away).
+constexpr int kDownTerms = 3;
 // y [T*k + T*n_shared][H] fp32: route weight x (down + bias) per row position
 hipError_t launch_down_gemm(const uint8_t *act_q, const uint8_t *act_s, int T, int H, int F, int E,
                             int k, int n_shared, const ExpertPtrs &ex, const ExpertPtrs &sh,

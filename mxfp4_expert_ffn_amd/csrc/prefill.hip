@@ -2,18 +2,20 @@
 // block-scaled matrix cores (MXFP4 weights as operand A, FP8-term activations
 // as operand B).
 //
-// The kTerms FP8 terms of an activation row are laid along K: for each
-// 128-wide step, term n of 16 rows is one B operand (column c = row c of the
-// group), and the kTerms instructions accumulate into the same result. So a
-// 16x16 result tile holds 16 weight rows x 16 activation rows outright.
+// The FP8 terms of an activation row are laid along K: for each 128-wide
+// step, term n of 16 rows is one B operand (column c = row c of the group),
+// and the terms' instructions accumulate into the same result. So a 16x16
+// result tile holds 16 weight rows x 16 activation rows outright. gate/up
+// uses all kTerms terms of a float32 input and three of a bfloat16 one; down
+// uses kDownTerms of the SwiGLU output.
 //
 // A work item is (tile of up to 16*NG rows of one expert, weight-row block).
 // Its workgroup of W wavefronts streams the block's weight rows once per tile:
 // each wavefront has its own rows and NA A fragments per step, read as
 // contiguous kilobytes from the tiled plane 2-3 steps ahead. The tile's rows x
 // terms are staged 2 steps ahead through double-buffered LDS and shared by the
-// W wavefronts. Per step a wavefront issues NA x NG x kTerms matrix-core
-// instructions, less for row groups of 16 the tile does not fill. Items are
+// W wavefronts. Per step a wavefront issues NA x NG x (terms used)
+// matrix-core instructions, less for row groups of 16 the tile does not fill. Items are
 // dealt so that the row blocks of one tile run back to back on one
 // accelerator die and share its activation rows in L2.
 //
@@ -111,7 +113,8 @@ __device__ __forceinline__ bool find_item(int nrb, int bm, const int32_t *offset
 // LDS holds a step's B pieces in fragment order: piece p = ((term * NG +
 // group) * 8 + chunk) * 16 + column, so the 16 lanes of one k-group read 256
 // contiguous bytes; the B scale bytes sit in lane order, [term][k-group][row].
-template <int NG, int W, int NA>
+// All kTerms terms are staged; the first NT of them meet the A fragments.
+template <int NG, int W, int NA, int NT>
 __device__ __forceinline__ void gemm_mainloop(const uint8_t *const (&aq)[NA],
                                               const uint8_t *const (&as)[NA], const ALane &al,
                                               int NS, const uint8_t *bq, const uint8_t *bs, int Kb,
@@ -174,7 +177,7 @@ __device__ __forceinline__ void gemm_mainloop(const uint8_t *const (&aq)[NA],
             for (int g = 0; g < NG; ++g) {
                 if (g < ngroups) {  // uniform: row groups the tile fills
 #pragma unroll
-                    for (int t = 0; t < kTerms; ++t) {
+                    for (int t = 0; t < NT; ++t) {
                         const int pc = ((t * NG + g) * 8 + kh) * 16 + col;
                         const uint4 blo = *reinterpret_cast<const uint4 *>(buf + 16 * pc);
                         const uint4 bhi = *reinterpret_cast<const uint4 *>(buf + 16 * (pc + 64));
@@ -227,8 +230,9 @@ __device__ __forceinline__ void load_pre(const int32_t *mprefix, int G, int *s_p
     __syncthreads();
 }
 
-// gate/up: grid = kXcds-rounded max_tiles x ceil(pad128(F) / kGateUpRows) items.
-template <int NG, int W, int NA>
+// gate/up: grid = kXcds-rounded max_tiles x ceil(pad128(F) / kGateUpRows) items;
+// NT terms of the expert input take part.
+template <int NG, int W, int NA, int NT>
 __global__ __launch_bounds__(64 * W) void gate_up_gemm_kernel(
     const uint8_t *xq, const uint8_t *xs, int T, int H, int F, int E, int k, int n_shared,
     ExpertPtrs ex, ExpertPtrs sh, SwigluConsts sc, const int32_t *offsets, const int32_t *perm,
@@ -284,7 +288,7 @@ __global__ __launch_bounds__(64 * W) void gate_up_gemm_kernel(
 #pragma unroll
         for (int g = 0; g < NG; ++g) acc[j][g] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     const int Kp = pad128(H);
-    gemm_mainloop<NG, W, NA>(aq, as, al, Kp / 128, xq, xs, Kp, s_brow, tl.n, sB, sBs, acc);
+    gemm_mainloop<NG, W, NA, NT>(aq, as, al, Kp / 128, xq, xs, Kp, s_brow, tl.n, sB, sBs, acc);
 
     // epilogue: SwiGLU of the workgroup's features into LDS, then one
     // 32-feature block per (row, block) to FP8 terms
@@ -394,7 +398,8 @@ __global__ __launch_bounds__(64 * W) void down_gemm_kernel(
 #pragma unroll
         for (int g = 0; g < NG; ++g) acc[j][g] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     const int Fp = pad128(F);
-    gemm_mainloop<NG, W, NA>(aq, as, al, Fp / 128, act_q, act_s, Fp, s_brow, tl.n, sB, sBs, acc);
+    gemm_mainloop<NG, W, NA, kDownTerms>(aq, as, al, Fp / 128, act_q, act_s, Fp, s_brow, tl.n, sB,
+                                         sBs, acc);
 
     // y[p][h] = route weight x (down + bias), four consecutive h per lane
     const int col = lane & 15, kh = lane >> 4;
@@ -469,20 +474,24 @@ int gemm_tile_rows(int T, int k, int E, int n_shared) {
 hipError_t launch_gate_up_gemm(const uint8_t *xq, const uint8_t *xs, int T, int H, int F, int E,
                                int k, int n_shared, const ExpertPtrs &ex, const ExpertPtrs &sh,
                                SwigluConsts c, const int32_t *offsets, const int32_t *perm,
-                               const int32_t *mprefix, int tile_rows, int max_tiles, uint8_t *act_q,
-                               uint8_t *act_s, hipStream_t s) {
-#define MOE_GU(NG, W, NA)                                                                           \
+                               const int32_t *mprefix, int tile_rows, int max_tiles, int x_terms,
+                               uint8_t *act_q, uint8_t *act_s, hipStream_t s) {
+#define MOE_GU(NG, W, NA, NT)                                                                       \
     do {                                                                                            \
         using Gm = Geo<NG, W, NA>;                                                                  \
         const int grid = items((pad128(F) + Gm::kGateUpRows - 1) / Gm::kGateUpRows, max_tiles);    \
         if (grid == 0) return hipSuccess;                                                           \
-        launch_kernel(gate_up_gemm_kernel<NG, W, NA>, grid, 64 * (W), s, xq, xs, T, H, F, E, k,     \
-                      n_shared, ex, sh, c, offsets, perm, mprefix, act_q, act_s);                   \
+        launch_kernel(gate_up_gemm_kernel<NG, W, NA, NT>, grid, 64 * (W), s, xq, xs, T, H, F, E,   \
+                      k, n_shared, ex, sh, c, offsets, perm, mprefix, act_q, act_s);                \
     } while (0)
-    switch (tile_rows) {
-    case 16: MOE_GU(1, 4, 4); break;
-    case 32: MOE_GU(2, 4, 4); break;
-    case 64: MOE_GU(4, 8, 2); break;
+    if (x_terms != 3 && x_terms != kTerms) return hipErrorInvalidValue;
+    switch (tile_rows * 10 + x_terms) {
+    case 163: MOE_GU(1, 4, 4, 3); break;
+    case 164: MOE_GU(1, 4, 4, 4); break;
+    case 323: MOE_GU(2, 4, 4, 3); break;
+    case 324: MOE_GU(2, 4, 4, 4); break;
+    case 643: MOE_GU(4, 8, 2, 3); break;
+    case 644: MOE_GU(4, 8, 2, 4); break;
     default: return hipErrorInvalidValue;
     }
 #undef MOE_GU
