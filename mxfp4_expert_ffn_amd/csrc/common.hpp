@@ -230,27 +230,17 @@ namespace moe {
 // what terms 0..n-1 left over, so every extra term adds about four
 // significant bits (kTerms = 4: ~16 bits, float32-level products).
 
-// OCP E4M3 code of x, |x| < 448, rounded to nearest (ties to even).
+// OCP E4M3 code of x, |x| < 448, rounded to nearest (ties to even), and its
+// value: the gfx950 conversion instructions, which round to nearest even with
+// subnormals (measured bit for bit against a software encoder of the format on
+// 2^20 values, ties and subnormals included: no differences). No branches, so
+// the term loops below stay straight-line code.
 __device__ __forceinline__ uint32_t e4m3_encode(float x) {
-    const uint32_t sign = (__float_as_uint(x) >> 24) & 0x80u;
-    const float ax = fabsf(x);
-    uint32_t code;
-    if (ax < 0.015625f) {  // below 2^-6: subnormals, steps of 2^-9 (8 * 2^-9 is the first normal)
-        code = static_cast<uint32_t>(__float2int_rn(ax * 512.0f));
-    } else {
-        const uint32_t ab = __float_as_uint(ax);
-        const uint32_t r = ab + 0x7FFFFu + ((ab >> 20) & 1u);  // round the mantissa to 3 bits
-        code = ((((r >> 23) & 0xffu) - 120u) << 3) | ((r >> 20) & 7u);
-        code = code > 0x7Eu ? 0x7Eu : code;
-    }
-    return sign | code;
+    return static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(x, 0.0f, 0, false)) & 0xffu;
 }
 
 __device__ __forceinline__ float e4m3_decode(uint32_t c) {
-    const uint32_t e = (c >> 3) & 15u, m = c & 7u;
-    const float v = e == 0 ? static_cast<float>(m) * 0.001953125f
-                           : __uint_as_float(((e + 120u) << 23) | (m << 20));
-    return (c & 0x80u) ? -v : v;
+    return __builtin_amdgcn_cvt_f32_fp8(static_cast<int>(c), 0);
 }
 
 // 2^e as float32 for e in [-126, 127].
