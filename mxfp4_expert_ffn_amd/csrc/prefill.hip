@@ -52,9 +52,11 @@ struct Geo {
     static constexpr int kGURowsWave = 8 * NA;             // gate/up features per wavefront
     static constexpr int kGateUpRows = W * kGURowsWave;    // features per gate/up workgroup
     static constexpr int kDownRows = W * 16 * NA;          // hidden rows per down workgroup
-    // K-steps of A fragments in flight: 3, or 2 where a step's matrix-core
-    // work is long (64-row tiles) and registers are short
-    static constexpr int kASlots = NG >= 4 ? 2 : 3;
+    // K-steps of A fragments in flight: 3 for 32-row tiles; 2 for 16-row
+    // tiles (120 VGPRs: four workgroups per CU, which beats three with a
+    // deeper ring) and for 64-row tiles (long matrix-core work per step,
+    // registers short)
+    static constexpr int kASlots = NG == 2 ? 3 : 2;
     static_assert(kPieces % kThreads == 0, "B staging divides evenly");
     static_assert(kScales <= kThreads, "one scale dword per thread at most");
     static_assert(kGateUpRows % 32 == 0, "gate/up blocks hold whole 32-feature MX blocks");
@@ -459,13 +461,16 @@ int items(int nrb, int max_tiles) {
 
 }  // namespace
 
-// 16-row tiles for experts of about 16 rows, 32 above. 64-row tiles (8
+// 16-row tiles, at four workgroups per CU, up to 96 rows per expert on
+// average (measured faster than 32-row tiles at 16, 56 and 64 rows per
+// expert: the T=128 layer, the DS4-shaped layer, the 24-layer stack); 32-row
+// tiles above, where the weights' re-reads per tile dominate. 64-row tiles (8
 // wavefronts x 2 A fragments) are built but not chosen: at 2 A fragments per
 // B operand their LDS reads run at the LDS limit (measured slower on the
 // 24-layer stack and the DS4-shaped layer).
 int gemm_tile_rows(int T, int k, int E, int n_shared) {
     const double avg = static_cast<double>(T) * (k + n_shared) / (E + n_shared);
-    return avg >= 20.0 ? 32 : 16;
+    return avg > 96.0 ? 32 : 16;
 }
 
 // Tiles of 16 and 32 rows: 4 wavefronts with 4 A fragments each; 64-row

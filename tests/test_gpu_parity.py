@@ -276,6 +276,8 @@ EDGE = {
     "single_expert": _small(1, T=9, E=1, k=1),
     "k_equals_E": _small(1, T=6, E=4, k=4),
     "crowded": _small(1, T=50, E=2, k=2, H=192, F=96),
+    # past 96 rows per expert: the grouped GEMMs take 32-row tiles
+    "deep_tiles": _small(1, T=120, E=2, k=2, H=192, F=160),
     "bf16_shared_scale": _small(5, T=19, H=256, F=128, E=12, k=6),
     "norm": _small(4, T=21, H=256, F=192, E=8, k=4, layers=1),
     "max_H": _small(1, T=3, H=16384, F=64, E=2, k=1),
