@@ -67,9 +67,10 @@ hipError_t launch_rmsnorm(const void *x, int x_bf16, const float *gamma, int T, 
                           double *xn64, float *xn32, hipStream_t s);
 // Router: split-K partial logits partial[splits][T][E] (fp64, bias not added).
 // GEMV form for T <= kRouterGemvMaxT (one wavefront per expert and
-// 2048-wide hidden slice), tiled form otherwise (slices sized for enough
-// workgroups, at most 16).
+// 2048-wide hidden slice), tiled form otherwise (slices sized for about 512
+// workgroups, at most kRouterMaxSplits).
 constexpr int kRouterGemvMaxT = 16;
+constexpr int kRouterMaxSplits = 64;
 constexpr int kRouterGemvSlice = 2048;
 struct RouterPlan {
     bool gemv;

@@ -103,11 +103,16 @@ __device__ __forceinline__ void quantize_terms_group(const void *q_in, int q_bf1
 }
 
 // Stand-alone form of the FP8-term quantisation, for batches the tiled router
-// takes: 8 blocks of 32 values per workgroup.
+// takes: 8 blocks of 32 values per workgroup and round, over a grid-stride
+// loop (few, long-lived workgroups rather than one per 8 blocks). The loop
+// runs per wavefront, both halves together, as the group maximum needs.
 __global__ __launch_bounds__(256) void quantize_terms_kernel(const void *q_in, int q_bf16, int T,
                                                              int H, int Kp, uint8_t *xq,
                                                              uint8_t *xs) {
-    quantize_terms_group(q_in, q_bf16, T, H, Kp, xq, xs, blockIdx.x * 8 + (threadIdx.x >> 5));
+    const int total = T * (Kp / 32);
+    const int half = (threadIdx.x >> 5) & 1;
+    for (int g0 = blockIdx.x * 8 + 2 * (threadIdx.x >> 6); g0 < total; g0 += gridDim.x * 8)
+        quantize_terms_group(q_in, q_bf16, T, H, Kp, xq, xs, g0 + half);
 }
 
 template <int KIND>
@@ -159,11 +164,19 @@ __global__ __launch_bounds__(256) void router_gemv_kernel(const void *x, const f
 }
 
 // Tiled router for larger batches: a workgroup computes the fp64 partial
-// logits of 64 tokens x 64 experts over one K slice, each of its 256 threads
-// 4 tokens x 4 experts. K advances 32 at a time through double-buffered LDS
-// tiles kept in the inputs' own precision (widened exactly to fp64 when
-// read); the next chunk's loads are in flight during the current chunk's
-// FMAs. Tokens and experts past T and E are clamped on load and not written.
+// logits of 64 tokens x 64 experts over one K slice on the fp64 matrix cores
+// (v_mfma_f64_16x16x4_f64): each of its 4 wavefronts holds 32 tokens x 32
+// experts as 2 x 2 result tiles. K advances 32 at a time through
+// double-buffered LDS tiles kept in the inputs' own precision (widened
+// exactly to fp64 when read), 4 per instruction; the next chunk's loads are
+// in flight during the current chunk's instructions. Tokens and experts past
+// T and E are clamped on load and not written.
+//
+// Instruction lanes (measured on gfx950): operand A lane l = A[l % 16][l / 16]
+// (token, k), operand B lane l = B[l / 16][l % 16] (k, expert); result lane l
+// holds D[4v + l / 16][l % 16], v = 0..3.
+typedef double f64x4_t __attribute__((ext_vector_type(4)));
+
 template <int KIND>
 __global__ __launch_bounds__(256) void router_tiled_kernel(const void *x, const float *w, int T,
                                                            int H, int E, int slice,
@@ -199,38 +212,46 @@ __global__ __launch_bounds__(256) void router_tiled_kernel(const void *x, const 
             wsm[buf][lk + i][lr] = wv[i];
         }
     };
-    const int ti = tid >> 4, ei = tid & 15;  // 4 tokens 4*ti.., 4 experts 4*ei..
-    double acc[4][4] = {};
+    const int lane = tid & 63, wave = tid >> 6;
+    const int tb = (wave & 1) * 32, eb = (wave >> 1) * 32;  // the wavefront's tokens, experts
+    const int col = lane & 15, kq = lane >> 4;
+    f64x4_t acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = f64x4_t{0.0, 0.0, 0.0, 0.0};
     load(hbeg);
     int buf = 0;
     for (int h0 = hbeg; h0 < hend; h0 += 32) {
         store(buf);
         __syncthreads();
         if (h0 + 32 < hend) load(h0 + 32);
-#pragma unroll 8
-        for (int c = 0; c < 32; ++c) {
-            double a[4], b[4];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                a[q] = static_cast<double>(xs[buf][c][4 * ti + q]);
-                b[q] = static_cast<double>(wsm[buf][c][4 * ei + q]);
-            }
+        for (int ks = 0; ks < 8; ++ks) {
+            const int kk = 4 * ks + kq;
+            double a[2], b[2];
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+            for (int i = 0; i < 2; ++i) a[i] = static_cast<double>(xs[buf][kk][tb + 16 * i + col]);
 #pragma unroll
-                for (int j = 0; j < 4; ++j) acc[i][j] = fma(a[i], b[j], acc[i][j]);
+            for (int j = 0; j < 2; ++j) b[j] = static_cast<double>(wsm[buf][kk][eb + 16 * j + col]);
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[i], b[j], acc[i][j], 0, 0, 0);
         }
         buf ^= 1;
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int t = t0 + 4 * ti + i;
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int e = e0 + 4 * ei + j;
-            if (t < T && e < E) partial[(static_cast<size_t>(s) * T + t) * E + e] = acc[i][j];
-        }
-    }
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int t = t0 + tb + 16 * i + 4 * v + kq;
+                const int e = e0 + eb + 16 * j + col;
+                if (t < T && e < E) partial[(static_cast<size_t>(s) * T + t) * E + e] = acc[i][j][v];
+            }
 }
 
 // ---------------------------------------------------------------- top-k
@@ -284,7 +305,8 @@ __global__ __launch_bounds__(256) void topk_kernel(const double *partial, int S,
 // eight bit-plane ballots and ranked by lane; per-wave counts are prefix-summed per expert in
 // wave order, so a route's rank counts exactly the earlier routes of its
 // expert: the permutation is stable (ascending token). Then counts, the
-// exclusive scan, the M-tile prefix for the grouped GEMMs, perm and inv.
+// exclusive scan and the M-tile prefix for the grouped GEMMs (a workgroup
+// scan, one group per thread), perm and inv.
 // Group E (when n_shared) is the shared expert: T rows, identity order.
 __global__ __launch_bounds__(1024) void permute_kernel(
     const int32_t *idx, int T, int E, int k, int n_shared, int bm, int32_t *counts,
@@ -298,12 +320,14 @@ __global__ __launch_bounds__(1024) void permute_kernel(
     const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     for (int e = tid; e < E; e += 1024) base[e] = 0;
     __syncthreads();
+    int e_next = tid < R ? idx[tid] : 0;  // the next chunk's experts load during this one
     for (int c0 = 0; c0 < R; c0 += 1024) {
         for (int i = tid; i < 16 * kMaxE; i += 1024) wcnt[i / kMaxE][i % kMaxE] = 0;
-        __syncthreads();
         const int r = c0 + tid;
         const bool valid = r < R;
-        const int e = valid ? idx[r] : 0;
+        const int e = e_next;
+        if (r + 1024 < R) e_next = idx[r + 1024];
+        __syncthreads();
         // lanes holding the same expert: the intersection of the 8 bit-plane
         // ballots of the expert index
         static_assert(kMaxE <= 256, "expert indices fit 8 bit planes");
@@ -330,24 +354,48 @@ __global__ __launch_bounds__(1024) void permute_kernel(
         if (valid) rank[r] = wcnt[w][e] + myrank;
         __syncthreads();
     }
+    // counts, their exclusive scan and the tile prefix: one group per thread
+    // (G <= kMaxE + 1 <= 1024), wavefront scans, then the totals of the
+    // wavefronts before
     const int G = E + n_shared;
-    if (tid == 0) {
-        int off = 0, mt = 0;
-        for (int g = 0; g < G; ++g) {
-            const int c = g < E ? base[g] : T;
+    __shared__ int wsum_c[16], wsum_t[16];
+    {
+        const int g = tid;
+        const int c = g < G ? (g < E ? base[g] : T) : 0;
+        const int nt = (c + bm - 1) / bm;
+        int sc = c, st = nt;  // inclusive scans within the wavefront
+        for (int d = 1; d < 64; d <<= 1) {
+            const int oc = __shfl_up(sc, d), ot = __shfl_up(st, d);
+            if (lane >= d) {
+                sc += oc;
+                st += ot;
+            }
+        }
+        if (lane == 63) {
+            wsum_c[w] = sc;
+            wsum_t[w] = st;
+        }
+        __syncthreads();
+        int pc = 0, pt = 0;
+        for (int ww = 0; ww < w; ++ww) {
+            pc += wsum_c[ww];
+            pt += wsum_t[ww];
+        }
+        const int off = pc + sc - c, mt = pt + st - nt;
+        if (g < G) {
             start[g] = off;
             offsets[g] = off;
             mprefix[g] = mt;
             counts[g] = c;
             if (out_counts && g < E) out_counts[g] = c;
             if (out_offsets && g < E) out_offsets[g] = off;
-            off += c;
-            mt += (c + bm - 1) / bm;
         }
-        start[G] = off;
-        offsets[G] = off;
-        mprefix[G] = mt;
-        if (out_offsets) out_offsets[E] = R;
+        if (g == G - 1) {
+            start[G] = off + c;
+            offsets[G] = off + c;
+            mprefix[G] = mt + nt;
+        }
+        if (out_offsets && g == 0) out_offsets[E] = R;
     }
     __syncthreads();
     for (int r = tid; r < R; r += 1024) {
@@ -380,7 +428,7 @@ RouterPlan router_plan(int T, int H, int E) {
     }
     const int tiles = ((T + 63) / 64) * ((E + 63) / 64);
     int want = (512 + tiles - 1) / tiles;
-    want = want < 1 ? 1 : (want > 16 ? 16 : want);
+    want = want < 1 ? 1 : (want > kRouterMaxSplits ? kRouterMaxSplits : want);
     const int units = H / 32;
     if (want > units) want = units;
     p.gemv = false;
@@ -430,7 +478,8 @@ bool router_quantizes(int T) { return T <= kRouterGemvMaxT; }
 
 hipError_t launch_quantize(const TermsOut &terms, int T, int H, hipStream_t s) {
     const int Kp = pad128(H);
-    launch_kernel(quantize_terms_kernel, (T * (Kp / 32) + 7) / 8, 256, s, terms.in, terms.in_bf16,
+    const int wgs = (T * (Kp / 32) + 7) / 8;
+    launch_kernel(quantize_terms_kernel, wgs < 2048 ? wgs : 2048, 256, s, terms.in, terms.in_bf16,
                   T, H, Kp, terms.q, terms.scales);
     return hipGetLastError();
 }
