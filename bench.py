@@ -10,6 +10,8 @@ input (weights and activations resident in HBM before timing):
   stack   24 gpt-oss-20b-shaped layers (RMSNorm + MoE), T=512
   ds4     DeepSeek-V4-Flash-shaped layer, T=2048, 256 experts top-6 + shared
   tiny    T=8, H=F=256, 8 experts top-2
+  decode_stack  T=1 tokens through 24 gpt-oss-20b-shaped layers (RMSNorm + MoE),
+          16 tokens per step, each layer's output the next layer's input
 Each step's calls are captured once in a HIP graph and replayed; W warm-up
 steps, then exactly K timed steps between two synchronisations. The last
 timed step is launched eagerly with the library's moe_profile_next_launch
@@ -50,6 +52,10 @@ WORKLOADS = {
                 steps=50),
     "tiny": dict(config=1, name="tiny_T8_H256_E8_top2", kernel="decode_gate_up", copies=1,
                  steps=200),
+    # T=1 decode through the 24-layer stack's weights (RMSNorm + MoE per layer):
+    # 16 independent tokens per step, each through all 24 layers in turn
+    "decode_stack": dict(config=4, name="gptoss20b_decode_stack24_T1_16tok",
+                         kernel="decode_gate_up", copies=1, steps=10, tokens=16),
 }
 KERNEL_SOURCES = {"decode_gate_up": "decode.hip", "decode_down": "decode.hip",
                   "gate_up_gemm": "prefill.hip", "down_gemm": "prefill.hip"}
@@ -164,7 +170,22 @@ class Setup:
             self.xd = torch.from_numpy(x).cuda()
         self.ws = workspace(self.shape)
         self.tokens_per_step = cfg.T * cfg.calls
-        if cfg.path == "decode" and cfg.T == 1:
+        # "calls": independent T=1 decode calls; "decode_stack": T=1 tokens
+        # through every layer; "decode": one decode call; "prefill"
+        if "tokens" in spec:
+            self.mode = "decode_stack"
+        elif cfg.path == "decode":
+            self.mode = "calls" if cfg.T == 1 else "decode"
+        else:
+            self.mode = "prefill"
+        if self.mode == "decode_stack":
+            self.ntok = spec["tokens"]
+            self.tokens_per_step = self.ntok
+            self.step_shape = mx.make_shape(**cfg.shape_kwargs(1))
+            self.ws = workspace(self.step_shape)
+            self.out = torch.empty((self.ntok, 2, cfg.H), dtype=torch.float32, device="cuda")
+            self.xrows = [self.xd[i:i + 1] for i in range(self.ntok)]
+        elif self.mode == "calls":
             # one step = cfg.calls independent T=1 calls
             self.step_shape = mx.make_shape(**cfg.shape_kwargs(1))
             self.ws = workspace(self.step_shape)
@@ -180,14 +201,23 @@ class Setup:
         """Closures making up one step (weights copy chosen per call/step)."""
         mx, cfg = self.mx, self.cfg
         calls = []
-        if cfg.path == "decode" and cfg.T == 1:
+        if self.mode == "decode_stack":
+            for i in range(self.ntok):
+                src = self.xrows[i]
+                for l, dl in enumerate(self.layers):
+                    dst = self.out[i, l % 2].view(1, cfg.H)
+                    calls.append(lambda dl=dl, src=src, dst=dst: mx.moe_forward_decode(
+                        self.step_shape, src, dl.router_w, dl.router_b, dl.experts_copy(0), dst,
+                        self.ws, norm_w=dl.norm_w))
+                    src = dst
+        elif self.mode == "calls":
             dl = self.layers[0]
             for i in range(cfg.calls):
                 ex = dl.experts_copy(i)
                 calls.append(lambda i=i, ex=ex: mx.moe_forward_decode(
                     self.step_shape, self.xrows[i], dl.router_w, dl.router_b, ex, self.orows[i],
                     self.ws))
-        elif cfg.path == "decode":
+        elif self.mode == "decode":
             dl = self.layers[0]
             calls.append(lambda: mx.moe_forward_decode(
                 self.shape, self.xd, dl.router_w, dl.router_b, dl.experts_copy(step), self.out,
@@ -214,7 +244,7 @@ class Setup:
         pad = lambda n: (n + 127) // 128 * 128
         terms = lambda n: 4 * pad(n) + 4 * pad(n) // 32
         if self.spec["kernel"] == "decode_gate_up":
-            T = 1 if cfg.T == 1 else cfg.T
+            T = 1 if self.mode in ("calls", "decode_stack") else cfg.T
             routes = T * k + T * cfg.n_shared
             splits = (H + 2047) // 2048
             byts = routes * 2 * (mat + 4 * F) + T * terms(H) + routes * terms(F) + T * splits * E * 8
@@ -233,8 +263,10 @@ class Setup:
         cfg = self.cfg
         H, F, k = cfg.H, cfg.F, cfg.k
         expert = 3 * F * H * 17 // 32 + 4 * (2 * F + H)
-        if cfg.path == "decode" and cfg.T == 1:
+        if self.mode == "calls":
             return cfg.calls * k * expert
+        if self.mode == "decode_stack":
+            return self.ntok * cfg.layers * k * expert
         tot = 0
         for counts in counts_per_call:
             tot += (sum(1 for c in counts if c > 0) + cfg.n_shared) * expert
@@ -246,7 +278,7 @@ def route_counts(setup):
     import torch
     mx, cfg = setup.mx, setup.cfg
     res = []
-    if cfg.path == "decode":
+    if setup.mode != "prefill":
         return res
     src = setup.xd
     bufs = (setup.out, setup.out2)
@@ -285,7 +317,17 @@ def cpu_baseline(setup, budget_s: float):
     except Exception:  # pragma: no cover
         cores = 1
     x = setup.x_host
-    if cfg.path == "decode" and cfg.T == 1:
+    if setup.mode == "decode_stack":
+        # the oracle on layer 0 only (the one layer kept on the host), scaled to
+        # the stack's layer count: tokens through all layers per second
+        n = 4
+        t0 = time.time()
+        omoe.block_for_config(cfg, layer, x[:n])
+        dt = time.time() - t0
+        return dict(value=n / (dt * cfg.layers), unit="tokens/s", cores=cores, kind="oracle",
+                    sample=f"{n} tokens through layer 0 (RMSNorm + MoE) in one fp64 oracle "
+                           f"call ({dt:.1f} s), times {cfg.layers} layers")
+    if setup.mode == "calls":
         n = 96
         t0 = time.time()
         omoe.block_for_config(cfg, layer, x[:n])
@@ -342,7 +384,7 @@ def main():
     stream = torch.cuda.current_stream().cuda_stream
 
     counts = route_counts(setup)
-    ncopies_graph = 1 if (cfg.path == "decode" and cfg.T == 1) else setup.copies
+    ncopies_graph = 1 if setup.mode in ("calls", "decode_stack") else setup.copies
     plain = [setup.step_calls(c) for c in range(ncopies_graph)]
     for calls in plain:          # eager run once (validates arguments, warms code objects)
         for c in calls:
@@ -413,7 +455,7 @@ def main():
         "dtype": DTYPE,
         "data": "synthetic",
         "config": {
-            "workload": spec["name"], "T": cfg.T, "H": cfg.H, "F": cfg.F, "E": cfg.E,
+            "workload": spec["name"], "T": int(setup.step_shape.T), "H": cfg.H, "F": cfg.F, "E": cfg.E,
             "k": cfg.k, "n_shared": cfg.n_shared, "layers": cfg.layers,
             "tokens_per_step": setup.tokens_per_step, "weights": "mxfp4 (e2m1 + e8m0/32) + fp32 bias",
             "activations": cfg.act_dtype, "weight_copies": setup.copies,

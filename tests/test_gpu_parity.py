@@ -266,6 +266,41 @@ def test_prefill_stack24_teacher_forced():
     print(f"config 4 stack: worst per-layer max|err|/rms = {worst:.2e}")
 
 
+def test_config4_decode_stack():
+    """T=1 decode through the 24 layers of config 4 (RMSNorm + MoE each), the
+    output of each layer the input of the next; every layer's routing and
+    layers 0, 11 and 23's outputs against the oracle on the GPU's own layer
+    input (teacher forcing)."""
+    cfg = config_by_id(4)
+    _announce("decode config 4 layers: one token at T=1 through 24 layers, teacher forcing")
+    x, _ = make_activations(cfg, rows=1)
+    shape = shape_of(cfg, 1)
+    h = torch.from_numpy(x).cuda()
+    ws = workspace(shape)
+    check_layers = {0, 11, 23}
+    worst = 0.0
+    for l in range(cfg.layers):
+        layer = make_layer(cfg, l)
+        dl = upload(cfg, layer)
+        ro = route_buffers(1, cfg.k, cfg.E)
+        out = torch.full_like(h, float("nan"))
+        mx.moe_forward_decode(shape, h, dl.router_w, dl.router_b, dl.experts_copy(0), out, ws,
+                              norm_w=dl.norm_w, route_out=ro)
+        torch.cuda.synchronize()
+        hin = h.cpu().numpy()
+        got = to_np(ro)
+        ref = _oracle(cfg, layer, hin)
+        check_routing(got["topk_idx"], got["topk_w"], ref, layer.router_w, layer.router_b, 1.0)
+        check_permutation(got, got["topk_idx"], cfg.E)
+        if l in check_layers:
+            err = rel_err(out.cpu().numpy(), hin + ref["delta"])
+            worst = max(worst, err)
+            assert err <= TOL, (l, err)
+        h = out
+        del dl
+    print(f"config 4 decode stack: worst per-layer max|err|/rms = {worst:.2e}")
+
+
 # ---------------------------------------------------------------- edge cases
 def _small(cid, **kw):
     return scaled(config_by_id(cid), **kw)
