@@ -12,7 +12,7 @@ constexpr int kMaxK = 8;   // experts per token
 constexpr int kMaxE = 256; // routed experts
 constexpr int kTerms = 4;  // FP8 terms per activation on the block-scaled matrix cores
 
-// Grouped GEMMs: tiles of 16, 32 or 64 routed rows of one expert
+// Grouped GEMMs: tiles of 16 or 32 routed rows of one expert
 // (gemm_tile_rows), which the permutation's tile prefix also uses.
 // Decode GEMVs: 32 weight rows per workgroup, K split over 8 wavefronts.
 constexpr int kDecodeRows = 32;
@@ -139,7 +139,7 @@ hipError_t launch_decode_down(const DecodeArgs &a, hipStream_t s);
 // prefill (any T) -------------------------------------------------------------
 // Rows in expert order: position p < T*k is route perm[p]; p >= T*k is the
 // shared expert of token p - T*k. act_q / act_s are indexed by p. tile_rows
-// (16, 32 or 64) comes from gemm_tile_rows, max_tiles bounds the tile count.
+// (16 or 32) comes from gemm_tile_rows, max_tiles bounds the tile count.
 int gemm_tile_rows(int T, int k, int E, int n_shared);
 // x_terms: FP8 terms of the expert input that take part, 3 or kTerms (three
 // carry a bfloat16 input as closely as four; a float32 one needs four).

@@ -54,9 +54,9 @@ struct Geo {
     static constexpr int kDownRows = W * 16 * NA;          // hidden rows per down workgroup
     // K-steps of A fragments in flight: 3 for 32-row tiles; 2 for 16-row
     // tiles (120 VGPRs: four workgroups per CU, which beats three with a
-    // deeper ring) and for 64-row tiles (long matrix-core work per step,
-    // registers short)
+    // deeper ring)
     static constexpr int kASlots = NG == 2 ? 3 : 2;
+    static_assert(NG == 1 || NG == 2, "16- or 32-row tiles");
     static_assert(kPieces % kThreads == 0, "B staging divides evenly");
     static_assert(kScales <= kThreads, "one scale dword per thread at most");
     static_assert(kGateUpRows % 32 == 0, "gate/up blocks hold whole 32-feature MX blocks");
@@ -464,18 +464,16 @@ int items(int nrb, int max_tiles) {
 // 16-row tiles, at four workgroups per CU, up to 96 rows per expert on
 // average (measured faster than 32-row tiles at 16, 56 and 64 rows per
 // expert: the T=128 layer, the DS4-shaped layer, the 24-layer stack); 32-row
-// tiles above, where the weights' re-reads per tile dominate. 64-row tiles (8
-// wavefronts x 2 A fragments) are built but not chosen: at 2 A fragments per
-// B operand their LDS reads run at the LDS limit (measured slower on the
-// 24-layer stack and the DS4-shaped layer).
+// tiles above, where the weights' re-reads per tile dominate. (64-row tiles
+// measured slower on every workload: with 2 A fragments per wavefront their
+// LDS reads of B hit the LDS limit; with 4 their registers allow one
+// wavefront per SIMD.)
 int gemm_tile_rows(int T, int k, int E, int n_shared) {
     const double avg = static_cast<double>(T) * (k + n_shared) / (E + n_shared);
     return avg > 96.0 ? 32 : 16;
 }
 
-// Tiles of 16 and 32 rows: 4 wavefronts with 4 A fragments each; 64-row
-// tiles: 8 wavefronts with 2 (the accumulators and B staging of a 64-row tile
-// leave no room for 4).
+// Tiles of 16 and 32 rows: 4 wavefronts with 4 A fragments each.
 hipError_t launch_gate_up_gemm(const uint8_t *xq, const uint8_t *xs, int T, int H, int F, int E,
                                int k, int n_shared, const ExpertPtrs &ex, const ExpertPtrs &sh,
                                SwigluConsts c, const int32_t *offsets, const int32_t *perm,
@@ -495,8 +493,6 @@ hipError_t launch_gate_up_gemm(const uint8_t *xq, const uint8_t *xs, int T, int 
     case 164: MOE_GU(1, 4, 4, 4); break;
     case 323: MOE_GU(2, 4, 4, 3); break;
     case 324: MOE_GU(2, 4, 4, 4); break;
-    case 643: MOE_GU(4, 8, 2, 3); break;
-    case 644: MOE_GU(4, 8, 2, 4); break;
     default: return hipErrorInvalidValue;
     }
 #undef MOE_GU
@@ -519,7 +515,6 @@ hipError_t launch_down_gemm(const uint8_t *act_q, const uint8_t *act_s, int T, i
     switch (tile_rows) {
     case 16: MOE_DN(1, 4, 4); break;
     case 32: MOE_DN(2, 4, 4); break;
-    case 64: MOE_DN(4, 8, 2); break;
     default: return hipErrorInvalidValue;
     }
 #undef MOE_DN
