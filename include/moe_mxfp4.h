@@ -162,6 +162,7 @@ size_t moe_workspace_bytes(const moe_shape *shape);
  *   x        [T, H] float32 or bfloat16 (shape->act_dtype), device
  *   norm_w   [H] float32 RMSNorm weight or NULL (no norm), device
  *   router_w [E, H] float32, router_b [E] float32, device
+ *   x, norm_w and router_w 16-byte aligned (MOE_ERR_INVALID_ARG otherwise)
  *   out      non-NULL; NULL fields are not written (see moe_route_out)
  *   ws       >= moe_workspace_bytes(shape) bytes, 256-byte aligned, device
  * Pages: goosedump `mixture_of_experts_batch` (router matmul, add_bias_batch,
@@ -177,6 +178,8 @@ int moe_route(const moe_shape *shape, const void *x, const float *norm_w,
  *   shared   n_shared packed blobs (same layout) or NULL when n_shared == 0
  *   out      [T, H] float32, device; may alias a float32 hidden
  *   route_out NULL, or routing results to export (fields may be NULL)
+ *   norm_w, router_w, router_b, ws as for moe_route
+ *   hidden, out, norm_w and router_w 16-byte aligned, expert blobs 256-byte
  * Pages: goosedump `mixture_of_experts` (router matvec, add_bias,
  * top_experts, softmax, per expert: matrix_vector_pair, biases, swiglu,
  * matrix_vector, bias, times the route weight, summed over slots). */
@@ -219,8 +222,8 @@ typedef enum moe_kernel_id {
     MOE_KERNEL_DECODE_DOWN = 5,
     MOE_KERNEL_GATE_UP_GEMM = 6,
     MOE_KERNEL_DOWN_GEMM = 7,
-    MOE_KERNEL_QUANTIZE = 8,        /* FP8 terms of the expert input, when it is
-                                       its own kernel (T > 16) */
+    MOE_KERNEL_QUANTIZE = 8,        /* reserved: the FP8 terms of the expert input
+                                       are made inside the router launch */
     MOE_KERNEL_COMBINE = 9          /* prefill: residual + sum of the routes' outputs */
 } moe_kernel_id;
 

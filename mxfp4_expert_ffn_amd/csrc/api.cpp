@@ -91,8 +91,7 @@ void layout_of(const moe_shape *s, moe_blob_layout *L) {
 }
 
 struct Workspace {
-    double *xn64;
-    float *xn32;
+    double *rinv;     // RMSNorm scale per token [T]
     double *partial;  // router split-K partial logits [splits][T][E]
     int splits;
     int32_t *idx;
@@ -117,8 +116,7 @@ Workspace carve(const moe_shape *s, uint8_t *base) {
         o = align_up(o + bytes, 256);
         return p;
     };
-    w.xn64 = reinterpret_cast<double *>(take(T * H * 8));
-    w.xn32 = reinterpret_cast<float *>(take(T * H * 4));
+    w.rinv = reinterpret_cast<double *>(take(T * 8));
     const moe::RouterPlan rp = moe::router_plan(s->T, s->H, s->E);
     w.splits = rp.splits;
     w.partial = reinterpret_cast<double *>(take(static_cast<uint64_t>(rp.splits) * T * E * 8));
@@ -205,8 +203,9 @@ int check_forward(const moe_shape *s, const void *hidden, const float *norm_w,
         return fail(MOE_ERR_INVALID_ARG, "hidden, router_w, router_b, experts and out must be non-NULL");
     if (s->n_shared && !shared) return fail(MOE_ERR_INVALID_ARG, "n_shared=1 needs a shared expert blob");
     if (!s->n_shared && shared) return fail(MOE_ERR_INVALID_ARG, "shared blob given with n_shared=0");
-    if (!aligned(hidden, 16) || !aligned(out, 16) || !aligned(router_w, 16))
-        return fail(MOE_ERR_INVALID_ARG, "hidden, out and router_w must be 16-byte aligned");
+    if (!aligned(hidden, 16) || !aligned(out, 16) || !aligned(router_w, 16) ||
+        (norm_w && !aligned(norm_w, 16)))
+        return fail(MOE_ERR_INVALID_ARG, "hidden, out, router_w and norm_w must be 16-byte aligned");
     if (!aligned(experts, 256) || (shared && !aligned(shared, 256)))
         return fail(MOE_ERR_INVALID_ARG, "expert blobs must be 256-byte aligned");
     if (norm_w && !(s->rms_eps >= 0.f)) return fail(MOE_ERR_INVALID_ARG, "rms_eps must be >= 0");
@@ -218,31 +217,24 @@ int check_forward(const moe_shape *s, const void *hidden, const float *norm_w,
 // RMSNorm (optional), the router's partial logits and, with `terms`, the FP8
 // terms of the expert input (in the router's grid for small T, else their own
 // kernel).
+// RMSNorm scale (with a norm) and router. `terms`: the router launch also
+// makes the FP8 terms of the expert input. Returns the expert input in `in`.
 int route_front(const moe_shape *s, const void *x, const float *norm_w, const float *router_w,
-                const Workspace &w, bool terms, hipStream_t st) {
+                const Workspace &w, bool terms, moe::RouteIn *in, hipStream_t st) {
     const int bf16 = s->act_dtype == MOE_BF16;
-    const void *rin = x;
-    int kind = bf16;
-    const void *ein = x;
-    int ein_bf16 = bf16;
+    *in = moe::RouteIn{x, bf16, nullptr, nullptr};
     if (norm_w) {
         MOE_TRY(launch(MOE_KERNEL_RMSNORM, "rmsnorm", st, [&] {
-            return moe::launch_rmsnorm(x, bf16, norm_w, s->T, s->H, s->rms_eps, w.xn64, w.xn32, st);
+            return moe::launch_rms_inv(x, bf16, s->T, s->H, s->rms_eps, w.rinv, st);
         }));
-        rin = w.xn64;
-        kind = 2;
-        ein = w.xn32;
-        ein_bf16 = 0;
+        in->inv = w.rinv;
+        in->gamma = norm_w;
     }
-    const moe::TermsOut tq{ein, ein_bf16, w.xq, w.xs};
-    const bool fused = terms && moe::router_quantizes(s->T);
+    const moe::TermsOut tq{w.xq, w.xs};
     MOE_TRY(launch(MOE_KERNEL_ROUTER, "router", st, [&] {
-        return moe::launch_router(rin, kind, router_w, s->T, s->H, s->E, w.partial,
-                                  fused ? &tq : nullptr, st);
+        return moe::launch_router(*in, router_w, s->T, s->H, s->E, w.partial, terms ? &tq : nullptr,
+                                  st);
     }));
-    if (terms && !fused)
-        MOE_TRY(launch(MOE_KERNEL_QUANTIZE, "quantize", st,
-                       [&] { return moe::launch_quantize(tq, s->T, s->H, st); }));
     return MOE_OK;
 }
 
@@ -319,21 +311,21 @@ int moe_route(const moe_shape *s, const void *x, const float *norm_w, const floa
     if (s->T == 0) return ok();
     if (!x || !router_w || !router_b || !out)
         return fail(MOE_ERR_INVALID_ARG, "x, router_w, router_b and out must be non-NULL");
-    if (!aligned(x, 16) || !aligned(router_w, 16))
-        return fail(MOE_ERR_INVALID_ARG, "x and router_w must be 16-byte aligned");
+    if (!aligned(x, 16) || !aligned(router_w, 16) || (norm_w && !aligned(norm_w, 16)))
+        return fail(MOE_ERR_INVALID_ARG, "x, router_w and norm_w must be 16-byte aligned");
     if (norm_w && !(s->rms_eps >= 0.f)) return fail(MOE_ERR_INVALID_ARG, "rms_eps must be >= 0");
     MOE_TRY(check_ws(s, ws, ws_bytes));
     if (s->T == 0) return ok();
     const Workspace w = carve(s, static_cast<uint8_t *>(ws));
-    MOE_TRY(route_front(s, x, norm_w, router_w, w, false, st));
+    moe::RouteIn in;
+    MOE_TRY(route_front(s, x, norm_w, router_w, w, false, &in, st));
     MOE_TRY(launch(MOE_KERNEL_TOPK, "topk", st, [&] {
         return moe::launch_topk(w.partial, w.splits, router_b, s->T, s->E, s->k, s->route_scale,
-                                w.idx, w.wts, out->topk_idx, out->topk_w, nullptr, 0, s->H,
-                                nullptr, st);
+                                w.idx, w.wts, out->topk_idx, out->topk_w, st);
     }));
     MOE_TRY(launch(MOE_KERNEL_PERMUTE, "permute", st, [&] { return moe::launch_permute(w.idx, s->T, s->E, s->k, 0, 16, w.counts, w.offsets, w.perm,
                                           w.inv, w.rank, w.mprefix, out->counts, out->offsets,
-                                          out->perm, out->inv, st); }));
+                                          out->perm, out->inv, nullptr, s->H, nullptr, st); }));
     return ok();
 }
 
@@ -347,7 +339,8 @@ int moe_forward_decode(const moe_shape *s, const void *hidden, const float *norm
         return fail(MOE_ERR_UNSUPPORTED, "decode takes H, F <= 8192");
     if (s->T == 0) return ok();
     const Workspace w = carve(s, static_cast<uint8_t *>(ws));
-    MOE_TRY(route_front(s, hidden, norm_w, router_w, w, true, st));
+    moe::RouteIn in;
+    MOE_TRY(route_front(s, hidden, norm_w, router_w, w, true, &in, st));
     moe::DecodeArgs a{};
     a.xq = w.xq;
     a.xs = w.xs;
@@ -381,7 +374,7 @@ int moe_forward_decode(const moe_shape *s, const void *hidden, const float *norm
         MOE_TRY(launch(MOE_KERNEL_PERMUTE, "permute", st, [&] {
             return moe::launch_permute(w.idx, s->T, s->E, s->k, 0, 16, w.counts, w.offsets, w.perm,
                                        w.inv, w.rank, w.mprefix, ro->counts, ro->offsets,
-                                       ro->perm, ro->inv, st);
+                                       ro->perm, ro->inv, nullptr, s->H, nullptr, st);
         }));
     return ok();
 }
@@ -399,18 +392,23 @@ int moe_forward_prefill(const moe_shape *s, const void *hidden, const float *nor
             return fail(MOE_ERR_UNSUPPORTED, "prefill needs T*(k+n_shared)*4*pad128(F) and T*4*pad128(H) below 2^32");
     }
     const Workspace w = carve(s, static_cast<uint8_t *>(ws));
-    MOE_TRY(route_front(s, hidden, norm_w, router_w, w, true, st));
+    // the FP8 terms of the expert input ride in the router launch in its
+    // GEMV form, else beside the one-workgroup permutation
+    moe::RouteIn in;
+    const bool router_terms = moe::router_plan(s->T, s->H, s->E).gemv;
+    MOE_TRY(route_front(s, hidden, norm_w, router_w, w, router_terms, &in, st));
     MOE_TRY(launch(MOE_KERNEL_TOPK, "topk", st, [&] {
         return moe::launch_topk(w.partial, w.splits, router_b, s->T, s->E, s->k, s->route_scale,
                                 w.idx, w.wts, ro ? ro->topk_idx : nullptr,
-                                ro ? ro->topk_w : nullptr, nullptr, 0, s->H, nullptr, st);
+                                ro ? ro->topk_w : nullptr, st);
     }));
     const int bm = moe::gemm_tile_rows(s->T, s->k, s->E, s->n_shared);
+    const moe::TermsOut tq{w.xq, w.xs};
     MOE_TRY(launch(MOE_KERNEL_PERMUTE, "permute", st, [&] {
         return moe::launch_permute(w.idx, s->T, s->E, s->k, s->n_shared, bm, w.counts, w.offsets,
                                    w.perm, w.inv, w.rank, w.mprefix, ro ? ro->counts : nullptr,
                                    ro ? ro->offsets : nullptr, ro ? ro->perm : nullptr,
-                                   ro ? ro->inv : nullptr, st);
+                                   ro ? ro->inv : nullptr, &in, s->H, router_terms ? nullptr : &tq, st);
     }));
     const moe::ExpertPtrs ex = expert_ptrs(s, experts);
     const moe::ExpertPtrs sh = expert_ptrs(s, shared);

@@ -63,8 +63,18 @@ struct SwigluConsts {
 };
 
 // routing -----------------------------------------------------------------
-hipError_t launch_rmsnorm(const void *x, int x_bf16, const float *gamma, int T, int H, float eps,
-                          double *xn64, float *xn32, hipStream_t s);
+// Input of the router and of the expert path: x (float32, or bf16 bits) or,
+// with an RMSNorm, the fp64 value (x[t][h] * inv[t]) * gamma[h], which the
+// router takes as is and the expert path rounds to float32.
+struct RouteIn {
+    const void *x;
+    int bf16;
+    const double *inv;   // [T] RMSNorm scale, or NULL: no norm
+    const float *gamma;  // [H] norm weight (16-byte aligned) when inv is set
+};
+// RMSNorm scale inv[t] = 1 / sqrt(sum_h x[t][h]^2 / H + eps), summed in fp64.
+hipError_t launch_rms_inv(const void *x, int x_bf16, int T, int H, float eps, double *inv,
+                          hipStream_t s);
 // Router: split-K partial logits partial[splits][T][E] (fp64, bias not added).
 // GEMV form for T <= kRouterGemvMaxT (one wavefront per expert and
 // 2048-wide hidden slice), tiled form otherwise (slices sized for about 512
@@ -72,39 +82,38 @@ hipError_t launch_rmsnorm(const void *x, int x_bf16, const float *gamma, int T, 
 constexpr int kRouterGemvMaxT = 16;
 constexpr int kRouterMaxSplits = 64;
 constexpr int kRouterGemvSlice = 2048;
+// Most quantisation workgroups beside the tiled router (grid-stride beyond).
+constexpr int kQuantizeMaxWgs = 1024;
 struct RouterPlan {
     bool gemv;
     int slice;   // hidden units per split
     int splits;  // S
 };
 RouterPlan router_plan(int T, int H, int E);
-// FP8-term quantisation of the expert input (every forward): q
-// [T][kTerms][Kp] E4M3 codes, scales [T][kTerms][Kp/32] E8M0 bytes, Kp =
-// pad128(H), zero codes past H. It rides in the GEMV router's grid, or runs as
-// its own kernel beside the tiled router.
+// FP8-term quantisation of the expert input (every forward), done by extra
+// workgroups of the router launch: q [T][kTerms][Kp] E4M3 codes, scales
+// [T][kTerms][Kp/32] E8M0 bytes, Kp = pad128(H), zero codes past H.
 struct TermsOut {
-    const void *in;
-    int in_bf16;
     uint8_t *q;
     uint8_t *scales;
 };
-// in_kind: 0 float32, 1 bf16 bits, 2 float64
-// `terms` is honoured only where router_quantizes(T); otherwise it must be
-// NULL and launch_quantize does that work.
-hipError_t launch_router(const void *x, int in_kind, const float *w, int T, int H, int E,
-                         double *partial, const TermsOut *terms, hipStream_t s);
-bool router_quantizes(int T);  // true when launch_router's grid also quantises
-hipError_t launch_quantize(const TermsOut &terms, int T, int H, hipStream_t s);
+// `terms` NULL: router only.
+hipError_t launch_router(const RouteIn &in, const float *w, int T, int H, int E, double *partial,
+                         const TermsOut *terms, hipStream_t s);
 hipError_t launch_topk(const double *partial, int S, const float *bias, int T, int E, int k,
                        float route_scale, int32_t *idx, float *wts, int32_t *out_idx, float *out_w,
-                       const void *resid, int resid_bf16, int H, float *out, hipStream_t s);
+                       hipStream_t s);
 // mprefix[g] = tiles of tile_rows rows before group g (groups: E experts,
-// then the shared expert's T rows when n_shared).
+// then the shared expert's T rows when n_shared). With `terms` (and `qin`,
+// the expert input) the launch's other workgroups make the FP8 terms, as
+// launch_router would; the permutation itself is one workgroup, so they run
+// on otherwise idle compute units.
+constexpr int kPermuteQuantizeWgs = 512;
 hipError_t launch_permute(const int32_t *idx, int T, int E, int k, int n_shared, int tile_rows,
                           int32_t *counts, int32_t *offsets, int32_t *perm, int32_t *inv,
                           int32_t *rank, int32_t *mprefix, int32_t *out_counts,
                           int32_t *out_offsets, int32_t *out_perm, int32_t *out_inv,
-                          hipStream_t s);
+                          const RouteIn *qin, int H, const TermsOut *terms, hipStream_t s);
 
 // decode (T <= 64) -----------------------------------------------------------
 // Route r < T*k is slot r % k of token r / k; r >= T*k is the shared expert of
@@ -132,7 +141,7 @@ struct DecodeArgs {
     uint8_t *act_q, *act_s;
 };
 // gate/up (which also selects the experts and seeds out with the residual),
-// then down; both after launch_router (+ launch_quantize).
+// then down; both after launch_router.
 hipError_t launch_decode_gate_up(const DecodeArgs &a, hipStream_t s);
 hipError_t launch_decode_down(const DecodeArgs &a, hipStream_t s);
 

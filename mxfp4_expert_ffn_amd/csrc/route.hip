@@ -1,4 +1,4 @@
-// Routing kernels: RMSNorm, router logits (fp64), top-k + route weights,
+// Routing kernels: RMSNorm scale, router logits (fp64), top-k + route weights,
 // per-expert histogram / exclusive scan / stable permutation.
 //
 // Pages: goosedump `gpt_oss.rs` `mixture_of_experts_batch` (router matmul,
@@ -14,85 +14,94 @@ namespace moe {
 
 namespace {
 
+// x[i] widened exactly to fp64; KIND 0 float32, 1 bf16 bits.
 template <int KIND>
 __device__ __forceinline__ double load_in(const void *x, size_t i) {
     if constexpr (KIND == 0) return static_cast<double>(static_cast<const float *>(x)[i]);
-    else if constexpr (KIND == 1) return static_cast<double>(bf16_bits_to_f32(static_cast<const uint16_t *>(x)[i]));
-    else return static_cast<const double *>(x)[i];
+    else return static_cast<double>(bf16_bits_to_f32(static_cast<const uint16_t *>(x)[i]));
 }
 
-// ---------------------------------------------------------------- RMSNorm
-// One workgroup per token: fp64 sum of squares, inv = 1/sqrt(ss/H + eps),
-// xn = x * inv * gamma kept in fp64 (for the router) and float32 (experts).
-template <int KIND>
-__global__ __launch_bounds__(256) void rmsnorm_kernel(const void *x, const float *gamma, int H,
-                                                      float eps, double *xn64, float *xn32) {
-    const int t = blockIdx.x;
-    const size_t row = static_cast<size_t>(t) * H;
-    double ss = 0.0;
-    for (int h = threadIdx.x; h < H; h += blockDim.x) {
-        const double v = load_in<KIND>(x, row + h);
-        ss = fma(v, v, ss);
-    }
-    __shared__ double part[4];
-    ss = wave_sum_f64(ss);
-    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = ss;
-    __syncthreads();
-    const double total = part[0] + part[1] + part[2] + part[3];
-    const double inv = 1.0 / sqrt(total / H + static_cast<double>(eps));
-    for (int h = threadIdx.x; h < H; h += blockDim.x) {
-        const double v = load_in<KIND>(x, row + h) * inv * static_cast<double>(gamma[h]);
-        xn64[row + h] = v;
-        xn32[row + h] = static_cast<float>(v);
-    }
-}
-
-// ---------------------------------------------------------------- router logits
-// Both router kernels write split-K partial sums partial[s][t][e] (fp64) over
-// hidden-dimension slices; consumers add the S partials in split order and
-// the bias (gather_logits), so the logits are deterministic. fp32 x fp32
-// products are exact in fp64.
-
-// Few tokens: one wavefront per (expert, hidden slice of kRouterGemvSlice
-// units); lane l holds the router weights of units 4(l + 64i) .. +3 of the
-// slice in registers (all loads issued at once), then each token's
-// activations are loaded the same way and reduced with a wave sum.
+// Four consecutive inputs x[i..i+3] (i a multiple of 4) widened to fp64.
 template <int KIND>
 __device__ __forceinline__ void load4(const void *x, size_t i, double (&v)[4]) {
     if constexpr (KIND == 0) {
         const float4 f = *reinterpret_cast<const float4 *>(static_cast<const float *>(x) + i);
         v[0] = f.x; v[1] = f.y; v[2] = f.z; v[3] = f.w;
-    } else if constexpr (KIND == 1) {
+    } else {
         const uint2 u = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(x) + i);
         v[0] = __uint_as_float(u.x << 16); v[1] = __uint_as_float(u.x & 0xffff0000u);
         v[2] = __uint_as_float(u.y << 16); v[3] = __uint_as_float(u.y & 0xffff0000u);
-    } else {
-        const double *d = static_cast<const double *>(x) + i;
-        v[0] = d[0]; v[1] = d[1]; v[2] = d[2]; v[3] = d[3];
     }
 }
 
-// Workgroups past the router's own quantise the expert input into FP8 terms
-// for the block-scaled decode kernels: one half-wavefront per 32-value block
-// of k (the unit an E8M0 scale of the matrix core's operand B covers); codes
-// go to xq[t][n][k] (zero past H), scales to xs[t][n][k / 32].
-__device__ __forceinline__ void quantize_terms_group(const void *q_in, int q_bf16, int T, int H,
-                                                     int Kp, uint8_t *xq, uint8_t *xs, int gidx) {
-    const int lane = threadIdx.x & 63, i = lane & 31;
-    const int nb = Kp / 32;  // blocks per token
-    const bool on = gidx < T * nb;
-    const int g = on ? gidx : 0;
-    const int t = g / nb, blk = g - t * nb;
-    const int kk = 32 * blk + i;
-    float v = 0.f;
-    if (on && kk < H) {
-        const size_t at = static_cast<size_t>(t) * H + kk;
-        v = q_bf16 ? bf16_bits_to_f32(static_cast<const uint16_t *>(q_in)[at])
-                   : static_cast<const float *>(q_in)[at];
+// ---------------------------------------------------------------- RMSNorm
+// One workgroup per token: fp64 sum of squares, inv[t] = 1/sqrt(ss/H + eps).
+// Each thread takes groups of 4 consecutive values (H is a multiple of 32),
+// loading up to 4 groups before it adds them. The normalised input
+// (x * inv[t]) * gamma[h] is formed in fp64, in that order, where it is read
+// (router, FP8-term quantisation), so it never goes through memory.
+template <int KIND>
+__global__ __launch_bounds__(256) void rms_inv_kernel(const void *x, int H, float eps,
+                                                      double *inv) {
+    constexpr int kU = 4;
+    const int t = blockIdx.x;
+    const size_t row = static_cast<size_t>(t) * H;
+    const int groups = H / 4;
+    double ss = 0.0;
+    for (int g0 = threadIdx.x; g0 < groups; g0 += kU * 256) {
+        double v[kU][4];
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+            const int g = g0 + 256 * u;
+            load4<KIND>(x, row + 4 * static_cast<size_t>(g < groups ? g : 0), v[u]);
+        }
+#pragma unroll
+        for (int u = 0; u < kU; ++u)
+            if (g0 + 256 * u < groups)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) ss = fma(v[u][j], v[u][j], ss);
     }
+    __shared__ double part[4];
+    ss = wave_sum_f64(ss);
+    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = ss;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const double total = part[0] + part[1] + part[2] + part[3];
+        inv[t] = 1.0 / sqrt(total / H + static_cast<double>(eps));
+    }
+}
+
+// ---------------------------------------------------------------- FP8 terms
+// Quantisation of the expert input into FP8 terms for the block-scaled
+// matrix-core kernels, done by the workgroups past a router launch's own:
+// one half-wavefront per 32-value block of k (the unit an E8M0 scale of the
+// instruction's operand covers); codes go to xq[t][n][k] (zero past H),
+// scales to xs[t][n][k / 32]. With a norm the value is
+// float32((x * inv[t]) * gamma[k]).
+
+// The lane's value of block gidx (0 past the last block or past H).
+__device__ __forceinline__ float quantize_input(const RouteIn &in, int T, int H, int nb,
+                                                int gidx) {
+    const int i = threadIdx.x & 31;
+    if (gidx >= T * nb) return 0.f;
+    const int t = gidx / nb, kk = 32 * (gidx - t * nb) + i;
+    if (kk >= H) return 0.f;
+    const size_t at = static_cast<size_t>(t) * H + kk;
+    const double x = in.bf16 ? load_in<1>(in.x, at) : load_in<0>(in.x, at);
+    return in.inv ? static_cast<float>(x * in.inv[t] * static_cast<double>(in.gamma[kk]))
+                  : static_cast<float>(x);
+}
+
+// Terms of block gidx from the lanes' values; every lane of the wavefront
+// takes part (the group maximum is a half-wavefront reduction).
+__device__ __forceinline__ void quantize_store(float v, int T, int nb, int Kp, uint8_t *xq,
+                                               uint8_t *xs, int gidx) {
+    const int i = threadIdx.x & 31;
     uint32_t codes, scales;
     fp8_terms_group(v, codes, scales);
-    if (on) {
+    if (gidx < T * nb) {
+        const int t = gidx / nb, blk = gidx - t * nb;
+        const int kk = 32 * blk + i;
 #pragma unroll
         for (int n = 0; n < kTerms; ++n) {
             xq[(static_cast<size_t>(t) * kTerms + n) * Kp + kk] = static_cast<uint8_t>(codes >> (8 * n));
@@ -102,30 +111,50 @@ __device__ __forceinline__ void quantize_terms_group(const void *q_in, int q_bf1
     }
 }
 
-// Stand-alone form of the FP8-term quantisation, for batches the tiled router
-// takes: 8 blocks of 32 values per workgroup and round, over a grid-stride
-// loop (few, long-lived workgroups rather than one per 8 blocks). The loop
-// runs per wavefront, both halves together, as the group maximum needs.
-__global__ __launch_bounds__(256) void quantize_terms_kernel(const void *q_in, int q_bf16, int T,
-                                                             int H, int Kp, uint8_t *xq,
-                                                             uint8_t *xs) {
-    const int total = T * (Kp / 32);
+// Workgroups [first, gridDim.x) of a router or permutation launch:
+// blockDim.x / 32 blocks of 32 values per workgroup and round, in a
+// grid-stride loop that loads kU rounds before it quantises them. The loop
+// and its guards are per wavefront (both halves together), as the group
+// maximum needs.
+__device__ __forceinline__ void quantize_terms_wgs(const RouteIn &in, int T, int H, int Kp,
+                                                   uint8_t *xq, uint8_t *xs, int first) {
+    constexpr int kU = 4;
+    const int nb = Kp / 32;
+    const int total = T * nb;
     const int half = (threadIdx.x >> 5) & 1;
-    for (int g0 = blockIdx.x * 8 + 2 * (threadIdx.x >> 6); g0 < total; g0 += gridDim.x * 8)
-        quantize_terms_group(q_in, q_bf16, T, H, Kp, xq, xs, g0 + half);
+    const int per_wg = static_cast<int>(blockDim.x) / 32;
+    const int stride = (static_cast<int>(gridDim.x) - first) * per_wg;
+    for (int g0 = (static_cast<int>(blockIdx.x) - first) * per_wg + 2 * (threadIdx.x >> 6);
+         g0 < total; g0 += kU * stride) {
+        float v[kU];
+#pragma unroll
+        for (int u = 0; u < kU; ++u) v[u] = quantize_input(in, T, H, nb, g0 + u * stride + half);
+#pragma unroll
+        for (int u = 0; u < kU; ++u)
+            if (g0 + u * stride < total) quantize_store(v[u], T, nb, Kp, xq, xs, g0 + u * stride + half);
+    }
 }
 
-template <int KIND>
-__global__ __launch_bounds__(256) void router_gemv_kernel(const void *x, const float *w, int T,
+// ---------------------------------------------------------------- router logits
+// Both router kernels write split-K partial sums partial[s][t][e] (fp64) over
+// hidden-dimension slices; top-k adds the S partials in a fixed order and
+// then the bias, so the logits are deterministic. fp32 x fp32 products are
+// exact in fp64.
+
+// Few tokens: one wavefront per (expert, hidden slice of kRouterGemvSlice
+// units); lane l holds the router weights (and norm weights) of units
+// 4(l + 64i) .. +3 of the slice in registers (all loads issued at once), then
+// each token's activations are loaded the same way and reduced with a wave
+// sum. Workgroups past router_wgs quantise the expert input.
+template <int KIND, bool NORM>
+__global__ __launch_bounds__(256) void router_gemv_kernel(RouteIn in, const float *w, int T,
                                                           int H, int E, double *partial,
-                                                          int router_wgs, const void *q_in,
-                                                          int q_bf16, int Kp, uint8_t *xq,
+                                                          int router_wgs, int Kp, uint8_t *xq,
                                                           uint8_t *xs) {
     constexpr int NV = kRouterGemvSlice / 256;  // float4 per lane
     const int lane = threadIdx.x & 63;
     if (static_cast<int>(blockIdx.x) >= router_wgs) {
-        const int gidx = (blockIdx.x - router_wgs) * 8 + (threadIdx.x >> 5);
-        quantize_terms_group(q_in, q_bf16, T, H, Kp, xq, xs, gidx);
+        quantize_terms_wgs(in, T, H, Kp, xq, xs, router_wgs);
         return;
     }
     const int item = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -133,20 +162,31 @@ __global__ __launch_bounds__(256) void router_gemv_kernel(const void *x, const f
     if (item >= E * S) return;  // whole wavefront; no workgroup barrier below
     const int e = item / S, s = item - e * S;
     const int hbase = s * kRouterGemvSlice;
-    float4 wr[NV];
+    float4 wr[NV], gm[NV];
     bool on[NV];
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
         const int h = hbase + 4 * (lane + 64 * i);
         on[i] = h < H;
         wr[i] = *reinterpret_cast<const float4 *>(w + static_cast<size_t>(e) * H + (on[i] ? h : 0));
+        if constexpr (NORM) gm[i] = *reinterpret_cast<const float4 *>(in.gamma + (on[i] ? h : 0));
     }
     for (int t = 0; t < T; ++t) {
         double xv[NV][4];
 #pragma unroll
         for (int i = 0; i < NV; ++i) {
             const int h = hbase + 4 * (lane + 64 * i);
-            load4<KIND>(x, static_cast<size_t>(t) * H + (on[i] ? h : 0), xv[i]);
+            load4<KIND>(in.x, static_cast<size_t>(t) * H + (on[i] ? h : 0), xv[i]);
+        }
+        if constexpr (NORM) {
+            const double r = in.inv[t];
+#pragma unroll
+            for (int i = 0; i < NV; ++i) {
+                xv[i][0] = xv[i][0] * r * static_cast<double>(gm[i].x);
+                xv[i][1] = xv[i][1] * r * static_cast<double>(gm[i].y);
+                xv[i][2] = xv[i][2] * r * static_cast<double>(gm[i].z);
+                xv[i][3] = xv[i][3] * r * static_cast<double>(gm[i].w);
+            }
         }
         double acc = 0.0;
 #pragma unroll
@@ -166,49 +206,69 @@ __global__ __launch_bounds__(256) void router_gemv_kernel(const void *x, const f
 // Tiled router for larger batches: a workgroup computes the fp64 partial
 // logits of 64 tokens x 64 experts over one K slice on the fp64 matrix cores
 // (v_mfma_f64_16x16x4_f64): each of its 4 wavefronts holds 32 tokens x 32
-// experts as 2 x 2 result tiles. K advances 32 at a time through
-// double-buffered LDS tiles kept in the inputs' own precision (widened
+// experts as 2 x 2 tiles of 16 x 16. K advances in chunks of 32 through
+// double-buffered LDS tiles (float32, or fp64 once normalised; widened
 // exactly to fp64 when read), 4 per instruction; the next chunk's loads are
 // in flight during the current chunk's instructions. Tokens and experts past
-// T and E are clamped on load and not written.
+// T and E are clamped on load and not written. Workgroup b < router_wgs takes
+// token tile b % tiles_t, expert tile (b / tiles_t) % tiles_e and split
+// b / (tiles_t * tiles_e); the rest quantise the expert input.
 //
 // Instruction lanes (measured on gfx950): operand A lane l = A[l % 16][l / 16]
 // (token, k), operand B lane l = B[l / 16][l % 16] (k, expert); result lane l
 // holds D[4v + l / 16][l % 16], v = 0..3.
 typedef double f64x4_t __attribute__((ext_vector_type(4)));
 
-template <int KIND>
-__global__ __launch_bounds__(256) void router_tiled_kernel(const void *x, const float *w, int T,
-                                                           int H, int E, int slice,
-                                                           double *partial) {
-    typedef typename std::conditional<KIND == 2, double, float>::type XT;
+template <int KIND, bool NORM>
+__global__ __launch_bounds__(256) void router_tiled_kernel(RouteIn in, const float *w, int T,
+                                                           int H, int E, int slice, int tiles_t,
+                                                           int tiles_e, int router_wgs,
+                                                           double *partial, int Kp, uint8_t *xq,
+                                                           uint8_t *xs) {
+    typedef typename std::conditional<NORM, double, float>::type XT;
     constexpr int kPad = 4;
-    __shared__ __align__(16) XT xs[2][32][64 + kPad];     // [k][token]
+    __shared__ __align__(16) XT xsm[2][32][64 + kPad];    // [k][token]
     __shared__ __align__(16) float wsm[2][32][64 + kPad];  // [k][expert]
+    const int b = blockIdx.x;
+    if (b >= router_wgs) {
+        quantize_terms_wgs(in, T, H, Kp, xq, xs, router_wgs);
+        return;
+    }
     const int tid = threadIdx.x;
-    const int t0 = blockIdx.x * 64, e0 = blockIdx.y * 64, s = blockIdx.z;
+    const int t0 = (b % tiles_t) * 64, e0 = ((b / tiles_t) % tiles_e) * 64;
+    const int s = b / (tiles_t * tiles_e);
     const int hbeg = s * slice, hend = min(H, hbeg + slice);
     // loads: thread -> (row tid / 4, k part 8 * (tid % 4)) of the 64 x 32 chunk
     const int lr = tid >> 2, lk = 8 * (tid & 3);
-    const size_t xrow = static_cast<size_t>(min(t0 + lr, T - 1)) * H;
+    const int trow = min(t0 + lr, T - 1);
+    const size_t xrow = static_cast<size_t>(trow) * H;
     const float *wrow = w + static_cast<size_t>(min(e0 + lr, E - 1)) * H;
+    double rinv = 0.0;
+    if constexpr (NORM) rinv = in.inv[trow];
     XT xv[8];
     float wv[8];
     auto load = [&](int h0) {
+        const int h = h0 + lk;
+        if constexpr (NORM) {
+            const float4 g0 = *reinterpret_cast<const float4 *>(in.gamma + h);
+            const float4 g1 = *reinterpret_cast<const float4 *>(in.gamma + h + 4);
+            const float g[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            if (KIND == 1) xv[i] = bf16_bits_to_f32(static_cast<const uint16_t *>(x)[xrow + h0 + lk + i]);
-            else xv[i] = static_cast<const XT *>(x)[xrow + h0 + lk + i];
+            for (int i = 0; i < 8; ++i)
+                xv[i] = load_in<KIND>(in.x, xrow + h + i) * rinv * static_cast<double>(g[i]);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) xv[i] = static_cast<float>(load_in<KIND>(in.x, xrow + h + i));
         }
-        const float4 a = *reinterpret_cast<const float4 *>(wrow + h0 + lk);
-        const float4 b = *reinterpret_cast<const float4 *>(wrow + h0 + lk + 4);
+        const float4 a = *reinterpret_cast<const float4 *>(wrow + h);
+        const float4 c = *reinterpret_cast<const float4 *>(wrow + h + 4);
         wv[0] = a.x; wv[1] = a.y; wv[2] = a.z; wv[3] = a.w;
-        wv[4] = b.x; wv[5] = b.y; wv[6] = b.z; wv[7] = b.w;
+        wv[4] = c.x; wv[5] = c.y; wv[6] = c.z; wv[7] = c.w;
     };
     auto store = [&](int buf) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            xs[buf][lk + i][lr] = xv[i];
+            xsm[buf][lk + i][lr] = xv[i];
             wsm[buf][lk + i][lr] = wv[i];
         }
     };
@@ -229,16 +289,16 @@ __global__ __launch_bounds__(256) void router_tiled_kernel(const void *x, const 
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks) {
             const int kk = 4 * ks + kq;
-            double a[2], b[2];
+            double a[2], bb[2];
 #pragma unroll
-            for (int i = 0; i < 2; ++i) a[i] = static_cast<double>(xs[buf][kk][tb + 16 * i + col]);
+            for (int i = 0; i < 2; ++i) a[i] = static_cast<double>(xsm[buf][kk][tb + 16 * i + col]);
 #pragma unroll
-            for (int j = 0; j < 2; ++j) b[j] = static_cast<double>(wsm[buf][kk][eb + 16 * j + col]);
+            for (int j = 0; j < 2; ++j) bb[j] = static_cast<double>(wsm[buf][kk][eb + 16 * j + col]);
 #pragma unroll
             for (int i = 0; i < 2; ++i)
 #pragma unroll
                 for (int j = 0; j < 2; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[i], b[j], acc[i][j], 0, 0, 0);
+                    acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[i], bb[j], acc[i][j], 0, 0, 0);
         }
         buf ^= 1;
     }
@@ -255,46 +315,75 @@ __global__ __launch_bounds__(256) void router_tiled_kernel(const void *x, const 
 }
 
 // ---------------------------------------------------------------- top-k
-// One wavefront per token: logits from the router partials, top-k, route
-// weights; optionally copies the residual into `out` (the grouped down GEMM
-// then adds into it).
+// One workgroup per token. Wavefront w adds the router partials of splits
+// w, w + 4, w + 8, ... for the lane's experts e = lane + 64q (q < NQ, so
+// E <= 64 NQ), issuing the loads of up to 16 / NQ splits at once (indices
+// clamped, extra values masked): with at most 64 splits and E <= 64 the whole
+// gather is one memory round trip. The four sums are added in wavefront
+// order through LDS, then the bias; experts >= E get -inf. Wavefront 0 then
+// takes top-k and the route weights.
+template <int NQ>
+__device__ __forceinline__ void gather_logits_wg(const double *partial, int S, int T, int t,
+                                                 int E, const float *bias, double *red,
+                                                 double (&v)[4]) {
+    constexpr int kU = 16 / NQ;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    double acc[NQ];
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) acc[q] = 0.0;
+    for (int s0 = wave; s0 < S; s0 += 4 * kU) {
+        double part[kU][NQ];
+#pragma unroll
+        for (int i = 0; i < kU; ++i) {
+            const double *row = partial + (static_cast<size_t>(min(s0 + 4 * i, S - 1)) * T + t) * E;
+#pragma unroll
+            for (int q = 0; q < NQ; ++q) part[i][q] = row[min(lane + 64 * q, E - 1)];
+        }
+#pragma unroll
+        for (int i = 0; i < kU; ++i)
+#pragma unroll
+            for (int q = 0; q < NQ; ++q)
+                if (s0 + 4 * i < S) acc[q] += part[i][q];
+    }
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) red[wave * 256 + lane + 64 * q] = acc[q];
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int e = lane + 64 * q;
+        if (q < NQ && e < E) {
+            const double sum = ((red[e] + red[256 + e]) + red[512 + e]) + red[768 + e];
+            v[q] = sum + static_cast<double>(bias[e]);
+        } else {
+            v[q] = -INFINITY;
+        }
+    }
+}
+
 __global__ __launch_bounds__(256) void topk_kernel(const double *partial, int S, const float *bias,
                                                    int T, int E, int k, float route_scale,
                                                    int32_t *idx, float *wts, int32_t *out_idx,
-                                                   float *out_w, const void *resid,
-                                                   int resid_bf16, int H, float *out) {
+                                                   float *out_w) {
+    __shared__ double red[4 * 256];
+    const int t = blockIdx.x;
     const int lane = threadIdx.x & 63;
-    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (t >= T) return;
     double v[4];
-    if (E <= 64) gather_logits<1>(partial, S, T, t, E, bias, v);
-    else if (E <= 128) gather_logits<2>(partial, S, T, t, E, bias, v);
-    else gather_logits<4>(partial, S, T, t, E, bias, v);
+    if (E <= 64) gather_logits_wg<1>(partial, S, T, t, E, bias, red, v);
+    else if (E <= 128) gather_logits_wg<2>(partial, S, T, t, E, bias, red, v);
+    else gather_logits_wg<4>(partial, S, T, t, E, bias, red, v);
+    if (threadIdx.x >= 64) return;  // after the workgroup barrier
     int sel[kMaxK];
     double val[kMaxK];
     wave_topk(v, E, k, sel, val);
-    float w[kMaxK];
-    route_softmax(val, k, route_scale, w);
+    float wt[kMaxK];
+    route_softmax(val, k, route_scale, wt);
 #pragma unroll
     for (int j = 0; j < kMaxK; ++j) {
         if (j < k && lane == j) {
             idx[t * k + j] = sel[j];
-            wts[t * k + j] = w[j];
+            wts[t * k + j] = wt[j];
             if (out_idx) out_idx[t * k + j] = sel[j];
-            if (out_w) out_w[t * k + j] = w[j];
-        }
-    }
-    if (out) {
-        float *o = out + static_cast<size_t>(t) * H;
-        if (resid_bf16) {
-            const uint16_t *r = static_cast<const uint16_t *>(resid) + static_cast<size_t>(t) * H;
-            for (int h = lane; h < H; h += 64) o[h] = bf16_bits_to_f32(r[h]);
-        } else {
-            const float4 *r = reinterpret_cast<const float4 *>(static_cast<const float *>(resid) +
-                                                               static_cast<size_t>(t) * H);
-            float4 *o4 = reinterpret_cast<float4 *>(o);
-            if (static_cast<const void *>(r) != static_cast<const void *>(o4))
-                for (int h = lane; h < H / 4; h += 64) o4[h] = r[h];
+            if (out_w) out_w[t * k + j] = wt[j];
         }
     }
 }
@@ -311,10 +400,15 @@ __global__ __launch_bounds__(256) void topk_kernel(const double *partial, int S,
 __global__ __launch_bounds__(1024) void permute_kernel(
     const int32_t *idx, int T, int E, int k, int n_shared, int bm, int32_t *counts,
     int32_t *offsets, int32_t *perm, int32_t *inv, int32_t *rank, int32_t *mprefix,
-    int32_t *out_counts, int32_t *out_offsets, int32_t *out_perm, int32_t *out_inv) {
+    int32_t *out_counts, int32_t *out_offsets, int32_t *out_perm, int32_t *out_inv, RouteIn qin,
+    int H, int Kp, uint8_t *xq, uint8_t *xs) {
     __shared__ int wcnt[16][kMaxE];
     __shared__ int base[kMaxE + 1];
     __shared__ int start[kMaxE + 2];
+    if (blockIdx.x > 0) {
+        quantize_terms_wgs(qin, T, H, Kp, xq, xs, 1);
+        return;
+    }
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
     const int R = T * k;
     const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
@@ -409,12 +503,10 @@ __global__ __launch_bounds__(1024) void permute_kernel(
 
 }  // namespace
 
-hipError_t launch_rmsnorm(const void *x, int x_bf16, const float *gamma, int T, int H, float eps,
-                          double *xn64, float *xn32, hipStream_t s) {
-    if (x_bf16)
-        launch_kernel(rmsnorm_kernel<1>, T, 256, s, x, gamma, H, eps, xn64, xn32);
-    else
-        launch_kernel(rmsnorm_kernel<0>, T, 256, s, x, gamma, H, eps, xn64, xn32);
+hipError_t launch_rms_inv(const void *x, int x_bf16, int T, int H, float eps, double *inv,
+                          hipStream_t s) {
+    if (x_bf16) launch_kernel(rms_inv_kernel<1>, T, 256, s, x, H, eps, inv);
+    else launch_kernel(rms_inv_kernel<0>, T, 256, s, x, H, eps, inv);
     return hipGetLastError();
 }
 
@@ -437,58 +529,47 @@ RouterPlan router_plan(int T, int H, int E) {
     return p;
 }
 
-hipError_t launch_router(const void *x, int in_kind, const float *w, int T, int H, int E,
-                         double *partial, const TermsOut *terms, hipStream_t s) {
-    const RouterPlan p = router_plan(T, H, E);
+namespace {
+template <int KIND, bool NORM>
+void router_launch(const RouterPlan &p, const RouteIn &in, const float *w, int T, int H, int E,
+                   double *partial, int qwant, uint8_t *xq, uint8_t *xs, hipStream_t s) {
+    const int Kp = pad128(H);
     if (p.gemv) {
         const int rwgs = (E * p.splits + 3) / 4;
-        int qwgs = 0, Kp = 0;
-        if (terms) {
-            Kp = 128 * ((H + 127) / 128);
-            qwgs = (T * (Kp / 32) + 7) / 8;
-        }
-        const void *qin = terms ? terms->in : nullptr;
-        const int qbf = terms ? terms->in_bf16 : 0;
-        uint8_t *xq = terms ? terms->q : nullptr;
-        uint8_t *xs = terms ? terms->scales : nullptr;
-        const int grid = rwgs + qwgs;
-        if (in_kind == 0)
-            launch_kernel(router_gemv_kernel<0>, grid, 256, s, x, w, T, H, E, partial, rwgs, qin,
-                          qbf, Kp, xq, xs);
-        else if (in_kind == 1)
-            launch_kernel(router_gemv_kernel<1>, grid, 256, s, x, w, T, H, E, partial, rwgs, qin,
-                          qbf, Kp, xq, xs);
-        else
-            launch_kernel(router_gemv_kernel<2>, grid, 256, s, x, w, T, H, E, partial, rwgs, qin,
-                          qbf, Kp, xq, xs);
+        launch_kernel(router_gemv_kernel<KIND, NORM>, rwgs + qwant, 256, s, in, w, T, H, E,
+                      partial, rwgs, Kp, xq, xs);
     } else {
-        if (terms) return hipErrorInvalidValue;  // see router_quantizes
-        const dim3 grid((T + 63) / 64, (E + 63) / 64, p.splits);
-        if (in_kind == 0)
-            launch_kernel(router_tiled_kernel<0>, grid, 256, s, x, w, T, H, E, p.slice, partial);
-        else if (in_kind == 1)
-            launch_kernel(router_tiled_kernel<1>, grid, 256, s, x, w, T, H, E, p.slice, partial);
-        else
-            launch_kernel(router_tiled_kernel<2>, grid, 256, s, x, w, T, H, E, p.slice, partial);
+        const int tt = (T + 63) / 64, te = (E + 63) / 64;
+        const int rwgs = tt * te * p.splits;
+        const int qwgs = qwant < kQuantizeMaxWgs ? qwant : kQuantizeMaxWgs;
+        launch_kernel(router_tiled_kernel<KIND, NORM>, rwgs + qwgs, 256, s, in, w, T, H, E,
+                      p.slice, tt, te, rwgs, partial, Kp, xq, xs);
     }
-    return hipGetLastError();
 }
+}  // namespace
 
-bool router_quantizes(int T) { return T <= kRouterGemvMaxT; }
-
-hipError_t launch_quantize(const TermsOut &terms, int T, int H, hipStream_t s) {
-    const int Kp = pad128(H);
-    const int wgs = (T * (Kp / 32) + 7) / 8;
-    launch_kernel(quantize_terms_kernel, wgs < 2048 ? wgs : 2048, 256, s, terms.in, terms.in_bf16,
-                  T, H, Kp, terms.q, terms.scales);
+hipError_t launch_router(const RouteIn &in, const float *w, int T, int H, int E, double *partial,
+                         const TermsOut *terms, hipStream_t s) {
+    const RouterPlan p = router_plan(T, H, E);
+    // quantisation workgroups: one round of 8 blocks of 32 values each
+    const int qwant = terms ? (T * (pad128(H) / 32) + 7) / 8 : 0;
+    uint8_t *xq = terms ? terms->q : nullptr;
+    uint8_t *xs = terms ? terms->scales : nullptr;
+    if (in.inv) {
+        if (in.bf16) router_launch<1, true>(p, in, w, T, H, E, partial, qwant, xq, xs, s);
+        else router_launch<0, true>(p, in, w, T, H, E, partial, qwant, xq, xs, s);
+    } else {
+        if (in.bf16) router_launch<1, false>(p, in, w, T, H, E, partial, qwant, xq, xs, s);
+        else router_launch<0, false>(p, in, w, T, H, E, partial, qwant, xq, xs, s);
+    }
     return hipGetLastError();
 }
 
 hipError_t launch_topk(const double *partial, int S, const float *bias, int T, int E, int k,
                        float route_scale, int32_t *idx, float *wts, int32_t *out_idx, float *out_w,
-                       const void *resid, int resid_bf16, int H, float *out, hipStream_t s) {
-    launch_kernel(topk_kernel, (T + 3) / 4, 256, s, partial, S, bias, T, E, k, route_scale, idx,
-                  wts, out_idx, out_w, resid, resid_bf16, H, out);
+                       hipStream_t s) {
+    launch_kernel(topk_kernel, T, 256, s, partial, S, bias, T, E, k, route_scale, idx, wts,
+                  out_idx, out_w);
     return hipGetLastError();
 }
 
@@ -496,9 +577,19 @@ hipError_t launch_permute(const int32_t *idx, int T, int E, int k, int n_shared,
                           int32_t *counts,
                           int32_t *offsets, int32_t *perm, int32_t *inv, int32_t *rank,
                           int32_t *mprefix, int32_t *out_counts, int32_t *out_offsets,
-                          int32_t *out_perm, int32_t *out_inv, hipStream_t s) {
-    launch_kernel(permute_kernel, 1, 1024, s, idx, T, E, k, n_shared, tile_rows, counts, offsets,
-                  perm, inv, rank, mprefix, out_counts, out_offsets, out_perm, out_inv);
+                          int32_t *out_perm, int32_t *out_inv, const RouteIn *qin, int H,
+                          const TermsOut *terms, hipStream_t s) {
+    const int Kp = pad128(H);
+    int qwgs = 0;
+    if (terms) {
+        const int want = (T * (Kp / 32) + 31) / 32;  // one round of 32 blocks each
+        qwgs = want < kPermuteQuantizeWgs ? want : kPermuteQuantizeWgs;
+    }
+    const RouteIn none{nullptr, 0, nullptr, nullptr};
+    launch_kernel(permute_kernel, 1 + qwgs, 1024, s, idx, T, E, k, n_shared, tile_rows, counts,
+                  offsets, perm, inv, rank, mprefix, out_counts, out_offsets, out_perm, out_inv,
+                  terms ? *qin : none, H, Kp, terms ? terms->q : nullptr,
+                  terms ? terms->scales : nullptr);
     return hipGetLastError();
 }
 
