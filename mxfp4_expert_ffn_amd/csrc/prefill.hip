@@ -53,8 +53,8 @@ struct Geo {
     static constexpr int kGateUpRows = W * kGURowsWave;    // features per gate/up workgroup
     static constexpr int kDownRows = W * 16 * NA;          // hidden rows per down workgroup
     // K-steps of A fragments in flight: 3 for 32-row tiles; 2 for 16-row
-    // tiles (120 VGPRs: four workgroups per CU, which beats three with a
-    // deeper ring)
+    // tiles (at most 128 VGPRs: four workgroups per CU, which beats three
+    // with a deeper ring)
     static constexpr int kASlots = NG == 2 ? 3 : 2;
     static_assert(NG == 1 || NG == 2, "16- or 32-row tiles");
     static_assert(kPieces % kThreads == 0, "B staging divides evenly");
@@ -178,16 +178,27 @@ __device__ __forceinline__ void gemm_mainloop(const uint8_t *const (&aq)[NA],
 #pragma unroll
             for (int g = 0; g < NG; ++g) {
                 if (g < ngroups) {  // uniform: row groups the tile fills
+                    // term t + 1's LDS reads are issued before term t's
+                    // instructions (two B operands live), so the reads'
+                    // latency hides behind the matrix core; the scheduling
+                    // barriers keep the compiler from hoisting every term's
+                    // reads into registers the tile needs
+                    uint4 blo[2], bhi[2];
+                    uint32_t bsc[2];
+                    auto rd = [&](int t, int sl) __attribute__((always_inline)) {
+                        const int pc = ((t * NG + g) * 8 + kh) * 16 + col;
+                        blo[sl] = *reinterpret_cast<const uint4 *>(buf + 16 * pc);
+                        bhi[sl] = *reinterpret_cast<const uint4 *>(buf + 16 * (pc + 64));
+                        bsc[sl] = sbuf[(t * 4 + kh) * Gm::kRows + 16 * g + col];
+                    };
+                    rd(0, 0);
 #pragma unroll
                     for (int t = 0; t < NT; ++t) {
-                        const int pc = ((t * NG + g) * 8 + kh) * 16 + col;
-                        const uint4 blo = *reinterpret_cast<const uint4 *>(buf + 16 * pc);
-                        const uint4 bhi = *reinterpret_cast<const uint4 *>(buf + 16 * (pc + 64));
-                        const uint32_t bsc = sbuf[(t * 4 + kh) * Gm::kRows + 16 * g + col];
+                        if (t + 1 < NT) rd(t + 1, (t + 1) & 1);
+                        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                        for (int j = 0; j < NA; ++j) acc[j][g] = mx_mfma(asl.a[j], blo, bhi, bsc, acc[j][g]);
-                        // one term's B operand live at a time: keeps the scheduler from
-                        // hoisting every term's reads into registers the tile needs
+                        for (int j = 0; j < NA; ++j)
+                            acc[j][g] = mx_mfma(asl.a[j], blo[t & 1], bhi[t & 1], bsc[t & 1], acc[j][g]);
                         __builtin_amdgcn_sched_barrier(0);
                     }
                 }
@@ -234,8 +245,9 @@ __device__ __forceinline__ void load_pre(const int32_t *mprefix, int G, int *s_p
 
 // gate/up: grid = kXcds-rounded max_tiles x ceil(pad128(F) / kGateUpRows) items;
 // NT terms of the expert input take part.
+// 16-row tiles are held to 4 wavefronts per SIMD (128 VGPRs, no spills).
 template <int NG, int W, int NA, int NT>
-__global__ __launch_bounds__(64 * W) void gate_up_gemm_kernel(
+__global__ __launch_bounds__(64 * W, NG == 1 ? 4 : 2) void gate_up_gemm_kernel(
     const uint8_t *xq, const uint8_t *xs, int T, int H, int F, int E, int k, int n_shared,
     ExpertPtrs ex, ExpertPtrs sh, SwigluConsts sc, const int32_t *offsets, const int32_t *perm,
     const int32_t *mprefix, uint8_t *act_q, uint8_t *act_s) {
