@@ -20,6 +20,10 @@ dispatches give its live average duration for the roofline object. Expert
 weights are held in several device copies, cycled between calls, so that the
 256 MB Infinity Cache cannot serve them from one call to the next.
 
+With --route-profile every call also adds its expert selections to a
+[layers][E] uint64 table on the device (the route profile of the library's
+route_out), so the timed steps include that recording.
+
 Prints one JSON line (rank 0, N=1 only).
 """
 from __future__ import annotations
@@ -169,6 +173,7 @@ class Setup:
         else:
             self.xd = torch.from_numpy(x).cuda()
         self.ws = workspace(self.shape)
+        self.profile = None  # [layers][E] int64 route profile table, when recording
         self.tokens_per_step = cfg.T * cfg.calls
         # "calls": independent T=1 decode calls; "decode_stack": T=1 tokens
         # through every layer; "decode": one decode call; "prefill"
@@ -197,6 +202,9 @@ class Setup:
             self.out = torch.empty((cfg.T, cfg.H), dtype=torch.float32, device="cuda")
             self.out2 = torch.empty_like(self.out)
 
+    def _ro(self, layer: int):
+        return None if self.profile is None else {"route_counts": self.profile[layer]}
+
     def step_calls(self, step: int):
         """Closures making up one step (weights copy chosen per call/step)."""
         mx, cfg = self.mx, self.cfg
@@ -206,9 +214,9 @@ class Setup:
                 src = self.xrows[i]
                 for l, dl in enumerate(self.layers):
                     dst = self.out[i, l % 2].view(1, cfg.H)
-                    calls.append(lambda dl=dl, src=src, dst=dst: mx.moe_forward_decode(
+                    calls.append(lambda dl=dl, src=src, dst=dst, l=l: mx.moe_forward_decode(
                         self.step_shape, src, dl.router_w, dl.router_b, dl.experts_copy(0), dst,
-                        self.ws, norm_w=dl.norm_w))
+                        self.ws, norm_w=dl.norm_w, route_out=self._ro(l)))
                     src = dst
         elif self.mode == "calls":
             dl = self.layers[0]
@@ -216,20 +224,20 @@ class Setup:
                 ex = dl.experts_copy(i)
                 calls.append(lambda i=i, ex=ex: mx.moe_forward_decode(
                     self.step_shape, self.xrows[i], dl.router_w, dl.router_b, ex, self.orows[i],
-                    self.ws))
+                    self.ws, route_out=self._ro(0)))
         elif self.mode == "decode":
             dl = self.layers[0]
             calls.append(lambda: mx.moe_forward_decode(
                 self.shape, self.xd, dl.router_w, dl.router_b, dl.experts_copy(step), self.out,
-                self.ws, norm_w=dl.norm_w, shared=dl.shared_copy(step)))
+                self.ws, norm_w=dl.norm_w, shared=dl.shared_copy(step), route_out=self._ro(0)))
         else:
             src = self.xd
             bufs = (self.out, self.out2)
             for l, dl in enumerate(self.layers):
                 dst = bufs[l % 2]
-                calls.append(lambda dl=dl, src=src, dst=dst: mx.moe_forward_prefill(
+                calls.append(lambda dl=dl, src=src, dst=dst, l=l: mx.moe_forward_prefill(
                     self.shape, src, dl.router_w, dl.router_b, dl.experts_copy(step), dst,
-                    self.ws, norm_w=dl.norm_w, shared=dl.shared_copy(step)))
+                    self.ws, norm_w=dl.norm_w, shared=dl.shared_copy(step), route_out=self._ro(l)))
                 src = dst
         return calls
 
@@ -359,6 +367,8 @@ def main():
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of HIP graphs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds for the oracle sample")
+    ap.add_argument("--route-profile", action="store_true",
+                    help="record every call's expert selections into a device route profile")
     ap.add_argument("--calibrate-copy-gib", type=float, default=0.0,
                     help="also run one device copy of this many GiB (PMC byte calibration)")
     args = ap.parse_args()
@@ -384,6 +394,8 @@ def main():
     stream = torch.cuda.current_stream().cuda_stream
 
     counts = route_counts(setup)
+    if args.route_profile:
+        setup.profile = torch.zeros((cfg.layers, cfg.E), dtype=torch.int64, device="cuda")
     ncopies_graph = 1 if setup.mode in ("calls", "decode_stack") else setup.copies
     plain = [setup.step_calls(c) for c in range(ncopies_graph)]
     for calls in plain:          # eager run once (validates arguments, warms code objects)
@@ -460,6 +472,7 @@ def main():
             "tokens_per_step": setup.tokens_per_step, "weights": "mxfp4 (e2m1 + e8m0/32) + fp32 bias",
             "activations": cfg.act_dtype, "weight_copies": setup.copies,
             "launch": "eager" if graphs is None else "hip_graph",
+            "route_profile": args.route_profile,
         },
         "roofline": {
             "kernel": kernel, "bound": bound, "achieved": round(achieved, 2), "peak": peak,
@@ -476,6 +489,14 @@ def main():
             "frac_of_hbm_peak": round(block_gbps / HBM_PEAK_GBPS, 4),
         },
     }
+    if setup.profile is not None:
+        # every executed step recorded T*k selections per layer: the eager
+        # validation pass(es), the warm-up and the timed steps
+        runs = ncopies_graph + args.warmup + args.steps
+        summ = mx.moe_route_profile_summary(setup.profile.cpu().numpy())
+        summ["selections_expected"] = runs * setup.tokens_per_step * cfg.k * cfg.layers
+        del summ["layer_unique"]
+        result["route_profile"] = summ
     if args.calibrate_copy_gib > 0:
         n = int(args.calibrate_copy_gib * (1 << 30)) // 4
         a = torch.empty(n, dtype=torch.float32, device="cuda").fill_(1.0)

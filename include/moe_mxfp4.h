@@ -130,9 +130,19 @@ typedef struct moe_expert_planes {
  *   perm     [T*k]  int32  route id t*k+j at each position, grouped by expert,
  *                          ascending token inside a group
  *   inv      [T*k]  int32  position of route t*k+j, perm[inv[r]] == r
+ *   route_counts [E] uint64  accumulated, not overwritten: each call adds its
+ *                          routes per expert (the T*k selections; the shared
+ *                          expert is not a selection). Zero it once, then pass
+ *                          the same table (or row `layer` of a [layers][E]
+ *                          table) on every call to profile expert use. Calls
+ *                          that add into one table must be ordered (one stream).
+ *                          A counter wraps after 2^64 selections (the page's
+ *                          counter saturates; neither is reachable in practice).
  * Pages: goosedump `top_experts` (strict-greater insertion: descending value,
  * lower index first on ties), `mixture_of_experts_batch` (routes pushed per
- * expert in token order), `route_output_index` (route id token*k + slot). */
+ * expert in token order), `route_output_index` (route id token*k + slot),
+ * `ExpertRouteProfile::record` (one count per selected expert per layer,
+ * called from `mixture_of_experts` and `mixture_of_experts_batch`). */
 typedef struct moe_route_out {
     int32_t *topk_idx;
     float *topk_w;
@@ -140,7 +150,20 @@ typedef struct moe_route_out {
     int32_t *offsets;
     int32_t *perm;
     int32_t *inv;
+    uint64_t *route_counts;
 } moe_route_out;
+
+/* Summary of a route profile table. Host only.
+ *   counts       [layers][E] uint64, host: route_counts tables read back
+ *   selections   out: sum of all counters, saturating at UINT64_MAX
+ *   unique_layer_experts  out: number of (layer, expert) counters that are nonzero
+ *   layer_unique [layers] int32 out (or NULL): nonzero counters of each layer
+ * Returns MOE_OK, or MOE_ERR_INVALID_ARG (NULL counts or outputs, layers < 0,
+ * E < 1). Page: goosedump `ExpertRouteProfile` (`selections`,
+ * `unique_layer_experts`, `layer_unique_counts`). */
+int moe_route_profile_summary(const uint64_t *counts, int32_t layers, int32_t E,
+                              uint64_t *selections, uint64_t *unique_layer_experts,
+                              int32_t *layer_unique);
 
 /* Fill *layout for experts of this shape (uses H and F only). Host only.
  * Returns MOE_OK or MOE_ERR_INVALID_ARG. */

@@ -19,10 +19,14 @@ from ._lib import MOE_BF16, MOE_F32, MoeBlobLayout, MoeExpertPlanes, MoeRouteOut
 __all__ = [
     "MoeError", "MoeShape", "make_shape", "moe_blob_layout_get", "moe_pack_experts",
     "moe_workspace_bytes", "moe_route", "moe_forward_decode", "moe_forward_prefill",
-    "moe_dequant_debug", "moe_last_error", "moe_profile_next_launch", "ROUTE_FIELDS",
+    "moe_dequant_debug", "moe_last_error", "moe_profile_next_launch", "moe_route_profile_summary",
+    "ROUTE_FIELDS",
 ]
 
-ROUTE_FIELDS = ("topk_idx", "topk_w", "counts", "offsets", "perm", "inv")
+# route_counts: an int64 [E] device tensor the call adds its selections per
+# expert to (the C side's uint64 route profile row)
+ROUTE_FIELDS = ("topk_idx", "topk_w", "counts", "offsets", "perm", "inv", "route_counts")
+_ROUTE_DTYPES = {"topk_w": "float32", "route_counts": "int64"}
 
 
 class MoeError(RuntimeError):
@@ -75,7 +79,7 @@ def _route_out(route_out):
     ro = MoeRouteOut()
     for f in ROUTE_FIELDS:
         t = route_out.get(f)
-        dt = torch.float32 if f == "topk_w" else torch.int32
+        dt = getattr(torch, _ROUTE_DTYPES.get(f, "int32"))
         setattr(ro, f, None if t is None else _ptr(t, f, dt).value)
     return ctypes.byref(ro)
 
@@ -162,3 +166,19 @@ def moe_profile_next_launch(kernel, start_event: int, stop_event: int):
     kid = _lib.KERNELS[kernel] if isinstance(kernel, str) else int(kernel)
     _check(_lib.load().moe_profile_next_launch(kid, ctypes.c_void_p(start_event),
                                                ctypes.c_void_p(stop_event)))
+
+
+def moe_route_profile_summary(counts) -> dict:
+    """Summary of a host route profile table [layers][E] (uint64 or int64):
+    total selections (saturating), nonzero (layer, expert) counters and the
+    nonzero counters of each layer (goosedump `ExpertRouteProfile`)."""
+    c = np.ascontiguousarray(counts).view(np.uint64) if np.asarray(counts).dtype == np.int64 \
+        else np.ascontiguousarray(counts, dtype=np.uint64)
+    if c.ndim != 2:
+        raise ValueError("counts must be [layers, E]")
+    sel, uniq = ctypes.c_uint64(), ctypes.c_uint64()
+    per = np.zeros(c.shape[0], dtype=np.int32)
+    _check(_lib.load().moe_route_profile_summary(
+        c.ctypes.data_as(ctypes.c_void_p), c.shape[0], c.shape[1], ctypes.byref(sel),
+        ctypes.byref(uniq), per.ctypes.data_as(ctypes.c_void_p)))
+    return dict(selections=sel.value, unique_layer_experts=uniq.value, layer_unique=per.tolist())

@@ -42,7 +42,7 @@ class MoeExpertPlanes(ctypes.Structure):
 
 class MoeRouteOut(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
-        "topk_idx", "topk_w", "counts", "offsets", "perm", "inv")]
+        "topk_idx", "topk_w", "counts", "offsets", "perm", "inv", "route_counts")]
 
 
 # every symbol the header declares, with its ctypes signature
@@ -61,6 +61,7 @@ SIGNATURES = {
     "moe_dequant_debug": (ctypes.c_int, [ctypes.POINTER(MoeShape), _P, ctypes.c_int32,
                                          ctypes.c_int32, _P, _P]),
     "moe_profile_next_launch": (ctypes.c_int, [ctypes.c_int32, _P, _P]),
+    "moe_route_profile_summary": (ctypes.c_int, [_P, ctypes.c_int32, ctypes.c_int32, _P, _P, _P]),
     "moe_last_error": (ctypes.c_char_p, []),
 }
 

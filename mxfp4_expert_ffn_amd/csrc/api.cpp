@@ -4,6 +4,7 @@
 #include "moe_mxfp4.h"
 
 #include <cmath>
+#include <cstdint>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -304,6 +305,28 @@ size_t moe_workspace_bytes(const moe_shape *shape) {
     return carve(shape, nullptr).bytes;
 }
 
+int moe_route_profile_summary(const uint64_t *counts, int32_t layers, int32_t E,
+                              uint64_t *selections, uint64_t *unique_layer_experts,
+                              int32_t *layer_unique) {
+    if (!counts || !selections || !unique_layer_experts)
+        return fail(MOE_ERR_INVALID_ARG, "counts, selections and unique_layer_experts must be non-NULL");
+    if (layers < 0 || E < 1) return fail(MOE_ERR_INVALID_ARG, "need layers >= 0 and E >= 1");
+    uint64_t total = 0, unique = 0;
+    for (int32_t l = 0; l < layers; ++l) {
+        int32_t nz = 0;
+        for (int32_t e = 0; e < E; ++e) {
+            const uint64_t c = counts[static_cast<size_t>(l) * E + e];
+            total = c > UINT64_MAX - total ? UINT64_MAX : total + c;  // saturating, as the page's fold
+            nz += c != 0;
+        }
+        unique += static_cast<uint64_t>(nz);
+        if (layer_unique) layer_unique[l] = nz;
+    }
+    *selections = total;
+    *unique_layer_experts = unique;
+    return ok();
+}
+
 int moe_route(const moe_shape *s, const void *x, const float *norm_w, const float *router_w,
               const float *router_b, const moe_route_out *out, void *ws, size_t ws_bytes,
               hipStream_t st) {
@@ -325,7 +348,8 @@ int moe_route(const moe_shape *s, const void *x, const float *norm_w, const floa
     }));
     MOE_TRY(launch(MOE_KERNEL_PERMUTE, "permute", st, [&] { return moe::launch_permute(w.idx, s->T, s->E, s->k, 0, 16, w.counts, w.offsets, w.perm,
                                           w.inv, w.rank, w.mprefix, out->counts, out->offsets,
-                                          out->perm, out->inv, nullptr, s->H, nullptr, st); }));
+                                          out->perm, out->inv, out->route_counts, nullptr, s->H,
+                                          nullptr, st); }));
     return ok();
 }
 
@@ -361,6 +385,7 @@ int moe_forward_decode(const moe_shape *s, const void *hidden, const float *norm
     a.wts = w.wts;
     a.out_idx = ro ? ro->topk_idx : nullptr;
     a.out_w = ro ? ro->topk_w : nullptr;
+    a.route_counts = ro ? ro->route_counts : nullptr;  // added where the experts are published
     a.resid = hidden;
     a.resid_bf16 = s->act_dtype == MOE_BF16;
     a.out = out;
@@ -374,7 +399,7 @@ int moe_forward_decode(const moe_shape *s, const void *hidden, const float *norm
         MOE_TRY(launch(MOE_KERNEL_PERMUTE, "permute", st, [&] {
             return moe::launch_permute(w.idx, s->T, s->E, s->k, 0, 16, w.counts, w.offsets, w.perm,
                                        w.inv, w.rank, w.mprefix, ro->counts, ro->offsets,
-                                       ro->perm, ro->inv, nullptr, s->H, nullptr, st);
+                                       ro->perm, ro->inv, nullptr, nullptr, s->H, nullptr, st);
         }));
     return ok();
 }
@@ -408,7 +433,8 @@ int moe_forward_prefill(const moe_shape *s, const void *hidden, const float *nor
         return moe::launch_permute(w.idx, s->T, s->E, s->k, s->n_shared, bm, w.counts, w.offsets,
                                    w.perm, w.inv, w.rank, w.mprefix, ro ? ro->counts : nullptr,
                                    ro ? ro->offsets : nullptr, ro ? ro->perm : nullptr,
-                                   ro ? ro->inv : nullptr, &in, s->H, router_terms ? nullptr : &tq, st);
+                                   ro ? ro->inv : nullptr, ro ? ro->route_counts : nullptr, &in,
+                                   s->H, router_terms ? nullptr : &tq, st);
     }));
     const moe::ExpertPtrs ex = expert_ptrs(s, experts);
     const moe::ExpertPtrs sh = expert_ptrs(s, shared);

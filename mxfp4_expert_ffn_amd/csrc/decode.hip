@@ -58,6 +58,9 @@ __device__ __forceinline__ const uint8_t *route_blob(const DecodeArgs &a, int r,
                 a.wts[t * a.k + jj] = wv[jj];
                 if (a.out_idx) a.out_idx[t * a.k + jj] = sel[jj];
                 if (a.out_w) a.out_w[t * a.k + jj] = wv[jj];
+                // route profile (goosedump ExpertRouteProfile::record): one per selection
+                if (a.route_counts)
+                    atomicAdd(reinterpret_cast<unsigned long long *>(a.route_counts + sel[jj]), 1ull);
             }
         }
     }

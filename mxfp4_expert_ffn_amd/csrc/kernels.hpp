@@ -113,7 +113,8 @@ hipError_t launch_permute(const int32_t *idx, int T, int E, int k, int n_shared,
                           int32_t *counts, int32_t *offsets, int32_t *perm, int32_t *inv,
                           int32_t *rank, int32_t *mprefix, int32_t *out_counts,
                           int32_t *out_offsets, int32_t *out_perm, int32_t *out_inv,
-                          const RouteIn *qin, int H, const TermsOut *terms, hipStream_t s);
+                          uint64_t *route_counts, const RouteIn *qin, int H,
+                          const TermsOut *terms, hipStream_t s);
 
 // decode (T <= 64) -----------------------------------------------------------
 // Route r < T*k is slot r % k of token r / k; r >= T*k is the shared expert of
@@ -135,6 +136,7 @@ struct DecodeArgs {
     float *wts;
     int32_t *out_idx;  // optional exports (NULL: not written)
     float *out_w;
+    uint64_t *route_counts;  // optional [E] profile: += 1 per selection (NULL: off)
     const void *resid;
     int resid_bf16;
     float *out;

@@ -400,8 +400,8 @@ __global__ __launch_bounds__(256) void topk_kernel(const double *partial, int S,
 __global__ __launch_bounds__(1024) void permute_kernel(
     const int32_t *idx, int T, int E, int k, int n_shared, int bm, int32_t *counts,
     int32_t *offsets, int32_t *perm, int32_t *inv, int32_t *rank, int32_t *mprefix,
-    int32_t *out_counts, int32_t *out_offsets, int32_t *out_perm, int32_t *out_inv, RouteIn qin,
-    int H, int Kp, uint8_t *xq, uint8_t *xs) {
+    int32_t *out_counts, int32_t *out_offsets, int32_t *out_perm, int32_t *out_inv,
+    uint64_t *route_counts, RouteIn qin, int H, int Kp, uint8_t *xq, uint8_t *xs) {
     __shared__ int wcnt[16][kMaxE];
     __shared__ int base[kMaxE + 1];
     __shared__ int start[kMaxE + 2];
@@ -482,6 +482,10 @@ __global__ __launch_bounds__(1024) void permute_kernel(
             mprefix[g] = mt;
             counts[g] = c;
             if (out_counts && g < E) out_counts[g] = c;
+            // route profile: this call's selections of expert g (one atomic per expert)
+            if (route_counts && g < E && c > 0)
+                atomicAdd(reinterpret_cast<unsigned long long *>(route_counts + g),
+                          static_cast<unsigned long long>(c));
             if (out_offsets && g < E) out_offsets[g] = off;
         }
         if (g == G - 1) {
@@ -577,8 +581,8 @@ hipError_t launch_permute(const int32_t *idx, int T, int E, int k, int n_shared,
                           int32_t *counts,
                           int32_t *offsets, int32_t *perm, int32_t *inv, int32_t *rank,
                           int32_t *mprefix, int32_t *out_counts, int32_t *out_offsets,
-                          int32_t *out_perm, int32_t *out_inv, const RouteIn *qin, int H,
-                          const TermsOut *terms, hipStream_t s) {
+                          int32_t *out_perm, int32_t *out_inv, uint64_t *route_counts,
+                          const RouteIn *qin, int H, const TermsOut *terms, hipStream_t s) {
     const int Kp = pad128(H);
     int qwgs = 0;
     if (terms) {
@@ -588,7 +592,7 @@ hipError_t launch_permute(const int32_t *idx, int T, int E, int k, int n_shared,
     const RouteIn none{nullptr, 0, nullptr, nullptr};
     launch_kernel(permute_kernel, 1 + qwgs, 1024, s, idx, T, E, k, n_shared, tile_rows, counts,
                   offsets, perm, inv, rank, mprefix, out_counts, out_offsets, out_perm, out_inv,
-                  terms ? *qin : none, H, Kp, terms ? terms->q : nullptr,
+                  route_counts, terms ? *qin : none, H, Kp, terms ? terms->q : nullptr,
                   terms ? terms->scales : nullptr);
     return hipGetLastError();
 }
