@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Throughput of the routed MXFP4 MoE block on one MI355X (gfx950).
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode|prefill|stack|ds4|tiny]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--route-profile]
 
 A step is one pass of the whole block over one batch of seeded synthetic
 input (weights and activations resident in HBM before timing):
@@ -9,6 +9,7 @@ input (weights and activations resident in HBM before timing):
   prefill gpt-oss-20b-shaped layer, T=128, Zipf(1.1)-skewed expert loads
   stack   24 gpt-oss-20b-shaped layers (RMSNorm + MoE), T=512
   ds4     DeepSeek-V4-Flash-shaped layer, T=2048, 256 experts top-6 + shared
+  ds4_pro DeepSeek-V4-Pro-shaped layer, T=2048, H=7168, F=3072, 384 experts top-6 + shared
   tiny    T=8, H=F=256, 8 experts top-2
   decode_stack  T=1 tokens through 24 gpt-oss-20b-shaped layers (RMSNorm + MoE),
           16 tokens per step, each layer's output the next layer's input
@@ -56,6 +57,10 @@ WORKLOADS = {
                 steps=50),
     "tiny": dict(config=1, name="tiny_T8_H256_E8_top2", kernel="decode_gate_up", copies=1,
                  steps=200),
+    # DeepSeek-V4-Pro-shaped layer (H=7168, F=3072, 384 experts top-6 + shared,
+    # route scale 2.5), at the Flash workload's batch and recipe: 13.6 GB per copy
+    "ds4_pro": dict(config=6, name="ds4pro_T2048_E384_top6_shared", kernel="gate_up_gemm",
+                    copies=2, steps=20),
     # T=1 decode through the 24-layer stack's weights (RMSNorm + MoE per layer):
     # 16 independent tokens per step, each through all 24 layers in turn
     "decode_stack": dict(config=4, name="gptoss20b_decode_stack24_T1_16tok",
@@ -345,9 +350,12 @@ def cpu_baseline(setup, budget_s: float):
                            f"one fp64 oracle call ({dt:.1f} s)")
     # prefill-type: all T tokens of the first layer if the budget allows, else a token subset
     n = cfg.T
+    # about 0.35 s of dequantise-and-multiply per expert at H*F = 4096*2048
+    # (measured), scaled by the expert's size
+    per_expert = 0.35 * cfg.H * cfg.F / (4096 * 2048)
     est_experts = min(cfg.E, cfg.T * cfg.k) + cfg.n_shared
-    if est_experts * 0.35 > budget_s:
-        n = max(1, int(cfg.T * budget_s / (est_experts * 0.35)))
+    if est_experts * per_expert > budget_s:
+        n = max(1, int(cfg.T * budget_s / (est_experts * per_expert)))
     toks = np.arange(n)
     t0 = time.time()
     omoe.block_for_config(cfg, layer, x[:cfg.T], tokens=toks)

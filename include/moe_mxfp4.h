@@ -29,7 +29,7 @@
  *   value with one E8M0 scale per 32 values and term (each value is carried
  *   to within about 2^-16 of its block's largest magnitude); products
  *   accumulate in float32. Router logits are accumulated in float64.
- * - Shape limits: 1 <= E <= 256, 1 <= k <= min(E, 8), H and F multiples of
+ * - Shape limits: 1 <= E <= 512, 1 <= k <= min(E, 8), H and F multiples of
  *   32 and at most 16384, 0 <= T, n_shared in {0, 1}. Decode additionally
  *   needs T <= 64 and H, F <= 8192. With T = 0 a call only validates the
  *   shape and returns MOE_OK.

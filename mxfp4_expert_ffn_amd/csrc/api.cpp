@@ -50,7 +50,7 @@ bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 int check_shape(const moe_shape *s) {
     if (!s) return fail(MOE_ERR_INVALID_ARG, "shape is NULL");
     if (s->T < 0 || s->T > (1 << 20)) return fail(MOE_ERR_INVALID_ARG, "T=%d outside [0, 2^20]", s->T);
-    if (s->E < 1 || s->E > moe::kMaxE) return fail(MOE_ERR_INVALID_ARG, "E=%d outside [1, 256]", s->E);
+    if (s->E < 1 || s->E > moe::kMaxE) return fail(MOE_ERR_INVALID_ARG, "E=%d outside [1, 512]", s->E);
     if (s->k < 1 || s->k > moe::kMaxK || s->k > s->E)
         return fail(MOE_ERR_INVALID_ARG, "k=%d outside [1, min(E, 8)]", s->k);
     if (s->H < 32 || s->H > 16384 || s->H % 32)

@@ -133,7 +133,7 @@ __device__ __forceinline__ float swiglu(float g, float u, float alpha, float lim
 constexpr int kGatherUnroll = 8;
 template <int NQ>
 __device__ __forceinline__ void gather_logits(const double *partial, int S, int T, int t, int E,
-                                              const float *bias, double (&v)[4]) {
+                                              const float *bias, double (&v)[kMaxQ]) {
     const int lane = threadIdx.x & (kWave - 1);
     double acc[NQ];
 #pragma unroll
@@ -153,47 +153,48 @@ __device__ __forceinline__ void gather_logits(const double *partial, int S, int 
                 if (s0 + i < S) acc[q] += part[i][q];
     }
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < kMaxQ; ++q) {
         const int e = lane + kWave * q;
         v[q] = (q < NQ && e < E) ? acc[q < NQ ? q : 0] + static_cast<double>(bias[min(e, E - 1)])
                                  : -INFINITY;
     }
 }
 
-// Top-k of one token's fp64 logits (E <= 256) by one wavefront; v holds the
-// lane's experts l, l+64, l+128, l+192. Each round takes the wave maximum over
-// the experts still in play, then the lowest expert index holding it (ballot
-// per quarter: lanes are in index order inside a quarter, quarters in index
-// order), and retires it; so the result is by descending value with equal
-// values in ascending index order. A NaN logit counts as -inf, so every
+// Top-k of one token's fp64 logits (E <= 64 NQ <= kMaxE) by one wavefront;
+// vin[q] holds the lane's expert l + 64q. Each round takes the wave maximum
+// over the experts still in play, then the lowest expert index holding it
+// (ballot per group of 64: lanes are in index order inside a group, groups in
+// index order), and retires it; so the result is by descending value with
+// equal values in ascending index order. A NaN logit counts as -inf, so every
 // returned index is a distinct valid expert whatever the input.
 // sel[j] and val[j] are uniform across the wave on return.
-__device__ __forceinline__ void wave_topk(const double (&vin)[4], int E, int k, int *sel,
+template <int NQ>
+__device__ __forceinline__ void wave_topk(const double (&vin)[kMaxQ], int E, int k, int *sel,
                                           double *val) {
     const int lane = threadIdx.x & (kWave - 1);
-    double v[4];
-    bool alive[4];
+    double v[NQ];
+    bool alive[NQ];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < NQ; ++q) {
         alive[q] = lane + kWave * q < E;
         v[q] = vin[q] == vin[q] ? vin[q] : -INFINITY;
     }
     for (int j = 0; j < k; ++j) {
         double m = -INFINITY;
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
+        for (int q = 0; q < NQ; ++q)
             if (alive[q]) m = fmax(m, v[q]);
         m = wave_max_f64(m);
         int chosen = -1;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
+        for (int q = 0; q < NQ; ++q) {
             const uint64_t hit = __ballot(alive[q] && v[q] == m);
             if (chosen < 0 && hit) chosen = kWave * q + (__ffsll(static_cast<long long>(hit)) - 1);
         }
         sel[j] = chosen;
         val[j] = m;
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
+        for (int q = 0; q < NQ; ++q)
             if (lane + kWave * q == chosen) alive[q] = false;
     }
 }

@@ -25,11 +25,20 @@ namespace {
 __device__ __forceinline__ void route_token(const double *partial, int S, const float *router_b,
                                             int T, int t, int E, int k, int (&sel)[kMaxK],
                                             double (&val)[kMaxK]) {
-    double v[4];
-    if (E <= 64) gather_logits<1>(partial, S, T, t, E, router_b, v);
-    else if (E <= 128) gather_logits<2>(partial, S, T, t, E, router_b, v);
-    else gather_logits<4>(partial, S, T, t, E, router_b, v);
-    wave_topk(v, E, k, sel, val);
+    double v[kMaxQ];
+    if (E <= 64) {
+        gather_logits<1>(partial, S, T, t, E, router_b, v);
+        wave_topk<1>(v, E, k, sel, val);
+    } else if (E <= 128) {
+        gather_logits<2>(partial, S, T, t, E, router_b, v);
+        wave_topk<2>(v, E, k, sel, val);
+    } else if (E <= 256) {
+        gather_logits<4>(partial, S, T, t, E, router_b, v);
+        wave_topk<4>(v, E, k, sel, val);
+    } else {
+        gather_logits<8>(partial, S, T, t, E, router_b, v);
+        wave_topk<8>(v, E, k, sel, val);
+    }
 }
 
 // Expert blob of route r, selected by the calling wavefront itself (top-k of

@@ -9,7 +9,8 @@ namespace moe {
 
 constexpr int kXcds = 8;   // MI355X: 8 accelerator dies; workgroups are dealt round-robin
 constexpr int kMaxK = 8;   // experts per token
-constexpr int kMaxE = 256; // routed experts
+constexpr int kMaxE = 512; // routed experts (DeepSeek-V4-Pro has 384)
+constexpr int kMaxQ = kMaxE / 64;  // experts per lane in a wavefront's top-k
 constexpr int kTerms = 4;  // FP8 terms per activation on the block-scaled matrix cores
 
 // Grouped GEMMs: tiles of 16 or 32 routed rows of one expert

@@ -225,12 +225,21 @@ __device__ __forceinline__ void gemm_mainloop(const uint8_t *const (&aq)[NA],
             step(I1{}, b1, a2, s0 + 5);
         }
     } else {
+        // the prologue issues its loads in the loop's own order (B(s), A(s),
+        // B(s+1), A(s+1)), held there by scheduling barriers: the memory
+        // waits at the loop head merge the prologue's order with the loop's,
+        // and any other order makes every iteration wait for the next step's
+        // loads as well
         ASlot a0, a1;
         BSlot b0, b1;
-        fill_a(a0, 0);
         fill_b(b0, 0);
-        fill_a(a1, 1);
+        __builtin_amdgcn_sched_barrier(0);
+        fill_a(a0, 0);
+        __builtin_amdgcn_sched_barrier(0);
         fill_b(b1, 1);
+        __builtin_amdgcn_sched_barrier(0);
+        fill_a(a1, 1);
+        __builtin_amdgcn_sched_barrier(0);
         for (int s0 = 0; s0 < NS; s0 += 2) {
             step(I0{}, b0, a0, s0);
             step(I1{}, b1, a1, s0 + 1);

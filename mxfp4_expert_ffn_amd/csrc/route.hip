@@ -325,8 +325,8 @@ __global__ __launch_bounds__(256) void router_tiled_kernel(RouteIn in, const flo
 template <int NQ>
 __device__ __forceinline__ void gather_logits_wg(const double *partial, int S, int T, int t,
                                                  int E, const float *bias, double *red,
-                                                 double (&v)[4]) {
-    constexpr int kU = 16 / NQ;
+                                                 double (&v)[kMaxQ]) {
+    constexpr int kU = NQ <= 16 ? 16 / NQ : 1;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     double acc[NQ];
 #pragma unroll
@@ -346,13 +346,14 @@ __device__ __forceinline__ void gather_logits_wg(const double *partial, int S, i
                 if (s0 + 4 * i < S) acc[q] += part[i][q];
     }
 #pragma unroll
-    for (int q = 0; q < NQ; ++q) red[wave * 256 + lane + 64 * q] = acc[q];
+    for (int q = 0; q < NQ; ++q) red[wave * kMaxE + lane + 64 * q] = acc[q];
     __syncthreads();
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < kMaxQ; ++q) {
         const int e = lane + 64 * q;
         if (q < NQ && e < E) {
-            const double sum = ((red[e] + red[256 + e]) + red[512 + e]) + red[768 + e];
+            const double sum =
+                ((red[e] + red[kMaxE + e]) + red[2 * kMaxE + e]) + red[3 * kMaxE + e];
             v[q] = sum + static_cast<double>(bias[e]);
         } else {
             v[q] = -INFINITY;
@@ -364,17 +365,21 @@ __global__ __launch_bounds__(256) void topk_kernel(const double *partial, int S,
                                                    int T, int E, int k, float route_scale,
                                                    int32_t *idx, float *wts, int32_t *out_idx,
                                                    float *out_w) {
-    __shared__ double red[4 * 256];
+    __shared__ double red[4 * kMaxE];
     const int t = blockIdx.x;
     const int lane = threadIdx.x & 63;
-    double v[4];
+    double v[kMaxQ];
     if (E <= 64) gather_logits_wg<1>(partial, S, T, t, E, bias, red, v);
     else if (E <= 128) gather_logits_wg<2>(partial, S, T, t, E, bias, red, v);
-    else gather_logits_wg<4>(partial, S, T, t, E, bias, red, v);
+    else if (E <= 256) gather_logits_wg<4>(partial, S, T, t, E, bias, red, v);
+    else gather_logits_wg<8>(partial, S, T, t, E, bias, red, v);
     if (threadIdx.x >= 64) return;  // after the workgroup barrier
     int sel[kMaxK];
     double val[kMaxK];
-    wave_topk(v, E, k, sel, val);
+    if (E <= 64) wave_topk<1>(v, E, k, sel, val);
+    else if (E <= 128) wave_topk<2>(v, E, k, sel, val);
+    else if (E <= 256) wave_topk<4>(v, E, k, sel, val);
+    else wave_topk<8>(v, E, k, sel, val);
     float wt[kMaxK];
     route_softmax(val, k, route_scale, wt);
 #pragma unroll
@@ -391,7 +396,7 @@ __global__ __launch_bounds__(256) void topk_kernel(const double *partial, int S,
 // ---------------------------------------------------------------- permutation
 // One workgroup of 1024 threads. Routes r = t*k + j are taken in chunks of
 // 1024; inside a wavefront the lanes holding the same expert are found with
-// eight bit-plane ballots and ranked by lane; per-wave counts are prefix-summed per expert in
+// nine bit-plane ballots and ranked by lane; per-wave counts are prefix-summed per expert in
 // wave order, so a route's rank counts exactly the earlier routes of its
 // expert: the permutation is stable (ascending token). Then counts, the
 // exclusive scan and the M-tile prefix for the grouped GEMMs (a workgroup
@@ -422,12 +427,12 @@ __global__ __launch_bounds__(1024) void permute_kernel(
         const int e = e_next;
         if (r + 1024 < R) e_next = idx[r + 1024];
         __syncthreads();
-        // lanes holding the same expert: the intersection of the 8 bit-plane
-        // ballots of the expert index
-        static_assert(kMaxE <= 256, "expert indices fit 8 bit planes");
+        // lanes holding the same expert: the intersection of the bit-plane
+        // ballots of the expert index (9 planes: E <= 512)
+        static_assert(kMaxE <= 512, "expert indices fit 9 bit planes");
         uint64_t eq = __ballot(valid);
 #pragma unroll
-        for (int b = 0; b < 8; ++b) {
+        for (int b = 0; b < 9; ++b) {
             const bool bit = (e >> b) & 1;
             const uint64_t plane = __ballot(bit);
             eq &= bit ? plane : ~plane;

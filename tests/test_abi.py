@@ -145,7 +145,7 @@ def _call(fn_name, shape, **over):
 @pytest.mark.parametrize("case", [
     ("k > E", dict(k=9, E=8), {}, _lib.MOE_ERR_INVALID_ARG),
     ("k = 0", dict(k=0), {}, _lib.MOE_ERR_INVALID_ARG),
-    ("E > 256", dict(E=257), {}, _lib.MOE_ERR_INVALID_ARG),
+    ("E > 512", dict(E=513), {}, _lib.MOE_ERR_INVALID_ARG),
     ("H % 32", dict(H=100), {}, _lib.MOE_ERR_INVALID_ARG),
     ("F % 32", dict(F=40), {}, _lib.MOE_ERR_INVALID_ARG),
     ("null hidden", {}, dict(hidden=None), _lib.MOE_ERR_INVALID_ARG),

@@ -98,7 +98,8 @@ def test_dequant_bitexact_config_weights(cid, experts):
 
 
 # ---------------------------------------------------------------- routing
-@pytest.mark.parametrize("cid,T", [(1, 8), (2, 16), (2, 1000), (3, 128), (4, 512), (5, 2048)])
+@pytest.mark.parametrize("cid,T", [(1, 8), (2, 16), (2, 1000), (3, 128), (4, 512), (5, 2048),
+                                   (6, 2048)])
 def test_route_parity(cid, T):
     cfg = config_by_id(cid)
     _announce(f"route config {cid} T={T}")
@@ -233,6 +234,37 @@ def test_prefill_ds4_flash_full_size_sampled():
     assert err <= TOL
 
 
+def test_ds4_pro_full_size_sampled():
+    """The DeepSeek-V4-Pro shape (H=7168, F=3072, 384 experts top-6 + shared,
+    route scale 2.5) at T=2048: prefill on 8 sampled tokens, and 4 tokens as
+    T=1 decode calls."""
+    cfg = config_by_id(6)
+    _announce("prefill config 6 (DS4-Pro shape) T=2048 (8 sampled tokens) + 4 decode calls")
+    layer = make_layer(cfg)
+    x, xb = make_activations(cfg)
+    dl = upload(cfg, layer)
+    xd = device_input(cfg, x, xb)
+    out, ro = run_forward("prefill", shape_of(cfg), dl, xd)
+    ro = to_np(ro)
+    toks = np.random.default_rng(6).choice(cfg.T, 8, replace=False)
+    ref = _oracle(cfg, layer, x, tokens=toks)
+    check_routing(ro["topk_idx"], ro["topk_w"], ref, layer.router_w, layer.router_b, 2.5)
+    check_permutation(ro, ro["topk_idx"], cfg.E)
+    err = rel_err(out.cpu().numpy()[toks], x[toks] + ref["delta"])
+    print(f"config 6 prefill: max|err|/rms = {err:.2e}")
+    assert err <= TOL
+    shape1 = shape_of(cfg, 1)
+    ws1 = workspace(shape1)
+    dec = torch.full((4, cfg.H), float("nan"), dtype=torch.float32, device="cuda")
+    for i, t in enumerate(toks[:4]):
+        mx.moe_forward_decode(shape1, xd[t:t + 1], dl.router_w, dl.router_b, dl.experts_copy(0),
+                              dec[i:i + 1], ws1, shared=dl.shared_copy(0))
+    torch.cuda.synchronize()
+    err = rel_err(dec.cpu().numpy(), x[toks[:4]] + ref["delta"][:4])
+    print(f"config 6 decode: max|err|/rms = {err:.2e}")
+    assert err <= TOL
+
+
 def test_prefill_stack24_teacher_forced():
     cfg = config_by_id(4)
     _announce("prefill config 4: 24 layers T=512, per-layer teacher forcing")
@@ -323,6 +355,10 @@ EDGE = {
     "narrow": _small(2, T=11, H=96, F=160, E=6, k=3),
     # a decode batch past the GEMV router (tiled router + its own quantise)
     "decode_T40": _small(2, T=40, H=512, F=384, E=16, k=4),
+    # more than 256 experts: eight per lane in the top-k, a ninth bit plane in
+    # the permutation (the DS4-Pro expert count, and the maximum with k = 8)
+    "pro_experts": _small(6, T=64, H=256, F=128, E=384, k=6),
+    "max_E": _small(1, T=40, H=128, F=64, E=512, k=8),
 }
 
 

@@ -357,6 +357,12 @@ def test_config_constants_match_pages():
     assert (c5.H, c5.F, c5.E, c5.k, c5.n_shared) == (d["n_embd"], d["n_ff_exp"], d["n_expert"],
                                                      d["n_expert_used"], d["n_expert_shared"])
     assert c5.route_scale == d["expert_weight_scale"] and c5.limit == d["swiglu_clamp_exp"]
+    p, c6 = pages["ds4_pro"], config_by_id(6)
+    assert (c6.H, c6.F, c6.E, c6.k, c6.n_shared) == (p["n_embd"], p["n_ff_exp"], p["n_expert"],
+                                                     p["n_expert_used"], p["n_expert_shared"])
+    assert c6.route_scale == p["expert_weight_scale"] and c6.limit == p["swiglu_clamp_exp"]
+    assert (c6.alpha, c6.up_offset, c6.act_dtype, c6.router, c6.T) == (
+        c5.alpha, c5.up_offset, c5.act_dtype, c5.router, c5.T)
 
 
 def test_stack_chains_float32_outputs():

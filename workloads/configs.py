@@ -1,4 +1,5 @@
-"""The five workload configurations, as data.
+"""The workload configurations, as data: the five of the block, and a sixth
+with the DeepSeek-V4-Pro shape (a next step after the five).
 
 Model constants come from the pages:
 - gpt-oss-20b (goosedump 0.12.31 `src/engine/model/gpt_oss.rs`, constants block):
@@ -8,6 +9,10 @@ Model constants come from the pages:
 - DeepSeek-V4-Flash (antirez `ds4.c`, `DS4_SHAPE_FLASH`): n_embd 4096,
   n_ff_exp 2048, 256 routed experts, 6 used, 1 shared expert, expert weight
   scale 1.5, SwiGLU clamp 10 (`DS4_DEFAULT_SWIGLU_CLAMP_EXP`).
+- DeepSeek-V4-Pro (`DS4_SHAPE_PRO`): n_embd 7168, n_ff_exp 3072, 384 routed
+  experts, 6 used, 1 shared, expert weight scale 2.5, the same default clamp.
+  Everything the page leaves open (batch, router, activations, SwiGLU alpha
+  and offset) follows the Flash workload.
 
 Value distributions (codes, scales, biases, router, activations) are the
 synthetic recipe of the workload list; see `gen.py`.
@@ -65,6 +70,9 @@ CONFIGS = (
               router_b_std=0.5, layers=24, rms_eps=1e-5),
     MoeConfig(5, "ds4_flash", T=2048, H=4096, F=2048, E=256, k=6,
               alpha=1.0, limit=10.0, up_offset=0.0, route_scale=1.5,
+              n_shared=1, act_dtype="bf16", router="uniform"),
+    MoeConfig(6, "ds4_pro", T=2048, H=7168, F=3072, E=384, k=6,
+              alpha=1.0, limit=10.0, up_offset=0.0, route_scale=2.5,
               n_shared=1, act_dtype="bf16", router="uniform"),
 )
 
