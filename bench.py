@@ -259,7 +259,7 @@ class Setup:
         if self.spec["kernel"] == "decode_gate_up":
             T = 1 if self.mode in ("calls", "decode_stack") else cfg.T
             routes = T * k + T * cfg.n_shared
-            splits = (H + 2047) // 2048
+            splits = (H + 511) // 512    # the router's split-K partials (512-wide slices)
             byts = routes * 2 * (mat + 4 * F) + T * terms(H) + routes * terms(F) + T * splits * E * 8
             return dict(bytes=byts, flops=routes * 4 * H * F, units=routes,
                         unit="route (token, selected expert)")
@@ -348,14 +348,20 @@ def cpu_baseline(setup, budget_s: float):
         return dict(value=n / dt, unit="tokens/s", cores=cores, kind="oracle",
                     sample=f"first {n} of the {cfg.calls} decode tokens of layer 0, batched in "
                            f"one fp64 oracle call ({dt:.1f} s)")
-    # prefill-type: all T tokens of the first layer if the budget allows, else a token subset
+    # prefill-type: all T tokens of the first layer if the budget allows, else
+    # the first n tokens. The oracle's time goes into dequantising each expert
+    # the sample touches (about 0.08 s per expert at H*F = 4096*2048, measured
+    # on the GPU host, scaled by the expert's size), so n is the largest count
+    # whose expected number of distinct experts, E(1 - (1 - k/E)^n) plus the
+    # shared one, fits the budget
+    per_expert = 0.08 * cfg.H * cfg.F / (4096 * 2048)
+
+    def experts_touched(m):
+        return cfg.E * (1.0 - (1.0 - cfg.k / cfg.E) ** m) + cfg.n_shared
+
     n = cfg.T
-    # about 0.35 s of dequantise-and-multiply per expert at H*F = 4096*2048
-    # (measured), scaled by the expert's size
-    per_expert = 0.35 * cfg.H * cfg.F / (4096 * 2048)
-    est_experts = min(cfg.E, cfg.T * cfg.k) + cfg.n_shared
-    if est_experts * per_expert > budget_s:
-        n = max(1, int(cfg.T * budget_s / (est_experts * per_expert)))
+    while n > 1 and experts_touched(n) * per_expert > budget_s:
+        n = int(n * 0.9)
     toks = np.arange(n)
     t0 = time.time()
     omoe.block_for_config(cfg, layer, x[:cfg.T], tokens=toks)

@@ -78,11 +78,13 @@ hipError_t launch_rms_inv(const void *x, int x_bf16, int T, int H, float eps, do
                           hipStream_t s);
 // Router: split-K partial logits partial[splits][T][E] (fp64, bias not added).
 // GEMV form for T <= kRouterGemvMaxT (one wavefront per expert and
-// 2048-wide hidden slice), tiled form otherwise (slices sized for about 512
+// 512-wide hidden slice), tiled form otherwise (slices sized for about 512
 // workgroups, at most kRouterMaxSplits).
 constexpr int kRouterGemvMaxT = 16;
 constexpr int kRouterMaxSplits = 64;
-constexpr int kRouterGemvSlice = 2048;
+// 512-wide slices: 2048 and 1024 were 1-3% slower per decode token, 256 much
+// slower (the gate/up kernel's gather of the partials grows)
+constexpr int kRouterGemvSlice = 512;
 // Most quantisation workgroups beside the tiled router (grid-stride beyond).
 constexpr int kQuantizeMaxWgs = 1024;
 struct RouterPlan {
