@@ -221,9 +221,9 @@ int check_forward(const moe_shape *s, const void *hidden, const float *norm_w,
 // RMSNorm scale (with a norm) and router. `terms`: the router launch also
 // makes the FP8 terms of the expert input. Returns the expert input in `in`.
 int route_front(const moe_shape *s, const void *x, const float *norm_w, const float *router_w,
-                const Workspace &w, bool terms, moe::RouteIn *in, hipStream_t st) {
+                const Workspace &w, bool terms, float *seed, moe::RouteIn *in, hipStream_t st) {
     const int bf16 = s->act_dtype == MOE_BF16;
-    *in = moe::RouteIn{x, bf16, nullptr, nullptr};
+    *in = moe::RouteIn{x, bf16, nullptr, nullptr, seed};
     if (norm_w) {
         MOE_TRY(launch(MOE_KERNEL_RMSNORM, "rmsnorm", st, [&] {
             return moe::launch_rms_inv(x, bf16, s->T, s->H, s->rms_eps, w.rinv, st);
@@ -341,7 +341,7 @@ int moe_route(const moe_shape *s, const void *x, const float *norm_w, const floa
     if (s->T == 0) return ok();
     const Workspace w = carve(s, static_cast<uint8_t *>(ws));
     moe::RouteIn in;
-    MOE_TRY(route_front(s, x, norm_w, router_w, w, false, &in, st));
+    MOE_TRY(route_front(s, x, norm_w, router_w, w, false, nullptr, &in, st));
     MOE_TRY(launch(MOE_KERNEL_TOPK, "topk", st, [&] {
         return moe::launch_topk(w.partial, w.splits, router_b, s->T, s->E, s->k, s->route_scale,
                                 w.idx, w.wts, out->topk_idx, out->topk_w, st);
@@ -364,7 +364,10 @@ int moe_forward_decode(const moe_shape *s, const void *hidden, const float *norm
     if (s->T == 0) return ok();
     const Workspace w = carve(s, static_cast<uint8_t *>(ws));
     moe::RouteIn in;
-    MOE_TRY(route_front(s, hidden, norm_w, router_w, w, true, &in, st));
+    // the router launch's quantisation seeds out with the residual, unless out
+    // already is the float32 input (in place)
+    const bool in_place = s->act_dtype == MOE_F32 && static_cast<const void *>(out) == hidden;
+    MOE_TRY(route_front(s, hidden, norm_w, router_w, w, true, in_place ? nullptr : out, &in, st));
     moe::DecodeArgs a{};
     a.xq = w.xq;
     a.xs = w.xs;
@@ -386,8 +389,6 @@ int moe_forward_decode(const moe_shape *s, const void *hidden, const float *norm
     a.out_idx = ro ? ro->topk_idx : nullptr;
     a.out_w = ro ? ro->topk_w : nullptr;
     a.route_counts = ro ? ro->route_counts : nullptr;  // added where the experts are published
-    a.resid = hidden;
-    a.resid_bf16 = s->act_dtype == MOE_BF16;
     a.out = out;
     a.act_q = w.act_q;
     a.act_s = w.act_s;
@@ -421,7 +422,7 @@ int moe_forward_prefill(const moe_shape *s, const void *hidden, const float *nor
     // GEMV form, else beside the one-workgroup permutation
     moe::RouteIn in;
     const bool router_terms = moe::router_plan(s->T, s->H, s->E).gemv;
-    MOE_TRY(route_front(s, hidden, norm_w, router_w, w, router_terms, &in, st));
+    MOE_TRY(route_front(s, hidden, norm_w, router_w, w, router_terms, nullptr, &in, st));
     MOE_TRY(launch(MOE_KERNEL_TOPK, "topk", st, [&] {
         return moe::launch_topk(w.partial, w.splits, router_b, s->T, s->E, s->k, s->route_scale,
                                 w.idx, w.wts, ro ? ro->topk_idx : nullptr,

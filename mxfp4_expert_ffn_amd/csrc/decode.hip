@@ -78,9 +78,10 @@ __device__ __forceinline__ const uint8_t *route_blob(const DecodeArgs &a, int r,
 
 // gate/up + biases + clamped SwiGLU for 32 features (block fb) of route r;
 // writes the activation block's FP8 terms and scales (blocks past F write the
-// zero padding of the down GEMV's operand). Workgroups of slot 0 also seed
-// out[t] with the residual, a share each. s_part: kDecodeWaves * 4 * 16
-// floats of LDS.
+// zero padding of the down GEMV's operand). out[t] already holds the residual
+// (seeded by the router launch's quantisation), so nothing here delays the
+// router-partials load and the top-k. s_part: kDecodeWaves * 4 * 16 floats of
+// LDS.
 template <int SPW>
 __device__ __forceinline__ void gate_up_item(const DecodeArgs &a, int r, int fb, float *s_part) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -89,17 +90,6 @@ __device__ __forceinline__ void gate_up_item(const DecodeArgs &a, int r, int fb,
     const int j = r < R ? r - t * a.k : -1;
     const int H = a.H, F = a.F;
     const int Kp = pad128(H), Fp = pad128(F), nbp = Fp / 32;
-    if (j == 0) {  // residual seed, unless out already is the float32 residual
-        float *o = a.out + static_cast<size_t>(t) * H;
-        const float *rf = static_cast<const float *>(a.resid) + static_cast<size_t>(t) * H;
-        if (a.resid_bf16 || o != rf) {
-            const uint16_t *rb = static_cast<const uint16_t *>(a.resid) + static_cast<size_t>(t) * H;
-            const int share = (H + nbp - 1) / nbp;
-            const int end = min(H, (fb + 1) * share);
-            for (int h = fb * share + threadIdx.x; h < end; h += blockDim.x)
-                o[h] = a.resid_bf16 ? bf16_bits_to_f32(rb[h]) : rf[h];
-        }
-    }
     uint8_t *aq = a.act_q + static_cast<size_t>(r) * kTerms * Fp;
     uint8_t *as = a.act_s + static_cast<size_t>(r) * kTerms * nbp;
     if (32 * fb >= F) {  // K padding of the down GEMV's operand: zero codes, by wavefront 0

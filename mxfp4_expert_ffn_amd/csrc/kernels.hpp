@@ -72,6 +72,8 @@ struct RouteIn {
     int bf16;
     const double *inv;   // [T] RMSNorm scale, or NULL: no norm
     const float *gamma;  // [H] norm weight (16-byte aligned) when inv is set
+    float *seed;         // [T][H]: the quantisation also writes the raw input here
+                         // as float32 (decode's residual seed), or NULL
 };
 // RMSNorm scale inv[t] = 1 / sqrt(sum_h x[t][h]^2 / H + eps), summed in fp64.
 hipError_t launch_rms_inv(const void *x, int x_bf16, int T, int H, float eps, double *inv,
@@ -140,13 +142,12 @@ struct DecodeArgs {
     int32_t *out_idx;  // optional exports (NULL: not written)
     float *out_w;
     uint64_t *route_counts;  // optional [E] profile: += 1 per selection (NULL: off)
-    const void *resid;
-    int resid_bf16;
     float *out;
     uint8_t *act_q, *act_s;
 };
-// gate/up (which also selects the experts and seeds out with the residual),
-// then down; both after launch_router.
+// gate/up (which also selects the experts), then down; both after
+// launch_router, whose quantisation seeds out with the residual (RouteIn::seed)
+// unless out already is the float32 input.
 hipError_t launch_decode_gate_up(const DecodeArgs &a, hipStream_t s);
 hipError_t launch_decode_down(const DecodeArgs &a, hipStream_t s);
 

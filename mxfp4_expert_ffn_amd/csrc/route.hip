@@ -77,7 +77,9 @@ __global__ __launch_bounds__(256) void rms_inv_kernel(const void *x, int H, floa
 // one half-wavefront per 32-value block of k (the unit an E8M0 scale of the
 // instruction's operand covers); codes go to xq[t][n][k] (zero past H),
 // scales to xs[t][n][k / 32]. With a norm the value is
-// float32((x * inv[t]) * gamma[k]).
+// float32((x * inv[t]) * gamma[k]). With a seed buffer the raw input value is
+// also stored there as float32 (decode's residual: the store rides on the load
+// the quantisation makes anyway, ahead of every expert launch).
 
 // The lane's value of block gidx (0 past the last block or past H).
 __device__ __forceinline__ float quantize_input(const RouteIn &in, int T, int H, int nb,
@@ -88,6 +90,7 @@ __device__ __forceinline__ float quantize_input(const RouteIn &in, int T, int H,
     if (kk >= H) return 0.f;
     const size_t at = static_cast<size_t>(t) * H + kk;
     const double x = in.bf16 ? load_in<1>(in.x, at) : load_in<0>(in.x, at);
+    if (in.seed) in.seed[at] = static_cast<float>(x);  // exact: the input is f32 or bf16
     return in.inv ? static_cast<float>(x * in.inv[t] * static_cast<double>(in.gamma[kk]))
                   : static_cast<float>(x);
 }
@@ -594,7 +597,7 @@ hipError_t launch_permute(const int32_t *idx, int T, int E, int k, int n_shared,
         const int want = (T * (Kp / 32) + 31) / 32;  // one round of 32 blocks each
         qwgs = want < kPermuteQuantizeWgs ? want : kPermuteQuantizeWgs;
     }
-    const RouteIn none{nullptr, 0, nullptr, nullptr};
+    const RouteIn none{nullptr, 0, nullptr, nullptr, nullptr};
     launch_kernel(permute_kernel, 1 + qwgs, 1024, s, idx, T, E, k, n_shared, tile_rows, counts,
                   offsets, perm, inv, rank, mprefix, out_counts, out_offsets, out_perm, out_inv,
                   route_counts, terms ? *qin : none, H, Kp, terms ? terms->q : nullptr,
