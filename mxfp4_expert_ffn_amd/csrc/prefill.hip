@@ -73,7 +73,8 @@ struct Tile {
 // tiles x the row blocks) row block by row block, and inside a row block tile
 // by tile: all tiles of an expert that need the same weight rows run side by
 // side and share them in L2, and a tile's row blocks follow each other (its
-// activation rows stay in L2 too). False when past the real tiles.
+// activation rows stay in L2 too); groups with many tiles and row blocks go
+// tile by tile instead (below). False when past the real tiles.
 __device__ __forceinline__ bool find_item(int nrb, int bm, const int32_t *offsets,
                                           const int *s_pre, int G, int &rb, Tile &tl) {
     // the real item count splits evenly over the dies (the grid is an upper
@@ -92,8 +93,19 @@ __device__ __forceinline__ bool find_item(int nrb, int bm, const int32_t *offset
     }
     const int nt = s_pre[lo + 1] - s_pre[lo];  // >= 1: a group with no tiles owns no items
     const int local = item - s_pre[lo] * nrb;
-    rb = local / nt;
-    const int tile = local - rb * nt;
+    // a group with many tiles and many row blocks (the shared expert at the
+    // DeepSeek-V4-Pro shape) runs tile by tile, a tile's row blocks back to
+    // back, so its activation rows stay in L2 while the weights stream (7%
+    // faster per step there); with fewer row blocks (the Flash shape, 16) the
+    // row-block order measured 1% faster, and routed experts have few tiles
+    int tile;
+    if (nt >= 16 && nrb >= 20) {
+        tile = local / nrb;
+        rb = local - tile * nrb;
+    } else {
+        rb = local / nt;
+        tile = local - rb * nt;
+    }
     tl.g = lo;
     tl.p0 = offsets[lo] + tile * bm;
     tl.n = min(bm, offsets[lo + 1] - tl.p0);

@@ -359,6 +359,9 @@ EDGE = {
     # the permutation (the DS4-Pro expert count, and the maximum with k = 8)
     "pro_experts": _small(6, T=64, H=256, F=128, E=384, k=6),
     "max_E": _small(1, T=40, H=128, F=64, E=512, k=8),
+    # a group with 16 tiles and 20 gate/up row blocks (the shared expert here)
+    # runs tile by tile in the grouped GEMMs
+    "tile_major": _small(5, T=256, H=256, F=2560, E=4, k=2),
 }
 
 
