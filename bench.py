@@ -2,6 +2,7 @@
 """Throughput of the routed MXFP4 MoE block on one MI355X (gfx950).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--route-profile]
+                    [--route-locality]
 
 A step is one pass of the whole block over one batch of seeded synthetic
 input (weights and activations resident in HBM before timing):
@@ -23,7 +24,11 @@ weights are held in several device copies, cycled between calls, so that the
 
 With --route-profile every call also adds its expert selections to a
 [layers][E] uint64 table on the device (the route profile of the library's
-route_out), so the timed steps include that recording.
+route_out), so the timed steps include that recording. With --route-locality
+(T=1 workloads) one more step runs after the timed region, eagerly, with each
+call exporting its selections and route weights; the library's
+moe_route_locality then reports that trace's adjacent-token overlap and the hit
+rates of simulated per-layer expert caches.
 
 Prints one JSON line (rank 0, N=1 only).
 """
@@ -179,6 +184,7 @@ class Setup:
             self.xd = torch.from_numpy(x).cuda()
         self.ws = workspace(self.shape)
         self.profile = None  # [layers][E] int64 route profile table, when recording
+        self.trace = None    # (idx, w) [positions, layers, k] device tensors, when tracing
         self.tokens_per_step = cfg.T * cfg.calls
         # "calls": independent T=1 decode calls; "decode_stack": T=1 tokens
         # through every layer; "decode": one decode call; "prefill"
@@ -207,8 +213,14 @@ class Setup:
             self.out = torch.empty((cfg.T, cfg.H), dtype=torch.float32, device="cuda")
             self.out2 = torch.empty_like(self.out)
 
-    def _ro(self, layer: int):
-        return None if self.profile is None else {"route_counts": self.profile[layer]}
+    def _ro(self, layer: int, pos: int = 0):
+        ro = {}
+        if self.profile is not None:
+            ro["route_counts"] = self.profile[layer]
+        if self.trace is not None:
+            ro["topk_idx"] = self.trace[0][pos, layer:layer + 1]
+            ro["topk_w"] = self.trace[1][pos, layer:layer + 1]
+        return ro or None
 
     def step_calls(self, step: int):
         """Closures making up one step (weights copy chosen per call/step)."""
@@ -219,9 +231,9 @@ class Setup:
                 src = self.xrows[i]
                 for l, dl in enumerate(self.layers):
                     dst = self.out[i, l % 2].view(1, cfg.H)
-                    calls.append(lambda dl=dl, src=src, dst=dst, l=l: mx.moe_forward_decode(
+                    calls.append(lambda dl=dl, src=src, dst=dst, l=l, i=i: mx.moe_forward_decode(
                         self.step_shape, src, dl.router_w, dl.router_b, dl.experts_copy(0), dst,
-                        self.ws, norm_w=dl.norm_w, route_out=self._ro(l)))
+                        self.ws, norm_w=dl.norm_w, route_out=self._ro(l, i)))
                     src = dst
         elif self.mode == "calls":
             dl = self.layers[0]
@@ -229,7 +241,7 @@ class Setup:
                 ex = dl.experts_copy(i)
                 calls.append(lambda i=i, ex=ex: mx.moe_forward_decode(
                     self.step_shape, self.xrows[i], dl.router_w, dl.router_b, ex, self.orows[i],
-                    self.ws, route_out=self._ro(0)))
+                    self.ws, route_out=self._ro(0, i)))
         elif self.mode == "decode":
             dl = self.layers[0]
             calls.append(lambda: mx.moe_forward_decode(
@@ -371,6 +383,36 @@ def cpu_baseline(setup, budget_s: float):
                        f"fp64 oracle call ({dt:.1f} s)")
 
 
+def route_locality(setup) -> dict:
+    """One untimed step with every call exporting its selections and route
+    weights: the decode trace's locality, from the library's host profiler."""
+    import torch
+    mx, cfg = setup.mx, setup.cfg
+    P = setup.ntok if setup.mode == "decode_stack" else cfg.calls
+    L = len(setup.layers)
+    setup.trace = (torch.full((P, L, cfg.k), -1, dtype=torch.int32, device="cuda"),
+                   torch.zeros((P, L, cfg.k), dtype=torch.float32, device="cuda"))
+    for c in setup.step_calls(0):
+        c()
+    torch.cuda.synchronize()
+    idx, w = (t.cpu().numpy() for t in setup.trace)
+    setup.trace = None
+    r = mx.moe_route_locality(idx, w, cfg.E)
+    sel = int(r["hist"].sum())
+    tw = float(r["weight_hist"].sum())
+    pairs = int(r["adjacent_pairs"].sum())
+    order = mx.moe_route_hotlist(r["hist"], r["weight_hist"])
+    return {
+        "positions": P, "layers": L, "k": cfg.k, "selections": sel,
+        "cache_sizes": r["caps"].tolist(),
+        "hit_rate": [round(int(h) / sel, 6) for h in r["cache_hits"].sum(axis=1)],
+        "weighted_hit_rate": [round(float(h) / tw, 6) for h in r["cache_weight_hits"].sum(axis=1)],
+        "mean_adjacent_overlap": round(float(r["overlap_sum"].sum()) / pairs, 6) if pairs else 0.0,
+        "mean_adjacent_jaccard": round(float(r["jaccard_sum"].sum()) / pairs, 6) if pairs else 0.0,
+        "hottest": [[int(i) // cfg.E, int(i) % cfg.E, int(r["hist"].flat[i])] for i in order[:4]],
+    }
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -383,6 +425,9 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds for the oracle sample")
     ap.add_argument("--route-profile", action="store_true",
                     help="record every call's expert selections into a device route profile")
+    ap.add_argument("--route-locality", action="store_true",
+                    help="after timing, one untimed step recording its decode trace, and the "
+                         "trace's expert locality (T=1 workloads)")
     ap.add_argument("--calibrate-copy-gib", type=float, default=0.0,
                     help="also run one device copy of this many GiB (PMC byte calibration)")
     args = ap.parse_args()
@@ -394,6 +439,8 @@ def main():
         args.steps = WORKLOADS[args.workload]["steps"]
     if args.steps < 1:
         sys.exit("--steps must be >= 1")
+    if args.route_locality and args.workload not in ("decode", "decode_stack"):
+        sys.exit("--route-locality needs a T=1 workload (decode, decode_stack)")
 
     import torch
     import mxfp4_expert_ffn_amd as mx
@@ -511,6 +558,8 @@ def main():
         summ["selections_expected"] = runs * setup.tokens_per_step * cfg.k * cfg.layers
         del summ["layer_unique"]
         result["route_profile"] = summ
+    if args.route_locality:
+        result["route_locality"] = route_locality(setup)
     if args.calibrate_copy_gib > 0:
         n = int(args.calibrate_copy_gib * (1 << 30)) // 4
         a = torch.empty(n, dtype=torch.float32, device="cuda").fill_(1.0)

@@ -165,6 +165,63 @@ int moe_route_profile_summary(const uint64_t *counts, int32_t layers, int32_t E,
                               uint64_t *selections, uint64_t *unique_layer_experts,
                               int32_t *layer_unique);
 
+/* Outputs of moe_route_locality, host arrays owned by the caller; every one is
+ * overwritten.
+ *   hist              [layers][E]     selections of each expert
+ *   weight_hist       [layers][E]     sum of their route weights (float64)
+ *   cache_hits        [n_caps][layers] hits of the simulated cache of size caps[c]
+ *   cache_weight_hits [n_caps][layers] route weight of those hits
+ *   adjacent_pairs    [layers]        tokens compared with the one before them
+ *   overlap_sum       [layers]        sum over those pairs of |shared| / k
+ *   jaccard_sum       [layers]        sum of |shared| / (2k - |shared|)
+ * The cache arrays may be NULL when n_caps is 0. */
+typedef struct moe_locality_out {
+    uint64_t *hist;
+    double *weight_hist;
+    uint64_t *cache_hits;
+    double *cache_weight_hits;
+    uint64_t *adjacent_pairs;
+    double *overlap_sum;
+    double *jaccard_sum;
+} moe_locality_out;
+
+/* Routed-expert locality of a decode trace. Host only.
+ *   idx      [positions][layers][k] int32, host: the selected experts of
+ *            consecutive decode positions (topk_idx of one T=1 call per layer
+ *            and position, read back)
+ *   weights  [positions][layers][k] float32, host: their route weights (topk_w)
+ *   caps     [n_caps] int32, host: cache sizes, each in [1, E] (ds4.c's
+ *            candidates are 1, 2, 4, ..., 256, 384, those not above E)
+ * Per layer, in position order and slot order 0..k-1, each selection of an
+ * expert in [0, E) counts in hist / weight_hist and is offered to one cache per
+ * size: a list of at most caps[c] experts, most recent first, where a present
+ * expert is a hit (added to cache_hits / cache_weight_hits) and moves to the
+ * front, and an absent one is put at the front, the last entry dropping out
+ * past caps[c]. From the second position on, each token is compared with the
+ * previous one: |shared| counts the previous token's slots whose expert the
+ * current token also selected (indices outside [0, E) included). Every
+ * call starts from empty caches and zeroed outputs.
+ * Returns MOE_OK, or MOE_ERR_INVALID_ARG (a NULL input or output, positions < 0,
+ * layers < 1, k < 1, E < 1, n_caps outside [0, 16], a size outside [1, E]).
+ * Page: antirez ds4.c, the Metal routed-expert locality profiler (its record
+ * and cache-use steps). */
+int moe_route_locality(const int32_t *idx, const float *weights, int64_t positions,
+                       int32_t layers, int32_t k, int32_t E, const int32_t *caps,
+                       int32_t n_caps, const moe_locality_out *out);
+
+/* Hotlist order of a locality histogram. Host only.
+ *   hist, weight_hist  [layers][E], as moe_route_locality writes them
+ *   order              [layers * E] int32 out: every layer * E + expert, ranked by
+ *                      count (descending), route weight (descending), layer, then
+ *                      expert (ascending). A layer's own ranking is this order
+ *                      restricted to that layer.
+ * Returns MOE_OK or MOE_ERR_INVALID_ARG (NULL pointer, layers < 1, E < 1,
+ * layers * E above 2^31 - 1, or a weight sum that is not finite).
+ * Page: antirez ds4.c, the profiler's layer and hotlist writers (their sort
+ * orders). */
+int moe_route_hotlist(const uint64_t *hist, const double *weight_hist, int32_t layers,
+                      int32_t E, int32_t *order);
+
 /* Fill *layout for experts of this shape (uses H and F only). Host only.
  * Returns MOE_OK or MOE_ERR_INVALID_ARG. */
 int moe_blob_layout_get(const moe_shape *shape, moe_blob_layout *layout);

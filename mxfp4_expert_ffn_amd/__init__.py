@@ -14,13 +14,14 @@ import ctypes
 import numpy as np
 
 from . import _lib
-from ._lib import MOE_BF16, MOE_F32, MoeBlobLayout, MoeExpertPlanes, MoeRouteOut, MoeShape
+from ._lib import (MOE_BF16, MOE_F32, MoeBlobLayout, MoeExpertPlanes, MoeLocalityOut, MoeRouteOut,
+                   MoeShape)
 
 __all__ = [
     "MoeError", "MoeShape", "make_shape", "moe_blob_layout_get", "moe_pack_experts",
     "moe_workspace_bytes", "moe_route", "moe_forward_decode", "moe_forward_prefill",
     "moe_dequant_debug", "moe_last_error", "moe_profile_next_launch", "moe_route_profile_summary",
-    "ROUTE_FIELDS",
+    "moe_route_locality", "moe_route_hotlist", "LOCALITY_CACHE_SIZES", "ROUTE_FIELDS",
 ]
 
 # route_counts: an int64 [E] device tensor the call adds its selections per
@@ -182,3 +183,52 @@ def moe_route_profile_summary(counts) -> dict:
         c.ctypes.data_as(ctypes.c_void_p), c.shape[0], c.shape[1], ctypes.byref(sel),
         ctypes.byref(uniq), per.ctypes.data_as(ctypes.c_void_p)))
     return dict(selections=sel.value, unique_layer_experts=uniq.value, layer_unique=per.tolist())
+
+
+# cache sizes the locality profile simulates by default: ds4.c's candidates
+# (those not above E are used)
+LOCALITY_CACHE_SIZES = (1, 2, 4, 8, 16, 32, 64, 128, 256, 384)
+
+
+def _host(a, dtype):
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+def moe_route_locality(idx, weights, E: int, caps=None) -> dict:
+    """Locality of a decode trace (antirez ds4.c's routed-expert locality
+    profiler): idx and weights [positions, layers, k] (host arrays, or what a
+    T=1 call's topk_idx / topk_w hold, copied back per position and layer).
+    Returns the library's per-layer counts, route-weight sums, adjacent-token
+    overlap and Jaccard sums, and the hits of each simulated cache size."""
+    ix = _host(idx, np.int32)
+    w = _host(weights, np.float32)
+    if ix.ndim != 3 or w.shape != ix.shape:
+        raise ValueError("idx and weights must both be [positions, layers, k]")
+    P, L, k = ix.shape
+    cs = _host([c for c in LOCALITY_CACHE_SIZES if c <= E] if caps is None else caps, np.int32)
+    r = dict(caps=cs, hist=np.zeros((L, E), np.uint64), weight_hist=np.zeros((L, E), np.float64),
+             cache_hits=np.zeros((cs.size, L), np.uint64),
+             cache_weight_hits=np.zeros((cs.size, L), np.float64),
+             adjacent_pairs=np.zeros(L, np.uint64), overlap_sum=np.zeros(L, np.float64),
+             jaccard_sum=np.zeros(L, np.float64))
+    vp = ctypes.c_void_p
+    out = MoeLocalityOut(*(vp(r[n].ctypes.data) for n in (
+        "hist", "weight_hist", "cache_hits", "cache_weight_hits", "adjacent_pairs", "overlap_sum",
+        "jaccard_sum")))
+    _check(_lib.load().moe_route_locality(vp(ix.ctypes.data), vp(w.ctypes.data), P, L, k, int(E),
+                                          vp(cs.ctypes.data), cs.size, ctypes.byref(out)))
+    return r
+
+
+def moe_route_hotlist(hist, weight_hist) -> np.ndarray:
+    """Every layer * E + expert of a locality histogram [layers, E], ranked by
+    count and route weight (descending), then layer and expert."""
+    h = _host(hist, np.uint64)
+    wh = _host(weight_hist, np.float64)
+    if h.ndim != 2 or wh.shape != h.shape:
+        raise ValueError("hist and weight_hist must both be [layers, E]")
+    order = np.zeros(h.size, np.int32)
+    vp = ctypes.c_void_p
+    _check(_lib.load().moe_route_hotlist(vp(h.ctypes.data), vp(wh.ctypes.data), h.shape[0],
+                                         h.shape[1], vp(order.ctypes.data)))
+    return order

@@ -45,6 +45,12 @@ class MoeRouteOut(ctypes.Structure):
         "topk_idx", "topk_w", "counts", "offsets", "perm", "inv", "route_counts")]
 
 
+class MoeLocalityOut(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in (
+        "hist", "weight_hist", "cache_hits", "cache_weight_hits", "adjacent_pairs",
+        "overlap_sum", "jaccard_sum")]
+
+
 # every symbol the header declares, with its ctypes signature
 _P = ctypes.c_void_p
 SIGNATURES = {
@@ -62,6 +68,10 @@ SIGNATURES = {
                                          ctypes.c_int32, _P, _P]),
     "moe_profile_next_launch": (ctypes.c_int, [ctypes.c_int32, _P, _P]),
     "moe_route_profile_summary": (ctypes.c_int, [_P, ctypes.c_int32, ctypes.c_int32, _P, _P, _P]),
+    "moe_route_locality": (ctypes.c_int, [_P, _P, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                          ctypes.c_int32, _P, ctypes.c_int32,
+                                          ctypes.POINTER(MoeLocalityOut)]),
+    "moe_route_hotlist": (ctypes.c_int, [_P, _P, ctypes.c_int32, ctypes.c_int32, _P]),
     "moe_last_error": (ctypes.c_char_p, []),
 }
 

@@ -10,6 +10,7 @@
 #include <cstring>
 #include <string>
 
+#include "host_status.hpp"
 #include "kernels.hpp"
 
 namespace {
@@ -42,6 +43,13 @@ int ok() {
     g_last_error.clear();
     return MOE_OK;
 }
+
+}  // namespace
+
+int moe::host_fail(int code, const char *msg) { return fail(code, "%s", msg); }
+int moe::host_ok() { return ok(); }
+
+namespace {
 
 constexpr uint64_t align_up(uint64_t v, uint64_t a) { return (v + a - 1) / a * a; }
 

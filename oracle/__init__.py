@@ -14,10 +14,12 @@ Modules:
 - `brute`  the same block in pure Python loops (no numpy) for tiny inputs,
            with top-k by subset enumeration; it pins `moe`.
 - `route_profile`  per-(layer, expert) selection counters and their summaries.
+- `route_locality`  adjacent-token overlap and simulated per-layer expert caches
+           over a decode trace, with the rankings of its reports.
 
 Pins against what the pages and mathematics fix live in `tests/` (run with
 `-m "not gpu"`). Parity status per function is stated in each docstring;
 the clamped-SwiGLU body is a reading (no page prints it) and is marked
 "parity unpinned by the pages" where it is defined.
 """
-from . import mxfp4, moe, brute, route_profile  # noqa: F401
+from . import mxfp4, moe, brute, route_profile, route_locality  # noqa: F401
