@@ -362,6 +362,11 @@ EDGE = {
     # a group with 16 tiles and 20 gate/up row blocks (the shared expert here)
     # runs tile by tile in the grouped GEMMs
     "tile_major": _small(5, T=256, H=256, F=2560, E=4, k=2),
+    # the largest expert hidden size the library takes (prefill only; decode
+    # stops at 8192)
+    "max_F": _small(1, T=3, H=64, F=16384, E=2, k=1),
+    # the largest decode batch, bf16 input with a shared expert
+    "decode_T64": _small(5, T=64, H=256, F=128, E=12, k=6),
 }
 
 
@@ -380,6 +385,50 @@ def test_edge_cases(name, path):
     err = _check_block(cfg, layer, x, out.cpu().numpy(), ro)
     check_permutation(ro, ro["topk_idx"], cfg.E)
     print(f"edge {name} {path}: max|err|/rms = {err:.2e}")
+
+
+def _degenerate_rows(H, rng):
+    """Token rows whose values stress the FP8-term encoding of the expert input:
+    zeros, negative zeros, one nonzero 32-value block, a constant row, rows
+    scaled by 2^-60 and 2^20, and exact +-1."""
+    x = np.zeros((8, H), np.float32)
+    x[1] = -0.0
+    x[2, 32:64] = rng.normal(0.0, 1.0, 32)
+    x[3] = 0.5
+    x[4] = rng.normal(0.0, 1.0, H) * 2.0 ** -60
+    x[5] = rng.normal(0.0, 1.0, H) * 2.0 ** 20
+    x[6] = rng.normal(0.0, 1.0, H)
+    x[7] = np.where(np.arange(H) % 2 == 0, 1.0, -1.0)
+    return x
+
+
+@pytest.mark.parametrize("cid", [1, 4, 5])
+@pytest.mark.parametrize("path", ["decode", "prefill"])
+def test_degenerate_token_values(cid, path):
+    from workloads.gen import _round_to_bf16_bits, bf16_bits_to_f32
+    base = {1: dict(H=256, F=256), 4: dict(H=256, F=192, E=8, k=4, layers=1),
+            5: dict(H=256, F=128, E=12, k=6)}[cid]
+    cfg = _small(cid, T=8, **base)
+    _announce(f"degenerate token values, config {cid} {path}")
+    layer = make_layer(cfg)
+    x = _degenerate_rows(cfg.H, np.random.default_rng(11))
+    xb = None
+    if cfg.act_dtype == "bf16":
+        xb = _round_to_bf16_bits(x)
+        x = bf16_bits_to_f32(xb)
+    dl = upload(cfg, layer)
+    out, ro = run_forward(path, shape_of(cfg), dl, device_input(cfg, x, xb))
+    out = out.cpu().numpy()
+    ro = to_np(ro)
+    ref = _oracle(cfg, layer, x)
+    check_routing(ro["topk_idx"], ro["topk_w"], ref, layer.router_w, layer.router_b,
+                  cfg.route_scale)
+    want = x + ref["delta"]
+    assert np.isfinite(out).all()
+    # each token against its own output's RMS (stricter than the block-wide bar)
+    for t in range(cfg.T):
+        err = rel_err(out[t:t + 1], want[t:t + 1])
+        assert err <= TOL, f"token {t}: max|err|/rms = {err:.3e}"
 
 
 def test_decode_limit_is_an_error():
