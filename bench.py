@@ -568,6 +568,28 @@ def main():
         b.copy_(a)
         torch.cuda.synchronize()
         result["calibration_copy_bytes"] = 2 * 4 * n
+        # the copy's own rate (read + write bytes over its best of five runs):
+        # what a plain streaming kernel sustains on this GPU
+        best = None
+        for _ in range(5):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            b.copy_(a)
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1)
+            best = ms if best is None else min(best, ms)
+        result["calibration_copy_GBps"] = round(2 * 4 * n / (best / 1e3) / 1e9, 1)
+        best = None  # a read-only stream: torch's sum over the same buffer
+        for _ in range(5):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            a.sum()
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1)
+            best = ms if best is None else min(best, ms)
+        result["calibration_read_GBps"] = round(4 * n / (best / 1e3) / 1e9, 1)
         del a, b
     ev.destroy_all()
     if not args.no_cpu_baseline:
