@@ -330,7 +330,13 @@ def capture(calls):
 
 
 def cpu_baseline(setup, budget_s: float):
-    """The oracle, as it stands, on a bounded sample of the same workload."""
+    """The oracle, as it stands, on a bounded sample of the same workload.
+
+    One unit of work is an oracle call of the workload's own shape: a T=1 call
+    per token for the decode workloads, the batched call for the others. Units
+    run until at least half the budget has gone, so the sample takes between
+    budget / 2 and budget / 2 plus one unit. The host keeps layer 0 only: for a
+    layer stack the rate is layer 0's divided by the layer count."""
     import numpy as np
     from oracle import moe as omoe
     cfg = setup.cfg
@@ -342,24 +348,25 @@ def cpu_baseline(setup, budget_s: float):
     except Exception:  # pragma: no cover
         cores = 1
     x = setup.x_host
-    if setup.mode == "decode_stack":
-        # the oracle on layer 0 only (the one layer kept on the host), scaled to
-        # the stack's layer count: tokens through all layers per second
-        n = 4
-        t0 = time.time()
-        omoe.block_for_config(cfg, layer, x[:n])
-        dt = time.time() - t0
-        return dict(value=n / (dt * cfg.layers), unit="tokens/s", cores=cores, kind="oracle",
-                    sample=f"{n} tokens through layer 0 (RMSNorm + MoE) in one fp64 oracle "
-                           f"call ({dt:.1f} s), times {cfg.layers} layers")
-    if setup.mode == "calls":
-        n = 96
-        t0 = time.time()
-        omoe.block_for_config(cfg, layer, x[:n])
-        dt = time.time() - t0
-        return dict(value=n / dt, unit="tokens/s", cores=cores, kind="oracle",
-                    sample=f"first {n} of the {cfg.calls} decode tokens of layer 0, batched in "
-                           f"one fp64 oracle call ({dt:.1f} s)")
+    layers = cfg.layers
+
+    def run_units(unit, tokens_per_unit):
+        n_units, t0 = 0, time.time()
+        while True:
+            unit(n_units)
+            n_units += 1
+            dt = time.time() - t0
+            if dt >= budget_s / 2:
+                return n_units * tokens_per_unit, dt, n_units
+
+    if setup.mode in ("calls", "decode_stack"):
+        ntok = setup.ntok if setup.mode == "decode_stack" else cfg.calls
+        n, dt, _ = run_units(lambda i: omoe.block_for_config(cfg, layer, x[i % ntok:i % ntok + 1]), 1)
+        what = "RMSNorm + MoE " if layer.norm_w is not None else ""
+        scaled = f", divided by {layers} layers" if layers > 1 else ""
+        return dict(value=n / dt / layers, unit="tokens/s", cores=cores, kind="oracle",
+                    sample=f"{n} T=1 fp64 oracle calls ({what}layer 0), one per decode token, "
+                           f"in {dt:.1f} s{scaled}")
     # prefill-type: all T tokens of the first layer if the budget allows, else
     # the first n tokens. The oracle's time goes into dequantising each expert
     # the sample touches (about 0.08 s per expert at H*F = 4096*2048, measured
@@ -375,12 +382,11 @@ def cpu_baseline(setup, budget_s: float):
     while n > 1 and experts_touched(n) * per_expert > budget_s:
         n = int(n * 0.9)
     toks = np.arange(n)
-    t0 = time.time()
-    omoe.block_for_config(cfg, layer, x[:cfg.T], tokens=toks)
-    dt = time.time() - t0
-    return dict(value=n / dt, unit="tokens/s", cores=cores, kind="oracle",
-                sample=f"{n} of {cfg.T} tokens of layer 0 (routing for all {cfg.T}) in one "
-                       f"fp64 oracle call ({dt:.1f} s)")
+    done, dt, calls = run_units(lambda i: omoe.block_for_config(cfg, layer, x[:cfg.T], tokens=toks), n)
+    scaled = f", divided by {layers} layers" if layers > 1 else ""
+    return dict(value=done / dt / layers, unit="tokens/s", cores=cores, kind="oracle",
+                sample=f"{calls} fp64 oracle call(s) of layer 0, each on {n} of {cfg.T} tokens "
+                       f"(routing for all {cfg.T}), in {dt:.1f} s{scaled}")
 
 
 def route_locality(setup) -> dict:
