@@ -175,6 +175,7 @@ def test_library_equals_oracle_on_random_traces(seed):
     idx, w = _random_trace(rng, 50, 3, 4, 16, pool=11)
     _assert_library_equals_oracle(idx, w, 16)
     _assert_library_equals_oracle(idx, w, 16, caps=[3, 1, 16, 7])
+    _assert_library_equals_oracle(idx, w, 16, caps=[])  # adjacency and histogram only
 
 
 def _routed_trace(cfg, P, layers):
