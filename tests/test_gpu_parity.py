@@ -431,6 +431,23 @@ def test_degenerate_token_values(cid, path):
         assert err <= TOL, f"token {t}: max|err|/rms = {err:.3e}"
 
 
+@pytest.mark.parametrize("path", ["decode", "prefill"])
+def test_single_token_norm_rows(path):
+    # T = 1 with an RMSNorm: the router launch's wavefronts compute the norm
+    # scale themselves (no separate launch); every degenerate row on its own
+    cfg = _small(4, T=1, H=256, F=192, E=8, k=4, layers=1)
+    _announce(f"single-token RMSNorm rows {path}")
+    layer = make_layer(cfg)
+    dl = upload(cfg, layer)
+    rows = _degenerate_rows(cfg.H, np.random.default_rng(12))
+    for t in range(rows.shape[0]):
+        x = rows[t:t + 1]
+        out, ro = run_forward(path, shape_of(cfg), dl, torch.from_numpy(x).cuda())
+        err = _check_block(cfg, layer, x, out.cpu().numpy(), to_np(ro))
+        assert np.isfinite(out.cpu().numpy()).all(), t
+        print(f"row {t}: max|err|/rms = {err:.2e}")
+
+
 def test_decode_limit_is_an_error():
     cfg = _small(1, T=65)
     shape = shape_of(cfg)
