@@ -6,7 +6,9 @@
 
 A step is one pass of the whole block over one batch of seeded synthetic
 input (weights and activations resident in HBM before timing):
-  decode  gpt-oss-20b-shaped layer, 1000 tokens as T=1 calls (default)
+  suite   (default) decode as the headline line, with prefill, stack and ds4
+          measured after it and nested under "workloads"
+  decode  gpt-oss-20b-shaped layer, 1000 tokens as T=1 calls
   prefill gpt-oss-20b-shaped layer, T=128, Zipf(1.1)-skewed expert loads
   stack   24 gpt-oss-20b-shaped layers (RMSNorm + MoE), T=512
   ds4     DeepSeek-V4-Flash-shaped layer, T=2048, 256 experts top-6 + shared
@@ -15,10 +17,12 @@ input (weights and activations resident in HBM before timing):
   decode_stack  T=1 tokens through 24 gpt-oss-20b-shaped layers (RMSNorm + MoE),
           16 tokens per step, each layer's output the next layer's input
 Each step's calls are captured once in a HIP graph and replayed; W warm-up
-steps, then exactly K timed steps between two synchronisations. The last
-timed step is launched eagerly with the library's moe_profile_next_launch
-hook armed on every call, so HIP events stamped by the dominant kernel's own
-dispatches give its live average duration for the roofline object. Expert
+steps, then exactly K timed steps between two synchronisations (--steps and
+--warmup set the headline workload's; nested workloads use their own step
+counts). After the timed region, one more step is launched eagerly with the
+library's moe_profile_next_launch hook armed on every call, so HIP events
+stamped by the dominant kernel's own dispatches give its live average
+duration for the roofline object; that step is not part of `value`. Expert
 weights are held in several device copies, cycled between calls, so that the
 256 MB Infinity Cache cannot serve them from one call to the next.
 
@@ -115,6 +119,10 @@ class HipEvents:
         for e in self.made:
             self.lib.hipEventDestroy(ctypes.c_void_p(e))
         self.made = []
+
+
+def pad128(n: int) -> int:
+    return (n + 127) // 128 * 128
 
 
 def source_sha(kernel: str) -> str:
@@ -259,22 +267,25 @@ class Setup:
         return calls
 
     # algorithmic work of the dominant kernel per launch and of the block per step:
-    # the expert weights it must read (codes + scales + biases) plus its
-    # activation operands in and out in the formats it uses (FP8 terms:
-    # 4 codes + 4 scale bytes per 32 values)
+    # the expert weights it must read (codes + scales + biases) of every distinct
+    # expert a call selects, once, plus its activation operands in and out in the
+    # formats it uses (FP8 terms: 4 codes + 4 scale bytes per 32 values)
     def algorithmic(self, counts_per_call):
         cfg = self.cfg
         H, F, k, E = cfg.H, cfg.F, cfg.k, cfg.E
         mat = F * H * 17 // 32            # codes + scales of one [F,H] matrix
-        pad = lambda n: (n + 127) // 128 * 128
-        terms = lambda n: 4 * pad(n) + 4 * pad(n) // 32
+        terms = lambda n: 4 * pad128(n) + 4 * pad128(n) // 32
         if self.spec["kernel"] == "decode_gate_up":
             T = 1 if self.mode in ("calls", "decode_stack") else cfg.T
             routes = T * k + T * cfg.n_shared
+            # T=1: the k selections are distinct experts; batches count them
+            distinct = ([sum(1 for c in counts if c > 0) for counts in counts_per_call]
+                        if counts_per_call else [T * k])
+            active = sum(distinct) / len(distinct) + cfg.n_shared
             splits = (H + 511) // 512    # the router's split-K partials (512-wide slices)
-            byts = routes * 2 * (mat + 4 * F) + T * terms(H) + routes * terms(F) + T * splits * E * 8
+            byts = active * 2 * (mat + 4 * F) + T * terms(H) + routes * terms(F) + T * splits * E * 8
             return dict(bytes=byts, flops=routes * 4 * H * F, units=routes,
-                        unit="route (token, selected expert)")
+                        unit="route (token, selected expert)", active_experts=active)
         # gate/up GEMM: weights of every active expert once, x terms once, act terms out
         T = cfg.T
         active = [sum(1 for c in counts if c > 0) + cfg.n_shared for counts in counts_per_call]
@@ -283,6 +294,36 @@ class Setup:
         return dict(bytes=sum(per) / len(per), flops=4.0 * rows * H * F, units=rows,
                     unit="routed row (token, expert) of the grouped GEMM",
                     active_experts=sum(active) / len(active))
+
+    def issued_flops(self, counts_per_call):
+        """Matrix-core flops the dominant kernel issues per launch, from its
+        structure: every 16x16x128 block-scaled instruction counts
+        2 * 16 * 16 * 128 flops, the zero columns, padded rows and FP8 terms
+        included."""
+        cfg = self.cfg
+        H, F, k = cfg.H, cfg.F, cfg.k
+        per_mfma = 2 * 16 * 16 * 128
+        if self.spec["kernel"] == "decode_gate_up":
+            # per route: F/32 items x 8 wavefronts x their K-steps x 4 tiles;
+            # a wavefront runs rounds of spw steps (steps past K run with a
+            # zero operand but still issue)
+            T = 1 if self.mode in ("calls", "decode_stack") else cfg.T
+            routes = T * k + T * cfg.n_shared
+            ns = pad128(H) // 128
+            spw = min(4, max(1, -(-ns // 8)))
+            steps = sum(spw for w in range(8) for s0 in range(w * spw, ns, 8 * spw))
+            return routes * (F // 32) * steps * 4 * per_mfma
+        # gate/up GEMM: per 16-row group of an expert's rows, every 128-feature
+        # row block of gate and up, every 128-wide K-step, every FP8 term used
+        nt = 3 if cfg.act_dtype == "bf16" and cfg.rms_eps is None else 4
+        nrb = -(-pad128(F) // 128)
+        tot = []
+        for counts in counts_per_call:
+            groups = sum(-(-c // 16) for c in counts)
+            if cfg.n_shared:
+                groups += -(-cfg.T // 16)
+            tot.append(groups * nrb * 4 * 4 * (pad128(H) // 128) * nt * per_mfma)
+        return sum(tot) / len(tot)
 
     def block_bytes_per_step(self, counts_per_call):
         cfg = self.cfg
@@ -299,10 +340,19 @@ class Setup:
 
 
 def route_counts(setup):
-    """Per-call expert histograms of one step (for algorithmic byte counts)."""
+    """Per-call expert histograms of one step (for algorithmic byte counts):
+    every layer of a prefill workload, or the one call of a batched decode."""
     import torch
     mx, cfg = setup.mx, setup.cfg
     res = []
+    if setup.mode == "decode":
+        dl = setup.layers[0]
+        counts = torch.empty(cfg.E, dtype=torch.int32, device="cuda")
+        mx.moe_forward_decode(setup.shape, setup.xd, dl.router_w, dl.router_b, dl.experts_copy(0),
+                              setup.out, setup.ws, norm_w=dl.norm_w, shared=dl.shared_copy(0),
+                              route_out={"counts": counts})
+        torch.cuda.synchronize()
+        return [counts.cpu().tolist()]
     if setup.mode != "prefill":
         return res
     src = setup.xd
@@ -327,6 +377,32 @@ def capture(calls):
         for c in calls:
             c()
     return g
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline_full(setup, budget_s: float) -> dict:
+    """cpu_baseline with the host's CPU model and, for the single-layer
+    gpt-oss workloads, the same oracle with its BLAS held to one thread (on
+    half the budget)."""
+    r = cpu_baseline(setup, budget_s)
+    r["cpu_model"] = cpu_model()
+    r["host_cpus"] = len(os.sched_getaffinity(0))
+    if setup.cfg.config_id in (1, 2, 3):
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1, user_api="blas"):
+            r1 = cpu_baseline(setup, budget_s / 2)
+        r["one_thread"] = {"value": r1["value"], "sample": r1["sample"]}
+    return r
 
 
 def cpu_baseline(setup, budget_s: float):
@@ -419,44 +495,18 @@ def route_locality(setup) -> dict:
     }
 
 
-def main():
-    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=None, help="timed steps (default per workload)")
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", choices=sorted(WORKLOADS), default="decode")
-    ap.add_argument("--copies", type=int, default=None, help="device copies of the expert weights")
-    ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of HIP graphs")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds for the oracle sample")
-    ap.add_argument("--route-profile", action="store_true",
-                    help="record every call's expert selections into a device route profile")
-    ap.add_argument("--route-locality", action="store_true",
-                    help="after timing, one untimed step recording its decode trace, and the "
-                         "trace's expert locality (T=1 workloads)")
-    ap.add_argument("--calibrate-copy-gib", type=float, default=0.0,
-                    help="also run one device copy of this many GiB (PMC byte calibration)")
-    args = ap.parse_args()
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(run with --gpus 1).", file=sys.stderr)
-        sys.exit(2)
-    if args.steps is None:
-        args.steps = WORKLOADS[args.workload]["steps"]
-    if args.steps < 1:
-        sys.exit("--steps must be >= 1")
-    if args.route_locality and args.workload not in ("decode", "decode_stack"):
-        sys.exit("--route-locality needs a T=1 workload (decode, decode_stack)")
+# the default run: the decode headline, then these workloads nested under
+# "workloads" (each with its own step count)
+SUITE = (("prefill", "prefill_T128"), ("stack", "stack_T512"), ("ds4", "ds4"))
 
+
+def measure(wl: str, args, steps: int, warmup: int) -> dict:
+    """Time one workload: K graph-replayed steps, then one instrumented eager
+    step for the dominant kernel's own duration. Frees its device memory."""
     import torch
-    import mxfp4_expert_ffn_amd as mx
-    if not torch.cuda.is_available():
-        sys.exit("no GPU visible")
-    mx._lib.load()
-    torch.cuda.set_device(0)
 
-    setup = Setup(args.workload, args.copies)
-    spec, cfg = setup.spec, setup.cfg
+    setup = Setup(wl, args.copies)
+    spec, cfg, mx = setup.spec, setup.cfg, setup.mx
     ev = HipEvents()
     stream = torch.cuda.current_stream().cuda_stream
 
@@ -471,68 +521,65 @@ def main():
     torch.cuda.synchronize()
 
     kernel = spec["kernel"]
-    last = args.steps - 1
-    last_calls = setup.step_calls(last % ncopies_graph)
-    pairs = [(ev.create(), ev.create()) for _ in last_calls]
+    inst_calls = setup.step_calls(steps % ncopies_graph)
+    pairs = [(ev.create(), ev.create()) for _ in inst_calls]
     graphs = None if args.no_graph else [capture(calls) for calls in plain]
     torch.cuda.synchronize()
 
-    def run_step(s, instrument=False):
-        if instrument:     # eager, timing hook armed on every call of the step
-            for i, c in enumerate(last_calls):
-                mx.moe_profile_next_launch(kernel, pairs[i][0], pairs[i][1])
-                c()
-        elif graphs is None:
+    def run_step(s):
+        if graphs is None:
             for c in plain[s % ncopies_graph]:
                 c()
         else:
             graphs[s % ncopies_graph].replay()
 
-    for s in range(args.warmup):
+    for s in range(warmup):
         run_step(s)
     torch.cuda.synchronize()
     t_start, t_stop = ev.create(), ev.create()
     torch.cuda.synchronize()
     ev.record(t_start, stream)
-    for s in range(args.steps):
-        run_step(s, instrument=(s == last))
+    for s in range(steps):
+        run_step(s)
     ev.record(t_stop, stream)
     torch.cuda.synchronize()
     total_ms = ev.elapsed_ms(t_start, t_stop)
+    # outside the timed region: the dominant kernel's own duration, from HIP
+    # events its dispatches stamp (eager, the hook armed on every call). A few
+    # untimed replays go first, without a synchronisation, so the instrumented
+    # calls queue behind them and run back to back on a busy GPU, as the timed
+    # steps do, rather than one by one behind the host
+    for s in range(3):
+        run_step(steps + s)
+    for i, c in enumerate(inst_calls):
+        mx.moe_profile_next_launch(kernel, pairs[i][0], pairs[i][1])
+        c()
+    torch.cuda.synchronize()
     kern_ms = [ev.elapsed_ms(a, b) for a, b in pairs]
     kern_avg_ms = sum(kern_ms) / len(kern_ms)
-
-    ms_per_step = total_ms / args.steps
-    value = setup.tokens_per_step * args.steps / (total_ms / 1e3)
+    ms_per_step = total_ms / steps
+    value = setup.tokens_per_step * steps / (total_ms / 1e3)
     alg = setup.algorithmic(counts)
+    issued = setup.issued_flops(counts)
     kern_s = kern_avg_ms / 1e3
-    if kernel.startswith("decode"):
+    traffic = traffic_from_profile(kernel, wl)
+    t_hbm = alg["bytes"] / (HBM_PEAK_GBPS * 1e9)
+    t_mfma = alg["flops"] / (FP8_PEAK_TFLOPS * 1e12)
+    if kernel.startswith("decode") or t_hbm >= t_mfma:
         achieved, peak, unit, bound = alg["bytes"] / kern_s / 1e9, HBM_PEAK_GBPS, "GB/s", "hbm"
-        traffic = traffic_from_profile(kernel, args.workload)
     else:
-        t_hbm = alg["bytes"] / (HBM_PEAK_GBPS * 1e9)
-        t_mfma = alg["flops"] / (FP8_PEAK_TFLOPS * 1e12)
-        if t_hbm >= t_mfma:
-            achieved, peak, unit, bound = alg["bytes"] / kern_s / 1e9, HBM_PEAK_GBPS, "GB/s", "hbm"
-        else:
-            achieved, peak, unit, bound = alg["flops"] / kern_s / 1e12, FP8_PEAK_TFLOPS, "TFLOP/s", "mfma"
-        traffic = traffic_from_profile(kernel, args.workload)
+        achieved, peak, unit, bound = alg["flops"] / kern_s / 1e12, FP8_PEAK_TFLOPS, "TFLOP/s", "mfma"
     block_bytes = setup.block_bytes_per_step(counts)
     block_gbps = block_bytes / (ms_per_step / 1e3) / 1e9
+    nominal_tf = alg["flops"] / kern_s / 1e12
+    issued_tf = issued / kern_s / 1e12
 
     result = {
-        "metric": METRIC,
         "value": round(value, 1),
         "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
+        "steps": steps,
+        "warmup": warmup,
         "ms_per_step": round(ms_per_step, 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": DTYPE,
-        "data": "synthetic",
         "config": {
             "workload": spec["name"], "T": int(setup.step_shape.T), "H": cfg.H, "F": cfg.F, "E": cfg.E,
             "k": cfg.k, "n_shared": cfg.n_shared, "layers": cfg.layers,
@@ -549,6 +596,18 @@ def main():
             "algorithmic_bytes_per_launch": int(alg["bytes"]),
             "algorithmic_flops_per_launch": int(alg["flops"]),
             "units_per_launch": alg["units"], "unit_of_work": alg["unit"],
+            "active_experts_per_launch": round(alg["active_experts"], 2),
+            # matrix-core view of the same launch: nominal = the block's own
+            # 4*H*F (gate/up) flops per unit; issued = every instruction the
+            # kernel runs (FP8 terms, zero columns, padded rows)
+            "mfma": {
+                "peak_TFLOPs": FP8_PEAK_TFLOPS, "peak_dtype": "fp8 (fp4 x fp8 scaled MFMA)",
+                "nominal_TFLOPs": round(nominal_tf, 2),
+                "nominal_frac": round(nominal_tf / FP8_PEAK_TFLOPS, 4),
+                "issued_flops_per_launch": int(issued),
+                "issued_TFLOPs": round(issued_tf, 2),
+                "issued_frac": round(issued_tf / FP8_PEAK_TFLOPS, 4),
+            },
         },
         "block": {
             "expert_bytes_per_step": int(block_bytes),
@@ -558,51 +617,117 @@ def main():
     }
     if setup.profile is not None:
         # every executed step recorded T*k selections per layer: the eager
-        # validation pass(es), the warm-up and the timed steps
-        runs = ncopies_graph + args.warmup + args.steps
+        # validation pass(es), the warm-up, the timed steps, the three replays
+        # and the instrumented step after them
+        runs = ncopies_graph + warmup + steps + 3 + 1
         summ = mx.moe_route_profile_summary(setup.profile.cpu().numpy())
         summ["selections_expected"] = runs * setup.tokens_per_step * cfg.k * cfg.layers
         del summ["layer_unique"]
         result["route_profile"] = summ
     if args.route_locality:
         result["route_locality"] = route_locality(setup)
-    if args.calibrate_copy_gib > 0:
-        n = int(args.calibrate_copy_gib * (1 << 30)) // 4
-        a = torch.empty(n, dtype=torch.float32, device="cuda").fill_(1.0)
-        b = torch.empty_like(a)
-        torch.cuda.synchronize()
-        b.copy_(a)
-        torch.cuda.synchronize()
-        result["calibration_copy_bytes"] = 2 * 4 * n
-        # the copy's own rate (read + write bytes over its best of five runs):
-        # what a plain streaming kernel sustains on this GPU
-        best = None
-        for _ in range(5):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-            b.copy_(a)
-            e1.record()
-            torch.cuda.synchronize()
-            ms = e0.elapsed_time(e1)
-            best = ms if best is None else min(best, ms)
-        result["calibration_copy_GBps"] = round(2 * 4 * n / (best / 1e3) / 1e9, 1)
-        best = None  # a read-only stream: torch's sum over the same buffer
-        for _ in range(5):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-            a.sum()
-            e1.record()
-            torch.cuda.synchronize()
-            ms = e0.elapsed_time(e1)
-            best = ms if best is None else min(best, ms)
-        result["calibration_read_GBps"] = round(4 * n / (best / 1e3) / 1e9, 1)
-        del a, b
     ev.destroy_all()
     if not args.no_cpu_baseline:
-        log("[bench] timing the CPU oracle baseline")
-        result["cpu_baseline"] = cpu_baseline(setup, args.cpu_budget)
+        log(f"[bench] {wl}: timing the CPU oracle baseline")
+        result["cpu_baseline"] = cpu_baseline_full(setup, args.cpu_budget)
     else:
         result["cpu_baseline"] = None
+    del graphs, plain, inst_calls, setup
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    log(f"[bench] {wl}: {result['value']:.1f} tokens/s, {kernel} {result['roofline']['frac']:.3f} "
+        f"of {bound} peak")
+    return result
+
+
+def calibrate(result: dict, gib: float):
+    import torch
+    n = int(gib * (1 << 30)) // 4
+    a = torch.empty(n, dtype=torch.float32, device="cuda").fill_(1.0)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    b.copy_(a)
+    torch.cuda.synchronize()
+    result["calibration_copy_bytes"] = 2 * 4 * n
+    # the copy's own rate (read + write bytes over its best of five runs):
+    # what a plain streaming kernel sustains on this GPU
+    best = None
+    for _ in range(5):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        b.copy_(a)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        best = ms if best is None else min(best, ms)
+    result["calibration_copy_GBps"] = round(2 * 4 * n / (best / 1e3) / 1e9, 1)
+    best = None  # a read-only stream: torch's sum over the same buffer
+    for _ in range(5):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        a.sum()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        best = ms if best is None else min(best, ms)
+    result["calibration_read_GBps"] = round(4 * n / (best / 1e3) / 1e9, 1)
+    del a, b
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None, help="timed steps (default per workload)")
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", choices=["suite"] + sorted(WORKLOADS), default="suite")
+    ap.add_argument("--copies", type=int, default=None, help="device copies of the expert weights")
+    ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of HIP graphs")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds for the oracle sample")
+    ap.add_argument("--route-profile", action="store_true",
+                    help="record every call's expert selections into a device route profile")
+    ap.add_argument("--route-locality", action="store_true",
+                    help="after timing, one untimed step recording its decode trace, and the "
+                         "trace's expert locality (T=1 workloads)")
+    ap.add_argument("--calibrate-copy-gib", type=float, default=0.0,
+                    help="also run one device copy of this many GiB (PMC byte calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+    head = "decode" if args.workload == "suite" else args.workload
+    if args.steps is None:
+        args.steps = WORKLOADS[head]["steps"]
+    if args.steps < 1:
+        sys.exit("--steps must be >= 1")
+    if args.route_locality and head not in ("decode", "decode_stack"):
+        sys.exit("--route-locality needs a T=1 workload (decode, decode_stack)")
+    if args.workload == "suite" and args.copies is not None:
+        sys.exit("--copies applies to a single --workload")
+
+    import torch
+    import mxfp4_expert_ffn_amd as mx
+    if not torch.cuda.is_available():
+        sys.exit("no GPU visible")
+    mx._lib.load()
+    torch.cuda.set_device(0)
+
+    r = measure(head, args, args.steps, args.warmup)
+    result = {
+        "metric": METRIC, "value": r.pop("value"), "unit": r.pop("unit"), "n_gpus": 1,
+        "steps": r.pop("steps"), "warmup": r.pop("warmup"), "ms_per_step": r.pop("ms_per_step"),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": DTYPE,
+        "data": "synthetic",
+    }
+    result.update(r)
+    if args.workload == "suite":
+        args.route_locality = False
+        result["workloads"] = {}
+        for wl, key in SUITE:
+            result["workloads"][key] = measure(wl, args, WORKLOADS[wl]["steps"], args.warmup)
+    if args.calibrate_copy_gib > 0:
+        calibrate(result, args.calibrate_copy_gib)
     print(json.dumps(result), flush=True)
 
 

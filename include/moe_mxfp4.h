@@ -25,10 +25,13 @@
  *   and moe_last_error() describes the problem.
  * - Row-major layouts; [A,B] means A rows of B contiguous elements.
  * - Numerics: weights are used exactly as stored. Activations meet them on
- *   the gfx950 block-scaled matrix cores as a sum of 4 FP8 (E4M3) terms per
- *   value with one E8M0 scale per 32 values and term (each value is carried
- *   to within about 2^-16 of its block's largest magnitude); products
- *   accumulate in float32. Router logits are accumulated in float64.
+ *   the gfx950 block-scaled matrix cores as a sum of FP8 (E4M3) terms per
+ *   value with one E8M0 scale per 32 values and term; n terms carry a value
+ *   to within about 2^-4n of its block's largest magnitude. Decode uses four
+ *   terms everywhere; prefill uses four for the expert input (three for a
+ *   bfloat16 input without RMSNorm, which three hold as closely) and three
+ *   for the SwiGLU output. Products accumulate in float32. Router logits are
+ *   accumulated in float64.
  * - Shape limits: 1 <= E <= 512, 1 <= k <= min(E, 8), H and F multiples of
  *   32 and at most 16384, 0 <= T, n_shared in {0, 1}. Decode additionally
  *   needs T <= 64 and H, F <= 8192. With T = 0 a call only validates the
@@ -234,7 +237,12 @@ int moe_pack_experts(const moe_shape *shape, int32_t n, const moe_expert_planes 
 
 /* Device workspace bytes that moe_route / moe_forward_decode /
  * moe_forward_prefill need for this shape (the largest of the three).
- * Returns 0 for an invalid shape. Host only. */
+ * Returns 0 for an invalid shape. Host only. The caller allocates the
+ * workspace once per shape and passes it to every call, so no call allocates
+ * (page: antirez ds4.c keeps every decode temporary in one preallocated
+ * scratch, `ds4_cpu_decode_scratch`, and its allocation guard,
+ * `ds4_alloc_guard_begin` / `_check`, rejects allocations during a guarded
+ * phase). */
 size_t moe_workspace_bytes(const moe_shape *shape);
 
 /* Routing only: optional RMSNorm, router logits in fp64, top-k, route weights,
@@ -281,7 +289,10 @@ int moe_forward_prefill(const moe_shape *shape, const void *hidden, const float 
                         const uint8_t *shared, float *out, const moe_route_out *route_out,
                         void *ws, size_t ws_bytes, hipStream_t stream);
 
-/* Export the weights the kernels compute with, for bit-exact checks.
+/* Export the weights the kernels compute with, for bit-exact checks against
+ * the MXFP4 definition (page: antirez ds4.c `dsv4_e2m1fn_value_cpu`, the
+ * eight E2M1 magnitudes and the sign bit, times the block's power-of-two
+ * scale).
  *   blob   one packed expert, device
  *   which  0 gate [F, H], 1 up [F, H], 2 down [H, F]
  *   path   0: decoded with the gfx950 scaled FP4-to-float32 converts;
@@ -317,7 +328,11 @@ typedef enum moe_kernel_id {
  * Host only; MOE_OK or MOE_ERR_INVALID_ARG. */
 int moe_profile_next_launch(int32_t kernel, hipEvent_t start, hipEvent_t stop);
 
-/* Message of the last failing call on this thread ("" if none). */
+/* Message of the last failing call on this thread ("" if none). Every call
+ * returns a moe_status and leaves its reason here (page: turbospark-runtime
+ * `produce_real_gpt_oss` rejects requests it does not support with a typed
+ * error carrying a message, `RealForwardError::Unsupported`; a C caller gets
+ * MOE_ERR_UNSUPPORTED and this text). */
 const char *moe_last_error(void);
 
 #ifdef __cplusplus

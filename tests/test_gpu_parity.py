@@ -433,8 +433,8 @@ def test_degenerate_token_values(cid, path):
 
 @pytest.mark.parametrize("path", ["decode", "prefill"])
 def test_single_token_norm_rows(path):
-    # T = 1 with an RMSNorm: the router launch's wavefronts compute the norm
-    # scale themselves (no separate launch); every degenerate row on its own
+    # T = 1 with an RMSNorm: rms_inv_kernel computes the token's norm scale,
+    # then the router launch reads it; every degenerate row on its own
     cfg = _small(4, T=1, H=256, F=192, E=8, k=4, layers=1)
     _announce(f"single-token RMSNorm rows {path}")
     layer = make_layer(cfg)
