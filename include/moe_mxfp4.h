@@ -289,6 +289,30 @@ int moe_forward_prefill(const moe_shape *shape, const void *hidden, const float 
                         const uint8_t *shared, float *out, const moe_route_out *route_out,
                         void *ws, size_t ws_bytes, hipStream_t stream);
 
+/* Size of the fixed device scratch of moe_forward_decode_noalloc: 32 MiB per
+ * GPU, enough for every decode shape up to T = 64 at gpt-oss-20b and
+ * DeepSeek-V4-Flash sizes. */
+#define MOE_NOALLOC_SCRATCH_BYTES (32u << 20)
+
+/* moe_forward_decode without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, serving loops and
+ * harnesses that forbid hipMalloc): the workspace is a fixed device array of
+ * MOE_NOALLOC_SCRATCH_BYTES inside the library, one per GPU, held from module
+ * load until the process ends. The call allocates nothing, on the host or the
+ * device; the caller still owns every input and output.
+ *   arguments, layouts, results and errors as for moe_forward_decode
+ *   MOE_ERR_UNSUPPORTED when moe_workspace_bytes(shape) exceeds
+ *       MOE_NOALLOC_SCRATCH_BYTES (checked first, before any device call)
+ * Every call on one GPU shares that GPU's array (nothing in it needs to start
+ * zeroed; each call writes what it reads). Calls that overlap on one GPU -
+ * on different streams, or from different host threads without ordering -
+ * race on it and give undefined results; order them on one stream. The device
+ * is the calling thread's current HIP device, which must own `stream`. */
+int moe_forward_decode_noalloc(const moe_shape *shape, const void *hidden, const float *norm_w,
+                               const float *router_w, const float *router_b,
+                               const uint8_t *experts, const uint8_t *shared, float *out,
+                               const moe_route_out *route_out, hipStream_t stream);
+
 /* Export the weights the kernels compute with, for bit-exact checks against
  * the MXFP4 definition (page: antirez ds4.c `dsv4_e2m1fn_value_cpu`, the
  * eight E2M1 magnitudes and the sign bit, times the block's power-of-two

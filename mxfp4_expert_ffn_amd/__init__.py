@@ -20,6 +20,7 @@ from ._lib import (MOE_BF16, MOE_F32, MoeBlobLayout, MoeExpertPlanes, MoeLocalit
 __all__ = [
     "MoeError", "MoeShape", "make_shape", "moe_blob_layout_get", "moe_pack_experts",
     "moe_workspace_bytes", "moe_route", "moe_forward_decode", "moe_forward_prefill",
+    "moe_forward_decode_noalloc",
     "moe_dequant_debug", "moe_last_error", "moe_profile_next_launch", "moe_route_profile_summary",
     "moe_route_locality", "moe_route_hotlist", "LOCALITY_CACHE_SIZES", "ROUTE_FIELDS",
 ]
@@ -152,6 +153,21 @@ def moe_forward_prefill(shape, hidden, router_w, router_b, experts, out, ws, nor
                         shared=None, route_out=None, stream=None):
     _forward(_lib.load().moe_forward_prefill, shape, hidden, router_w, router_b, experts, out, ws,
              norm_w, shared, route_out, stream)
+
+
+def moe_forward_decode_noalloc(shape, hidden, router_w, router_b, experts, out, norm_w=None,
+                               shared=None, route_out=None, stream=None):
+    """moe_forward_decode with the library's fixed per-GPU scratch as its
+    workspace: no allocation; calls on one GPU must be ordered on one stream."""
+    import torch
+    rc = _lib.load().moe_forward_decode_noalloc(
+        ctypes.byref(shape),
+        _ptr(hidden, "hidden", (torch.float32, torch.bfloat16, torch.int16, torch.uint16)),
+        _ptr(norm_w, "norm_w", torch.float32, optional=True),
+        _ptr(router_w, "router_w", torch.float32), _ptr(router_b, "router_b", torch.float32),
+        _ptr(experts, "experts", torch.uint8), _ptr(shared, "shared", torch.uint8, optional=True),
+        _ptr(out, "out", torch.float32), _route_out(route_out), _stream(stream))
+    _check(rc)
 
 
 def moe_dequant_debug(shape, blob, which: int, path: int, out, stream=None):

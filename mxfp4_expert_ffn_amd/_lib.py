@@ -11,6 +11,7 @@ MOE_ERR_INVALID_ARG = -1
 MOE_ERR_UNSUPPORTED = -2
 MOE_ERR_WORKSPACE = -3
 MOE_ERR_HIP = -4
+MOE_NOALLOC_SCRATCH_BYTES = 32 << 20  # the fixed device scratch per GPU
 MOE_F32 = 0
 MOE_BF16 = 1
 
@@ -64,6 +65,8 @@ SIGNATURES = {
                                           ctypes.POINTER(MoeRouteOut), _P, ctypes.c_size_t, _P]),
     "moe_forward_prefill": (ctypes.c_int, [ctypes.POINTER(MoeShape), _P, _P, _P, _P, _P, _P, _P,
                                            ctypes.POINTER(MoeRouteOut), _P, ctypes.c_size_t, _P]),
+    "moe_forward_decode_noalloc": (ctypes.c_int, [ctypes.POINTER(MoeShape), _P, _P, _P, _P, _P,
+                                                  _P, _P, ctypes.POINTER(MoeRouteOut), _P]),
     "moe_dequant_debug": (ctypes.c_int, [ctypes.POINTER(MoeShape), _P, ctypes.c_int32,
                                          ctypes.c_int32, _P, _P]),
     "moe_profile_next_launch": (ctypes.c_int, [ctypes.c_int32, _P, _P]),

@@ -26,7 +26,8 @@ FLAGS = [
     "-Wno-unused-command-line-argument",
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]
-SOURCES = ["route.hip", "decode.hip", "prefill.hip", "dequant.hip", "api.cpp", "locality.cpp"]
+SOURCES = ["route.hip", "decode.hip", "prefill.hip", "dequant.hip", "noalloc.hip", "api.cpp",
+           "locality.cpp"]
 
 
 def hipcc() -> str:

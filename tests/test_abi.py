@@ -190,3 +190,24 @@ def test_dequant_debug_rejects_bad_arguments():
     assert lib.moe_dequant_debug(ctypes.byref(s), FAKE, 3, 0, FAKE, None) == _lib.MOE_ERR_INVALID_ARG
     assert lib.moe_dequant_debug(ctypes.byref(s), FAKE, 0, 3, FAKE, None) == _lib.MOE_ERR_INVALID_ARG
     assert lib.moe_dequant_debug(ctypes.byref(s), FAKE + 8, 0, 0, FAKE, None) == _lib.MOE_ERR_INVALID_ARG
+
+
+def test_noalloc_decode_rejects_shapes_past_its_scratch():
+    # the size check runs before any device call, so it holds without a GPU
+    lib = _lib.load()
+    big = mx.make_shape(T=64, H=8192, F=8192, E=512, k=8, n_shared=1)
+    assert mx.moe_workspace_bytes(big) > _lib.MOE_NOALLOC_SCRATCH_BYTES
+    rc = lib.moe_forward_decode_noalloc(ctypes.byref(big), None, None, None, None, None, None, None,
+                                        None, None)
+    assert rc == _lib.MOE_ERR_UNSUPPORTED
+    assert "MOE_NOALLOC_SCRATCH_BYTES" in mx.moe_last_error()
+    bad = mx.make_shape(T=1, H=100, F=64, E=4, k=2)  # H not a multiple of 32
+    assert lib.moe_forward_decode_noalloc(ctypes.byref(bad), None, None, None, None, None, None,
+                                          None, None, None) == _lib.MOE_ERR_INVALID_ARG
+
+
+def test_noalloc_scratch_covers_the_decode_workloads():
+    for cid in (1, 2, 4, 5):
+        cfg = config_by_id(cid)
+        s = mx.make_shape(**cfg.shape_kwargs(64 if cid != 1 else cfg.T))
+        assert mx.moe_workspace_bytes(s) <= _lib.MOE_NOALLOC_SCRATCH_BYTES, cid
