@@ -4,7 +4,9 @@ from __future__ import annotations
 import ctypes
 import os
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_mxfp4.so")
+# the in-tree build; MOE_MXFP4_LIB names another build of the same sources
+LIB_PATH = os.environ.get("MOE_MXFP4_LIB") or os.path.join(
+    os.path.dirname(os.path.abspath(__file__)), "libmoe_mxfp4.so")
 
 MOE_OK = 0
 MOE_ERR_INVALID_ARG = -1

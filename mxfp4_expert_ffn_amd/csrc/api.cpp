@@ -194,6 +194,9 @@ int launch(int id, const char *what, hipStream_t st, Fn &&fn) {
     (void)st;
     const bool armed = g_hook.kernel == id;
     if (armed) moe::launch_events() = moe::LaunchEvents{g_hook.start, g_hook.stop};
+    // the check after the launch reads the thread's last HIP error: drop one
+    // left by an earlier, unrelated call so it is not taken for this launch's
+    (void)hipGetLastError();
     const int rc = hip_check(fn(), what);
     if (armed) {
         moe::launch_events() = moe::LaunchEvents{};

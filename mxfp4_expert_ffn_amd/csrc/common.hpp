@@ -127,17 +127,24 @@ __device__ __forceinline__ float swiglu(float g, float u, float alpha, float lim
 // ---------------------------------------------------------------- top-k
 // Logits of one token for the lane's experts e = lane + 64q (q < NQ, so
 // E <= 64 NQ): the router's split-K partial sums (partial[s][t][e], fp64)
-// added in split order, plus the bias; experts >= E get -inf. The loads of
-// each group of kGatherUnroll splits are issued together (indices clamped,
-// extra values masked) so the gather costs one memory round trip per group.
+// plus the bias; experts >= E get -inf. The partials are added in the one
+// order every top-k of the library uses: four running sums over the splits
+// s = c, c + 4, c + 8, ... (c = 0..3), each in increasing s, combined as
+// ((sum0 + sum1) + sum2) + sum3, then the bias (the workgroup top-k has
+// wavefront c make sum c). The loads of each group of kGatherUnroll splits
+// are issued together (indices clamped, extra values masked) so the gather
+// costs one memory round trip per group.
 constexpr int kGatherUnroll = 8;
+static_assert(kGatherUnroll % 4 == 0, "a group keeps each split in its residue class");
 template <int NQ>
 __device__ __forceinline__ void gather_logits(const double *partial, int S, int T, int t, int E,
                                               const float *bias, double (&v)[kMaxQ]) {
     const int lane = threadIdx.x & (kWave - 1);
-    double acc[NQ];
+    double acc[4][NQ];
 #pragma unroll
-    for (int q = 0; q < NQ; ++q) acc[q] = 0.0;
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) acc[c][q] = 0.0;
     for (int s0 = 0; s0 < S; s0 += kGatherUnroll) {
         double part[kGatherUnroll][NQ];
 #pragma unroll
@@ -150,13 +157,16 @@ __device__ __forceinline__ void gather_logits(const double *partial, int S, int 
         for (int i = 0; i < kGatherUnroll; ++i)
 #pragma unroll
             for (int q = 0; q < NQ; ++q)
-                if (s0 + i < S) acc[q] += part[i][q];
+                if (s0 + i < S) acc[i & 3][q] += part[i][q];
     }
 #pragma unroll
     for (int q = 0; q < kMaxQ; ++q) {
         const int e = lane + kWave * q;
-        v[q] = (q < NQ && e < E) ? acc[q < NQ ? q : 0] + static_cast<double>(bias[min(e, E - 1)])
-                                 : -INFINITY;
+        const int qq = q < NQ ? q : 0;
+        v[q] = (q < NQ && e < E)
+                   ? ((acc[0][qq] + acc[1][qq]) + acc[2][qq]) + acc[3][qq] +
+                         static_cast<double>(bias[min(e, E - 1)])
+                   : -INFINITY;
     }
 }
 

@@ -15,8 +15,9 @@ constexpr int kTerms = 4;  // FP8 terms per activation on the block-scaled matri
 
 // Grouped GEMMs: tiles of 16 or 32 routed rows of one expert
 // (gemm_tile_rows), which the permutation's tile prefix also uses.
-// Decode GEMVs: 32 weight rows per workgroup, K split over 8 wavefronts.
-constexpr int kDecodeRows = 32;
+// Decode GEMVs: 8 wavefronts per workgroup; gate/up takes 32 weight rows of
+// one route, K split over the wavefronts; down takes 16 output rows of one
+// token over all its routes.
 constexpr int kDecodeWaves = 8;
 
 // Packed MXFP4 plane of `rows` x K weights (rows and K multiples of 32), as
@@ -51,6 +52,14 @@ template <typename Kernel, typename... Args>
 inline void launch_kernel(Kernel kernel, dim3 grid, dim3 block, hipStream_t s, Args... args) {
     const LaunchEvents &ev = launch_events();
     hipExtLaunchKernelGGL(kernel, grid, block, 0, s, ev.start, ev.stop, 0, args...);
+}
+
+// Same with `shm` bytes of dynamic LDS.
+template <typename Kernel, typename... Args>
+inline void launch_kernel_shm(Kernel kernel, dim3 grid, dim3 block, size_t shm, hipStream_t s,
+                              Args... args) {
+    const LaunchEvents &ev = launch_events();
+    hipExtLaunchKernelGGL(kernel, grid, block, shm, s, ev.start, ev.stop, 0, args...);
 }
 
 struct ExpertPtrs {
@@ -123,8 +132,9 @@ hipError_t launch_permute(const int32_t *idx, int T, int E, int k, int n_shared,
 
 // decode (T <= 64) -----------------------------------------------------------
 // Route r < T*k is slot r % k of token r / k; r >= T*k is the shared expert of
-// token r - T*k. act_q / act_s: FP8 terms of the SwiGLU output per route,
-// [routes][kTerms][pad128(F)] codes and [routes][kTerms][pad128(F)/32] scales.
+// token r - T*k. act_q / act_s: FP8 terms of the SwiGLU output times the
+// route weight, per route, [routes][kTerms][pad128(F)] codes and
+// [routes][kTerms][pad128(F)/32] scales.
 // Every gate/up workgroup selects its token's experts itself (top-k of the
 // router's partial logits); slot 0's first feature block writes idx / wts and
 // the optional exports.
@@ -145,7 +155,8 @@ struct DecodeArgs {
     float *out;
     uint8_t *act_q, *act_s;
 };
-// gate/up (which also selects the experts), then down; both after
+// gate/up (which also selects the experts), then down, which adds every route
+// of a token into out in a fixed order (one writer per element); both after
 // launch_router, whose quantisation seeds out with the residual (RouteIn::seed)
 // unless out already is the float32 input.
 hipError_t launch_decode_gate_up(const DecodeArgs &a, hipStream_t s);

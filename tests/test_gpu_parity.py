@@ -495,3 +495,62 @@ def test_prefill_routing_is_deterministic():
     b = to_np(run_forward("prefill", shape_of(c2), dl, torch.from_numpy(x).cuda())[1])
     for k in a:
         assert a[k].tobytes() == b[k].tobytes(), k
+
+
+@pytest.mark.parametrize("T", [1, 8, 40])
+def test_route_and_decode_select_alike(T):
+    """moe_route and moe_forward_decode add the router's split-K partials in
+    one order, so they select the same experts with the same weights, also at
+    fp64 near-ties: each expert has a twin whose router row is a permutation
+    of its own, and the tokens are constant rows, so twins' logits are equal
+    in exact arithmetic and differ only by the rounding of their partial sums.
+    T = 40 takes the tiled router in both."""
+    _announce(f"route vs decode selections, T={T}")
+    H, F, E, k = 2880, 64, 32, 4
+    rng = np.random.default_rng(31 + T)
+    rw = rng.normal(0.0, 0.05, size=(E, H)).astype(np.float32)
+    for e in range(E // 2):
+        rw[e + E // 2] = rw[e][rng.permutation(H)]
+    half = rng.normal(0.0, 0.5, size=E // 2)
+    rb = np.concatenate([half, half]).astype(np.float32)   # twins share their bias
+    x = (rng.normal(0.0, 1.0, size=(T, 1)) * np.ones((1, H))).astype(np.float32)
+    cfg = scaled(config_by_id(2), T=T, H=H, F=F, E=E, k=k)
+    layer = make_layer(cfg)
+    layer.router_w, layer.router_b = rw, rb
+    dl = upload(cfg, layer)
+    shape = shape_of(cfg)
+    xd = torch.from_numpy(x).cuda()
+    ro_r, ro_d = route_buffers(T, k, E), route_buffers(T, k, E)
+    mx.moe_route(shape, xd, dl.router_w, dl.router_b, ro_r, workspace(shape))
+    out = torch.empty_like(xd)
+    mx.moe_forward_decode(shape, xd, dl.router_w, dl.router_b, dl.experts_copy(0), out,
+                          workspace(shape), route_out=ro_d)
+    torch.cuda.synchronize()
+    assert torch.equal(ro_r["topk_idx"], ro_d["topk_idx"])
+    assert torch.equal(ro_r["topk_w"], ro_d["topk_w"])
+    for f in ("counts", "offsets", "perm", "inv"):
+        assert torch.equal(ro_r[f], ro_d[f]), f
+    ref = omoe.top_k(omoe.router_logits(x, rw, rb), k)
+    # the oracle sums in another order: away from certified near-ties it agrees
+    check_routing(ro_d["topk_idx"].cpu().numpy(), ro_d["topk_w"].cpu().numpy(),
+                  dict(logits=omoe.router_logits(x, rw, rb), idx=ref,
+                       w=omoe.route_weights(omoe.router_logits(x, rw, rb), ref, 1.0), xn=x),
+                  rw, rb, 1.0, max_flips=T)
+
+
+@pytest.mark.parametrize("cid,T", [(2, 1), (5, 8)])
+def test_decode_is_deterministic(cid, T):
+    """Every route of a token is added by one workgroup in a fixed order: two
+    runs give the same bits."""
+    cfg = config_by_id(cid)
+    if cid == 5:
+        cfg = scaled(cfg, E=32)
+    _announce(f"decode determinism config {cid} T={T}")
+    layer = make_layer(cfg)
+    x, xb = make_activations(cfg, rows=T)
+    dl = upload(cfg, layer)
+    shape = shape_of(cfg, T)
+    xd = device_input(cfg, x, xb)
+    a, _ = run_forward("decode", shape, dl, xd)
+    b, _ = run_forward("decode", shape, dl, xd)
+    assert torch.equal(a, b)
