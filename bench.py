@@ -313,16 +313,18 @@ class Setup:
             spw = min(4, max(1, -(-ns // 8)))
             steps = sum(spw for w in range(8) for s0 in range(w * spw, ns, 8 * spw))
             return routes * (F // 32) * steps * 4 * per_mfma
-        # gate/up GEMM: per 16-row group of an expert's rows, every 128-feature
-        # row block of gate and up, every 128-wide K-step, every FP8 term used
-        nt = 3 if cfg.act_dtype == "bf16" and cfg.rms_eps is None else 4
-        nrb = -(-pad128(F) // 128)
+        # gate/up GEMM (the library's plan for this shape): per 16-row group of
+        # an expert's rows, every gate and up weight tile of every feature block
+        # of a work item, every 128-wide K-step, every FP8 term used
+        plan = self.mx.moe_prefill_plan(self.shape, with_norm=cfg.rms_eps is not None)
+        nt, fwg = plan["x_terms"], plan["gate_up_features"]
+        tiles = -(-pad128(F) // fwg) * (2 * fwg // 16)
         tot = []
         for counts in counts_per_call:
             groups = sum(-(-c // 16) for c in counts)
             if cfg.n_shared:
                 groups += -(-cfg.T // 16)
-            tot.append(groups * nrb * 4 * 4 * (pad128(H) // 128) * nt * per_mfma)
+            tot.append(groups * tiles * (pad128(H) // 128) * nt * per_mfma)
         return sum(tot) / len(tot)
 
     def block_bytes_per_step(self, counts_per_call):

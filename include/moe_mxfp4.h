@@ -28,10 +28,10 @@
  *   the gfx950 block-scaled matrix cores as a sum of FP8 (E4M3) terms per
  *   value with one E8M0 scale per 32 values and term; n terms carry a value
  *   to within about 2^-4n of its block's largest magnitude. Decode uses four
- *   terms everywhere; prefill uses four for the expert input (three for a
- *   bfloat16 input without RMSNorm, which three hold as closely) and three
- *   for the SwiGLU output. Products accumulate in float32. Router logits are
- *   accumulated in float64.
+ *   terms everywhere; prefill uses three for the SwiGLU output and, for the
+ *   expert input, four on 16-row tiles and three on larger tiles or for a
+ *   bfloat16 input without RMSNorm (moe_prefill_plan tells which). Products
+ *   accumulate in float32. Router logits are accumulated in float64.
  * - Shape limits: 1 <= E <= 512, 1 <= k <= min(E, 8), H and F multiples of
  *   32 and at most 16384, 0 <= T, n_shared in {0, 1}. Decode additionally
  *   needs T <= 64 and H, F <= 8192. With T = 0 a call only validates the
@@ -312,6 +312,22 @@ int moe_forward_decode_noalloc(const moe_shape *shape, const void *hidden, const
                                const float *router_w, const float *router_b,
                                const uint8_t *experts, const uint8_t *shared, float *out,
                                const moe_route_out *route_out, hipStream_t stream);
+
+/* How moe_forward_prefill tiles its grouped GEMMs for a shape (host only; for
+ * profilers and benchmarks that count the matrix-core work a call issues).
+ *   with_norm   nonzero when the call passes an RMSNorm weight
+ * Fills *plan; MOE_OK or MOE_ERR_INVALID_ARG (bad shape, NULL plan).
+ * Page: goosedump `mixture_of_experts_batch` groups a batch's routed rows by
+ * expert (`routes_by_expert`) and runs each expert over its rows; the plan is
+ * this library's tiling of those per-expert row groups. */
+typedef struct moe_prefill_plan_t {
+    int32_t tile_rows;         /* routed rows of one expert per tile: 16, 32 or 64 */
+    int32_t x_terms;           /* FP8 terms of the expert input in the gate/up products */
+    int32_t act_terms;         /* FP8 terms of the SwiGLU output in the down products */
+    int32_t gate_up_features;  /* features (gate and up rows each) per gate/up work item */
+    int32_t down_rows;         /* hidden rows per down work item */
+} moe_prefill_plan_t;
+int moe_prefill_plan(const moe_shape *shape, int32_t with_norm, moe_prefill_plan_t *plan);
 
 /* Export the weights the kernels compute with, for bit-exact checks against
  * the MXFP4 definition (page: antirez ds4.c `dsv4_e2m1fn_value_cpu`, the

@@ -20,7 +20,7 @@ from ._lib import (MOE_BF16, MOE_F32, MoeBlobLayout, MoeExpertPlanes, MoeLocalit
 __all__ = [
     "MoeError", "MoeShape", "make_shape", "moe_blob_layout_get", "moe_pack_experts",
     "moe_workspace_bytes", "moe_route", "moe_forward_decode", "moe_forward_prefill",
-    "moe_forward_decode_noalloc",
+    "moe_forward_decode_noalloc", "moe_prefill_plan",
     "moe_dequant_debug", "moe_last_error", "moe_profile_next_launch", "moe_route_profile_summary",
     "moe_route_locality", "moe_route_hotlist", "LOCALITY_CACHE_SIZES", "ROUTE_FIELDS",
 ]
@@ -168,6 +168,14 @@ def moe_forward_decode_noalloc(shape, hidden, router_w, router_b, experts, out, 
         _ptr(experts, "experts", torch.uint8), _ptr(shared, "shared", torch.uint8, optional=True),
         _ptr(out, "out", torch.float32), _route_out(route_out), _stream(stream))
     _check(rc)
+
+
+def moe_prefill_plan(shape, with_norm: bool = False) -> dict:
+    """The grouped GEMMs' tiling and FP8 term counts moe_forward_prefill uses
+    for this shape (host only)."""
+    p = _lib.MoePrefillPlan()
+    _check(_lib.load().moe_prefill_plan(ctypes.byref(shape), int(bool(with_norm)), ctypes.byref(p)))
+    return {name: getattr(p, name) for name, _ in p._fields_}
 
 
 def moe_dequant_debug(shape, blob, which: int, path: int, out, stream=None):

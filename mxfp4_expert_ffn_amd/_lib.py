@@ -48,6 +48,11 @@ class MoeRouteOut(ctypes.Structure):
         "topk_idx", "topk_w", "counts", "offsets", "perm", "inv", "route_counts")]
 
 
+class MoePrefillPlan(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "tile_rows", "x_terms", "act_terms", "gate_up_features", "down_rows")]
+
+
 class MoeLocalityOut(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
         "hist", "weight_hist", "cache_hits", "cache_weight_hits", "adjacent_pairs",
@@ -69,6 +74,8 @@ SIGNATURES = {
                                            ctypes.POINTER(MoeRouteOut), _P, ctypes.c_size_t, _P]),
     "moe_forward_decode_noalloc": (ctypes.c_int, [ctypes.POINTER(MoeShape), _P, _P, _P, _P, _P,
                                                   _P, _P, ctypes.POINTER(MoeRouteOut), _P]),
+    "moe_prefill_plan": (ctypes.c_int, [ctypes.POINTER(MoeShape), ctypes.c_int32,
+                                        ctypes.POINTER(MoePrefillPlan)]),
     "moe_dequant_debug": (ctypes.c_int, [ctypes.POINTER(MoeShape), _P, ctypes.c_int32,
                                          ctypes.c_int32, _P, _P]),
     "moe_profile_next_launch": (ctypes.c_int, [ctypes.c_int32, _P, _P]),

@@ -250,6 +250,11 @@ int route_front(const moe_shape *s, const void *x, const float *norm_w, const fl
     return MOE_OK;
 }
 
+// The grouped GEMMs' tiling and term counts for this call.
+moe::GemmPlan gemm_plan_of(const moe_shape *s, bool norm) {
+    return moe::gemm_plan(s->T, s->k, s->E, s->n_shared, s->F, s->act_dtype == MOE_BF16 && !norm);
+}
+
 // Upper bound on the grouped GEMMs' row tiles (the grid is sized by it).
 int max_tiles(const moe_shape *s, int bm) {
     const long long R = static_cast<long long>(s->T) * s->k;
@@ -439,7 +444,8 @@ int moe_forward_prefill(const moe_shape *s, const void *hidden, const float *nor
                                 w.idx, w.wts, ro ? ro->topk_idx : nullptr,
                                 ro ? ro->topk_w : nullptr, st);
     }));
-    const int bm = moe::gemm_tile_rows(s->T, s->k, s->E, s->n_shared);
+    const moe::GemmPlan plan = gemm_plan_of(s, norm_w != nullptr);
+    const int bm = plan.tile_rows;
     const moe::TermsOut tq{w.xq, w.xs};
     MOE_TRY(launch(MOE_KERNEL_PERMUTE, "permute", st, [&] {
         return moe::launch_permute(w.idx, s->T, s->E, s->k, s->n_shared, bm, w.counts, w.offsets,
@@ -453,10 +459,8 @@ int moe_forward_prefill(const moe_shape *s, const void *hidden, const float *nor
     const moe::SwigluConsts c{s->swiglu_alpha, s->swiglu_limit, s->swiglu_up_offset};
     const int mt = max_tiles(s, bm);
     MOE_TRY(launch(MOE_KERNEL_GATE_UP_GEMM, "gate_up_gemm", st, [&] {
-        // a bfloat16 input (no RMSNorm in between) needs only three FP8 terms
-        const int x_terms = s->act_dtype == MOE_BF16 && !norm_w ? 3 : moe::kTerms;
         return moe::launch_gate_up_gemm(w.xq, w.xs, s->T, s->H, s->F, s->E, s->k, s->n_shared, ex,
-                                        sh, c, w.offsets, w.perm, w.mprefix, bm, mt, x_terms,
+                                        sh, c, w.offsets, w.perm, w.mprefix, bm, mt, plan.x_terms,
                                         w.act_q, w.act_s, st);
     }));
     MOE_TRY(launch(MOE_KERNEL_DOWN_GEMM, "down_gemm", st, [&] {
@@ -467,6 +471,18 @@ int moe_forward_prefill(const moe_shape *s, const void *hidden, const float *nor
         return moe::launch_combine(w.y, w.inv, s->T, s->H, s->k, s->n_shared, hidden,
                                    s->act_dtype == MOE_BF16, out, st);
     }));
+    return ok();
+}
+
+int moe_prefill_plan(const moe_shape *s, int32_t with_norm, moe_prefill_plan_t *plan) {
+    MOE_TRY(check_shape(s));
+    if (!plan) return fail(MOE_ERR_INVALID_ARG, "plan must be non-NULL");
+    const moe::GemmPlan p = gemm_plan_of(s, with_norm != 0);
+    plan->tile_rows = p.tile_rows;
+    plan->x_terms = p.x_terms;
+    plan->act_terms = p.act_terms;
+    plan->gate_up_features = p.gate_up_features;
+    plan->down_rows = p.down_rows;
     return ok();
 }
 

@@ -13,8 +13,8 @@ constexpr int kMaxE = 512; // routed experts (DeepSeek-V4-Pro has 384)
 constexpr int kMaxQ = kMaxE / 64;  // experts per lane in a wavefront's top-k
 constexpr int kTerms = 4;  // FP8 terms per activation on the block-scaled matrix cores
 
-// Grouped GEMMs: tiles of 16 or 32 routed rows of one expert
-// (gemm_tile_rows), which the permutation's tile prefix also uses.
+// Grouped GEMMs: tiles of 16, 32 or 64 routed rows of one expert
+// (gemm_plan), which the permutation's tile prefix also uses.
 // Decode GEMVs: 8 wavefronts per workgroup; gate/up takes 32 weight rows of
 // one route, K split over the wavefronts; down takes 16 output rows of one
 // token over all its routes.
@@ -165,10 +165,19 @@ hipError_t launch_decode_down(const DecodeArgs &a, hipStream_t s);
 // prefill (any T) -------------------------------------------------------------
 // Rows in expert order: position p < T*k is route perm[p]; p >= T*k is the
 // shared expert of token p - T*k. act_q / act_s are indexed by p. tile_rows
-// (16 or 32) comes from gemm_tile_rows, max_tiles bounds the tile count.
-int gemm_tile_rows(int T, int k, int E, int n_shared);
-// x_terms: FP8 terms of the expert input that take part, 3 or kTerms (three
-// carry a bfloat16 input as closely as four; a float32 one needs four).
+// (16, 32 or 64) and x_terms come from gemm_plan, max_tiles bounds the tile
+// count.
+struct GemmPlan {
+    int tile_rows;         // activation rows per tile
+    int x_terms;           // FP8 terms of the expert input that take part (3 or kTerms)
+    int act_terms;         // FP8 terms of the SwiGLU output that take part
+    int gate_up_features;  // features per gate/up workgroup
+    int down_rows;         // hidden rows per down workgroup
+};
+// x_bf16_exact: the expert input is a bfloat16 value (no RMSNorm in between),
+// which three terms carry as closely as four.
+GemmPlan gemm_plan(int T, int k, int E, int n_shared, int F, bool x_bf16_exact);
+// x_terms: FP8 terms of the expert input that take part, 3 or kTerms.
 hipError_t launch_gate_up_gemm(const uint8_t *xq, const uint8_t *xs, int T, int H, int F, int E,
                                int k, int n_shared, const ExpertPtrs &ex, const ExpertPtrs &sh,
                                SwigluConsts c, const int32_t *offsets, const int32_t *perm,

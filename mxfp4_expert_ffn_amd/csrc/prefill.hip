@@ -54,9 +54,12 @@ struct Geo {
     static constexpr int kDownRows = W * 16 * NA;          // hidden rows per down workgroup
     // K-steps of A fragments in flight: 3 for 32-row tiles; 2 for 16-row
     // tiles (at most 128 VGPRs: four workgroups per CU, which beats three
-    // with a deeper ring)
+    // with a deeper ring) and for 64-row tiles
     static constexpr int kASlots = NG == 2 ? 3 : 2;
-    static_assert(NG == 1 || NG == 2, "16- or 32-row tiles");
+    // K-steps of B staged ahead in registers: 2, or 1 for 64-row tiles (a
+    // step of their B is 128 bytes per thread)
+    static constexpr int kBAhead = NG == 4 ? 1 : 2;
+    static_assert(NG == 1 || NG == 2 || NG == 4, "16-, 32- or 64-row tiles");
     static_assert(kPieces % kThreads == 0, "B staging divides evenly");
     static_assert(kScales <= kThreads, "one scale dword per thread at most");
     static_assert(kGateUpRows % 32 == 0, "gate/up blocks hold whole 32-feature MX blocks");
@@ -220,7 +223,58 @@ __device__ __forceinline__ void gemm_mainloop(const uint8_t *const (&aq)[NA],
     };
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
-    if constexpr (Gm::kASlots == 3) {
+    if constexpr (Gm::kBAhead == 1) {
+        // one B slot, refilled for the next step right after its data is in
+        // LDS; the A ring as for 16-row tiles
+        auto step1 = [&](auto lbuf, BSlot &bsl, ASlot &asl, int s) __attribute__((always_inline)) {
+            constexpr int L = decltype(lbuf)::value;
+            uint8_t *buf = sB + L * Gm::kBufBytes;
+            uint8_t *sbuf = sBs + L * 4 * Gm::kScales;
+#pragma unroll
+            for (int i = 0; i < Gm::kPerThread; ++i)
+                *reinterpret_cast<u32x4_t *>(buf + 16 * (tid + kThreads * i)) = bsl.b[i];
+            if (sc_on) {
+#pragma unroll
+                for (int h = 0; h < 4; ++h) sbuf[sdst + h * Gm::kRows] = static_cast<uint8_t>(bsl.s >> (8 * h));
+            }
+            fill_b(bsl, s + 1);
+            __syncthreads();
+            if (s < NS) {  // uniform; no loads inside
+#pragma unroll
+                for (int g = 0; g < NG; ++g) {
+                    if (g < ngroups) {  // uniform: row groups the tile fills
+                        // one term's B at a time: the other wavefront on the
+                        // SIMD covers the LDS latency, and the registers stay
+                        // within two wavefronts per SIMD
+#pragma unroll
+                        for (int t = 0; t < NT; ++t) {
+                            const int pc = ((t * NG + g) * 8 + kh) * 16 + col;
+                            const uint4 blo = *reinterpret_cast<const uint4 *>(buf + 16 * pc);
+                            const uint4 bhi = *reinterpret_cast<const uint4 *>(buf + 16 * (pc + 64));
+                            const uint32_t bsc = sbuf[(t * 4 + kh) * Gm::kRows + 16 * g + col];
+#pragma unroll
+                            for (int j = 0; j < NA; ++j)
+                                acc[j][g] = mx_mfma(asl.a[j], blo, bhi, bsc, acc[j][g]);
+                            __builtin_amdgcn_sched_barrier(0);
+                        }
+                    }
+                }
+            }
+            fill_a(asl, s + Gm::kASlots);
+        };
+        ASlot a0, a1;
+        BSlot b0;
+        fill_b(b0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        fill_a(a0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        fill_a(a1, 1);
+        __builtin_amdgcn_sched_barrier(0);
+        for (int s0 = 0; s0 < NS; s0 += 2) {
+            step1(I0{}, b0, a0, s0);
+            step1(I1{}, b0, a1, s0 + 1);
+        }
+    } else if constexpr (Gm::kASlots == 3) {
         ASlot a0, a1, a2;
         BSlot b0, b1;
         fill_a(a0, 0);
@@ -268,7 +322,7 @@ __device__ __forceinline__ void load_pre(const int32_t *mprefix, int G, int *s_p
 // NT terms of the expert input take part.
 // 16-row tiles are held to 4 wavefronts per SIMD (128 VGPRs, no spills).
 template <int NG, int W, int NA, int NT>
-__global__ __launch_bounds__(64 * W, NG == 1 ? 4 : 2) void gate_up_gemm_kernel(
+__global__ __launch_bounds__(64 * W, NG == 1 ? 4 : (W == 4 ? 2 : 1)) void gate_up_gemm_kernel(
     const uint8_t *xq, const uint8_t *xs, int T, int H, int F, int E, int k, int n_shared,
     ExpertPtrs ex, ExpertPtrs sh, SwigluConsts sc, const int32_t *offsets, const int32_t *perm,
     const int32_t *mprefix, uint8_t *act_q, uint8_t *act_s) {
@@ -487,6 +541,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const float *y, const int3
     *reinterpret_cast<float4 *>(out + static_cast<size_t>(t) * H + h) = a;
 }
 
+
 int items(int nrb, int max_tiles) {
     const long long n = static_cast<long long>(nrb) * max_tiles;
     return static_cast<int>((n + kXcds - 1) / kXcds * kXcds);
@@ -494,19 +549,39 @@ int items(int nrb, int max_tiles) {
 
 }  // namespace
 
-// 16-row tiles, at four workgroups per CU, up to 96 rows per expert on
-// average (measured faster than 32-row tiles at 16, 56 and 64 rows per
-// expert: the T=128 layer, the DS4-shaped layer, the 24-layer stack); 32-row
-// tiles above, where the weights' re-reads per tile dominate. (64-row tiles
-// measured slower on every workload: with 2 A fragments per wavefront their
-// LDS reads of B hit the LDS limit; with 4 their registers allow one
-// wavefront per SIMD.)
-int gemm_tile_rows(int T, int k, int E, int n_shared) {
-    const double avg = static_cast<double>(T) * (k + n_shared) / (E + n_shared);
-    return avg > 96.0 ? 32 : 16;
+// Tile rows and input terms of the grouped GEMMs for a shape, from the
+// average rows per group (an expert's routes, or the shared expert's T rows)
+// and the work items a tile size makes (tiles x weight-row blocks):
+//  - 64-row tiles (8 wavefronts, 256 features per gate/up workgroup) when
+//    groups average at least 30 rows and the items fill the GPU about eight
+//    times over: each weight fragment feeds up to 4 row groups, so an expert's
+//    weights stream once (DeepSeek-V4 Flash 1.91 -> 1.58 ms per layer, Pro
+//    5.54 -> 4.99 ms); with few items the last round runs mostly empty (the
+//    24-layer stack: 7.46 -> 8.71 ms);
+//  - 32-row tiles (8 wavefronts) from 24 rows on average (the stack, 64 rows
+//    per expert: 7.46 -> 6.98 ms);
+//  - 16-row tiles (4 wavefronts, four per CU) below (the T = 128 layer).
+// Tiles of 32 rows and more take three FP8 terms of the expert input (a
+// fourth does not fit two wavefronts' registers per SIMD at 64 rows and was
+// slower at 32); 16-row tiles take four of a float32 input.
+GemmPlan gemm_plan(int T, int k, int E, int n_shared, int F, bool x_bf16_exact) {
+    const double rows = static_cast<double>(T) * (k + n_shared);
+    const int groups = E + n_shared;
+    const double avg = rows / groups;
+    const double items64 = (rows / 64.0 + 0.5 * groups) * ((pad128(F) + 255) / 256);
+    GemmPlan p;
+    if (avg >= 30.0 && items64 >= 2048.0) p.tile_rows = 64;
+    else if (avg >= 24.0) p.tile_rows = 32;
+    else p.tile_rows = 16;
+    p.x_terms = (x_bf16_exact || p.tile_rows >= 32) ? 3 : kTerms;
+    p.act_terms = kDownTerms;
+    p.gate_up_features = p.tile_rows == 16 ? 128 : 256;
+    p.down_rows = p.tile_rows == 16 ? 256 : 512;
+    return p;
 }
 
-// Tiles of 16 and 32 rows: 4 wavefronts with 4 A fragments each.
+// 16-row tiles: 4 wavefronts with 4 A fragments each; 32- and 64-row tiles:
+// 8 wavefronts with 4 A fragments each.
 hipError_t launch_gate_up_gemm(const uint8_t *xq, const uint8_t *xs, int T, int H, int F, int E,
                                int k, int n_shared, const ExpertPtrs &ex, const ExpertPtrs &sh,
                                SwigluConsts c, const int32_t *offsets, const int32_t *perm,
@@ -524,8 +599,8 @@ hipError_t launch_gate_up_gemm(const uint8_t *xq, const uint8_t *xs, int T, int 
     switch (tile_rows * 10 + x_terms) {
     case 163: MOE_GU(1, 4, 4, 3); break;
     case 164: MOE_GU(1, 4, 4, 4); break;
-    case 323: MOE_GU(2, 4, 4, 3); break;
-    case 324: MOE_GU(2, 4, 4, 4); break;
+    case 323: MOE_GU(2, 8, 4, 3); break;
+    case 643: MOE_GU(4, 8, 4, 3); break;
     default: return hipErrorInvalidValue;
     }
 #undef MOE_GU
@@ -547,7 +622,8 @@ hipError_t launch_down_gemm(const uint8_t *act_q, const uint8_t *act_s, int T, i
     } while (0)
     switch (tile_rows) {
     case 16: MOE_DN(1, 4, 4); break;
-    case 32: MOE_DN(2, 4, 4); break;
+    case 32: MOE_DN(2, 8, 4); break;
+    case 64: MOE_DN(4, 8, 4); break;
     default: return hipErrorInvalidValue;
     }
 #undef MOE_DN

@@ -211,3 +211,20 @@ def test_noalloc_scratch_covers_the_decode_workloads():
         cfg = config_by_id(cid)
         s = mx.make_shape(**cfg.shape_kwargs(64 if cid != 1 else cfg.T))
         assert mx.moe_workspace_bytes(s) <= _lib.MOE_NOALLOC_SCRATCH_BYTES, cid
+
+
+@pytest.mark.parametrize("cid,tile,x_terms", [(1, 16, 4), (3, 16, 4), (4, 32, 3), (5, 64, 3), (6, 64, 3)])
+def test_prefill_plan_of_the_workloads(cid, tile, x_terms):
+    cfg = config_by_id(cid)
+    plan = mx.moe_prefill_plan(mx.make_shape(**cfg.shape_kwargs()), with_norm=cfg.rms_eps is not None)
+    assert plan["tile_rows"] == tile and plan["x_terms"] == x_terms
+    assert plan["act_terms"] == 3
+    assert plan["gate_up_features"] == (128 if tile == 16 else 256)
+    assert plan["down_rows"] == 2 * plan["gate_up_features"]
+
+
+def test_prefill_plan_rejects_bad_arguments():
+    with pytest.raises(mx.MoeError):
+        mx.moe_prefill_plan(mx.make_shape(T=4, H=100, F=64, E=4, k=2))
+    lib = _lib.load()
+    assert lib.moe_prefill_plan(ctypes.byref(_shape()), 0, None) == _lib.MOE_ERR_INVALID_ARG
