@@ -9,6 +9,7 @@ the only thing both sides consume is the seeded input generator in
 
 Modules:
 - `mxfp4`  decoding of E2M1 codes and E8M0 scales (closed form), plane dequant.
+- `act_quant`  the MX-FP4 round trip of activations (the quantised expert-input mode).
 - `moe`    the block: RMSNorm, router, top-k, route weights, permutation,
            clamped SwiGLU, expert FFN, combine, layer stack. numpy float64.
 - `brute`  the same block in pure Python loops (no numpy) for tiny inputs,
@@ -22,4 +23,4 @@ Pins against what the pages and mathematics fix live in `tests/` (run with
 the clamped-SwiGLU body is a reading (no page prints it) and is marked
 "parity unpinned by the pages" where it is defined.
 """
-from . import mxfp4, moe, brute, route_profile, route_locality  # noqa: F401
+from . import mxfp4, act_quant, moe, brute, route_profile, route_locality  # noqa: F401

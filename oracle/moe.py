@@ -19,6 +19,7 @@ from __future__ import annotations
 
 import numpy as np
 
+from . import act_quant as act_quant_mod
 from . import mxfp4
 
 
@@ -168,17 +169,27 @@ def route(xn, router_w, router_b, k: int, route_scale: float):
 
 def moe_block(layer, x: np.ndarray, k: int, alpha: float, limit: float, up_offset: float,
               route_scale: float = 1.0, rms_eps: float | None = None,
-              tokens=None, stats: dict | None = None) -> dict:
+              tokens=None, stats: dict | None = None, act_quant: int = 0) -> dict:
     """Run one block on x [T, H] (exact input values; the residual is x).
 
     Routing is computed for all T tokens; expert outputs only for `tokens`
     (all when None). Returns float64 `delta` (the MoE sum without residual)
     and the float32 `out` rows for `tokens`, plus the routing tensors.
+
+    act_quant 1: the experts' input (not the router's) is the float32 input
+    rounded through the MX-FP4 round trip of `act_quant.quantize_rows`, in
+    blocks of 32 along H (antirez `ds4.c`, the FP4 activation round trip;
+    goosedump `mixture_of_experts` quantises the expert input once,
+    `Q8Activation`). Reading: routing keeps the unquantised input, and the
+    SwiGLU output is not quantised.
     """
     x = np.asarray(x, dtype=np.float64)
     T = x.shape[0]
     xn = x if layer.norm_w is None else rms_norm(x, layer.norm_w, rms_eps)
     logits, idx, w = route(xn, layer.router_w, layer.router_b, k, route_scale)
+    xe = xn
+    if act_quant:
+        xe = act_quant_mod.quantize_rows(xn.astype(np.float32))[2]
     E = layer.router_w.shape[0]
     counts, offsets, perm, inv = permutation(idx, E)
     toks = np.arange(T) if tokens is None else np.asarray(tokens, dtype=np.int64)
@@ -188,16 +199,16 @@ def moe_block(layer, x: np.ndarray, k: int, alpha: float, limit: float, up_offse
     y = np.zeros((toks.size, k, x.shape[1]), dtype=np.float64)
     for e in np.unique(idx[toks]):
         rows, slots = np.nonzero(idx[toks] == e)
-        y[rows, slots] = expert_ffn(xn[toks[rows]], layer.experts, int(e),
+        y[rows, slots] = expert_ffn(xe[toks[rows]], layer.experts, int(e),
                                     alpha, limit, up_offset, stats)
     for j in range(k):                              # slot-ordered weighted sum
         delta += w[toks, j][:, None] * y[:, j]
     if layer.shared is not None:
         for s in range(layer.shared.n):
-            delta += expert_ffn(xn[toks], layer.shared, s, alpha, limit, up_offset, stats)
+            delta += expert_ffn(xe[toks], layer.shared, s, alpha, limit, up_offset, stats)
     out = (x[toks] + delta).astype(np.float32)
     return dict(out=out, delta=delta, logits=logits, idx=idx, w=w, counts=counts,
-                offsets=offsets, perm=perm, inv=inv, xn=xn, tokens=toks)
+                offsets=offsets, perm=perm, inv=inv, xn=xn, xe=xe, tokens=toks)
 
 
 def moe_stack(layers, x: np.ndarray, k: int, alpha: float, limit: float, up_offset: float,
@@ -216,6 +227,6 @@ def moe_stack(layers, x: np.ndarray, k: int, alpha: float, limit: float, up_offs
     return outs
 
 
-def block_for_config(cfg, layer, x, tokens=None, stats=None) -> dict:
+def block_for_config(cfg, layer, x, tokens=None, stats=None, act_quant: int = 0) -> dict:
     return moe_block(layer, x, cfg.k, cfg.alpha, cfg.limit, cfg.up_offset, cfg.route_scale,
-                     cfg.rms_eps, tokens=tokens, stats=stats)
+                     cfg.rms_eps, tokens=tokens, stats=stats, act_quant=act_quant)
