@@ -6,12 +6,14 @@
 
 A step is one pass of the whole block over one batch of seeded synthetic
 input (weights and activations resident in HBM before timing):
-  suite   (default) decode as the headline line, with prefill, stack and ds4
-          measured after it and nested under "workloads"
+  suite   (default) decode as the headline line, with prefill, stack, ds4 and
+          ds4_q4 measured after it and nested under "workloads"
   decode  gpt-oss-20b-shaped layer, 1000 tokens as T=1 calls
   prefill gpt-oss-20b-shaped layer, T=128, Zipf(1.1)-skewed expert loads
   stack   24 gpt-oss-20b-shaped layers (RMSNorm + MoE), T=512
   ds4     DeepSeek-V4-Flash-shaped layer, T=2048, 256 experts top-6 + shared
+  ds4_q4  ds4 in the quantised expert-input mode (MX-FP4 expert input, FP4 x FP4
+          gate/up products)
   ds4_pro DeepSeek-V4-Pro-shaped layer, T=2048, H=7168, F=3072, 384 experts top-6 + shared
   tiny    T=8, H=F=256, 8 experts top-2
   decode_stack  T=1 tokens through 24 gpt-oss-20b-shaped layers (RMSNorm + MoE),
@@ -53,6 +55,7 @@ if ROOT not in sys.path:
 METRIC = "MoE block tokens/s (decode T=1, prefill T=128/512) + % HBM/MFMA peak"
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
 FP8_PEAK_TFLOPS = 5000.0        # MI355X dense FP8 MFMA: the rate of the FP4 x FP8 scaled MFMA used
+FP4_PEAK_TFLOPS = 10100.0       # MI355X dense FP4 MFMA: the FP4 x FP4 rate (quantised expert input)
 DTYPE = "fp4xfp8"               # MXFP4 weights x FP8-term activations, float32 accumulation
 
 WORKLOADS = {
@@ -64,6 +67,9 @@ WORKLOADS = {
                   steps=20),
     "ds4": dict(config=5, name="ds4flash_T2048_E256_top6_shared", kernel="gate_up_gemm", copies=2,
                 steps=50),
+    # the same layer with the expert input rounded once to MX-FP4 (act_quant=1)
+    "ds4_q4": dict(config=5, name="ds4flash_T2048_E256_top6_shared_mxfp4_input",
+                   kernel="gate_up_gemm", copies=2, steps=50, act_quant=1),
     "tiny": dict(config=1, name="tiny_T8_H256_E8_top2", kernel="decode_gate_up", copies=1,
                  steps=200),
     # DeepSeek-V4-Pro-shaped layer (H=7168, F=3072, 384 experts top-6 + shared,
@@ -177,7 +183,8 @@ class Setup:
         n_layers = cfg.layers
         self.host_layers = []
         self.layers = []
-        self.shape = mx.make_shape(**cfg.shape_kwargs())
+        self.act_quant = spec.get("act_quant", 0)
+        self.shape = mx.make_shape(**cfg.shape_kwargs(), act_quant=self.act_quant)
         for l in range(n_layers):
             layer = make_layer(cfg, l)
             self.layers.append(upload_layer(self.shape, layer, copies=self.copies))
@@ -286,11 +293,13 @@ class Setup:
             byts = active * 2 * (mat + 4 * F) + T * terms(H) + routes * terms(F) + T * splits * E * 8
             return dict(bytes=byts, flops=routes * 4 * H * F, units=routes,
                         unit="route (token, selected expert)", active_experts=active)
-        # gate/up GEMM: weights of every active expert once, x terms once, act terms out
+        # gate/up GEMM: weights of every active expert once, x terms (or the
+        # MX-FP4 input: codes + scales) once, act terms out
         T = cfg.T
         active = [sum(1 for c in counts if c > 0) + cfg.n_shared for counts in counts_per_call]
         rows = T * k + T * cfg.n_shared
-        per = [a * 2 * (mat + 4 * F) + T * terms(H) + rows * terms(F) for a in active]
+        x_in = T * pad128(H) * 17 // 32 if self.act_quant else T * terms(H)
+        per = [a * 2 * (mat + 4 * F) + x_in + rows * terms(F) for a in active]
         return dict(bytes=sum(per) / len(per), flops=4.0 * rows * H * F, units=rows,
                     unit="routed row (token, expert) of the grouped GEMM",
                     active_experts=sum(active) / len(active))
@@ -315,9 +324,10 @@ class Setup:
             return routes * (F // 32) * steps * 4 * per_mfma
         # gate/up GEMM (the library's plan for this shape): per 16-row group of
         # an expert's rows, every gate and up weight tile of every feature block
-        # of a work item, every 128-wide K-step, every FP8 term used
+        # of a work item, every 128-wide K-step, every FP8 term used (one
+        # instruction for the MX-FP4 input: x_terms 0)
         plan = self.mx.moe_prefill_plan(self.shape, with_norm=cfg.rms_eps is not None)
-        nt, fwg = plan["x_terms"], plan["gate_up_features"]
+        nt, fwg = plan["x_terms"] or 1, plan["gate_up_features"]
         tiles = -(-pad128(F) // fwg) * (2 * fwg // 16)
         tot = []
         for counts in counts_per_call:
@@ -460,11 +470,13 @@ def cpu_baseline(setup, budget_s: float):
     while n > 1 and experts_touched(n) * per_expert > budget_s:
         n = int(n * 0.9)
     toks = np.arange(n)
-    done, dt, calls = run_units(lambda i: omoe.block_for_config(cfg, layer, x[:cfg.T], tokens=toks), n)
+    done, dt, calls = run_units(lambda i: omoe.block_for_config(cfg, layer, x[:cfg.T], tokens=toks,
+                                                                act_quant=setup.act_quant), n)
     scaled = f", divided by {layers} layers" if layers > 1 else ""
+    mode = ", MX-FP4 expert input" if setup.act_quant else ""
     return dict(value=done / dt / layers, unit="tokens/s", cores=cores, kind="oracle",
                 sample=f"{calls} fp64 oracle call(s) of layer 0, each on {n} of {cfg.T} tokens "
-                       f"(routing for all {cfg.T}), in {dt:.1f} s{scaled}")
+                       f"(routing for all {cfg.T}){mode}, in {dt:.1f} s{scaled}")
 
 
 def route_locality(setup) -> dict:
@@ -499,7 +511,7 @@ def route_locality(setup) -> dict:
 
 # the default run: the decode headline, then these workloads nested under
 # "workloads" (each with its own step count)
-SUITE = (("prefill", "prefill_T128"), ("stack", "stack_T512"), ("ds4", "ds4"))
+SUITE = (("prefill", "prefill_T128"), ("stack", "stack_T512"), ("ds4", "ds4"), ("ds4_q4", "ds4_q4"))
 
 
 def measure(wl: str, args, steps: int, warmup: int) -> dict:
@@ -565,12 +577,16 @@ def measure(wl: str, args, steps: int, warmup: int) -> dict:
     issued = setup.issued_flops(counts)
     kern_s = kern_avg_ms / 1e3
     traffic = traffic_from_profile(kernel, wl)
+    # the matrix-core peak of the instruction the kernel issues: FP4 x FP8
+    # (the FP8 rate), or FP4 x FP4 with the MX-FP4 expert input
+    mfma_peak = FP4_PEAK_TFLOPS if setup.act_quant else FP8_PEAK_TFLOPS
+    mfma_dtype = "fp4 (fp4 x fp4 scaled MFMA)" if setup.act_quant else "fp8 (fp4 x fp8 scaled MFMA)"
     t_hbm = alg["bytes"] / (HBM_PEAK_GBPS * 1e9)
-    t_mfma = alg["flops"] / (FP8_PEAK_TFLOPS * 1e12)
+    t_mfma = alg["flops"] / (mfma_peak * 1e12)
     if kernel.startswith("decode") or t_hbm >= t_mfma:
         achieved, peak, unit, bound = alg["bytes"] / kern_s / 1e9, HBM_PEAK_GBPS, "GB/s", "hbm"
     else:
-        achieved, peak, unit, bound = alg["flops"] / kern_s / 1e12, FP8_PEAK_TFLOPS, "TFLOP/s", "mfma"
+        achieved, peak, unit, bound = alg["flops"] / kern_s / 1e12, mfma_peak, "TFLOP/s", "mfma"
     block_bytes = setup.block_bytes_per_step(counts)
     block_gbps = block_bytes / (ms_per_step / 1e3) / 1e9
     nominal_tf = alg["flops"] / kern_s / 1e12
@@ -587,6 +603,7 @@ def measure(wl: str, args, steps: int, warmup: int) -> dict:
             "k": cfg.k, "n_shared": cfg.n_shared, "layers": cfg.layers,
             "tokens_per_step": setup.tokens_per_step, "weights": "mxfp4 (e2m1 + e8m0/32) + fp32 bias",
             "activations": cfg.act_dtype, "weight_copies": setup.copies,
+            "expert_input": "mxfp4 (rounded once)" if setup.act_quant else "exact (fp8 terms)",
             "launch": "eager" if graphs is None else "hip_graph",
             "route_profile": args.route_profile,
         },
@@ -603,12 +620,12 @@ def measure(wl: str, args, steps: int, warmup: int) -> dict:
             # 4*H*F (gate/up) flops per unit; issued = every instruction the
             # kernel runs (FP8 terms, zero columns, padded rows)
             "mfma": {
-                "peak_TFLOPs": FP8_PEAK_TFLOPS, "peak_dtype": "fp8 (fp4 x fp8 scaled MFMA)",
+                "peak_TFLOPs": mfma_peak, "peak_dtype": mfma_dtype,
                 "nominal_TFLOPs": round(nominal_tf, 2),
-                "nominal_frac": round(nominal_tf / FP8_PEAK_TFLOPS, 4),
+                "nominal_frac": round(nominal_tf / mfma_peak, 4),
                 "issued_flops_per_launch": int(issued),
                 "issued_TFLOPs": round(issued_tf, 2),
-                "issued_frac": round(issued_tf / FP8_PEAK_TFLOPS, 4),
+                "issued_frac": round(issued_tf / mfma_peak, 4),
             },
         },
         "block": {

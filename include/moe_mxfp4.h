@@ -68,7 +68,19 @@ typedef enum moe_dtype {
  * 1.0 / 10.0 / 0.0 (antirez ds4.c DS4_DEFAULT_SWIGLU_CLAMP_EXP).
  * route_scale: 1.0 for gpt-oss, 1.5 for DeepSeek-V4-Flash (ds4.c
  * DS4_SHAPE_FLASH expert_weight_scale). rms_eps is used only when a norm
- * weight is passed (1e-5 for gpt-oss). */
+ * weight is passed (1e-5 for gpt-oss).
+ * act_quant = 1 selects the quantised expert-input mode of
+ * moe_forward_prefill: the experts' input (the normalised hidden state, as
+ * float32) is rounded once to MX-FP4 - blocks of 32 values sharing the
+ * power-of-two scale 2^e, e the smallest integer with amax <= 6 * 2^e (amax
+ * held at no less than 6 * 2^-126), each value divided by it, clamped to
+ * +-6 and replaced by the nearest E2M1 value, ties to the even code (page:
+ * antirez ds4.c `dsv4_fp4_act_quantize_row_inplace_cpu`,
+ * `dsv4_e2m1fn_dequant_cpu`) - and reused by every expert row that takes
+ * the token (goosedump `mixture_of_experts`, `Q8Activation`). The gate/up
+ * products then run FP4 x FP4 on the matrix cores, one instruction each.
+ * Routing, the SwiGLU output and the residual are unaffected. The decode
+ * entry points reject the mode (MOE_ERR_UNSUPPORTED). */
 typedef struct moe_shape {
     int32_t T;          /* tokens */
     int32_t H;          /* hidden size */
@@ -82,6 +94,7 @@ typedef struct moe_shape {
     float swiglu_up_offset;
     float route_scale;
     float rms_eps;
+    int32_t act_quant;  /* 0: exact expert input; 1: MX-FP4 expert input (below) */
 } moe_shape;
 
 /* Byte layout of one packed expert blob. Offsets are from the blob start;
@@ -322,12 +335,28 @@ int moe_forward_decode_noalloc(const moe_shape *shape, const void *hidden, const
  * this library's tiling of those per-expert row groups. */
 typedef struct moe_prefill_plan_t {
     int32_t tile_rows;         /* routed rows of one expert per tile: 16, 32 or 64 */
-    int32_t x_terms;           /* FP8 terms of the expert input in the gate/up products */
+    int32_t x_terms;           /* FP8 terms of the expert input in the gate/up products;
+                                  0: the MX-FP4 expert input (act_quant = 1), one FP4 operand */
     int32_t act_terms;         /* FP8 terms of the SwiGLU output in the down products */
     int32_t gate_up_features;  /* features (gate and up rows each) per gate/up work item */
     int32_t down_rows;         /* hidden rows per down work item */
 } moe_prefill_plan_t;
 int moe_prefill_plan(const moe_shape *shape, int32_t with_norm, moe_prefill_plan_t *plan);
+
+/* Export the MX-FP4 expert input of the quantised mode (act_quant = 1) as
+ * the prefill kernels compute with it, for bit-exact checks against the
+ * round trip's definition (page: antirez ds4.c
+ * `dsv4_fp4_act_quantize_row_inplace_cpu`, `dsv4_e2m1fn_dequant_cpu`).
+ *   x, norm_w    as for moe_route (norm_w NULL: no norm)
+ *   codes  [T, H / 2] bytes, device: E2M1 codes (bit 3 the sign, bits 0-2
+ *          the magnitude index), element 2i in the low nibble of byte i
+ *   scales [T, H / 32] bytes, device: E8M0 scale byte e + 127 per block
+ *   ws     >= moe_workspace_bytes(shape) bytes, 256-byte aligned, device
+ * shape->act_quant is not read. MOE_ERR_INVALID_ARG on NULL pointers or a
+ * bad shape. */
+int moe_act_quant_debug(const moe_shape *shape, const void *x, const float *norm_w,
+                        uint8_t *codes, uint8_t *scales, void *ws, size_t ws_bytes,
+                        hipStream_t stream);
 
 /* Export the weights the kernels compute with, for bit-exact checks against
  * the MXFP4 definition (page: antirez ds4.c `dsv4_e2m1fn_value_cpu`, the

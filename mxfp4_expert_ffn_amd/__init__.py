@@ -21,7 +21,7 @@ __all__ = [
     "MoeError", "MoeShape", "make_shape", "moe_blob_layout_get", "moe_pack_experts",
     "moe_workspace_bytes", "moe_route", "moe_forward_decode", "moe_forward_prefill",
     "moe_forward_decode_noalloc", "moe_prefill_plan",
-    "moe_dequant_debug", "moe_last_error", "moe_profile_next_launch", "moe_route_profile_summary",
+    "moe_act_quant_debug", "moe_dequant_debug", "moe_last_error", "moe_profile_next_launch", "moe_route_profile_summary",
     "moe_route_locality", "moe_route_hotlist", "LOCALITY_CACHE_SIZES", "ROUTE_FIELDS",
 ]
 
@@ -38,11 +38,13 @@ class MoeError(RuntimeError):
 
 
 def make_shape(T, H, F, E, k, act_dtype="f32", n_shared=0, alpha=1.702, limit=7.0,
-               up_offset=1.0, route_scale=1.0, rms_eps=0.0) -> MoeShape:
+               up_offset=1.0, route_scale=1.0, rms_eps=0.0, act_quant=0) -> MoeShape:
+    """act_quant=1: the quantised expert-input mode (MX-FP4 expert input,
+    prefill only)."""
     return MoeShape(int(T), int(H), int(F), int(E), int(k),
                     MOE_BF16 if act_dtype == "bf16" else MOE_F32, int(n_shared),
                     float(alpha), float(limit), float(up_offset), float(route_scale),
-                    float(rms_eps))
+                    float(rms_eps), int(act_quant))
 
 
 def moe_last_error() -> str:
@@ -176,6 +178,20 @@ def moe_prefill_plan(shape, with_norm: bool = False) -> dict:
     p = _lib.MoePrefillPlan()
     _check(_lib.load().moe_prefill_plan(ctypes.byref(shape), int(bool(with_norm)), ctypes.byref(p)))
     return {name: getattr(p, name) for name, _ in p._fields_}
+
+
+def moe_act_quant_debug(shape, x, codes, scales, ws, norm_w=None, stream=None):
+    """The MX-FP4 expert input of the quantised mode: codes [T, H/2] and scale
+    bytes [T, H/32] (uint8 device tensors) as the prefill kernels use them."""
+    import torch
+    T, H = shape.T, shape.H
+    if codes.numel() != T * (H // 2) or scales.numel() != T * (H // 32):
+        raise ValueError("codes must hold T*H/2 bytes and scales T*H/32")
+    _check(_lib.load().moe_act_quant_debug(
+        ctypes.byref(shape), _ptr(x, "x", (torch.float32, torch.bfloat16, torch.int16, torch.uint16)),
+        _ptr(norm_w, "norm_w", torch.float32, optional=True), _ptr(codes, "codes", torch.uint8),
+        _ptr(scales, "scales", torch.uint8), _ptr(ws, "ws"), ws.numel() * ws.element_size(),
+        _stream(stream)))
 
 
 def moe_dequant_debug(shape, blob, which: int, path: int, out, stream=None):

@@ -29,6 +29,7 @@ class MoeShape(ctypes.Structure):
         ("n_shared", ctypes.c_int32), ("swiglu_alpha", ctypes.c_float),
         ("swiglu_limit", ctypes.c_float), ("swiglu_up_offset", ctypes.c_float),
         ("route_scale", ctypes.c_float), ("rms_eps", ctypes.c_float),
+        ("act_quant", ctypes.c_int32),
     ]
 
 
@@ -76,6 +77,8 @@ SIGNATURES = {
                                                   _P, _P, ctypes.POINTER(MoeRouteOut), _P]),
     "moe_prefill_plan": (ctypes.c_int, [ctypes.POINTER(MoeShape), ctypes.c_int32,
                                         ctypes.POINTER(MoePrefillPlan)]),
+    "moe_act_quant_debug": (ctypes.c_int, [ctypes.POINTER(MoeShape), _P, _P, _P, _P, _P,
+                                           ctypes.c_size_t, _P]),
     "moe_dequant_debug": (ctypes.c_int, [ctypes.POINTER(MoeShape), _P, ctypes.c_int32,
                                          ctypes.c_int32, _P, _P]),
     "moe_profile_next_launch": (ctypes.c_int, [ctypes.c_int32, _P, _P]),

@@ -74,6 +74,8 @@ int check_shape(const moe_shape *s) {
     if (!std::isfinite(s->swiglu_up_offset)) return fail(MOE_ERR_INVALID_ARG, "swiglu_up_offset is not finite");
     if (!std::isfinite(s->route_scale) || !(s->route_scale > 0.f))
         return fail(MOE_ERR_INVALID_ARG, "route_scale must be finite and > 0");
+    if (s->act_quant != 0 && s->act_quant != 1)
+        return fail(MOE_ERR_INVALID_ARG, "act_quant=%d must be 0 or 1", s->act_quant);
     return MOE_OK;
 }
 
@@ -185,6 +187,7 @@ struct ProfileHook {
     hipEvent_t start = nullptr, stop = nullptr;
 };
 thread_local ProfileHook g_hook;
+constexpr int kUnprofiled = -2;  // id of launches the hook never times
 
 // Launch through `fn` (one kernel, returning hipError_t). When the hook is
 // armed for kernel `id`, its events ride on that dispatch (hipExtLaunchKernel
@@ -242,7 +245,7 @@ int route_front(const moe_shape *s, const void *x, const float *norm_w, const fl
         in->inv = w.rinv;
         in->gamma = norm_w;
     }
-    const moe::TermsOut tq{w.xq, w.xs};
+    const moe::TermsOut tq{w.xq, w.xs, s->act_quant};
     MOE_TRY(launch(MOE_KERNEL_ROUTER, "router", st, [&] {
         return moe::launch_router(*in, router_w, s->T, s->H, s->E, w.partial, terms ? &tq : nullptr,
                                   st);
@@ -252,7 +255,8 @@ int route_front(const moe_shape *s, const void *x, const float *norm_w, const fl
 
 // The grouped GEMMs' tiling and term counts for this call.
 moe::GemmPlan gemm_plan_of(const moe_shape *s, bool norm) {
-    return moe::gemm_plan(s->T, s->k, s->E, s->n_shared, s->F, s->act_dtype == MOE_BF16 && !norm);
+    return moe::gemm_plan(s->T, s->k, s->E, s->n_shared, s->F, s->act_dtype == MOE_BF16 && !norm,
+                          s->act_quant != 0);
 }
 
 // Upper bound on the grouped GEMMs' row tiles (the grid is sized by it).
@@ -369,12 +373,37 @@ int moe_route(const moe_shape *s, const void *x, const float *norm_w, const floa
     return ok();
 }
 
+int moe_act_quant_debug(const moe_shape *s, const void *x, const float *norm_w, uint8_t *codes,
+                        uint8_t *scales, void *ws, size_t ws_bytes, hipStream_t st) {
+    MOE_TRY(check_shape(s));
+    if (s->T == 0) return ok();
+    if (!x || !codes || !scales) return fail(MOE_ERR_INVALID_ARG, "x, codes and scales must be non-NULL");
+    if (!aligned(x, 16) || (norm_w && !aligned(norm_w, 16)))
+        return fail(MOE_ERR_INVALID_ARG, "x and norm_w must be 16-byte aligned");
+    if (norm_w && !(s->rms_eps >= 0.f)) return fail(MOE_ERR_INVALID_ARG, "rms_eps must be >= 0");
+    MOE_TRY(check_ws(s, ws, ws_bytes));
+    const Workspace w = carve(s, static_cast<uint8_t *>(ws));
+    const int bf16 = s->act_dtype == MOE_BF16;
+    moe::RouteIn in{x, bf16, nullptr, nullptr, nullptr};
+    if (norm_w) {
+        MOE_TRY(launch(MOE_KERNEL_RMSNORM, "rmsnorm", st, [&] {
+            return moe::launch_rms_inv(x, bf16, s->T, s->H, s->rms_eps, w.rinv, st);
+        }));
+        in.inv = w.rinv;
+        in.gamma = norm_w;
+    }
+    MOE_TRY(launch(kUnprofiled, "act_fp4", st, [&] { return moe::launch_act_fp4(in, s->T, s->H, codes, scales, st); }));
+    return ok();
+}
+
 int moe_forward_decode(const moe_shape *s, const void *hidden, const float *norm_w,
                        const float *router_w, const float *router_b, const uint8_t *experts,
                        const uint8_t *shared, float *out, const moe_route_out *ro, void *ws,
                        size_t ws_bytes, hipStream_t st) {
     MOE_TRY(check_forward(s, hidden, norm_w, router_w, router_b, experts, shared, out, ws, ws_bytes));
     if (s->T > 64) return fail(MOE_ERR_UNSUPPORTED, "decode takes T <= 64 (T=%d); use prefill", s->T);
+    if (s->act_quant)
+        return fail(MOE_ERR_UNSUPPORTED, "the quantised expert-input mode is a prefill mode");
     if (s->H > 8192 || s->F > 8192)
         return fail(MOE_ERR_UNSUPPORTED, "decode takes H, F <= 8192");
     if (s->T == 0) return ok();
@@ -446,7 +475,7 @@ int moe_forward_prefill(const moe_shape *s, const void *hidden, const float *nor
     }));
     const moe::GemmPlan plan = gemm_plan_of(s, norm_w != nullptr);
     const int bm = plan.tile_rows;
-    const moe::TermsOut tq{w.xq, w.xs};
+    const moe::TermsOut tq{w.xq, w.xs, s->act_quant};
     MOE_TRY(launch(MOE_KERNEL_PERMUTE, "permute", st, [&] {
         return moe::launch_permute(w.idx, s->T, s->E, s->k, s->n_shared, bm, w.counts, w.offsets,
                                    w.perm, w.inv, w.rank, w.mprefix, ro ? ro->counts : nullptr,

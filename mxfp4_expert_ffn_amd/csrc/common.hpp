@@ -299,4 +299,37 @@ __device__ __forceinline__ void fp8_terms_group(float v, uint32_t &codes, uint32
     }
 }
 
+// ---------------------------------------------------------------- MX-FP4 activations
+// The MX-FP4 round trip of 32 activations held by the 32 lanes of a
+// half-wavefront (the quantised expert-input mode): one shared power-of-two
+// scale 2^e, the smallest with amax <= 6 * 2^e (amax held at no less than
+// 6 * 2^-126), and per value the E2M1 code of the nearest magnitude of
+// x / 2^e clamped to [-6, 6], ties to the even code, with the sign of x (a
+// value not below zero, -0 included, is positive). x / 2^e is exact, so the
+// thresholds decide exactly as a software quantiser on the same float32 x.
+// Returns the lane's code (0..15) and the block's E8M0 scale byte e + 127.
+// Every lane of the wavefront must take part (one half-wavefront maximum).
+__device__ __forceinline__ uint32_t fp4_act_code(float v, uint32_t &scale_byte) {
+    const float amax = fmaxf(half_wave_max(fabsf(v)), 7.052966104933725e-38f);  // 6 * 2^-126
+    const uint32_t bits = __float_as_uint(amax);
+    const int E = static_cast<int>((bits >> 23) & 0xffu) - 127;
+    const int e = (bits & 0x7fffffu) <= 0x400000u ? E - 2 : E - 1;  // amax <= 1.5 * 2^E: 6 * 2^(E-2) fits
+    scale_byte = static_cast<uint32_t>(e + 127);
+    const float a = fminf(fabsf(v) * pow2f(-e), 6.0f);
+    // nearest of {0, .5, 1, 1.5, 2, 3, 4, 6}; a midpoint goes to the even index
+    const uint32_t idx = static_cast<uint32_t>(a > 0.25f) + static_cast<uint32_t>(a >= 0.75f) +
+                         static_cast<uint32_t>(a > 1.25f) + static_cast<uint32_t>(a >= 1.75f) +
+                         static_cast<uint32_t>(a > 2.5f) + static_cast<uint32_t>(a >= 3.5f) +
+                         static_cast<uint32_t>(a > 5.0f);
+    return idx | (v < 0.0f ? 8u : 0u);
+}
+
+// The byte holding the codes of this lane and the next (even lanes: element
+// 2i in the low nibble); the value in odd lanes is meaningless.
+__device__ __forceinline__ uint32_t fp4_pack_pair(uint32_t code) {
+    const uint32_t next = static_cast<uint32_t>(
+        __builtin_amdgcn_update_dpp(0, static_cast<int>(code), 0x39, 0xf, 0xf, false));  // quad_perm [1,2,3,0]
+    return (code & 0xfu) | ((next & 0xfu) << 4);
+}
+
 }  // namespace moe

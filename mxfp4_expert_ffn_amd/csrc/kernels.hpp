@@ -107,10 +107,18 @@ RouterPlan router_plan(int T, int H, int E);
 // FP8-term quantisation of the expert input (every forward), done by extra
 // workgroups of the router launch: q [T][kTerms][Kp] E4M3 codes, scales
 // [T][kTerms][Kp/32] E8M0 bytes, Kp = pad128(H), zero codes past H.
+// fp4: the MX-FP4 round trip of the expert input instead (the quantised
+// expert-input mode): codes packed two per byte, q [T][Kp / 2], one E8M0
+// scale per 32 values, scales [T][Kp / 32], zero codes past H.
 struct TermsOut {
     uint8_t *q;
     uint8_t *scales;
+    int fp4;
 };
+// The MX-FP4 expert input alone, rows of H values: q [T][H / 2],
+// scales [T][H / 32] (the quantised mode's debug export).
+hipError_t launch_act_fp4(const RouteIn &in, int T, int H, uint8_t *q, uint8_t *scales,
+                          hipStream_t s);
 // `terms` NULL: router only.
 hipError_t launch_router(const RouteIn &in, const float *w, int T, int H, int E, double *partial,
                          const TermsOut *terms, hipStream_t s);
@@ -169,14 +177,16 @@ hipError_t launch_decode_down(const DecodeArgs &a, hipStream_t s);
 // count.
 struct GemmPlan {
     int tile_rows;         // activation rows per tile
-    int x_terms;           // FP8 terms of the expert input that take part (3 or kTerms)
+    int x_terms;           // FP8 terms of the expert input that take part (3 or kTerms), or 0:
+                           // the MX-FP4 expert input of the quantised mode
     int act_terms;         // FP8 terms of the SwiGLU output that take part
     int gate_up_features;  // features per gate/up workgroup
     int down_rows;         // hidden rows per down workgroup
 };
 // x_bf16_exact: the expert input is a bfloat16 value (no RMSNorm in between),
 // which three terms carry as closely as four.
-GemmPlan gemm_plan(int T, int k, int E, int n_shared, int F, bool x_bf16_exact);
+// x_fp4: the quantised expert-input mode.
+GemmPlan gemm_plan(int T, int k, int E, int n_shared, int F, bool x_bf16_exact, bool x_fp4);
 // x_terms: FP8 terms of the expert input that take part, 3 or kTerms.
 hipError_t launch_gate_up_gemm(const uint8_t *xq, const uint8_t *xs, int T, int H, int F, int E,
                                int k, int n_shared, const ExpertPtrs &ex, const ExpertPtrs &sh,

@@ -110,6 +110,20 @@ __device__ __forceinline__ f32x4_t mx_mfma(const AFrag &a, const BFrag &b, f32x4
     return mx_mfma(a, b.lo, b.hi, b.s, acc);
 }
 
+// Both operands FP4 (the quantised expert-input mode): B lane l is column
+// l % 16 with the 32 codes of MX block h = l / 16 of the step (k = 32h ..
+// 32h + 31, as for A), 16 bytes, and that block's scale byte.
+__device__ __forceinline__ f32x4_t mx_mfma_fp4(const AFrag &a, const uint4 &b, uint32_t bs,
+                                               f32x4_t acc) {
+    const i32x8_t A = {static_cast<int>(a.q.x), static_cast<int>(a.q.y), static_cast<int>(a.q.z),
+                       static_cast<int>(a.q.w), 0, 0, 0, 0};
+    const i32x8_t B = {static_cast<int>(b.x), static_cast<int>(b.y), static_cast<int>(b.z),
+                       static_cast<int>(b.w), 0, 0, 0, 0};
+    // cbsz 4 and blgp 4: both operands FP4 (E2M1)
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B, acc, 4, 4, 0, static_cast<int>(a.s),
+                                                             0, static_cast<int>(bs));
+}
+
 // Sum over the lane quad (the kTerms columns of one row).
 __device__ __forceinline__ float quad_sum(float v) {
     v += __builtin_amdgcn_update_dpp(0.0f, v, 0xB1, 0xf, 0xf, false);  // quad_perm [1,0,3,2]

@@ -313,13 +313,97 @@ __device__ __forceinline__ void gemm_mainloop(const uint8_t *const (&aq)[NA],
     }
 }
 
+// Main loop with an MX-FP4 expert input (the quantised expert-input mode):
+// both operands FP4, one block-scaled instruction per A fragment and row
+// group. A step's B is one 16-byte piece per (row, k-group): the 32 codes of
+// MX block 4s + h of the row, from the packed rows bq[row][Kb / 2] with their
+// scale bytes bs[row][Kb / 32]. Pieces are staged 2 steps ahead through
+// double-buffered LDS (piece (group * 4 + h) * 16 + column, the scale dword of
+// a row's four k-groups at its row), A fragments 2 steps ahead as in
+// gemm_mainloop. All loads are unconditional (threads past the pieces reload
+// one), so no branch sits between loads and matrix-core work.
+template <int NG, int W, int NA>
+__device__ __forceinline__ void gemm_mainloop_x4(const uint8_t *const (&aq)[NA],
+                                                 const uint8_t *const (&as)[NA], const ALane &al,
+                                                 int NS, const uint8_t *bq, const uint8_t *bs,
+                                                 int Kb, const int *s_brow, int n, uint8_t *sB,
+                                                 uint8_t *sBs, f32x4_t (&acc)[NA][NG]) {
+    constexpr int kThreads = 64 * W;
+    constexpr int kPieces = 64 * NG;     // per step
+    constexpr int kRows = 16 * NG;
+    constexpr int kBuf = 16 * kPieces;   // bytes per LDS buffer
+    static_assert(kPieces <= kThreads && kRows <= kThreads, "one piece per thread");
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int pc = tid % kPieces;
+    const uint32_t soff = static_cast<uint32_t>(s_brow[16 * (pc >> 6) + (pc & 15)]) * (Kb / 2) +
+                          16u * ((pc >> 4) & 3);
+    const uint32_t *ssrc =
+        reinterpret_cast<const uint32_t *>(bs + static_cast<size_t>(s_brow[tid % kRows]) * (Kb / 32));
+    const int ngroups = (n + 15) >> 4;
+    struct BSlot {
+        u32x4_t b;
+        uint32_t s;
+    };
+    struct ASlot {
+        AFrag a[NA];
+    };
+    auto fill_b = [&](BSlot &sl, int step) __attribute__((always_inline)) {
+        const int sd = min(step, NS - 1);
+        sl.b = *reinterpret_cast<const u32x4_t *>(bq + soff + 64u * sd);
+        sl.s = ssrc[sd];
+    };
+    auto fill_a = [&](ASlot &sl, int step) __attribute__((always_inline)) {
+        const int sd = min(step, NS - 1);
+#pragma unroll
+        for (int j = 0; j < NA; ++j) sl.a[j] = load_afrag(aq[j], as[j], al, sd);
+    };
+    const int col = lane & 15, kh = lane >> 4;
+    auto step = [&](auto lbuf, BSlot &bsl, ASlot &asl, int s) __attribute__((always_inline)) {
+        constexpr int L = decltype(lbuf)::value;
+        uint8_t *buf = sB + L * kBuf;
+        uint32_t *sbuf = reinterpret_cast<uint32_t *>(sBs) + L * kRows;
+        if (tid < kPieces) *reinterpret_cast<u32x4_t *>(buf + 16 * tid) = bsl.b;
+        if (tid < kRows) sbuf[tid] = bsl.s;
+        fill_b(bsl, s + 2);
+        __syncthreads();
+        if (s < NS) {  // uniform; no loads inside
+#pragma unroll
+            for (int g = 0; g < NG; ++g) {
+                if (g < ngroups) {  // uniform: row groups the tile fills
+                    const uint4 blo = *reinterpret_cast<const uint4 *>(buf + 16 * ((g * 4 + kh) * 16 + col));
+                    const uint32_t bsc = reinterpret_cast<const uint8_t *>(sbuf)[4 * (16 * g + col) + kh];
+#pragma unroll
+                    for (int j = 0; j < NA; ++j) acc[j][g] = mx_mfma_fp4(asl.a[j], blo, bsc, acc[j][g]);
+                }
+            }
+        }
+        fill_a(asl, s + 2);
+    };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    ASlot a0, a1;
+    BSlot b0, b1;
+    fill_b(b0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    fill_a(a0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    fill_b(b1, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    fill_a(a1, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    for (int s0 = 0; s0 < NS; s0 += 2) {
+        step(I0{}, b0, a0, s0);
+        step(I1{}, b1, a1, s0 + 1);
+    }
+}
+
 __device__ __forceinline__ void load_pre(const int32_t *mprefix, int G, int *s_pre) {
     for (int i = threadIdx.x; i <= G; i += blockDim.x) s_pre[i] = mprefix[i];
     __syncthreads();
 }
 
 // gate/up: grid = kXcds-rounded max_tiles x ceil(pad128(F) / kGateUpRows) items;
-// NT terms of the expert input take part.
+// NT FP8 terms of the expert input take part, or (NT = 0) its MX-FP4 codes.
 // 16-row tiles are held to 4 wavefronts per SIMD (128 VGPRs, no spills).
 template <int NG, int W, int NA, int NT>
 __global__ __launch_bounds__(64 * W, NG == 1 ? 4 : (W == 4 ? 2 : 1)) void gate_up_gemm_kernel(
@@ -336,7 +420,7 @@ __global__ __launch_bounds__(64 * W, NG == 1 ? 4 : (W == 4 ? 2 : 1)) void gate_u
     constexpr int kActBytes = Gm::kRows * kActStride * 4;
     constexpr int kStageBytes = 2 * Gm::kBufBytes;
     __shared__ __align__(16) uint8_t sB[kStageBytes > kActBytes ? kStageBytes : kActBytes];
-    __shared__ uint8_t sBs[2 * 4 * Gm::kScales];
+    __shared__ __align__(16) uint8_t sBs[2 * 4 * Gm::kScales];  // dword-read by the FP4 main loop
     __shared__ float s_bias[2][Gm::kGateUpRows];  // gate, up biases of the workgroup's features
     const int G = E + n_shared, R = T * k;
     load_pre(mprefix, G, s_pre);
@@ -377,7 +461,10 @@ __global__ __launch_bounds__(64 * W, NG == 1 ? 4 : (W == 4 ? 2 : 1)) void gate_u
 #pragma unroll
         for (int g = 0; g < NG; ++g) acc[j][g] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     const int Kp = pad128(H);
-    gemm_mainloop<NG, W, NA, NT>(aq, as, al, Kp / 128, xq, xs, Kp, s_brow, tl.n, sB, sBs, acc);
+    if constexpr (NT == 0)  // MX-FP4 expert input
+        gemm_mainloop_x4<NG, W, NA>(aq, as, al, Kp / 128, xq, xs, Kp, s_brow, tl.n, sB, sBs, acc);
+    else
+        gemm_mainloop<NG, W, NA, NT>(aq, as, al, Kp / 128, xq, xs, Kp, s_brow, tl.n, sB, sBs, acc);
 
     // epilogue: SwiGLU of the workgroup's features into LDS, then one
     // 32-feature block per (row, block) to FP8 terms
@@ -563,8 +650,9 @@ int items(int nrb, int max_tiles) {
 //  - 16-row tiles (4 wavefronts, four per CU) below (the T = 128 layer).
 // Tiles of 32 rows and more take three FP8 terms of the expert input (a
 // fourth does not fit two wavefronts' registers per SIMD at 64 rows and was
-// slower at 32); 16-row tiles take four of a float32 input.
-GemmPlan gemm_plan(int T, int k, int E, int n_shared, int F, bool x_bf16_exact) {
+// slower at 32); 16-row tiles take four of a float32 input. An MX-FP4
+// expert input (x_fp4) is one FP4 operand (x_terms 0).
+GemmPlan gemm_plan(int T, int k, int E, int n_shared, int F, bool x_bf16_exact, bool x_fp4) {
     const double rows = static_cast<double>(T) * (k + n_shared);
     const int groups = E + n_shared;
     const double avg = rows / groups;
@@ -573,7 +661,7 @@ GemmPlan gemm_plan(int T, int k, int E, int n_shared, int F, bool x_bf16_exact) 
     if (avg >= 30.0 && items64 >= 2048.0) p.tile_rows = 64;
     else if (avg >= 24.0) p.tile_rows = 32;
     else p.tile_rows = 16;
-    p.x_terms = (x_bf16_exact || p.tile_rows >= 32) ? 3 : kTerms;
+    p.x_terms = x_fp4 ? 0 : (x_bf16_exact || p.tile_rows >= 32) ? 3 : kTerms;
     p.act_terms = kDownTerms;
     p.gate_up_features = p.tile_rows == 16 ? 128 : 256;
     p.down_rows = p.tile_rows == 16 ? 256 : 512;
@@ -595,8 +683,11 @@ hipError_t launch_gate_up_gemm(const uint8_t *xq, const uint8_t *xs, int T, int 
         launch_kernel(gate_up_gemm_kernel<NG, W, NA, NT>, grid, 64 * (W), s, xq, xs, T, H, F, E,   \
                       k, n_shared, ex, sh, c, offsets, perm, mprefix, act_q, act_s);                \
     } while (0)
-    if (x_terms != 3 && x_terms != kTerms) return hipErrorInvalidValue;
+    if (x_terms != 0 && x_terms != 3 && x_terms != kTerms) return hipErrorInvalidValue;
     switch (tile_rows * 10 + x_terms) {
+    case 160: MOE_GU(1, 4, 4, 0); break;
+    case 320: MOE_GU(2, 8, 4, 0); break;
+    case 640: MOE_GU(4, 8, 4, 0); break;
     case 163: MOE_GU(1, 4, 4, 3); break;
     case 164: MOE_GU(1, 4, 4, 4); break;
     case 323: MOE_GU(2, 8, 4, 3); break;

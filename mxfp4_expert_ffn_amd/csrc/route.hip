@@ -96,10 +96,23 @@ __device__ __forceinline__ float quantize_input(const RouteIn &in, int T, int H,
 }
 
 // Terms of block gidx from the lanes' values; every lane of the wavefront
-// takes part (the group maximum is a half-wavefront reduction).
+// takes part (the group maximum is a half-wavefront reduction). fp4: the
+// MX-FP4 round trip instead, codes packed two per byte in xq[t][Kp / 2] and
+// the block's scale byte in xs[t][Kp / 32].
 __device__ __forceinline__ void quantize_store(float v, int T, int nb, int Kp, uint8_t *xq,
-                                               uint8_t *xs, int gidx) {
+                                               uint8_t *xs, int gidx, int fp4) {
     const int i = threadIdx.x & 31;
+    if (fp4) {
+        uint32_t sbyte;
+        const uint32_t pair = fp4_pack_pair(fp4_act_code(v, sbyte));
+        if (gidx < T * nb) {
+            const int t = gidx / nb, blk = gidx - t * nb;
+            if ((i & 1) == 0)
+                xq[static_cast<size_t>(t) * (Kp / 2) + 16 * blk + (i >> 1)] = static_cast<uint8_t>(pair);
+            if (i == 0) xs[static_cast<size_t>(t) * nb + blk] = static_cast<uint8_t>(sbyte);
+        }
+        return;
+    }
     uint32_t codes, scales;
     fp8_terms_group(v, codes, scales);
     if (gidx < T * nb) {
@@ -120,7 +133,7 @@ __device__ __forceinline__ void quantize_store(float v, int T, int nb, int Kp, u
 // and its guards are per wavefront (both halves together), as the group
 // maximum needs.
 __device__ __forceinline__ void quantize_terms_wgs(const RouteIn &in, int T, int H, int Kp,
-                                                   uint8_t *xq, uint8_t *xs, int first) {
+                                                   uint8_t *xq, uint8_t *xs, int first, int fp4) {
     constexpr int kU = 4;
     const int nb = Kp / 32;
     const int total = T * nb;
@@ -134,7 +147,7 @@ __device__ __forceinline__ void quantize_terms_wgs(const RouteIn &in, int T, int
         for (int u = 0; u < kU; ++u) v[u] = quantize_input(in, T, H, nb, g0 + u * stride + half);
 #pragma unroll
         for (int u = 0; u < kU; ++u)
-            if (g0 + u * stride < total) quantize_store(v[u], T, nb, Kp, xq, xs, g0 + u * stride + half);
+            if (g0 + u * stride < total) quantize_store(v[u], T, nb, Kp, xq, xs, g0 + u * stride + half, fp4);
     }
 }
 
@@ -153,11 +166,11 @@ template <int KIND, bool NORM>
 __global__ __launch_bounds__(256) void router_gemv_kernel(RouteIn in, const float *w, int T,
                                                           int H, int E, double *partial,
                                                           int router_wgs, int Kp, uint8_t *xq,
-                                                          uint8_t *xs) {
+                                                          uint8_t *xs, int fp4) {
     constexpr int NV = kRouterGemvSlice / 256;  // float4 per lane
     const int lane = threadIdx.x & 63;
     if (static_cast<int>(blockIdx.x) >= router_wgs) {
-        quantize_terms_wgs(in, T, H, Kp, xq, xs, router_wgs);
+        quantize_terms_wgs(in, T, H, Kp, xq, xs, router_wgs, fp4);
         return;
     }
     const int item = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -227,14 +240,14 @@ __global__ __launch_bounds__(256) void router_tiled_kernel(RouteIn in, const flo
                                                            int H, int E, int slice, int tiles_t,
                                                            int tiles_e, int router_wgs,
                                                            double *partial, int Kp, uint8_t *xq,
-                                                           uint8_t *xs) {
+                                                           uint8_t *xs, int fp4) {
     typedef typename std::conditional<NORM, double, float>::type XT;
     constexpr int kPad = 4;
     __shared__ __align__(16) XT xsm[2][32][64 + kPad];    // [k][token]
     __shared__ __align__(16) float wsm[2][32][64 + kPad];  // [k][expert]
     const int b = blockIdx.x;
     if (b >= router_wgs) {
-        quantize_terms_wgs(in, T, H, Kp, xq, xs, router_wgs);
+        quantize_terms_wgs(in, T, H, Kp, xq, xs, router_wgs, fp4);
         return;
     }
     const int tid = threadIdx.x;
@@ -409,12 +422,12 @@ __global__ __launch_bounds__(1024) void permute_kernel(
     const int32_t *idx, int T, int E, int k, int n_shared, int bm, int32_t *counts,
     int32_t *offsets, int32_t *perm, int32_t *inv, int32_t *rank, int32_t *mprefix,
     int32_t *out_counts, int32_t *out_offsets, int32_t *out_perm, int32_t *out_inv,
-    uint64_t *route_counts, RouteIn qin, int H, int Kp, uint8_t *xq, uint8_t *xs) {
+    uint64_t *route_counts, RouteIn qin, int H, int Kp, uint8_t *xq, uint8_t *xs, int fp4) {
     __shared__ int wcnt[16][kMaxE];
     __shared__ int base[kMaxE + 1];
     __shared__ int start[kMaxE + 2];
     if (blockIdx.x > 0) {
-        quantize_terms_wgs(qin, T, H, Kp, xq, xs, 1);
+        quantize_terms_wgs(qin, T, H, Kp, xq, xs, 1, fp4);
         return;
     }
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
@@ -544,18 +557,18 @@ RouterPlan router_plan(int T, int H, int E) {
 namespace {
 template <int KIND, bool NORM>
 void router_launch(const RouterPlan &p, const RouteIn &in, const float *w, int T, int H, int E,
-                   double *partial, int qwant, uint8_t *xq, uint8_t *xs, hipStream_t s) {
+                   double *partial, int qwant, uint8_t *xq, uint8_t *xs, int fp4, hipStream_t s) {
     const int Kp = pad128(H);
     if (p.gemv) {
         const int rwgs = (E * p.splits + 3) / 4;
         launch_kernel(router_gemv_kernel<KIND, NORM>, rwgs + qwant, 256, s, in, w, T, H, E,
-                      partial, rwgs, Kp, xq, xs);
+                      partial, rwgs, Kp, xq, xs, fp4);
     } else {
         const int tt = (T + 63) / 64, te = (E + 63) / 64;
         const int rwgs = tt * te * p.splits;
         const int qwgs = qwant < kQuantizeMaxWgs ? qwant : kQuantizeMaxWgs;
         launch_kernel(router_tiled_kernel<KIND, NORM>, rwgs + qwgs, 256, s, in, w, T, H, E,
-                      p.slice, tt, te, rwgs, partial, Kp, xq, xs);
+                      p.slice, tt, te, rwgs, partial, Kp, xq, xs, fp4);
     }
 }
 }  // namespace
@@ -567,13 +580,31 @@ hipError_t launch_router(const RouteIn &in, const float *w, int T, int H, int E,
     const int qwant = terms ? (T * (pad128(H) / 32) + 7) / 8 : 0;
     uint8_t *xq = terms ? terms->q : nullptr;
     uint8_t *xs = terms ? terms->scales : nullptr;
+    const int fp4 = terms ? terms->fp4 : 0;
     if (in.inv) {
-        if (in.bf16) router_launch<1, true>(p, in, w, T, H, E, partial, qwant, xq, xs, s);
-        else router_launch<0, true>(p, in, w, T, H, E, partial, qwant, xq, xs, s);
+        if (in.bf16) router_launch<1, true>(p, in, w, T, H, E, partial, qwant, xq, xs, fp4, s);
+        else router_launch<0, true>(p, in, w, T, H, E, partial, qwant, xq, xs, fp4, s);
     } else {
-        if (in.bf16) router_launch<1, false>(p, in, w, T, H, E, partial, qwant, xq, xs, s);
-        else router_launch<0, false>(p, in, w, T, H, E, partial, qwant, xq, xs, s);
+        if (in.bf16) router_launch<1, false>(p, in, w, T, H, E, partial, qwant, xq, xs, fp4, s);
+        else router_launch<0, false>(p, in, w, T, H, E, partial, qwant, xq, xs, fp4, s);
     }
+    return hipGetLastError();
+}
+
+namespace {
+// Rows of H values (the block count per row H / 32 in place of pad128(H) / 32,
+// so that rows are packed without padding).
+__global__ __launch_bounds__(256) void act_fp4_kernel(RouteIn in, int T, int H, uint8_t *q,
+                                                      uint8_t *scales) {
+    quantize_terms_wgs(in, T, H, H, q, scales, 0, 1);
+}
+}  // namespace
+
+hipError_t launch_act_fp4(const RouteIn &in, int T, int H, uint8_t *q, uint8_t *scales,
+                          hipStream_t s) {
+    const int want = (T * (H / 32) + 7) / 8;  // one round of 8 blocks per workgroup
+    launch_kernel(act_fp4_kernel, want < kQuantizeMaxWgs ? want : kQuantizeMaxWgs, 256, s, in, T, H,
+                  q, scales);
     return hipGetLastError();
 }
 
@@ -601,7 +632,7 @@ hipError_t launch_permute(const int32_t *idx, int T, int E, int k, int n_shared,
     launch_kernel(permute_kernel, 1 + qwgs, 1024, s, idx, T, E, k, n_shared, tile_rows, counts,
                   offsets, perm, inv, rank, mprefix, out_counts, out_offsets, out_perm, out_inv,
                   route_counts, terms ? *qin : none, H, Kp, terms ? terms->q : nullptr,
-                  terms ? terms->scales : nullptr);
+                  terms ? terms->scales : nullptr, terms ? terms->fp4 : 0);
     return hipGetLastError();
 }
 

@@ -156,6 +156,8 @@ def _call(fn_name, shape, **over):
     ("bad dtype", dict(act_dtype="x"), {}, None),
     ("small workspace", {}, dict(ws_bytes=1024), _lib.MOE_ERR_WORKSPACE),
     ("null workspace", {}, dict(ws=None), _lib.MOE_ERR_WORKSPACE),
+    ("act_quant 2", dict(act_quant=2), {}, _lib.MOE_ERR_INVALID_ARG),
+    ("act_quant -1", dict(act_quant=-1), {}, _lib.MOE_ERR_INVALID_ARG),
     ("misaligned workspace", {}, dict(ws=FAKE + 64), _lib.MOE_ERR_WORKSPACE),
     ("nonpositive limit", dict(limit=0.0), {}, _lib.MOE_ERR_INVALID_ARG),
     ("nonpositive scale", dict(route_scale=-1.0), {}, _lib.MOE_ERR_INVALID_ARG),
@@ -221,6 +223,36 @@ def test_prefill_plan_of_the_workloads(cid, tile, x_terms):
     assert plan["act_terms"] == 3
     assert plan["gate_up_features"] == (128 if tile == 16 else 256)
     assert plan["down_rows"] == 2 * plan["gate_up_features"]
+
+
+@pytest.mark.parametrize("cid", [3, 4, 5, 6])
+def test_prefill_plan_of_the_quantised_mode(cid):
+    cfg = config_by_id(cid)
+    kw = cfg.shape_kwargs()
+    exact = mx.moe_prefill_plan(mx.make_shape(**kw), with_norm=cfg.rms_eps is not None)
+    quant = mx.moe_prefill_plan(mx.make_shape(**kw, act_quant=1), with_norm=cfg.rms_eps is not None)
+    assert quant["x_terms"] == 0
+    assert {k: v for k, v in quant.items() if k != "x_terms"} == \
+        {k: v for k, v in exact.items() if k != "x_terms"}
+
+
+def test_decode_rejects_the_quantised_mode():
+    # the mode check runs before any device call
+    assert _call("moe_forward_decode", _shape(act_quant=1)) == _lib.MOE_ERR_UNSUPPORTED
+    assert _call("moe_forward_decode", _shape(T=64, act_quant=1)) == _lib.MOE_ERR_UNSUPPORTED
+
+
+def test_act_quant_debug_rejects_bad_arguments():
+    lib = _lib.load()
+    s = _shape()
+    fn = lib.moe_act_quant_debug
+    assert fn(ctypes.byref(s), None, None, FAKE, FAKE, FAKE, 1 << 40, None) == _lib.MOE_ERR_INVALID_ARG
+    assert fn(ctypes.byref(s), FAKE, None, None, FAKE, FAKE, 1 << 40, None) == _lib.MOE_ERR_INVALID_ARG
+    assert fn(ctypes.byref(s), FAKE + 4, None, FAKE, FAKE, FAKE, 1 << 40, None) == _lib.MOE_ERR_INVALID_ARG
+    assert fn(ctypes.byref(s), FAKE, None, FAKE, FAKE, FAKE, 16, None) == _lib.MOE_ERR_WORKSPACE
+    assert fn(ctypes.byref(_shape(H=100)), FAKE, None, FAKE, FAKE, FAKE, 1 << 40, None) == \
+        _lib.MOE_ERR_INVALID_ARG
+    assert fn(ctypes.byref(_shape(T=0)), None, None, None, None, None, 0, None) == 0
 
 
 def test_prefill_plan_rejects_bad_arguments():
