@@ -82,7 +82,10 @@ def expert(x, planes, e: int, H: int, F: int, alpha, limit, up_offset):
 
 
 def block(layer, x, k: int, alpha: float, limit: float, up_offset: float,
-          route_scale: float = 1.0, rms_eps=None):
+          route_scale: float = 1.0, rms_eps=None, token_ids=None):
+    """A layer with `sel_bias` ranks logits + bias in the subset enumeration
+    (weights from the logits alone); one with `tid2eid` takes row
+    token_ids[t] of the table as the token's experts, in row order."""
     T, H = len(x), len(x[0])
     E = len(layer.router_w)
     F = len(layer.experts.gate_bias[0])
@@ -95,7 +98,14 @@ def block(layer, x, k: int, alpha: float, limit: float, up_offset: float,
             xt = [xt[h] * inv * float(layer.norm_w[h]) for h in range(H)]
         logits = [math.fsum(float(layer.router_w[e][h]) * xt[h] for h in range(H))
                   + float(layer.router_b[e]) for e in range(E)]
-        sel = top_k_bruteforce(logits, k)
+        sel_bias = getattr(layer, "sel_bias", None)
+        tid2eid = getattr(layer, "tid2eid", None)
+        if tid2eid is not None:
+            sel = [int(e) for e in tid2eid[int(token_ids[t])]]
+        elif sel_bias is not None:
+            sel = top_k_bruteforce([logits[e] + float(sel_bias[e]) for e in range(E)], k)
+        else:
+            sel = top_k_bruteforce(logits, k)
         m = max(logits[e] for e in sel)
         z = [math.exp(logits[e] - m) for e in sel]
         s = math.fsum(z)

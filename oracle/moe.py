@@ -6,7 +6,8 @@ doc "One decoder layer"; goosedump `gpt_oss.rs`, `mixture_of_experts` and
 
     xn     = rms_norm(x)                          (only where the layer has a norm)
     logits = xn @ router^T + router_bias
-    idx    = top-k of logits (k largest; ties to the lower expert index)
+    idx    = top-k of logits (k largest; ties to the lower expert index), or of
+             logits + a selection-only bias, or a hash table's row (DeepSeek-V4)
     w      = route_scale * softmax(logits[idx])   (softmax over the k selected)
     y_j    = down_j(swiglu(gate_j(xn) + bg_j, up_j(xn) + bu_j)) + bd_j
     out    = resid + sum_j w_j * y_j  (+ shared expert with weight 1)
@@ -160,16 +161,51 @@ def expert_ffn(xr: np.ndarray, planes, e: int, alpha: float, limit: float, up_of
 # `prefill`). Shared expert: antirez `ds4.c` `DS4_SHAPE_FLASH`
 # (`n_expert_shared` 1) with no gate tensor for it; reading: weight 1.
 # --------------------------------------------------------------------------
-def route(xn, router_w, router_b, k: int, route_scale: float):
+def route(xn, router_w, router_b, k: int, route_scale: float, sel_bias=None, hash_rows=None):
     logits = router_logits(xn, router_w, router_b)
-    idx = top_k(logits, k)
+    idx, sel = select_experts(logits, k, sel_bias, hash_rows)
     w = route_weights(logits, idx, route_scale)
-    return logits, idx, w
+    return logits, idx, w, sel
+
+
+# --------------------------------------------------------------------------
+# DeepSeek-V4 routing variants. Page: antirez `ds4.c`: `ds4_layer_weights`
+# holds `ffn_exp_probs_b` and `ffn_gate_tid2eid`; `weights_validate_layout`
+# declares exp_probs_b F32 [n_expert] (optional) and tid2eid I32
+# [n_expert_used, n_vocab] for layers il < n_hash_layer (ggml order: the
+# first dimension is the contiguous one, so the table holds one row of k
+# experts per token id); `DS4_SHAPE_FLASH` sets n_hash_layer 3 and n_vocab
+# 129280. The routing arithmetic itself is cut off the page. Readings:
+#  - selection-only bias: the experts are the top-k (ties to the lower index)
+#    of logits + exp_probs_b, taken in float64; the bias takes no part in the
+#    weights, which stay route_scale * softmax over the selected experts'
+#    own logits, in selection order;
+#  - hash routing: a token with id v takes the k experts of table row v, in
+#    row order; the router still runs, and the weights are route_scale *
+#    softmax over those experts' logits.
+# Parity pinned by brute force over k-subsets (`brute.block`), closed forms
+# on constructed routers and the invariances in the tests.
+# --------------------------------------------------------------------------
+def select_experts(logits: np.ndarray, k: int, sel_bias=None, hash_rows=None):
+    """Returns (idx [T, k] int32, the values the selection ranked [T, E]).
+
+    hash_rows [T, k]: the table rows of the tokens' ids (experts in [0, E));
+    else the top-k of logits (+ sel_bias [E] when given)."""
+    logits = np.asarray(logits, dtype=np.float64)
+    T, E = logits.shape
+    if hash_rows is not None:
+        idx = np.asarray(hash_rows, dtype=np.int64)
+        if idx.shape != (T, k) or idx.min(initial=0) < 0 or idx.max(initial=0) >= E:
+            raise ValueError("hash rows must be [T, k] experts in [0, E)")
+        return idx.astype(np.int32), logits
+    sel = logits if sel_bias is None else logits + np.asarray(sel_bias, dtype=np.float64)[None, :]
+    return top_k(sel, k), sel
 
 
 def moe_block(layer, x: np.ndarray, k: int, alpha: float, limit: float, up_offset: float,
               route_scale: float = 1.0, rms_eps: float | None = None,
-              tokens=None, stats: dict | None = None, act_quant: int = 0) -> dict:
+              tokens=None, stats: dict | None = None, act_quant: int = 0,
+              token_ids=None) -> dict:
     """Run one block on x [T, H] (exact input values; the residual is x).
 
     Routing is computed for all T tokens; expert outputs only for `tokens`
@@ -182,11 +218,23 @@ def moe_block(layer, x: np.ndarray, k: int, alpha: float, limit: float, up_offse
     goosedump `mixture_of_experts` quantises the expert input once,
     `Q8Activation`). Reading: routing keeps the unquantised input, and the
     SwiGLU output is not quantised.
+
+    A layer with `sel_bias` [E] selects with the selection-only bias; one with
+    `tid2eid` [vocab, k] routes token t by table row token_ids[t] (see
+    `select_experts`).
     """
     x = np.asarray(x, dtype=np.float64)
     T = x.shape[0]
     xn = x if layer.norm_w is None else rms_norm(x, layer.norm_w, rms_eps)
-    logits, idx, w = route(xn, layer.router_w, layer.router_b, k, route_scale)
+    sel_bias = getattr(layer, "sel_bias", None)
+    tid2eid = getattr(layer, "tid2eid", None)
+    hash_rows = None
+    if tid2eid is not None:
+        if token_ids is None or len(token_ids) != T:
+            raise ValueError("hash routing needs one token id per row")
+        hash_rows = np.asarray(tid2eid)[np.asarray(token_ids, dtype=np.int64)]
+    logits, idx, w, sel = route(xn, layer.router_w, layer.router_b, k, route_scale, sel_bias,
+                                hash_rows)
     xe = xn
     if act_quant:
         xe = act_quant_mod.quantize_rows(xn.astype(np.float32))[2]
@@ -207,12 +255,13 @@ def moe_block(layer, x: np.ndarray, k: int, alpha: float, limit: float, up_offse
         for s in range(layer.shared.n):
             delta += expert_ffn(xe[toks], layer.shared, s, alpha, limit, up_offset, stats)
     out = (x[toks] + delta).astype(np.float32)
-    return dict(out=out, delta=delta, logits=logits, idx=idx, w=w, counts=counts,
-                offsets=offsets, perm=perm, inv=inv, xn=xn, xe=xe, tokens=toks)
+    return dict(out=out, delta=delta, logits=logits, sel=sel, idx=idx, w=w, counts=counts,
+                offsets=offsets, perm=perm, inv=inv, xn=xn, xe=xe, tokens=toks,
+                hashed=hash_rows is not None)
 
 
 def moe_stack(layers, x: np.ndarray, k: int, alpha: float, limit: float, up_offset: float,
-              route_scale: float = 1.0, rms_eps: float | None = None) -> list:
+              route_scale: float = 1.0, rms_eps: float | None = None, token_ids=None) -> list:
     """Chain blocks: each layer's float32 output is the next layer's input.
 
     Page: goosedump `prefill`/`forward` apply the MoE once per layer and carry
@@ -221,12 +270,15 @@ def moe_stack(layers, x: np.ndarray, k: int, alpha: float, limit: float, up_offs
     outs = []
     h = np.asarray(x, dtype=np.float32)
     for layer in layers:
-        r = moe_block(layer, h, k, alpha, limit, up_offset, route_scale, rms_eps)
+        r = moe_block(layer, h, k, alpha, limit, up_offset, route_scale, rms_eps,
+                      token_ids=token_ids)
         outs.append(r)
         h = r["out"]
     return outs
 
 
-def block_for_config(cfg, layer, x, tokens=None, stats=None, act_quant: int = 0) -> dict:
+def block_for_config(cfg, layer, x, tokens=None, stats=None, act_quant: int = 0,
+                     token_ids=None) -> dict:
     return moe_block(layer, x, cfg.k, cfg.alpha, cfg.limit, cfg.up_offset, cfg.route_scale,
-                     cfg.rms_eps, tokens=tokens, stats=stats, act_quant=act_quant)
+                     cfg.rms_eps, tokens=tokens, stats=stats, act_quant=act_quant,
+                     token_ids=token_ids)

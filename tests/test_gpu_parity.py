@@ -114,7 +114,7 @@ def test_route_parity(cid, T):
     torch.cuda.synchronize()
     got = to_np(ro)
     xn = x.astype(np.float64) if layer.norm_w is None else omoe.rms_norm(x, layer.norm_w, cfg.rms_eps)
-    logits, idx, w = omoe.route(xn, layer.router_w, layer.router_b, cfg.k, cfg.route_scale)
+    logits, idx, w, _ = omoe.route(xn, layer.router_w, layer.router_b, cfg.k, cfg.route_scale)
     ref = dict(logits=logits, idx=idx, w=w, xn=xn)
     check_routing(got["topk_idx"], got["topk_w"], ref, layer.router_w, layer.router_b,
                   cfg.route_scale)

@@ -189,7 +189,7 @@ def _routed_trace(cfg, P, layers):
         xn = x.astype(np.float64)
         if lay.norm_w is not None:
             xn = moe.rms_norm(xn, lay.norm_w, cfg.rms_eps)
-        _, i, ww = moe.route(xn, lay.router_w, lay.router_b, cfg.k, cfg.route_scale)
+        _, i, ww, _ = moe.route(xn, lay.router_w, lay.router_b, cfg.k, cfg.route_scale)
         idx[:, l], w[:, l] = i, ww
     return idx, w
 
@@ -258,7 +258,7 @@ def test_gpu_decode_trace_locality():
     for l in range(L):  # each layer's selections are the oracle's on the GPU's layer input
         lay = make_layer(cfg, l)
         xn = moe.rms_norm(inputs[l].astype(np.float64), lay.norm_w, cfg.rms_eps)
-        _, oi, ow = moe.route(xn, lay.router_w, lay.router_b, cfg.k, cfg.route_scale)
+        _, oi, ow, _ = moe.route(xn, lay.router_w, lay.router_b, cfg.k, cfg.route_scale)
         assert np.array_equal(gidx[:, l], oi), l
         assert np.allclose(gw[:, l], ow, rtol=1e-5, atol=1e-6), l
     r, _ = _assert_library_equals_oracle(gidx, gw, cfg.E)

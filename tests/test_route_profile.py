@@ -19,7 +19,7 @@ def _routing(cfg, T, layer=0):
     xn = x.astype(np.float64)
     if lay.norm_w is not None:
         xn = moe.rms_norm(xn, lay.norm_w, cfg.rms_eps)
-    _, idx, _ = moe.route(xn, lay.router_w, lay.router_b, cfg.k, cfg.route_scale)
+    _, idx, _, _ = moe.route(xn, lay.router_w, lay.router_b, cfg.k, cfg.route_scale)
     return idx
 
 

@@ -1,5 +1,6 @@
-"""The workload configurations, as data: the five of the block, and a sixth
-with the DeepSeek-V4-Pro shape (a next step after the five).
+"""The workload configurations, as data: the five of the block, a sixth with
+the DeepSeek-V4-Pro shape, and two DeepSeek-V4-Flash layers with the routing
+variants (selection-only bias; hash routing).
 
 Model constants come from the pages:
 - gpt-oss-20b (goosedump 0.12.31 `src/engine/model/gpt_oss.rs`, constants block):
@@ -9,6 +10,10 @@ Model constants come from the pages:
 - DeepSeek-V4-Flash (antirez `ds4.c`, `DS4_SHAPE_FLASH`): n_embd 4096,
   n_ff_exp 2048, 256 routed experts, 6 used, 1 shared expert, expert weight
   scale 1.5, SwiGLU clamp 10 (`DS4_DEFAULT_SWIGLU_CLAMP_EXP`).
+- DeepSeek-V4 routing variants (`ds4_layer_weights`, `weights_validate_layout`,
+  `DS4_SHAPE_FLASH`): the optional selection-only bias exp_probs_b [n_expert]
+  and, for the first n_hash_layer = 3 layers, the tid2eid table of
+  n_expert_used experts per token id over n_vocab = 129280 ids.
 - DeepSeek-V4-Pro (`DS4_SHAPE_PRO`): n_embd 7168, n_ff_exp 3072, 384 routed
   experts, 6 used, 1 shared, expert weight scale 2.5, the same default clamp.
   Everything the page leaves open (batch, router, activations, SwiGLU alpha
@@ -46,6 +51,8 @@ class MoeConfig:
     zipf_s: float = 1.1
     calls: int = 1          # independent block calls making up one pass
     path: str = "prefill"   # which entry point the workload exercises
+    sel_bias_std: float = 0.0  # selection-only expert bias ~ N(0, std^2) when > 0
+    hash_vocab: int = 0        # hash routing by token id over this vocabulary when > 0
 
     @property
     def R(self) -> int:
@@ -74,6 +81,15 @@ CONFIGS = (
     MoeConfig(6, "ds4_pro", T=2048, H=7168, F=3072, E=384, k=6,
               alpha=1.0, limit=10.0, up_offset=0.0, route_scale=2.5,
               n_shared=1, act_dtype="bf16", router="uniform"),
+    # DeepSeek-V4-Flash layer with the selection-only expert bias (exp_probs_b)
+    MoeConfig(7, "ds4_flash_selbias", T=2048, H=4096, F=2048, E=256, k=6,
+              alpha=1.0, limit=10.0, up_offset=0.0, route_scale=1.5,
+              n_shared=1, act_dtype="bf16", router="uniform", sel_bias_std=0.5),
+    # DeepSeek-V4-Flash hash-routed layer (one of the first n_hash_layer = 3):
+    # experts from the tid2eid table row of each token id, vocabulary 129280
+    MoeConfig(8, "ds4_flash_hash", T=2048, H=4096, F=2048, E=256, k=6,
+              alpha=1.0, limit=10.0, up_offset=0.0, route_scale=1.5,
+              n_shared=1, act_dtype="bf16", router="uniform", hash_vocab=129280),
 )
 
 

@@ -14,6 +14,10 @@ Recipe (identical for the oracle and the GPU harness):
 - Activations x ~ N(0, 1); for bf16 workloads x is drawn in fp32 and rounded
   to bf16 (nearest, ties to even); `x` then holds the exact widening.
 - RMSNorm weight gamma ~ 1 + N(0, 0.1) when the workload has a norm.
+- Routing variants (stream 4): selection-only bias [E] ~ N(0, sel_bias_std^2)
+  in fp32; hash table tid2eid [vocab, k] int32, each row k distinct experts
+  drawn uniformly without replacement. Token ids (stream 5) uniform over
+  the vocabulary, one per activation row.
 
 Arrays use the planar MXFP4 form: codes [E, rows, K/2] (element 2i in the low
 nibble of byte i), scale bytes [E, rows, K/32], biases [E, rows].
@@ -28,6 +32,7 @@ from .configs import MoeConfig
 
 BASE_SEED = 20261202
 STREAM_ROUTER, STREAM_EXPERTS, STREAM_ACT, STREAM_NORM = 0, 1, 2, 3
+STREAM_ROUTING, STREAM_TOKENS = 4, 5
 
 
 def rng_for(config_id: int, stream: int, layer: int = 0) -> np.random.Generator:
@@ -67,6 +72,8 @@ class Layer:
     experts: ExpertPlanes
     shared: ExpertPlanes | None = None
     norm_w: np.ndarray | None = None  # [H] f32
+    sel_bias: np.ndarray | None = None  # [E] f32 selection-only expert bias
+    tid2eid: np.ndarray | None = None   # [vocab, k] int32 hash-routing table
 
 
 @dataclass
@@ -124,7 +131,37 @@ def make_layer(cfg: MoeConfig, layer: int = 0) -> Layer:
     if cfg.rms_eps is not None:
         nrng = rng_for(cfg.config_id, STREAM_NORM, layer)
         norm_w = (1.0 + nrng.normal(0.0, 0.1, size=cfg.H)).astype(np.float32)
-    return Layer(rw, rb, experts, shared, norm_w)
+    sel_bias = tid2eid = None
+    if cfg.sel_bias_std > 0 or cfg.hash_vocab > 0:
+        rrng = rng_for(cfg.config_id, STREAM_ROUTING, layer)
+        if cfg.sel_bias_std > 0:
+            sel_bias = rrng.normal(0.0, cfg.sel_bias_std, size=cfg.E).astype(np.float32)
+        if cfg.hash_vocab > 0:
+            tid2eid = distinct_rows(rrng, cfg.hash_vocab, cfg.E, cfg.k)
+    return Layer(rw, rb, experts, shared, norm_w, sel_bias, tid2eid)
+
+
+def distinct_rows(rng: np.random.Generator, rows: int, n: int, k: int) -> np.ndarray:
+    """[rows, k] int32: each row k distinct values of 0..n-1, uniformly without
+    replacement (the j-th draw picks among the n - j values still free, then
+    steps over the earlier picks in ascending order)."""
+    out = np.empty((rows, k), dtype=np.int64)
+    for j in range(k):
+        c = rng.integers(0, n - j, size=rows)
+        taken = np.sort(out[:, :j], axis=1)
+        for i in range(j):
+            c = c + (c >= taken[:, i])
+        out[:, j] = c
+    return out.astype(np.int32)
+
+
+def make_token_ids(cfg: MoeConfig, rows: int | None = None) -> np.ndarray | None:
+    """Token ids [rows] int32 for hash-routed workloads (None otherwise)."""
+    if cfg.hash_vocab <= 0:
+        return None
+    rows = cfg.T * cfg.calls if rows is None else rows
+    rng = rng_for(cfg.config_id, STREAM_TOKENS)
+    return rng.integers(0, cfg.hash_vocab, size=rows).astype(np.int32)
 
 
 def _round_to_bf16_bits(x: np.ndarray) -> np.ndarray:
