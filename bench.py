@@ -6,14 +6,17 @@
 
 A step is one pass of the whole block over one batch of seeded synthetic
 input (weights and activations resident in HBM before timing):
-  suite   (default) decode as the headline line, with prefill, stack, ds4 and
-          ds4_q4 measured after it and nested under "workloads"
+  suite   (default) decode as the headline line, with prefill, stack, ds4,
+          ds4_q4, ds4_selbias and ds4_hash measured after it and nested under
+          "workloads"
   decode  gpt-oss-20b-shaped layer, 1000 tokens as T=1 calls
   prefill gpt-oss-20b-shaped layer, T=128, Zipf(1.1)-skewed expert loads
   stack   24 gpt-oss-20b-shaped layers (RMSNorm + MoE), T=512
   ds4     DeepSeek-V4-Flash-shaped layer, T=2048, 256 experts top-6 + shared
   ds4_q4  ds4 in the quantised expert-input mode (MX-FP4 expert input, FP4 x FP4
           gate/up products)
+  ds4_selbias  ds4 with the selection-only expert bias (exp_probs_b)
+  ds4_hash     ds4 hash-routed by token id (tid2eid table over 129280 ids)
   ds4_pro DeepSeek-V4-Pro-shaped layer, T=2048, H=7168, F=3072, 384 experts top-6 + shared
   tiny    T=8, H=F=256, 8 experts top-2
   decode_stack  T=1 tokens through 24 gpt-oss-20b-shaped layers (RMSNorm + MoE),
@@ -70,6 +73,11 @@ WORKLOADS = {
     # the same layer with the expert input rounded once to MX-FP4 (act_quant=1)
     "ds4_q4": dict(config=5, name="ds4flash_T2048_E256_top6_shared_mxfp4_input",
                    kernel="gate_up_gemm", copies=2, steps=50, act_quant=1),
+    # DeepSeek-V4 routing variants on the same layer shape
+    "ds4_selbias": dict(config=7, name="ds4flash_T2048_E256_top6_shared_selbias",
+                        kernel="gate_up_gemm", copies=2, steps=50),
+    "ds4_hash": dict(config=8, name="ds4flash_T2048_E256_top6_shared_hash129280",
+                     kernel="gate_up_gemm", copies=2, steps=50),
     "tiny": dict(config=1, name="tiny_T8_H256_E8_top2", kernel="decode_gate_up", copies=1,
                  steps=200),
     # DeepSeek-V4-Pro-shaped layer (H=7168, F=3072, 384 experts top-6 + shared,
@@ -169,7 +177,7 @@ class Setup:
 
         import mxfp4_expert_ffn_amd as mx
         from mxfp4_expert_ffn_amd.device import upload_layer, workspace
-        from workloads import config_by_id, make_layer
+        from workloads import config_by_id, make_layer, make_token_ids
         from workloads.gen import make_activations
 
         spec = WORKLOADS[wl]
@@ -180,6 +188,9 @@ class Setup:
         t0 = time.time()
         x, xb = make_activations(cfg)
         self.x_host = x
+        self.token_ids = make_token_ids(cfg)   # hash-routed workloads only
+        self.ids_dev = (None if self.token_ids is None
+                        else torch.from_numpy(self.token_ids).cuda())
         n_layers = cfg.layers
         self.host_layers = []
         self.layers = []
@@ -269,7 +280,8 @@ class Setup:
                 dst = bufs[l % 2]
                 calls.append(lambda dl=dl, src=src, dst=dst, l=l: mx.moe_forward_prefill(
                     self.shape, src, dl.router_w, dl.router_b, dl.experts_copy(step), dst,
-                    self.ws, norm_w=dl.norm_w, shared=dl.shared_copy(step), route_out=self._ro(l)))
+                    self.ws, norm_w=dl.norm_w, shared=dl.shared_copy(step), route_out=self._ro(l),
+                    routing=dl.routing(self.ids_dev)))
                 src = dst
         return calls
 
@@ -374,7 +386,7 @@ def route_counts(setup):
         dst = bufs[l % 2]
         mx.moe_forward_prefill(setup.shape, src, dl.router_w, dl.router_b, dl.experts_copy(0), dst,
                                setup.ws, norm_w=dl.norm_w, shared=dl.shared_copy(0),
-                               route_out={"counts": counts})
+                               route_out={"counts": counts}, routing=dl.routing(setup.ids_dev))
         torch.cuda.synchronize()
         res.append(counts.cpu().tolist())
         src = dst
@@ -470,8 +482,10 @@ def cpu_baseline(setup, budget_s: float):
     while n > 1 and experts_touched(n) * per_expert > budget_s:
         n = int(n * 0.9)
     toks = np.arange(n)
+    ids = None if setup.token_ids is None else setup.token_ids[:cfg.T]
     done, dt, calls = run_units(lambda i: omoe.block_for_config(cfg, layer, x[:cfg.T], tokens=toks,
-                                                                act_quant=setup.act_quant), n)
+                                                                act_quant=setup.act_quant,
+                                                                token_ids=ids), n)
     scaled = f", divided by {layers} layers" if layers > 1 else ""
     mode = ", MX-FP4 expert input" if setup.act_quant else ""
     return dict(value=done / dt / layers, unit="tokens/s", cores=cores, kind="oracle",
@@ -511,7 +525,8 @@ def route_locality(setup) -> dict:
 
 # the default run: the decode headline, then these workloads nested under
 # "workloads" (each with its own step count)
-SUITE = (("prefill", "prefill_T128"), ("stack", "stack_T512"), ("ds4", "ds4"), ("ds4_q4", "ds4_q4"))
+SUITE = (("prefill", "prefill_T128"), ("stack", "stack_T512"), ("ds4", "ds4"), ("ds4_q4", "ds4_q4"),
+         ("ds4_selbias", "ds4_selbias"), ("ds4_hash", "ds4_hash"))
 
 
 def measure(wl: str, args, steps: int, warmup: int) -> dict:

@@ -258,19 +258,47 @@ int moe_pack_experts(const moe_shape *shape, int32_t n, const moe_expert_planes 
  * phase). */
 size_t moe_workspace_bytes(const moe_shape *shape);
 
+/* DeepSeek-V4 routing variants (page: antirez ds4.c `ds4_layer_weights`
+ * holds `ffn_exp_probs_b` and `ffn_gate_tid2eid`; `weights_validate_layout`
+ * declares exp_probs_b F32 [n_expert], optional, and tid2eid I32
+ * [n_expert_used, n_vocab] for the layers below `n_hash_layer`, 3 in
+ * `DS4_SHAPE_FLASH`; the routing arithmetic itself is cut off the page).
+ * Pass NULL, or a struct with both pointers NULL, for plain top-k routing.
+ *   sel_bias   [E] float32, device, or NULL: selection-only bias. The k
+ *              experts are the top-k of logit + sel_bias (fp64; equal values
+ *              to the lower index); the route weights stay route_scale *
+ *              softmax over the selected experts' own logits.
+ *   tid2eid    [vocab, k] int32, device, or NULL: hash routing. Token t
+ *              takes the k experts of row token_ids[t], in row order, with
+ *              weights route_scale * softmax over their logits (the router
+ *              still runs); sel_bias is not read.
+ *   token_ids  [T] int32, device; required with tid2eid
+ *   vocab      rows of tid2eid, >= 1 with tid2eid
+ * Token ids outside [0, vocab) and table entries outside [0, E) are clamped
+ * into those ranges (results are then unspecified; every access stays in
+ * bounds). Rows should hold k distinct experts. MOE_ERR_INVALID_ARG for a
+ * table without ids or vocab < 1, or a pointer not 4-byte aligned. */
+typedef struct moe_routing {
+    const float *sel_bias;
+    const int32_t *tid2eid;
+    const int32_t *token_ids;
+    int32_t vocab;
+} moe_routing;
+
 /* Routing only: optional RMSNorm, router logits in fp64, top-k, route weights,
  * per-expert histogram, exclusive scan and stable permutation.
  *   x        [T, H] float32 or bfloat16 (shape->act_dtype), device
  *   norm_w   [H] float32 RMSNorm weight or NULL (no norm), device
  *   router_w [E, H] float32, router_b [E] float32, device
+ *   routing  NULL (plain top-k) or a routing variant (moe_routing)
  *   x, norm_w and router_w 16-byte aligned (MOE_ERR_INVALID_ARG otherwise)
  *   out      non-NULL; NULL fields are not written (see moe_route_out)
  *   ws       >= moe_workspace_bytes(shape) bytes, 256-byte aligned, device
  * Pages: goosedump `mixture_of_experts_batch` (router matmul, add_bias_batch,
  * top_experts, softmax, routes_by_expert). */
 int moe_route(const moe_shape *shape, const void *x, const float *norm_w,
-              const float *router_w, const float *router_b, const moe_route_out *out,
-              void *ws, size_t ws_bytes, hipStream_t stream);
+              const float *router_w, const float *router_b, const moe_routing *routing,
+              const moe_route_out *out, void *ws, size_t ws_bytes, hipStream_t stream);
 
 /* The whole block for a few tokens (T <= 64): streams only the k selected
  * experts' bytes per token with GEMV kernels on the matrix cores.
@@ -279,15 +307,16 @@ int moe_route(const moe_shape *shape, const void *x, const float *norm_w,
  *   shared   n_shared packed blobs (same layout) or NULL when n_shared == 0
  *   out      [T, H] float32, device; may alias a float32 hidden
  *   route_out NULL, or routing results to export (fields may be NULL)
- *   norm_w, router_w, router_b, ws as for moe_route
+ *   norm_w, router_w, router_b, routing, ws as for moe_route
  *   hidden, out, norm_w and router_w 16-byte aligned, expert blobs 256-byte
  * Pages: goosedump `mixture_of_experts` (router matvec, add_bias,
  * top_experts, softmax, per expert: matrix_vector_pair, biases, swiglu,
  * matrix_vector, bias, times the route weight, summed over slots). */
 int moe_forward_decode(const moe_shape *shape, const void *hidden, const float *norm_w,
-                       const float *router_w, const float *router_b, const uint8_t *experts,
-                       const uint8_t *shared, float *out, const moe_route_out *route_out,
-                       void *ws, size_t ws_bytes, hipStream_t stream);
+                       const float *router_w, const float *router_b, const moe_routing *routing,
+                       const uint8_t *experts, const uint8_t *shared, float *out,
+                       const moe_route_out *route_out, void *ws, size_t ws_bytes,
+                       hipStream_t stream);
 
 /* The whole block for a token batch: routing, permutation, grouped GEMMs on
  * the matrix cores (gate/up with bias and clamped SwiGLU fused; down with
@@ -298,9 +327,10 @@ int moe_forward_decode(const moe_shape *shape, const void *hidden, const float *
  * Pages: goosedump `mixture_of_experts_batch`, `expert_batch_output`,
  * `mix_expert_outputs`. */
 int moe_forward_prefill(const moe_shape *shape, const void *hidden, const float *norm_w,
-                        const float *router_w, const float *router_b, const uint8_t *experts,
-                        const uint8_t *shared, float *out, const moe_route_out *route_out,
-                        void *ws, size_t ws_bytes, hipStream_t stream);
+                        const float *router_w, const float *router_b, const moe_routing *routing,
+                        const uint8_t *experts, const uint8_t *shared, float *out,
+                        const moe_route_out *route_out, void *ws, size_t ws_bytes,
+                        hipStream_t stream);
 
 /* Size of the fixed device scratch of moe_forward_decode_noalloc: 32 MiB per
  * GPU, enough for every decode shape up to T = 64 at gpt-oss-20b and
@@ -322,7 +352,7 @@ int moe_forward_prefill(const moe_shape *shape, const void *hidden, const float 
  * race on it and give undefined results; order them on one stream. The device
  * is the calling thread's current HIP device, which must own `stream`. */
 int moe_forward_decode_noalloc(const moe_shape *shape, const void *hidden, const float *norm_w,
-                               const float *router_w, const float *router_b,
+                               const float *router_w, const float *router_b, const moe_routing *routing,
                                const uint8_t *experts, const uint8_t *shared, float *out,
                                const moe_route_out *route_out, hipStream_t stream);
 

@@ -88,6 +88,24 @@ def _route_out(route_out):
     return ctypes.byref(ro)
 
 
+def _routing(routing):
+    """routing: None, or a dict with "sel_bias" ([E] float32), or "tid2eid"
+    ([vocab, k] int32) and "token_ids" ([T] int32), device tensors."""
+    import torch
+    if routing is None:
+        return None
+    r = _lib.MoeRouting()
+    unknown = set(routing) - {"sel_bias", "tid2eid", "token_ids"}
+    if unknown:
+        raise ValueError(f"unknown routing fields {sorted(unknown)}")
+    b, tab, ids = routing.get("sel_bias"), routing.get("tid2eid"), routing.get("token_ids")
+    r.sel_bias = None if b is None else _ptr(b, "sel_bias", torch.float32).value
+    r.tid2eid = None if tab is None else _ptr(tab, "tid2eid", torch.int32).value
+    r.token_ids = None if ids is None else _ptr(ids, "token_ids", torch.int32).value
+    r.vocab = 0 if tab is None else int(tab.shape[0])
+    return ctypes.byref(r)
+
+
 def moe_blob_layout_get(shape: MoeShape) -> dict:
     L = MoeBlobLayout()
     _check(_lib.load().moe_blob_layout_get(ctypes.byref(shape), ctypes.byref(L)))
@@ -122,43 +140,44 @@ def moe_workspace_bytes(shape: MoeShape) -> int:
     return int(n)
 
 
-def moe_route(shape, x, router_w, router_b, route_out: dict, ws, norm_w=None, stream=None):
+def moe_route(shape, x, router_w, router_b, route_out: dict, ws, norm_w=None, stream=None,
+              routing=None):
     import torch
     rc = _lib.load().moe_route(
         ctypes.byref(shape), _ptr(x, "x", (torch.float32, torch.bfloat16, torch.int16, torch.uint16)),
         _ptr(norm_w, "norm_w", torch.float32, optional=True),
         _ptr(router_w, "router_w", torch.float32), _ptr(router_b, "router_b", torch.float32),
-        _route_out(route_out), _ptr(ws, "ws"), ws.numel() * ws.element_size(), _stream(stream))
+        _routing(routing), _route_out(route_out), _ptr(ws, "ws"), ws.numel() * ws.element_size(), _stream(stream))
     _check(rc)
 
 
 def _forward(fn, shape, hidden, router_w, router_b, experts, out, ws, norm_w, shared,
-             route_out, stream):
+             route_out, stream, routing):
     import torch
     rc = fn(ctypes.byref(shape),
             _ptr(hidden, "hidden", (torch.float32, torch.bfloat16, torch.int16, torch.uint16)),
             _ptr(norm_w, "norm_w", torch.float32, optional=True),
             _ptr(router_w, "router_w", torch.float32), _ptr(router_b, "router_b", torch.float32),
-            _ptr(experts, "experts", torch.uint8), _ptr(shared, "shared", torch.uint8, optional=True),
+            _routing(routing), _ptr(experts, "experts", torch.uint8), _ptr(shared, "shared", torch.uint8, optional=True),
             _ptr(out, "out", torch.float32), _route_out(route_out), _ptr(ws, "ws"),
             ws.numel() * ws.element_size(), _stream(stream))
     _check(rc)
 
 
 def moe_forward_decode(shape, hidden, router_w, router_b, experts, out, ws, norm_w=None,
-                       shared=None, route_out=None, stream=None):
+                       shared=None, route_out=None, stream=None, routing=None):
     _forward(_lib.load().moe_forward_decode, shape, hidden, router_w, router_b, experts, out, ws,
-             norm_w, shared, route_out, stream)
+             norm_w, shared, route_out, stream, routing)
 
 
 def moe_forward_prefill(shape, hidden, router_w, router_b, experts, out, ws, norm_w=None,
-                        shared=None, route_out=None, stream=None):
+                        shared=None, route_out=None, stream=None, routing=None):
     _forward(_lib.load().moe_forward_prefill, shape, hidden, router_w, router_b, experts, out, ws,
-             norm_w, shared, route_out, stream)
+             norm_w, shared, route_out, stream, routing)
 
 
 def moe_forward_decode_noalloc(shape, hidden, router_w, router_b, experts, out, norm_w=None,
-                               shared=None, route_out=None, stream=None):
+                               shared=None, route_out=None, stream=None, routing=None):
     """moe_forward_decode with the library's fixed per-GPU scratch as its
     workspace: no allocation; calls on one GPU must be ordered on one stream."""
     import torch
@@ -167,7 +186,8 @@ def moe_forward_decode_noalloc(shape, hidden, router_w, router_b, experts, out, 
         _ptr(hidden, "hidden", (torch.float32, torch.bfloat16, torch.int16, torch.uint16)),
         _ptr(norm_w, "norm_w", torch.float32, optional=True),
         _ptr(router_w, "router_w", torch.float32), _ptr(router_b, "router_b", torch.float32),
-        _ptr(experts, "experts", torch.uint8), _ptr(shared, "shared", torch.uint8, optional=True),
+        _routing(routing), _ptr(experts, "experts", torch.uint8),
+        _ptr(shared, "shared", torch.uint8, optional=True),
         _ptr(out, "out", torch.float32), _route_out(route_out), _stream(stream))
     _check(rc)
 

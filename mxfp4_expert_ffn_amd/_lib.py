@@ -49,6 +49,11 @@ class MoeRouteOut(ctypes.Structure):
         "topk_idx", "topk_w", "counts", "offsets", "perm", "inv", "route_counts")]
 
 
+class MoeRouting(ctypes.Structure):
+    _fields_ = [("sel_bias", ctypes.c_void_p), ("tid2eid", ctypes.c_void_p),
+                ("token_ids", ctypes.c_void_p), ("vocab", ctypes.c_int32)]
+
+
 class MoePrefillPlan(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "tile_rows", "x_terms", "act_terms", "gate_up_features", "down_rows")]
@@ -68,13 +73,17 @@ SIGNATURES = {
                                         ctypes.POINTER(MoeExpertPlanes), _P]),
     "moe_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(MoeShape)]),
     "moe_route": (ctypes.c_int, [ctypes.POINTER(MoeShape), _P, _P, _P, _P,
-                                 ctypes.POINTER(MoeRouteOut), _P, ctypes.c_size_t, _P]),
-    "moe_forward_decode": (ctypes.c_int, [ctypes.POINTER(MoeShape), _P, _P, _P, _P, _P, _P, _P,
+                                 ctypes.POINTER(MoeRouting), ctypes.POINTER(MoeRouteOut), _P,
+                                 ctypes.c_size_t, _P]),
+    "moe_forward_decode": (ctypes.c_int, [ctypes.POINTER(MoeShape), _P, _P, _P, _P,
+                                          ctypes.POINTER(MoeRouting), _P, _P, _P,
                                           ctypes.POINTER(MoeRouteOut), _P, ctypes.c_size_t, _P]),
-    "moe_forward_prefill": (ctypes.c_int, [ctypes.POINTER(MoeShape), _P, _P, _P, _P, _P, _P, _P,
+    "moe_forward_prefill": (ctypes.c_int, [ctypes.POINTER(MoeShape), _P, _P, _P, _P,
+                                           ctypes.POINTER(MoeRouting), _P, _P, _P,
                                            ctypes.POINTER(MoeRouteOut), _P, ctypes.c_size_t, _P]),
-    "moe_forward_decode_noalloc": (ctypes.c_int, [ctypes.POINTER(MoeShape), _P, _P, _P, _P, _P,
-                                                  _P, _P, ctypes.POINTER(MoeRouteOut), _P]),
+    "moe_forward_decode_noalloc": (ctypes.c_int, [ctypes.POINTER(MoeShape), _P, _P, _P, _P,
+                                                  ctypes.POINTER(MoeRouting), _P, _P, _P,
+                                                  ctypes.POINTER(MoeRouteOut), _P]),
     "moe_prefill_plan": (ctypes.c_int, [ctypes.POINTER(MoeShape), ctypes.c_int32,
                                         ctypes.POINTER(MoePrefillPlan)]),
     "moe_act_quant_debug": (ctypes.c_int, [ctypes.POINTER(MoeShape), _P, _P, _P, _P, _P,

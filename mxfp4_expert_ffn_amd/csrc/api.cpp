@@ -208,6 +208,24 @@ int launch(int id, const char *what, hipStream_t st, Fn &&fn) {
     return rc;
 }
 
+// The routing variant as the kernels take it (NULL: plain top-k).
+int route_sel_of(const moe_routing *r, moe::RouteSel *rs) {
+    *rs = moe::RouteSel{nullptr, nullptr, nullptr, 0};
+    if (!r) return MOE_OK;
+    if (r->tid2eid) {
+        if (!r->token_ids) return fail(MOE_ERR_INVALID_ARG, "hash routing (tid2eid) needs token_ids");
+        if (r->vocab < 1) return fail(MOE_ERR_INVALID_ARG, "hash routing needs vocab >= 1 (vocab=%d)", r->vocab);
+        if (!aligned(r->tid2eid, 4) || !aligned(r->token_ids, 4))
+            return fail(MOE_ERR_INVALID_ARG, "tid2eid and token_ids must be 4-byte aligned");
+        *rs = moe::RouteSel{nullptr, r->tid2eid, r->token_ids, r->vocab};
+        return MOE_OK;
+    }
+    if (r->sel_bias && !aligned(r->sel_bias, 4))
+        return fail(MOE_ERR_INVALID_ARG, "sel_bias must be 4-byte aligned");
+    rs->bias = r->sel_bias;
+    return MOE_OK;
+}
+
 // Shared argument checks of the two forward entry points.
 int check_forward(const moe_shape *s, const void *hidden, const float *norm_w,
                   const float *router_w, const float *router_b, const uint8_t *experts,
@@ -348,8 +366,8 @@ int moe_route_profile_summary(const uint64_t *counts, int32_t layers, int32_t E,
 }
 
 int moe_route(const moe_shape *s, const void *x, const float *norm_w, const float *router_w,
-              const float *router_b, const moe_route_out *out, void *ws, size_t ws_bytes,
-              hipStream_t st) {
+              const float *router_b, const moe_routing *routing, const moe_route_out *out, void *ws,
+              size_t ws_bytes, hipStream_t st) {
     MOE_TRY(check_shape(s));
     if (s->T == 0) return ok();
     if (!x || !router_w || !router_b || !out)
@@ -357,14 +375,15 @@ int moe_route(const moe_shape *s, const void *x, const float *norm_w, const floa
     if (!aligned(x, 16) || !aligned(router_w, 16) || (norm_w && !aligned(norm_w, 16)))
         return fail(MOE_ERR_INVALID_ARG, "x, router_w and norm_w must be 16-byte aligned");
     if (norm_w && !(s->rms_eps >= 0.f)) return fail(MOE_ERR_INVALID_ARG, "rms_eps must be >= 0");
+    moe::RouteSel rs;
+    MOE_TRY(route_sel_of(routing, &rs));
     MOE_TRY(check_ws(s, ws, ws_bytes));
-    if (s->T == 0) return ok();
     const Workspace w = carve(s, static_cast<uint8_t *>(ws));
     moe::RouteIn in;
     MOE_TRY(route_front(s, x, norm_w, router_w, w, false, nullptr, &in, st));
     MOE_TRY(launch(MOE_KERNEL_TOPK, "topk", st, [&] {
-        return moe::launch_topk(w.partial, w.splits, router_b, s->T, s->E, s->k, s->route_scale,
-                                w.idx, w.wts, out->topk_idx, out->topk_w, st);
+        return moe::launch_topk(w.partial, w.splits, router_b, rs, s->T, s->E, s->k,
+                                s->route_scale, w.idx, w.wts, out->topk_idx, out->topk_w, st);
     }));
     MOE_TRY(launch(MOE_KERNEL_PERMUTE, "permute", st, [&] { return moe::launch_permute(w.idx, s->T, s->E, s->k, 0, 16, w.counts, w.offsets, w.perm,
                                           w.inv, w.rank, w.mprefix, out->counts, out->offsets,
@@ -397,10 +416,12 @@ int moe_act_quant_debug(const moe_shape *s, const void *x, const float *norm_w, 
 }
 
 int moe_forward_decode(const moe_shape *s, const void *hidden, const float *norm_w,
-                       const float *router_w, const float *router_b, const uint8_t *experts,
-                       const uint8_t *shared, float *out, const moe_route_out *ro, void *ws,
-                       size_t ws_bytes, hipStream_t st) {
+                       const float *router_w, const float *router_b, const moe_routing *routing,
+                       const uint8_t *experts, const uint8_t *shared, float *out,
+                       const moe_route_out *ro, void *ws, size_t ws_bytes, hipStream_t st) {
     MOE_TRY(check_forward(s, hidden, norm_w, router_w, router_b, experts, shared, out, ws, ws_bytes));
+    moe::RouteSel rs;
+    MOE_TRY(route_sel_of(routing, &rs));
     if (s->T > 64) return fail(MOE_ERR_UNSUPPORTED, "decode takes T <= 64 (T=%d); use prefill", s->T);
     if (s->act_quant)
         return fail(MOE_ERR_UNSUPPORTED, "the quantised expert-input mode is a prefill mode");
@@ -419,6 +440,7 @@ int moe_forward_decode(const moe_shape *s, const void *hidden, const float *norm
     a.partial = w.partial;
     a.S = w.splits;
     a.router_b = router_b;
+    a.rs = rs;
     a.T = s->T;
     a.H = s->H;
     a.F = s->F;
@@ -451,10 +473,12 @@ int moe_forward_decode(const moe_shape *s, const void *hidden, const float *norm
 }
 
 int moe_forward_prefill(const moe_shape *s, const void *hidden, const float *norm_w,
-                        const float *router_w, const float *router_b, const uint8_t *experts,
-                        const uint8_t *shared, float *out, const moe_route_out *ro, void *ws,
-                        size_t ws_bytes, hipStream_t st) {
+                        const float *router_w, const float *router_b, const moe_routing *routing,
+                        const uint8_t *experts, const uint8_t *shared, float *out,
+                        const moe_route_out *ro, void *ws, size_t ws_bytes, hipStream_t st) {
     MOE_TRY(check_forward(s, hidden, norm_w, router_w, router_b, experts, shared, out, ws, ws_bytes));
+    moe::RouteSel rs;
+    MOE_TRY(route_sel_of(routing, &rs));
     if (s->T == 0) return ok();
     {  // the grouped GEMMs address FP8-term rows with 32-bit byte offsets
         const uint64_t rows = static_cast<uint64_t>(s->T) * (s->k + s->n_shared);
@@ -469,8 +493,8 @@ int moe_forward_prefill(const moe_shape *s, const void *hidden, const float *nor
     const bool router_terms = moe::router_plan(s->T, s->H, s->E).gemv;
     MOE_TRY(route_front(s, hidden, norm_w, router_w, w, router_terms, nullptr, &in, st));
     MOE_TRY(launch(MOE_KERNEL_TOPK, "topk", st, [&] {
-        return moe::launch_topk(w.partial, w.splits, router_b, s->T, s->E, s->k, s->route_scale,
-                                w.idx, w.wts, ro ? ro->topk_idx : nullptr,
+        return moe::launch_topk(w.partial, w.splits, router_b, rs, s->T, s->E, s->k,
+                                s->route_scale, w.idx, w.wts, ro ? ro->topk_idx : nullptr,
                                 ro ? ro->topk_w : nullptr, st);
     }));
     const moe::GemmPlan plan = gemm_plan_of(s, norm_w != nullptr);

@@ -189,7 +189,11 @@ __device__ __forceinline__ void wave_topk(const double (&vin)[kMaxQ], int E, int
         alive[q] = lane + kWave * q < E;
         v[q] = vin[q] == vin[q] ? vin[q] : -INFINITY;
     }
-    for (int j = 0; j < k; ++j) {
+    // rounds unrolled to kMaxK with a guard: constant indices keep sel / val
+    // in registers
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j) {
+        if (j >= k) break;
         double m = -INFINITY;
 #pragma unroll
         for (int q = 0; q < NQ; ++q)
@@ -209,15 +213,79 @@ __device__ __forceinline__ void wave_topk(const double (&vin)[kMaxQ], int E, int
     }
 }
 
-// Route weights: route_scale * softmax over the k selected logits, in fp64.
+// Route weights: route_scale * softmax over the k selected logits, in fp64
+// (shifted by their maximum, which plain top-k returns first).
 __device__ __forceinline__ void route_softmax(const double *val, int k, float scale, float *w) {
     double z[kMaxK];
-    double s = 0.0;
-    for (int j = 0; j < k; ++j) {
-        z[j] = exp(val[j] - val[0]);
-        s += z[j];
+    double m = val[0], s = 0.0;
+#pragma unroll
+    for (int j = 1; j < kMaxK; ++j)
+        if (j < k) m = fmax(m, val[j]);
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j) {
+        if (j < k) {
+            z[j] = exp(val[j] - m);
+            s += z[j];
+        }
     }
-    for (int j = 0; j < k; ++j) w[j] = static_cast<float>(scale * z[j] / s);
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j)
+        if (j < k) w[j] = static_cast<float>(scale * z[j] / s);
+}
+
+// Logit of expert e (wave-uniform) from the lanes' values v[q] (expert l + 64q).
+// Every group's value is read from lane e % 64 and the group e / 64 picked
+// among the read values (a pick among v[q] itself would become an indexed
+// access that puts v in scratch).
+template <int NQ>
+__device__ __forceinline__ double wave_logit(const double (&v)[kMaxQ], int e) {
+    const int l = e & (kWave - 1), g = e >> 6;
+    double x = 0.0;
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+        const int lo = __builtin_amdgcn_readlane(__double2loint(v[q]), l);
+        const int hi = __builtin_amdgcn_readlane(__double2hiint(v[q]), l);
+        if (g == q) x = __hiloint2double(hi, lo);
+    }
+    return x;
+}
+
+// The k experts of token t and their (unbiased) logits, by one wavefront:
+// plain top-k of v, top-k of v + bias, or the table row of the token's id.
+// Ids and table entries outside their ranges are clamped into them (every
+// access stays in bounds). sel / val are wave-uniform on return.
+template <int NQ>
+__device__ __forceinline__ void select_routes(const double (&v)[kMaxQ], const RouteSel &rs, int t,
+                                              int E, int k, int *sel, double *val) {
+    // slot loops run over kMaxK with a guard, so every array index is a
+    // compile-time constant (a runtime index would put sel / val in scratch)
+    if (rs.table) {
+        const int id = min(max(rs.ids[t], 0), rs.vocab - 1);
+#pragma unroll
+        for (int j = 0; j < kMaxK; ++j) {
+            if (j < k) {
+                const int e = min(max(rs.table[static_cast<size_t>(id) * k + j], 0), E - 1);
+                sel[j] = e;
+                val[j] = wave_logit<NQ>(v, e);
+            }
+        }
+        return;
+    }
+    if (rs.bias) {
+        const int lane = threadIdx.x & (kWave - 1);
+        double vb[kMaxQ];
+#pragma unroll
+        for (int q = 0; q < kMaxQ; ++q) {
+            const int e = lane + kWave * q;
+            vb[q] = (q < NQ && e < E) ? v[q] + static_cast<double>(rs.bias[e]) : -INFINITY;
+        }
+        wave_topk<NQ>(vb, E, k, sel, val);
+#pragma unroll
+        for (int j = 0; j < kMaxK; ++j)
+            if (j < k) val[j] = wave_logit<NQ>(v, sel[j]);
+        return;
+    }
+    wave_topk<NQ>(v, E, k, sel, val);
 }
 
 // ---------------------------------------------------------------- XCD tiles

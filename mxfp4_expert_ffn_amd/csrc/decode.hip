@@ -110,24 +110,25 @@ __device__ __forceinline__ BFrag lds_bfrag(const uint8_t *lds, const Staged &sg,
     return b;
 }
 
-// Top-k of token t's router logits (fp64 split-K partials + bias) by one
-// wavefront: the selected experts and their logits, in every lane.
+// The experts of token t (top-k of its router logits - fp64 split-K partials
+// + bias - or the routing variant's choice) by one wavefront: the selected
+// experts and their logits, in every lane.
 __device__ __forceinline__ void route_token(const double *partial, int S, const float *router_b,
-                                            int T, int t, int E, int k, int (&sel)[kMaxK],
-                                            double (&val)[kMaxK]) {
+                                            const RouteSel &rs, int T, int t, int E, int k,
+                                            int (&sel)[kMaxK], double (&val)[kMaxK]) {
     double v[kMaxQ];
     if (E <= 64) {
         gather_logits<1>(partial, S, T, t, E, router_b, v);
-        wave_topk<1>(v, E, k, sel, val);
+        select_routes<1>(v, rs, t, E, k, sel, val);
     } else if (E <= 128) {
         gather_logits<2>(partial, S, T, t, E, router_b, v);
-        wave_topk<2>(v, E, k, sel, val);
+        select_routes<2>(v, rs, t, E, k, sel, val);
     } else if (E <= 256) {
         gather_logits<4>(partial, S, T, t, E, router_b, v);
-        wave_topk<4>(v, E, k, sel, val);
+        select_routes<4>(v, rs, t, E, k, sel, val);
     } else {
         gather_logits<8>(partial, S, T, t, E, router_b, v);
-        wave_topk<8>(v, E, k, sel, val);
+        select_routes<8>(v, rs, t, E, k, sel, val);
     }
 }
 
@@ -144,7 +145,7 @@ __device__ __forceinline__ const uint8_t *route_blob(const DecodeArgs &a, int r,
     const int t = r / a.k, j = r - t * a.k;
     int sel[kMaxK];
     double val[kMaxK];
-    route_token(a.partial, a.S, a.router_b, a.T, t, a.E, a.k, sel, val);
+    route_token(a.partial, a.S, a.router_b, a.rs, a.T, t, a.E, a.k, sel, val);
     int mine = sel[0];
 #pragma unroll
     for (int jj = 1; jj < kMaxK; ++jj)

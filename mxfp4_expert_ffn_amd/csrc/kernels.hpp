@@ -122,9 +122,22 @@ hipError_t launch_act_fp4(const RouteIn &in, int T, int H, uint8_t *q, uint8_t *
 // `terms` NULL: router only.
 hipError_t launch_router(const RouteIn &in, const float *w, int T, int H, int E, double *partial,
                          const TermsOut *terms, hipStream_t s);
-hipError_t launch_topk(const double *partial, int S, const float *bias, int T, int E, int k,
-                       float route_scale, int32_t *idx, float *wts, int32_t *out_idx, float *out_w,
-                       hipStream_t s);
+// DeepSeek-V4 routing variants (page: antirez ds4.c `ds4_layer_weights`,
+// `weights_validate_layout`: exp_probs_b [n_expert]; tid2eid [n_expert_used,
+// n_vocab] for the first n_hash_layer layers). Readings: the selection-only
+// bias is added to the logits that top-k ranks, the weights stay the softmax
+// of the selected experts' own logits; a hash-routed token takes the k
+// experts of its id's table row, in row order, weighted by their logits.
+struct RouteSel {
+    const float *bias;     // [E] selection-only bias, or NULL
+    const int32_t *table;  // [vocab][k] experts per token id, or NULL (hash routing)
+    const int32_t *ids;    // [T] token ids (with table)
+    int vocab;
+};
+// rs: the routing variant (plain top-k when both pointers are NULL).
+hipError_t launch_topk(const double *partial, int S, const float *bias, const RouteSel &rs, int T,
+                       int E, int k, float route_scale, int32_t *idx, float *wts, int32_t *out_idx,
+                       float *out_w, hipStream_t s);
 // mprefix[g] = tiles of tile_rows rows before group g (groups: E experts,
 // then the shared expert's T rows when n_shared). With `terms` (and `qin`,
 // the expert input) the launch's other workgroups make the FP8 terms, as
@@ -151,6 +164,7 @@ struct DecodeArgs {
     const double *partial;   // router partial logits [S][T][E]
     int S;
     const float *router_b;
+    RouteSel rs;             // routing variant
     int T, H, F, E, k, n_shared;
     float route_scale;
     ExpertPtrs ex, sh;

@@ -50,9 +50,10 @@ int scratch_ptr(void **out) {
 
 extern "C" int moe_forward_decode_noalloc(const moe_shape *s, const void *hidden,
                                           const float *norm_w, const float *router_w,
-                                          const float *router_b, const uint8_t *experts,
-                                          const uint8_t *shared, float *out,
-                                          const moe_route_out *route_out, hipStream_t stream) {
+                                          const float *router_b, const moe_routing *routing,
+                                          const uint8_t *experts, const uint8_t *shared,
+                                          float *out, const moe_route_out *route_out,
+                                          hipStream_t stream) {
     // the size check comes first and touches no device
     const size_t need = moe_workspace_bytes(s);
     if (need == 0) return MOE_ERR_INVALID_ARG;  // moe_workspace_bytes left the message
@@ -61,11 +62,11 @@ extern "C" int moe_forward_decode_noalloc(const moe_shape *s, const void *hidden
                               "shape needs more workspace than the library's fixed "
                               "MOE_NOALLOC_SCRATCH_BYTES; use moe_forward_decode with a "
                               "caller workspace");
-    if (s->T == 0) return moe_forward_decode(s, hidden, norm_w, router_w, router_b, experts,
-                                             shared, out, route_out, nullptr, 0, stream);
+    if (s->T == 0) return moe_forward_decode(s, hidden, norm_w, router_w, router_b, routing,
+                                             experts, shared, out, route_out, nullptr, 0, stream);
     void *ws = nullptr;
     const int rc = scratch_ptr(&ws);
     if (rc != MOE_OK) return rc;
-    return moe_forward_decode(s, hidden, norm_w, router_w, router_b, experts, shared, out,
-                              route_out, ws, kScratchBytes, stream);
+    return moe_forward_decode(s, hidden, norm_w, router_w, router_b, routing, experts, shared,
+                              out, route_out, ws, kScratchBytes, stream);
 }

@@ -378,9 +378,9 @@ __device__ __forceinline__ void gather_logits_wg(const double *partial, int S, i
 }
 
 __global__ __launch_bounds__(256) void topk_kernel(const double *partial, int S, const float *bias,
-                                                   int T, int E, int k, float route_scale,
-                                                   int32_t *idx, float *wts, int32_t *out_idx,
-                                                   float *out_w) {
+                                                   RouteSel rs, int T, int E, int k,
+                                                   float route_scale, int32_t *idx, float *wts,
+                                                   int32_t *out_idx, float *out_w) {
     __shared__ double red[4 * kMaxE];
     const int t = blockIdx.x;
     const int lane = threadIdx.x & 63;
@@ -392,10 +392,10 @@ __global__ __launch_bounds__(256) void topk_kernel(const double *partial, int S,
     if (threadIdx.x >= 64) return;  // after the workgroup barrier
     int sel[kMaxK];
     double val[kMaxK];
-    if (E <= 64) wave_topk<1>(v, E, k, sel, val);
-    else if (E <= 128) wave_topk<2>(v, E, k, sel, val);
-    else if (E <= 256) wave_topk<4>(v, E, k, sel, val);
-    else wave_topk<8>(v, E, k, sel, val);
+    if (E <= 64) select_routes<1>(v, rs, t, E, k, sel, val);
+    else if (E <= 128) select_routes<2>(v, rs, t, E, k, sel, val);
+    else if (E <= 256) select_routes<4>(v, rs, t, E, k, sel, val);
+    else select_routes<8>(v, rs, t, E, k, sel, val);
     float wt[kMaxK];
     route_softmax(val, k, route_scale, wt);
 #pragma unroll
@@ -608,10 +608,10 @@ hipError_t launch_act_fp4(const RouteIn &in, int T, int H, uint8_t *q, uint8_t *
     return hipGetLastError();
 }
 
-hipError_t launch_topk(const double *partial, int S, const float *bias, int T, int E, int k,
-                       float route_scale, int32_t *idx, float *wts, int32_t *out_idx, float *out_w,
-                       hipStream_t s) {
-    launch_kernel(topk_kernel, T, 256, s, partial, S, bias, T, E, k, route_scale, idx, wts,
+hipError_t launch_topk(const double *partial, int S, const float *bias, const RouteSel &rs, int T,
+                       int E, int k, float route_scale, int32_t *idx, float *wts, int32_t *out_idx,
+                       float *out_w, hipStream_t s) {
+    launch_kernel(topk_kernel, T, 256, s, partial, S, bias, rs, T, E, k, route_scale, idx, wts,
                   out_idx, out_w);
     return hipGetLastError();
 }

@@ -34,7 +34,7 @@ def to_np(d):
     return {k: v.cpu().numpy() for k, v in d.items()}
 
 
-def run_forward(path, shape, dl, x_dev, out=None, route=True, copy=0):
+def run_forward(path, shape, dl, x_dev, out=None, route=True, copy=0, token_ids=None):
     T, H, k, E = shape.T, shape.H, shape.k, shape.E
     if out is None:
         out = torch.full((T, H), float("nan"), dtype=torch.float32, device="cuda")
@@ -42,7 +42,7 @@ def run_forward(path, shape, dl, x_dev, out=None, route=True, copy=0):
     ro = route_buffers(T, k, E) if route else None
     fn = mx.moe_forward_decode if path == "decode" else mx.moe_forward_prefill
     fn(shape, x_dev, dl.router_w, dl.router_b, dl.experts_copy(copy), out, ws, norm_w=dl.norm_w,
-       shared=dl.shared_copy(copy), route_out=ro)
+       shared=dl.shared_copy(copy), route_out=ro, routing=dl.routing(token_ids))
     torch.cuda.synchronize()
     return out, ro
 
@@ -62,8 +62,12 @@ def gap_bound(xn: np.ndarray, router_w: np.ndarray, router_b: np.ndarray) -> np.
 
 
 def check_routing(gpu_idx, gpu_w, ref, router_w, router_b, route_scale, max_flips=0):
-    """idx bit-exact except at certified near-ties; weights within 1e-6."""
-    logits, ridx = ref["logits"], ref["idx"]
+    """idx bit-exact except at certified near-ties of the values the selection
+    ranked (logits, or logits + selection-only bias); a hash-routed block has
+    no ties, its idx must equal the table rows; weights within 1e-6."""
+    logits, ridx = ref.get("sel", ref["logits"]), ref["idx"]
+    if ref.get("hashed"):
+        assert np.array_equal(gpu_idx, ridx)
     bound = gap_bound(ref["xn"], router_w, router_b)
     bad = np.nonzero(np.any(gpu_idx != ridx, axis=1))[0]
     flips = 0

@@ -132,13 +132,21 @@ FAKE = 1 << 20  # a non-NULL, aligned address; validation fails before any use
 
 def _call(fn_name, shape, **over):
     lib = _lib.load()
-    args = dict(hidden=FAKE, norm_w=None, router_w=FAKE, router_b=FAKE, experts=FAKE,
-                shared=None, out=FAKE, ro=None, ws=FAKE, ws_bytes=1 << 40, stream=None)
+    args = dict(hidden=FAKE, norm_w=None, router_w=FAKE, router_b=FAKE, routing=None,
+                experts=FAKE, shared=None, out=FAKE, ro=None, ws=FAKE, ws_bytes=1 << 40,
+                stream=None)
     args.update(over)
     fn = getattr(lib, fn_name)
     return fn(ctypes.byref(shape), args["hidden"], args["norm_w"], args["router_w"],
-              args["router_b"], args["experts"], args["shared"], args["out"], args["ro"],
-              args["ws"], args["ws_bytes"], args["stream"])
+              args["router_b"], args["routing"], args["experts"], args["shared"], args["out"],
+              args["ro"], args["ws"], args["ws_bytes"], args["stream"])
+
+
+def _routing(**kw):
+    r = _lib.MoeRouting()
+    for k, v in kw.items():
+        setattr(r, k, v)
+    return ctypes.byref(r)
 
 
 @pytest.mark.parametrize("fn", ["moe_forward_decode", "moe_forward_prefill"])
@@ -157,6 +165,12 @@ def _call(fn_name, shape, **over):
     ("small workspace", {}, dict(ws_bytes=1024), _lib.MOE_ERR_WORKSPACE),
     ("null workspace", {}, dict(ws=None), _lib.MOE_ERR_WORKSPACE),
     ("act_quant 2", dict(act_quant=2), {}, _lib.MOE_ERR_INVALID_ARG),
+    ("table without ids", {}, dict(routing=_routing(tid2eid=FAKE, vocab=10)), _lib.MOE_ERR_INVALID_ARG),
+    ("table with vocab 0", {}, dict(routing=_routing(tid2eid=FAKE, token_ids=FAKE)),
+     _lib.MOE_ERR_INVALID_ARG),
+    ("misaligned table", {}, dict(routing=_routing(tid2eid=FAKE + 2, token_ids=FAKE, vocab=4)),
+     _lib.MOE_ERR_INVALID_ARG),
+    ("misaligned bias", {}, dict(routing=_routing(sel_bias=FAKE + 1)), _lib.MOE_ERR_INVALID_ARG),
     ("act_quant -1", dict(act_quant=-1), {}, _lib.MOE_ERR_INVALID_ARG),
     ("misaligned workspace", {}, dict(ws=FAKE + 64), _lib.MOE_ERR_WORKSPACE),
     ("nonpositive limit", dict(limit=0.0), {}, _lib.MOE_ERR_INVALID_ARG),
@@ -200,12 +214,12 @@ def test_noalloc_decode_rejects_shapes_past_its_scratch():
     big = mx.make_shape(T=64, H=8192, F=8192, E=512, k=8, n_shared=1)
     assert mx.moe_workspace_bytes(big) > _lib.MOE_NOALLOC_SCRATCH_BYTES
     rc = lib.moe_forward_decode_noalloc(ctypes.byref(big), None, None, None, None, None, None, None,
-                                        None, None)
+                                        None, None, None)
     assert rc == _lib.MOE_ERR_UNSUPPORTED
     assert "MOE_NOALLOC_SCRATCH_BYTES" in mx.moe_last_error()
     bad = mx.make_shape(T=1, H=100, F=64, E=4, k=2)  # H not a multiple of 32
     assert lib.moe_forward_decode_noalloc(ctypes.byref(bad), None, None, None, None, None, None,
-                                          None, None, None) == _lib.MOE_ERR_INVALID_ARG
+                                          None, None, None, None) == _lib.MOE_ERR_INVALID_ARG
 
 
 def test_noalloc_scratch_covers_the_decode_workloads():

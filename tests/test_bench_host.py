@@ -94,7 +94,7 @@ def _standin(cid, mode, **kw):
     cfg = scaled(config_by_id(cid), **kw)
     x, _ = make_activations(cfg)
     return types.SimpleNamespace(cfg=cfg, host_layers=[make_layer(cfg, 0)], x_host=x, mode=mode,
-                                 act_quant=0, ntok=kw.get("T", cfg.T))
+                                 act_quant=0, token_ids=None, ntok=kw.get("T", cfg.T))
 
 
 class _Clock:
@@ -112,7 +112,7 @@ def _fake_oracle(monkeypatch, seconds_per_call):
     clock = _Clock()
     calls = []
 
-    def block(cfg, layer, x, tokens=None, stats=None, act_quant=0):
+    def block(cfg, layer, x, tokens=None, stats=None, act_quant=0, token_ids=None):
         calls.append((x.shape[0], None if tokens is None else len(tokens)))
         clock.t += seconds_per_call
 
