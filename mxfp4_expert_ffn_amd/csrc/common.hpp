@@ -133,14 +133,27 @@ __device__ __forceinline__ float swiglu(float g, float u, float alpha, float lim
 // ((sum0 + sum1) + sum2) + sum3, then the bias (the workgroup top-k has
 // wavefront c make sum c). The loads of each group of kGatherUnroll splits
 // are issued together (indices clamped, extra values masked) so the gather
-// costs one memory round trip per group.
+// costs one memory round trip per group; the biases load with the first
+// group, and `between` (loads of the caller's own, issued behind the first
+// group so that the sums wait only for the partials) runs right after it
+// (up to 128 experts; past that, before it).
 constexpr int kGatherUnroll = 8;
 static_assert(kGatherUnroll % 4 == 0, "a group keeps each split in its residue class");
-template <int NQ>
+struct NoLoads {
+    __device__ void operator()() const {}
+};
+template <int NQ, typename Between = NoLoads>
 __device__ __forceinline__ void gather_logits(const double *partial, int S, int T, int t, int E,
-                                              const float *bias, double (&v)[kMaxQ]) {
+                                              const float *bias, double (&v)[kMaxQ],
+                                              Between &&between = Between{}) {
     const int lane = threadIdx.x & (kWave - 1);
     double acc[4][NQ];
+    float bq[NQ];
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) bq[q] = bias[min(lane + kWave * q, E - 1)];
+    // with more than 128 experts a group's partials take too many registers to
+    // hold the caller's loads as well: those go out first
+    if constexpr (NQ > 2) between();
 #pragma unroll
     for (int c = 0; c < 4; ++c)
 #pragma unroll
@@ -153,6 +166,8 @@ __device__ __forceinline__ void gather_logits(const double *partial, int S, int 
 #pragma unroll
             for (int q = 0; q < NQ; ++q) part[i][q] = row[min(lane + kWave * q, E - 1)];
         }
+        if constexpr (NQ <= 2)
+            if (s0 == 0) between();
 #pragma unroll
         for (int i = 0; i < kGatherUnroll; ++i)
 #pragma unroll
@@ -164,8 +179,7 @@ __device__ __forceinline__ void gather_logits(const double *partial, int S, int 
         const int e = lane + kWave * q;
         const int qq = q < NQ ? q : 0;
         v[q] = (q < NQ && e < E)
-                   ? ((acc[0][qq] + acc[1][qq]) + acc[2][qq]) + acc[3][qq] +
-                         static_cast<double>(bias[min(e, E - 1)])
+                   ? ((acc[0][qq] + acc[1][qq]) + acc[2][qq]) + acc[3][qq] + static_cast<double>(bq[qq])
                    : -INFINITY;
     }
 }
@@ -213,24 +227,29 @@ __device__ __forceinline__ void wave_topk(const double (&vin)[kMaxQ], int E, int
     }
 }
 
-// Route weights: route_scale * softmax over the k selected logits, in fp64
-// (shifted by their maximum, which plain top-k returns first).
-__device__ __forceinline__ void route_softmax(const double *val, int k, float scale, float *w) {
-    double z[kMaxK];
-    double m = val[0], s = 0.0;
-#pragma unroll
-    for (int j = 1; j < kMaxK; ++j)
-        if (j < k) m = fmax(m, val[j]);
+// Route weight of slot `lane` (lanes < k; the others get 0): route_scale *
+// softmax over the k selected logits, in fp64, shifted by their maximum. The
+// lanes take one exponential each and the sum adds the slots in order (every
+// top-k of the library makes its weights here). v: the lane's slot logit.
+__device__ __forceinline__ float route_weight_lanes(double v, int k, float scale) {
+    const int lane = threadIdx.x & (kWave - 1);
+    double m = -INFINITY;
+    double vs[kMaxK];
 #pragma unroll
     for (int j = 0; j < kMaxK; ++j) {
-        if (j < k) {
-            z[j] = exp(val[j] - m);
-            s += z[j];
-        }
+        vs[j] = __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(v), j),
+                                 __builtin_amdgcn_readlane(__double2loint(v), j));
+        if (j == 0) m = vs[0];
+        else if (j < k) m = fmax(m, vs[j]);
     }
+    const double z = exp(v - m);
+    double s = 0.0;
 #pragma unroll
     for (int j = 0; j < kMaxK; ++j)
-        if (j < k) w[j] = static_cast<float>(scale * z[j] / s);
+        if (j < k)
+            s += __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(z), j),
+                                  __builtin_amdgcn_readlane(__double2loint(z), j));
+    return lane < k ? static_cast<float>(scale * z / s) : 0.0f;
 }
 
 // Logit of expert e (wave-uniform) from the lanes' values v[q] (expert l + 64q).

@@ -113,63 +113,78 @@ __device__ __forceinline__ BFrag lds_bfrag(const uint8_t *lds, const Staged &sg,
 // The experts of token t (top-k of its router logits - fp64 split-K partials
 // + bias - or the routing variant's choice) by one wavefront: the selected
 // experts and their logits, in every lane.
+// `between`: the caller's loads, issued behind the partials' (gather_logits).
+// SMALL_E: the kernel serves E <= 128 only (its registers are sized for that).
+template <bool SMALL_E, typename Between = NoLoads>
 __device__ __forceinline__ void route_token(const double *partial, int S, const float *router_b,
                                             const RouteSel &rs, int T, int t, int E, int k,
-                                            int (&sel)[kMaxK], double (&val)[kMaxK]) {
+                                            int (&sel)[kMaxK], double (&val)[kMaxK],
+                                            Between &&between = Between{}) {
     double v[kMaxQ];
-    if (E <= 64) {
-        gather_logits<1>(partial, S, T, t, E, router_b, v);
-        select_routes<1>(v, rs, t, E, k, sel, val);
-    } else if (E <= 128) {
-        gather_logits<2>(partial, S, T, t, E, router_b, v);
-        select_routes<2>(v, rs, t, E, k, sel, val);
+    if constexpr (SMALL_E) {
+        if (E <= 64) {
+            gather_logits<1>(partial, S, T, t, E, router_b, v, between);
+            select_routes<1>(v, rs, t, E, k, sel, val);
+        } else {
+            gather_logits<2>(partial, S, T, t, E, router_b, v, between);
+            select_routes<2>(v, rs, t, E, k, sel, val);
+        }
     } else if (E <= 256) {
-        gather_logits<4>(partial, S, T, t, E, router_b, v);
+        gather_logits<4>(partial, S, T, t, E, router_b, v, between);
         select_routes<4>(v, rs, t, E, k, sel, val);
     } else {
-        gather_logits<8>(partial, S, T, t, E, router_b, v);
+        gather_logits<8>(partial, S, T, t, E, router_b, v, between);
         select_routes<8>(v, rs, t, E, k, sel, val);
     }
 }
 
 // Expert blob of route r, selected by the calling wavefront itself (top-k of
-// the token's logits), and the route's weight (1 for the shared expert).
-// `publish` (wave-uniform) writes the token's experts and route weights to
-// idx / wts and the exports.
+// the token's logits), and the route's weight (1 for the shared expert;
+// `need_weight` false: not made). `publish` (wave-uniform) writes the token's
+// experts and route weights to idx / wts and the exports. `between`: the
+// caller's loads, issued behind the router partials' (for the shared
+// expert, at once).
+template <bool SMALL_E, typename Between>
 __device__ __forceinline__ const uint8_t *route_blob(const DecodeArgs &a, int r, bool publish,
-                                                     bool need_weight, float &weight) {
+                                                     bool need_weight, float &weight,
+                                                     Between &&between) {
     const int R = a.T * a.k;
     weight = 1.0f;
-    if (r >= R) return a.sh.base;
+    if (r >= R) {
+        between();
+        return a.sh.base;
+    }
     const int lane = threadIdx.x & 63;
     const int t = r / a.k, j = r - t * a.k;
     int sel[kMaxK];
     double val[kMaxK];
-    route_token(a.partial, a.S, a.router_b, a.rs, a.T, t, a.E, a.k, sel, val);
+    route_token<SMALL_E>(a.partial, a.S, a.router_b, a.rs, a.T, t, a.E, a.k, sel, val, between);
     int mine = sel[0];
 #pragma unroll
     for (int jj = 1; jj < kMaxK; ++jj)
         if (jj == j) mine = sel[jj];
     mine = __builtin_amdgcn_readfirstlane(mine);  // equal in every lane; lets loads take a scalar base
-    float wv[kMaxK];
     if (need_weight || publish) {  // wave-uniform: only the epilogue's wavefront needs it
-        route_softmax(val, a.k, a.route_scale, wv);
+        // lane jj takes slot jj's logit and expert; one exponential per lane
+        double v = val[0];
+        int e = sel[0];
 #pragma unroll
-        for (int jj = 0; jj < kMaxK; ++jj)
-            if (jj == j) weight = wv[jj];
-    }
-    if (publish) {
-#pragma unroll
-        for (int jj = 0; jj < kMaxK; ++jj) {
-            if (jj < a.k && lane == jj) {
-                a.idx[t * a.k + jj] = sel[jj];
-                a.wts[t * a.k + jj] = wv[jj];
-                if (a.out_idx) a.out_idx[t * a.k + jj] = sel[jj];
-                if (a.out_w) a.out_w[t * a.k + jj] = wv[jj];
-                // route profile (goosedump ExpertRouteProfile::record): one per selection
-                if (a.route_counts)
-                    atomicAdd(reinterpret_cast<unsigned long long *>(a.route_counts + sel[jj]), 1ull);
+        for (int jj = 1; jj < kMaxK; ++jj) {
+            if (lane == jj) {
+                v = val[jj];
+                e = sel[jj];
             }
+        }
+        const float wl = route_weight_lanes(v, a.k, a.route_scale);
+        weight = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), j));
+        if (publish && lane < a.k) {
+            a.idx[t * a.k + lane] = e;
+            a.wts[t * a.k + lane] = wl;
+            if (a.out_idx) a.out_idx[t * a.k + lane] = e;
+            if (a.out_w) a.out_w[t * a.k + lane] = wl;
+            // route profile (goosedump ExpertRouteProfile::record): one per selection
+            if (a.route_counts)
+                atomicAdd(reinterpret_cast<unsigned long long *>(a.route_counts + e), 1ull);
         }
     }
     return a.ex.base + static_cast<size_t>(mine) * a.ex.stride;
@@ -181,7 +196,7 @@ __device__ __forceinline__ const uint8_t *route_blob(const DecodeArgs &a, int r,
 // (seeded by the router launch's quantisation), so nothing here delays the
 // router-partials load and the top-k. s_part: kDecodeWaves * 4 * 16 floats of
 // LDS.
-template <int SPW, int CH>
+template <int SPW, int CH, bool SMALL_E>
 __device__ __forceinline__ void gate_up_item(const DecodeArgs &a, int r, int fb, float *s_part,
                                              uint8_t *lds) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -203,11 +218,12 @@ __device__ __forceinline__ void gate_up_item(const DecodeArgs &a, int r, int fb,
         return;
     }
     // the token's input terms, staged through LDS by the whole workgroup;
-    // their loads go out before the top-k
+    // their loads go out behind the router partials', so the top-k waits only
+    // for the partials
     const Staged sg{Kp, kTerms};
     dec_u32x4 stv[CH];
     uint32_t stsv = 0;
-    {
+    auto stage_loads = [&]() __attribute__((always_inline)) {
         const int tid = threadIdx.x, nthr = kDecodeWaves * 64;
         const int cq = kTerms * (Kp / 16), cs = kTerms * (Kp / 128);
 #pragma unroll
@@ -217,9 +233,10 @@ __device__ __forceinline__ void gate_up_item(const DecodeArgs &a, int r, int fb,
         }
         stsv = *reinterpret_cast<const uint32_t *>(a.xs + stage_scale_src(sg, min(tid, cs - 1), kTerms,
                                                                             t * kTerms, 0));
-    }
+    };
     float route_w;
-    const uint8_t *blob = route_blob(a, r, j == 0 && fb == 0 && w == 0, w == 0, route_w);
+    const uint8_t *blob =
+        route_blob<SMALL_E>(a, r, j == 0 && fb == 0 && w == 0, w == 0, route_w, stage_loads);
     // the epilogue's biases, loaded with the weights
     const int fe = 32 * fb + (lane & 31);
     const float bias_g = reinterpret_cast<const float *>(blob + a.ex.gate_b)[fe];
@@ -354,6 +371,8 @@ __device__ __forceinline__ void down_rows(const DecodeArgs &a, int t, int hb, fl
     }
     // lane j loads slot j's expert and weight (one vector load each), then
     // every slot moves to scalar registers with readlane: no branch, no chain
+    // (the staged terms' loads go first: measured faster than behind the
+    // weights)
     const int lj = min(lane, k - 1);
     const int ev = a.idx[t * k + lj];
     const float wv = a.wts[t * k + lj];
@@ -481,11 +500,11 @@ __device__ __forceinline__ void down_rows(const DecodeArgs &a, int t, int hb, fl
 // workgroups (dealt round-robin over the dies) take blocks of one route, so
 // every route's weights stream through all eight dies (0.8% faster per decode
 // token than routes along x, which put each route on two dies)
-template <int SPW, int CH>
+template <int SPW, int CH, bool SMALL_E>
 __global__ __launch_bounds__(kDecodeWaves * 64) void decode_gate_up_kernel(DecodeArgs a) {
     __shared__ float s_part[kDecodeWaves * 4 * 16];
     extern __shared__ __align__(16) uint8_t dyn_lds[];
-    gate_up_item<SPW, CH>(a, blockIdx.y, blockIdx.x, s_part, dyn_lds);
+    gate_up_item<SPW, CH, SMALL_E>(a, blockIdx.y, blockIdx.x, s_part, dyn_lds);
 }
 
 // grid.x = 16-row blocks of H, grid.y = tokens.
@@ -511,15 +530,21 @@ hipError_t launch_decode_gate_up(const DecodeArgs &a, hipStream_t s) {
     const int Kp = pad128(a.H);
     const int ch = (Kp / 4 + kDecodeWaves * 64 - 1) / (kDecodeWaves * 64);  // 16-byte chunks per thread
     const size_t shm = staged_bytes(Kp, kTerms);
+#define MOE_GU_DEC(SPW, CH)                                                                          \
+    do {                                                                                             \
+        if (a.E <= 128) launch_kernel_shm(decode_gate_up_kernel<SPW, CH, true>, grid, block, shm, s, a); \
+        else launch_kernel_shm(decode_gate_up_kernel<SPW, CH, false>, grid, block, shm, s, a);         \
+    } while (0)
     switch (decode_spw(a.H)) {  // K <= 1024: one chunk; <= 2048: one; <= 3072: two; else two or four
-    case 1: launch_kernel_shm(decode_gate_up_kernel<1, 1>, grid, block, shm, s, a); break;
-    case 2: launch_kernel_shm(decode_gate_up_kernel<2, 1>, grid, block, shm, s, a); break;
-    case 3: launch_kernel_shm(decode_gate_up_kernel<3, 2>, grid, block, shm, s, a); break;
+    case 1: MOE_GU_DEC(1, 1); break;
+    case 2: MOE_GU_DEC(2, 1); break;
+    case 3: MOE_GU_DEC(3, 2); break;
     default:
-        if (ch <= 2) launch_kernel_shm(decode_gate_up_kernel<4, 2>, grid, block, shm, s, a);
-        else launch_kernel_shm(decode_gate_up_kernel<4, 4>, grid, block, shm, s, a);
+        if (ch <= 2) MOE_GU_DEC(4, 2);
+        else MOE_GU_DEC(4, 4);
         break;
     }
+#undef MOE_GU_DEC
     return hipGetLastError();
 }
 

@@ -396,16 +396,22 @@ __global__ __launch_bounds__(256) void topk_kernel(const double *partial, int S,
     else if (E <= 128) select_routes<2>(v, rs, t, E, k, sel, val);
     else if (E <= 256) select_routes<4>(v, rs, t, E, k, sel, val);
     else select_routes<8>(v, rs, t, E, k, sel, val);
-    float wt[kMaxK];
-    route_softmax(val, k, route_scale, wt);
+    // lane j takes slot j's logit and expert; one exponential per lane
+    double vj = val[0];
+    int e = sel[0];
 #pragma unroll
-    for (int j = 0; j < kMaxK; ++j) {
-        if (j < k && lane == j) {
-            idx[t * k + j] = sel[j];
-            wts[t * k + j] = wt[j];
-            if (out_idx) out_idx[t * k + j] = sel[j];
-            if (out_w) out_w[t * k + j] = wt[j];
+    for (int j = 1; j < kMaxK; ++j) {
+        if (lane == j) {
+            vj = val[j];
+            e = sel[j];
         }
+    }
+    const float wl = route_weight_lanes(vj, k, route_scale);
+    if (lane < k) {
+        idx[t * k + lane] = e;
+        wts[t * k + lane] = wl;
+        if (out_idx) out_idx[t * k + lane] = e;
+        if (out_w) out_w[t * k + lane] = wl;
     }
 }
 
