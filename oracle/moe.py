@@ -142,7 +142,10 @@ def dequant_expert(planes, e: int):
 
 
 def expert_ffn(xr: np.ndarray, planes, e: int, alpha: float, limit: float, up_offset: float,
-               stats: dict | None = None) -> np.ndarray:
+               stats: dict | None = None, quant_act: bool = False) -> np.ndarray:
+    """quant_act: the SwiGLU output, as float32, goes through the MX-FP4 round
+    trip (blocks of 32 along F) before the down projection; `stats["act"]`
+    then collects the unrounded outputs (for the tests' rounding-edge bound)."""
     wg, wu, wd = dequant_expert(planes, e)
     g = xr @ wg.T + planes.gate_bias[e].astype(np.float64)
     u = xr @ wu.T + planes.up_bias[e].astype(np.float64)
@@ -151,6 +154,10 @@ def expert_ffn(xr: np.ndarray, planes, e: int, alpha: float, limit: float, up_of
         stats["up_clamped"] = stats.get("up_clamped", 0) + int(np.count_nonzero(np.abs(u) > limit))
         stats["elements"] = stats.get("elements", 0) + g.size
     a = swiglu(g, u, alpha, limit, up_offset)
+    if quant_act:
+        if stats is not None:
+            stats.setdefault("act", []).append((e, a))
+        a = act_quant_mod.quantize_rows(a.astype(np.float32))[2]
     return a @ wd.T + planes.down_bias[e].astype(np.float64)
 
 
@@ -218,6 +225,8 @@ def moe_block(layer, x: np.ndarray, k: int, alpha: float, limit: float, up_offse
     goosedump `mixture_of_experts` quantises the expert input once,
     `Q8Activation`). Reading: routing keeps the unquantised input, and the
     SwiGLU output is not quantised.
+    act_quant 2: as 1, and each expert's SwiGLU output (the down projection's
+    input, float32) goes through the same round trip along F.
 
     A layer with `sel_bias` [E] selects with the selection-only bias; one with
     `tid2eid` [vocab, k] routes token t by table row token_ids[t] (see
@@ -248,12 +257,13 @@ def moe_block(layer, x: np.ndarray, k: int, alpha: float, limit: float, up_offse
     for e in np.unique(idx[toks]):
         rows, slots = np.nonzero(idx[toks] == e)
         y[rows, slots] = expert_ffn(xe[toks[rows]], layer.experts, int(e),
-                                    alpha, limit, up_offset, stats)
+                                    alpha, limit, up_offset, stats, quant_act=act_quant == 2)
     for j in range(k):                              # slot-ordered weighted sum
         delta += w[toks, j][:, None] * y[:, j]
     if layer.shared is not None:
         for s in range(layer.shared.n):
-            delta += expert_ffn(xe[toks], layer.shared, s, alpha, limit, up_offset, stats)
+            delta += expert_ffn(xe[toks], layer.shared, s, alpha, limit, up_offset, stats,
+                                quant_act=act_quant == 2)
     out = (x[toks] + delta).astype(np.float32)
     return dict(out=out, delta=delta, logits=logits, sel=sel, idx=idx, w=w, counts=counts,
                 offsets=offsets, perm=perm, inv=inv, xn=xn, xe=xe, tokens=toks,

@@ -156,3 +156,40 @@ def test_block_mode_changes_general_inputs_but_not_routing():
     assert 1e-3 < diff < 1.0
     # the experts' input is exactly the round trip of the float32 input
     assert np.array_equal(b["xe"], aq.quantize_rows(x.astype(np.float32))[2])
+
+
+def test_mode2_single_expert_composition():
+    """act_quant 2 on one expert (E = k = 1, so the route weight is the route
+    scale): the block equals the composition written out with the page-table
+    decoding of the weights (`oracle.brute`), the pure-Python clamped SwiGLU,
+    and the round trip applied to the expert input and to the SwiGLU output."""
+    from oracle import brute
+    cfg = scaled(config_by_id(1), T=5, H=64, F=96, E=1, k=1, route_scale=1.5)
+    layer = make_layer(cfg)
+    x, _ = make_activations(cfg)
+    ex = layer.experts
+    wg = np.array(brute.decode_matrix(ex.gate_codes[0], ex.gate_scales[0], cfg.F, cfg.H))
+    wu = np.array(brute.decode_matrix(ex.up_codes[0], ex.up_scales[0], cfg.F, cfg.H))
+    wd = np.array(brute.decode_matrix(ex.down_codes[0], ex.down_scales[0], cfg.H, cfg.F))
+    xe = aq.quantize_rows(x)[2]
+    g = xe @ wg.T + ex.gate_bias[0]
+    u = xe @ wu.T + ex.up_bias[0]
+    h = np.vectorize(lambda a, b: brute.swiglu_scalar(a, b, cfg.alpha, cfg.limit, cfg.up_offset))(g, u)
+    hq = aq.quantize_rows(h.astype(np.float32))[2]
+    want = cfg.route_scale * (hq @ wd.T + ex.down_bias[0])
+    got = omoe.block_for_config(cfg, layer, x, act_quant=2)
+    assert np.allclose(got["delta"], want, rtol=1e-12, atol=1e-12 * np.abs(want).max())
+    # and it differs from mode 1, whose down input is the unrounded SwiGLU output
+    one = omoe.block_for_config(cfg, layer, x, act_quant=1)
+    assert not np.allclose(one["delta"], got["delta"], rtol=1e-6, atol=0)
+
+
+def test_mode2_collects_the_unrounded_swiglu_output():
+    cfg = scaled(config_by_id(1), T=4)
+    layer = make_layer(cfg)
+    x, _ = make_activations(cfg)
+    stats = {}
+    omoe.block_for_config(cfg, layer, x, stats=stats, act_quant=2)
+    acts = stats["act"]
+    assert len(acts) == len(np.unique(omoe.block_for_config(cfg, layer, x)["idx"]))
+    assert all(a.shape[1] == cfg.F for _, a in acts)
