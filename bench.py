@@ -15,6 +15,7 @@ input (weights and activations resident in HBM before timing):
   ds4     DeepSeek-V4-Flash-shaped layer, T=2048, 256 experts top-6 + shared
   ds4_q4  ds4 in the quantised expert-input mode (MX-FP4 expert input, FP4 x FP4
           gate/up products)
+  ds4_q4a ds4 in quantised mode 2 (the SwiGLU output MX-FP4 too: FP4 x FP4 down)
   ds4_selbias  ds4 with the selection-only expert bias (exp_probs_b)
   ds4_hash     ds4 hash-routed by token id (tid2eid table over 129280 ids)
   ds4_pro DeepSeek-V4-Pro-shaped layer, T=2048, H=7168, F=3072, 384 experts top-6 + shared
@@ -73,6 +74,9 @@ WORKLOADS = {
     # the same layer with the expert input rounded once to MX-FP4 (act_quant=1)
     "ds4_q4": dict(config=5, name="ds4flash_T2048_E256_top6_shared_mxfp4_input",
                    kernel="gate_up_gemm", copies=2, steps=50, act_quant=1),
+    # and the SwiGLU output rounded to MX-FP4 too (act_quant=2)
+    "ds4_q4a": dict(config=5, name="ds4flash_T2048_E256_top6_shared_mxfp4_input_and_act",
+                    kernel="gate_up_gemm", copies=2, steps=50, act_quant=2),
     # DeepSeek-V4 routing variants on the same layer shape
     "ds4_selbias": dict(config=7, name="ds4flash_T2048_E256_top6_shared_selbias",
                         kernel="gate_up_gemm", copies=2, steps=50),
@@ -311,7 +315,8 @@ class Setup:
         active = [sum(1 for c in counts if c > 0) + cfg.n_shared for counts in counts_per_call]
         rows = T * k + T * cfg.n_shared
         x_in = T * pad128(H) * 17 // 32 if self.act_quant else T * terms(H)
-        per = [a * 2 * (mat + 4 * F) + x_in + rows * terms(F) for a in active]
+        act_out = rows * pad128(F) * 17 // 32 if self.act_quant == 2 else rows * terms(F)
+        per = [a * 2 * (mat + 4 * F) + x_in + act_out for a in active]
         return dict(bytes=sum(per) / len(per), flops=4.0 * rows * H * F, units=rows,
                     unit="routed row (token, expert) of the grouped GEMM",
                     active_experts=sum(active) / len(active))
@@ -619,6 +624,7 @@ def measure(wl: str, args, steps: int, warmup: int) -> dict:
             "tokens_per_step": setup.tokens_per_step, "weights": "mxfp4 (e2m1 + e8m0/32) + fp32 bias",
             "activations": cfg.act_dtype, "weight_copies": setup.copies,
             "expert_input": "mxfp4 (rounded once)" if setup.act_quant else "exact (fp8 terms)",
+            "swiglu_output": "mxfp4" if setup.act_quant == 2 else "exact (fp8 terms)",
             "launch": "eager" if graphs is None else "hip_graph",
             "route_profile": args.route_profile,
         },

@@ -79,8 +79,11 @@ typedef enum moe_dtype {
  * `dsv4_e2m1fn_dequant_cpu`) - and reused by every expert row that takes
  * the token (goosedump `mixture_of_experts`, `Q8Activation`). The gate/up
  * products then run FP4 x FP4 on the matrix cores, one instruction each.
- * Routing, the SwiGLU output and the residual are unaffected. The decode
- * entry points reject the mode (MOE_ERR_UNSUPPORTED). */
+ * Routing, the SwiGLU output and the residual are unaffected.
+ * act_quant = 2 also rounds each routed row's SwiGLU output (float32, blocks
+ * of 32 along F) through the same round trip before the down projection,
+ * whose products then run FP4 x FP4 too. The decode entry points reject both
+ * modes (MOE_ERR_UNSUPPORTED). */
 typedef struct moe_shape {
     int32_t T;          /* tokens */
     int32_t H;          /* hidden size */
@@ -94,7 +97,7 @@ typedef struct moe_shape {
     float swiglu_up_offset;
     float route_scale;
     float rms_eps;
-    int32_t act_quant;  /* 0: exact expert input; 1: MX-FP4 expert input (below) */
+    int32_t act_quant;  /* 0: exact; 1: MX-FP4 expert input; 2: and MX-FP4 SwiGLU output */
 } moe_shape;
 
 /* Byte layout of one packed expert blob. Offsets are from the blob start;
@@ -367,7 +370,8 @@ typedef struct moe_prefill_plan_t {
     int32_t tile_rows;         /* routed rows of one expert per tile: 16, 32 or 64 */
     int32_t x_terms;           /* FP8 terms of the expert input in the gate/up products;
                                   0: the MX-FP4 expert input (act_quant = 1), one FP4 operand */
-    int32_t act_terms;         /* FP8 terms of the SwiGLU output in the down products */
+    int32_t act_terms;         /* FP8 terms of the SwiGLU output in the down products;
+                                  0: its MX-FP4 codes (act_quant = 2) */
     int32_t gate_up_features;  /* features (gate and up rows each) per gate/up work item */
     int32_t down_rows;         /* hidden rows per down work item */
 } moe_prefill_plan_t;

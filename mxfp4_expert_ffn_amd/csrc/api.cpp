@@ -74,8 +74,8 @@ int check_shape(const moe_shape *s) {
     if (!std::isfinite(s->swiglu_up_offset)) return fail(MOE_ERR_INVALID_ARG, "swiglu_up_offset is not finite");
     if (!std::isfinite(s->route_scale) || !(s->route_scale > 0.f))
         return fail(MOE_ERR_INVALID_ARG, "route_scale must be finite and > 0");
-    if (s->act_quant != 0 && s->act_quant != 1)
-        return fail(MOE_ERR_INVALID_ARG, "act_quant=%d must be 0 or 1", s->act_quant);
+    if (s->act_quant < 0 || s->act_quant > 2)
+        return fail(MOE_ERR_INVALID_ARG, "act_quant=%d must be 0, 1 or 2", s->act_quant);
     return MOE_OK;
 }
 
@@ -274,7 +274,7 @@ int route_front(const moe_shape *s, const void *x, const float *norm_w, const fl
 // The grouped GEMMs' tiling and term counts for this call.
 moe::GemmPlan gemm_plan_of(const moe_shape *s, bool norm) {
     return moe::gemm_plan(s->T, s->k, s->E, s->n_shared, s->F, s->act_dtype == MOE_BF16 && !norm,
-                          s->act_quant != 0);
+                          s->act_quant != 0, s->act_quant == 2);
 }
 
 // Upper bound on the grouped GEMMs' row tiles (the grid is sized by it).
@@ -514,11 +514,12 @@ int moe_forward_prefill(const moe_shape *s, const void *hidden, const float *nor
     MOE_TRY(launch(MOE_KERNEL_GATE_UP_GEMM, "gate_up_gemm", st, [&] {
         return moe::launch_gate_up_gemm(w.xq, w.xs, s->T, s->H, s->F, s->E, s->k, s->n_shared, ex,
                                         sh, c, w.offsets, w.perm, w.mprefix, bm, mt, plan.x_terms,
-                                        w.act_q, w.act_s, st);
+                                        plan.act_terms == 0, w.act_q, w.act_s, st);
     }));
     MOE_TRY(launch(MOE_KERNEL_DOWN_GEMM, "down_gemm", st, [&] {
         return moe::launch_down_gemm(w.act_q, w.act_s, s->T, s->H, s->F, s->E, s->k, s->n_shared,
-                                     ex, sh, w.offsets, w.perm, w.wts, w.mprefix, bm, mt, w.y, st);
+                                     ex, sh, w.offsets, w.perm, w.wts, w.mprefix, bm, mt,
+                                     plan.act_terms == 0, w.y, st);
     }));
     MOE_TRY(launch(MOE_KERNEL_COMBINE, "combine", st, [&] {
         return moe::launch_combine(w.y, w.inv, s->T, s->H, s->k, s->n_shared, hidden,

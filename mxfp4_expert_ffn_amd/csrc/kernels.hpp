@@ -193,30 +193,36 @@ struct GemmPlan {
     int tile_rows;         // activation rows per tile
     int x_terms;           // FP8 terms of the expert input that take part (3 or kTerms), or 0:
                            // the MX-FP4 expert input of the quantised mode
-    int act_terms;         // FP8 terms of the SwiGLU output that take part
+    int act_terms;         // FP8 terms of the SwiGLU output that take part, or 0: its
+                           // MX-FP4 codes (quantised mode 2)
     int gate_up_features;  // features per gate/up workgroup
     int down_rows;         // hidden rows per down workgroup
 };
 // x_bf16_exact: the expert input is a bfloat16 value (no RMSNorm in between),
 // which three terms carry as closely as four.
-// x_fp4: the quantised expert-input mode.
-GemmPlan gemm_plan(int T, int k, int E, int n_shared, int F, bool x_bf16_exact, bool x_fp4);
-// x_terms: FP8 terms of the expert input that take part, 3 or kTerms.
+// x_fp4: the quantised expert-input mode; act_fp4: its mode 2 (the SwiGLU
+// output quantised too).
+GemmPlan gemm_plan(int T, int k, int E, int n_shared, int F, bool x_bf16_exact, bool x_fp4,
+                   bool act_fp4);
+// x_terms: FP8 terms of the expert input that take part, 3 or kTerms, or 0
+// (MX-FP4 input); act_fp4: the SwiGLU output leaves as MX-FP4 codes (needs
+// x_terms 0).
 hipError_t launch_gate_up_gemm(const uint8_t *xq, const uint8_t *xs, int T, int H, int F, int E,
                                int k, int n_shared, const ExpertPtrs &ex, const ExpertPtrs &sh,
                                SwigluConsts c, const int32_t *offsets, const int32_t *perm,
                                const int32_t *mprefix, int tile_rows, int max_tiles, int x_terms,
-                               uint8_t *act_q, uint8_t *act_s, hipStream_t s);
+                               bool act_fp4, uint8_t *act_q, uint8_t *act_s, hipStream_t s);
 // FP8 terms of the SwiGLU output that take part in the grouped down GEMM:
 // the fourth moves the block output by under 3e-5 of its RMS on every
 // configuration (the down GEMM averages the third term's rounding away).
 constexpr int kDownTerms = 3;
-// y [T*k + T*n_shared][H] fp32: route weight x (down + bias) per row position
+// y [T*k + T*n_shared][H] fp32: route weight x (down + bias) per row position;
+// act_fp4: the activation rows are MX-FP4 codes (quantised mode 2)
 hipError_t launch_down_gemm(const uint8_t *act_q, const uint8_t *act_s, int T, int H, int F, int E,
                             int k, int n_shared, const ExpertPtrs &ex, const ExpertPtrs &sh,
                             const int32_t *offsets, const int32_t *perm, const float *wts,
-                            const int32_t *mprefix, int tile_rows, int max_tiles, float *y,
-                            hipStream_t s);
+                            const int32_t *mprefix, int tile_rows, int max_tiles, bool act_fp4,
+                            float *y, hipStream_t s);
 // out[t] = resid[t] + sum_j y[inv[t*k + j]] (+ y[T*k + t]); out may alias a float32 resid
 hipError_t launch_combine(const float *y, const int32_t *inv, int T, int H, int k, int n_shared,
                           const void *resid, int resid_bf16, float *out, hipStream_t s);

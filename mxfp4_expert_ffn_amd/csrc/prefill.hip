@@ -404,8 +404,10 @@ __device__ __forceinline__ void load_pre(const int32_t *mprefix, int G, int *s_p
 
 // gate/up: grid = kXcds-rounded max_tiles x ceil(pad128(F) / kGateUpRows) items;
 // NT FP8 terms of the expert input take part, or (NT = 0) its MX-FP4 codes.
+// Q4A: the SwiGLU output leaves as MX-FP4 codes (act_q [rows][Fp / 2], one
+// scale byte per 32 values in act_s [rows][Fp / 32]) instead of FP8 terms.
 // 16-row tiles are held to 4 wavefronts per SIMD (128 VGPRs, no spills).
-template <int NG, int W, int NA, int NT>
+template <int NG, int W, int NA, int NT, bool Q4A>
 __global__ __launch_bounds__(64 * W, NG == 1 ? 4 : (W == 4 ? 2 : 1)) void gate_up_gemm_kernel(
     const uint8_t *xq, const uint8_t *xs, int T, int H, int F, int E, int k, int n_shared,
     ExpertPtrs ex, ExpertPtrs sh, SwigluConsts sc, const int32_t *offsets, const int32_t *perm,
@@ -467,7 +469,7 @@ __global__ __launch_bounds__(64 * W, NG == 1 ? 4 : (W == 4 ? 2 : 1)) void gate_u
         gemm_mainloop<NG, W, NA, NT>(aq, as, al, Kp / 128, xq, xs, Kp, s_brow, tl.n, sB, sBs, acc);
 
     // epilogue: SwiGLU of the workgroup's features into LDS, then one
-    // 32-feature block per (row, block) to FP8 terms
+    // 32-feature block per (row, block) to FP8 terms (or MX-FP4 codes)
     __syncthreads();  // the staging buffers become the SwiGLU outputs
     float *sAct = reinterpret_cast<float *>(sB);
     const int col = lane & 15, kh = lane >> 4;
@@ -492,6 +494,26 @@ __global__ __launch_bounds__(64 * W, NG == 1 ? 4 : (W == 4 ? 2 : 1)) void gate_u
     constexpr int kBlocks = Gm::kGateUpRows / 32;
     const int half = lane >> 5, i = lane & 31, nbp = Fp / 32;
     const int ntask = tl.n * kBlocks;
+    if constexpr (Q4A) {
+        // one (row, block) per half-wavefront at a time; every lane takes part
+        // in the block maximum, blocks at or past F are zeros (code 0)
+        for (int task0 = 2 * w; task0 < ntask; task0 += 2 * W) {
+            const int task = task0 + half;
+            const bool on = task < ntask;
+            const int row = on ? task / kBlocks : 0;
+            const int blk = on ? task - row * kBlocks : 0;
+            const int fb = fw + 32 * blk;
+            const float v = on && fb < F ? sAct[row * kActStride + 32 * blk + i] : 0.f;
+            uint32_t sbyte;
+            const uint32_t pair = fp4_pack_pair(fp4_act_code(v, sbyte));
+            if (on && fb < Fp) {
+                const size_t p = static_cast<size_t>(tl.p0 + row);
+                if ((i & 1) == 0) act_q[p * (Fp / 2) + fb / 2 + (i >> 1)] = static_cast<uint8_t>(pair);
+                if (i == 0) act_s[p * nbp + fb / 32] = static_cast<uint8_t>(sbyte);
+            }
+        }
+        return;
+    }
     for (int task0 = 4 * w; task0 < ntask; task0 += 4 * W) {
         int row[2], fb[2];
         bool on[2];
@@ -525,8 +547,9 @@ __global__ __launch_bounds__(64 * W, NG == 1 ? 4 : (W == 4 ? 2 : 1)) void gate_u
     }
 }
 
-// down: grid = kXcds-rounded max_tiles x ceil(H / kDownRows) items.
-template <int NG, int W, int NA>
+// down: grid = kXcds-rounded max_tiles x ceil(H / kDownRows) items. A4: the
+// activation rows are MX-FP4 codes (FP4 x FP4 products) instead of FP8 terms.
+template <int NG, int W, int NA, bool A4>
 __global__ __launch_bounds__(64 * W) void down_gemm_kernel(
     const uint8_t *act_q, const uint8_t *act_s, int T, int H, int F, int E, int k, int n_shared,
     ExpertPtrs ex, ExpertPtrs sh, const int32_t *offsets, const int32_t *perm, const float *wts,
@@ -536,7 +559,7 @@ __global__ __launch_bounds__(64 * W) void down_gemm_kernel(
     __shared__ int s_brow[Gm::kRows];
     __shared__ float s_wt[Gm::kRows];
     __shared__ __align__(16) uint8_t sB[2 * Gm::kBufBytes];
-    __shared__ uint8_t sBs[2 * 4 * Gm::kScales];
+    __shared__ __align__(16) uint8_t sBs[2 * 4 * Gm::kScales];  // dword-read by the FP4 main loop
     __shared__ __align__(16) float s_bias[Gm::kDownRows];  // biases of the workgroup's hidden rows
     const int G = E + n_shared, R = T * k;
     load_pre(mprefix, G, s_pre);
@@ -574,8 +597,11 @@ __global__ __launch_bounds__(64 * W) void down_gemm_kernel(
 #pragma unroll
         for (int g = 0; g < NG; ++g) acc[j][g] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     const int Fp = pad128(F);
-    gemm_mainloop<NG, W, NA, kDownTerms>(aq, as, al, Fp / 128, act_q, act_s, Fp, s_brow, tl.n, sB,
-                                         sBs, acc);
+    if constexpr (A4)
+        gemm_mainloop_x4<NG, W, NA>(aq, as, al, Fp / 128, act_q, act_s, Fp, s_brow, tl.n, sB, sBs, acc);
+    else
+        gemm_mainloop<NG, W, NA, kDownTerms>(aq, as, al, Fp / 128, act_q, act_s, Fp, s_brow, tl.n, sB,
+                                             sBs, acc);
 
     // y[p][h] = route weight x (down + bias), four consecutive h per lane
     const int col = lane & 15, kh = lane >> 4;
@@ -652,7 +678,8 @@ int items(int nrb, int max_tiles) {
 // fourth does not fit two wavefronts' registers per SIMD at 64 rows and was
 // slower at 32); 16-row tiles take four of a float32 input. An MX-FP4
 // expert input (x_fp4) is one FP4 operand (x_terms 0).
-GemmPlan gemm_plan(int T, int k, int E, int n_shared, int F, bool x_bf16_exact, bool x_fp4) {
+GemmPlan gemm_plan(int T, int k, int E, int n_shared, int F, bool x_bf16_exact, bool x_fp4,
+                   bool act_fp4) {
     const double rows = static_cast<double>(T) * (k + n_shared);
     const int groups = E + n_shared;
     const double avg = rows / groups;
@@ -662,7 +689,7 @@ GemmPlan gemm_plan(int T, int k, int E, int n_shared, int F, bool x_bf16_exact, 
     else if (avg >= 24.0) p.tile_rows = 32;
     else p.tile_rows = 16;
     p.x_terms = x_fp4 ? 0 : (x_bf16_exact || p.tile_rows >= 32) ? 3 : kTerms;
-    p.act_terms = kDownTerms;
+    p.act_terms = act_fp4 ? 0 : kDownTerms;
     p.gate_up_features = p.tile_rows == 16 ? 128 : 256;
     p.down_rows = p.tile_rows == 16 ? 256 : 512;
     return p;
@@ -674,14 +701,23 @@ hipError_t launch_gate_up_gemm(const uint8_t *xq, const uint8_t *xs, int T, int 
                                int k, int n_shared, const ExpertPtrs &ex, const ExpertPtrs &sh,
                                SwigluConsts c, const int32_t *offsets, const int32_t *perm,
                                const int32_t *mprefix, int tile_rows, int max_tiles, int x_terms,
-                               uint8_t *act_q, uint8_t *act_s, hipStream_t s) {
+                               bool act_fp4, uint8_t *act_q, uint8_t *act_s, hipStream_t s) {
+    if (act_fp4 && x_terms != 0) return hipErrorInvalidValue;  // the FP4 output comes with the FP4 input
 #define MOE_GU(NG, W, NA, NT)                                                                       \
     do {                                                                                            \
         using Gm = Geo<NG, W, NA>;                                                                  \
         const int grid = items((pad128(F) + Gm::kGateUpRows - 1) / Gm::kGateUpRows, max_tiles);    \
         if (grid == 0) return hipSuccess;                                                           \
-        launch_kernel(gate_up_gemm_kernel<NG, W, NA, NT>, grid, 64 * (W), s, xq, xs, T, H, F, E,   \
-                      k, n_shared, ex, sh, c, offsets, perm, mprefix, act_q, act_s);                \
+        if constexpr ((NT) == 0) {  /* the FP4 output comes only with the FP4 input */          \
+            if (act_fp4) {                                                                          \
+                launch_kernel(gate_up_gemm_kernel<NG, W, NA, NT, true>, grid, 64 * (W), s, xq, xs, \
+                              T, H, F, E, k, n_shared, ex, sh, c, offsets, perm, mprefix, act_q,    \
+                              act_s);                                                               \
+                break;                                                                              \
+            }                                                                                       \
+        }                                                                                           \
+        launch_kernel(gate_up_gemm_kernel<NG, W, NA, NT, false>, grid, 64 * (W), s, xq, xs, T, H,  \
+                      F, E, k, n_shared, ex, sh, c, offsets, perm, mprefix, act_q, act_s);          \
     } while (0)
     if (x_terms != 0 && x_terms != 3 && x_terms != kTerms) return hipErrorInvalidValue;
     switch (tile_rows * 10 + x_terms) {
@@ -701,15 +737,19 @@ hipError_t launch_gate_up_gemm(const uint8_t *xq, const uint8_t *xs, int T, int 
 hipError_t launch_down_gemm(const uint8_t *act_q, const uint8_t *act_s, int T, int H, int F, int E,
                             int k, int n_shared, const ExpertPtrs &ex, const ExpertPtrs &sh,
                             const int32_t *offsets, const int32_t *perm, const float *wts,
-                            const int32_t *mprefix, int tile_rows, int max_tiles, float *y,
-                            hipStream_t s) {
+                            const int32_t *mprefix, int tile_rows, int max_tiles, bool act_fp4,
+                            float *y, hipStream_t s) {
 #define MOE_DN(NG, W, NA)                                                                           \
     do {                                                                                            \
         using Gm = Geo<NG, W, NA>;                                                                  \
         const int grid = items((H + Gm::kDownRows - 1) / Gm::kDownRows, max_tiles);                 \
         if (grid == 0) return hipSuccess;                                                           \
-        launch_kernel(down_gemm_kernel<NG, W, NA>, grid, 64 * (W), s, act_q, act_s, T, H, F, E, k,  \
-                      n_shared, ex, sh, offsets, perm, wts, mprefix, y);                            \
+        if (act_fp4)                                                                                \
+            launch_kernel(down_gemm_kernel<NG, W, NA, true>, grid, 64 * (W), s, act_q, act_s, T, H,  \
+                          F, E, k, n_shared, ex, sh, offsets, perm, wts, mprefix, y);               \
+        else                                                                                        \
+            launch_kernel(down_gemm_kernel<NG, W, NA, false>, grid, 64 * (W), s, act_q, act_s, T, H, \
+                          F, E, k, n_shared, ex, sh, offsets, perm, wts, mprefix, y);               \
     } while (0)
     switch (tile_rows) {
     case 16: MOE_DN(1, 4, 4); break;

@@ -145,7 +145,9 @@ def expert_ffn(xr: np.ndarray, planes, e: int, alpha: float, limit: float, up_of
                stats: dict | None = None, quant_act: bool = False) -> np.ndarray:
     """quant_act: the SwiGLU output, as float32, goes through the MX-FP4 round
     trip (blocks of 32 along F) before the down projection; `stats["act"]`
-    then collects the unrounded outputs (for the tests' rounding-edge bound)."""
+    then collects {"e", "a", "clamped"}: the expert, its unrounded outputs and
+    where both of their inputs were clamped (for the tests' rounding-edge
+    bound; the block adds the rows' tokens and slots)."""
     wg, wu, wd = dequant_expert(planes, e)
     g = xr @ wg.T + planes.gate_bias[e].astype(np.float64)
     u = xr @ wu.T + planes.up_bias[e].astype(np.float64)
@@ -156,7 +158,10 @@ def expert_ffn(xr: np.ndarray, planes, e: int, alpha: float, limit: float, up_of
     a = swiglu(g, u, alpha, limit, up_offset)
     if quant_act:
         if stats is not None:
-            stats.setdefault("act", []).append((e, a))
+            # values whose gate and up were both clamped come out as one constant
+            # (no accumulated product left in them)
+            both = (g >= limit) & (np.abs(u) >= limit)
+            stats.setdefault("act", []).append({"e": e, "a": a, "clamped": both})
         a = act_quant_mod.quantize_rows(a.astype(np.float32))[2]
     return a @ wd.T + planes.down_bias[e].astype(np.float64)
 
@@ -258,12 +263,16 @@ def moe_block(layer, x: np.ndarray, k: int, alpha: float, limit: float, up_offse
         rows, slots = np.nonzero(idx[toks] == e)
         y[rows, slots] = expert_ffn(xe[toks[rows]], layer.experts, int(e),
                                     alpha, limit, up_offset, stats, quant_act=act_quant == 2)
+        if act_quant == 2 and stats is not None:
+            stats["act"][-1].update(tokens=toks[rows], slots=slots, shared=False)
     for j in range(k):                              # slot-ordered weighted sum
         delta += w[toks, j][:, None] * y[:, j]
     if layer.shared is not None:
         for s in range(layer.shared.n):
             delta += expert_ffn(xe[toks], layer.shared, s, alpha, limit, up_offset, stats,
                                 quant_act=act_quant == 2)
+            if act_quant == 2 and stats is not None:
+                stats["act"][-1].update(tokens=toks, slots=None, shared=True)
     out = (x[toks] + delta).astype(np.float32)
     return dict(out=out, delta=delta, logits=logits, sel=sel, idx=idx, w=w, counts=counts,
                 offsets=offsets, perm=perm, inv=inv, xn=xn, xe=xe, tokens=toks,

@@ -164,7 +164,7 @@ def _routing(**kw):
     ("bad dtype", dict(act_dtype="x"), {}, None),
     ("small workspace", {}, dict(ws_bytes=1024), _lib.MOE_ERR_WORKSPACE),
     ("null workspace", {}, dict(ws=None), _lib.MOE_ERR_WORKSPACE),
-    ("act_quant 2", dict(act_quant=2), {}, _lib.MOE_ERR_INVALID_ARG),
+    ("act_quant 3", dict(act_quant=3), {}, _lib.MOE_ERR_INVALID_ARG),
     ("table without ids", {}, dict(routing=_routing(tid2eid=FAKE, vocab=10)), _lib.MOE_ERR_INVALID_ARG),
     ("table with vocab 0", {}, dict(routing=_routing(tid2eid=FAKE, token_ids=FAKE)),
      _lib.MOE_ERR_INVALID_ARG),
@@ -248,11 +248,15 @@ def test_prefill_plan_of_the_quantised_mode(cid):
     assert quant["x_terms"] == 0
     assert {k: v for k, v in quant.items() if k != "x_terms"} == \
         {k: v for k, v in exact.items() if k != "x_terms"}
+    both = mx.moe_prefill_plan(mx.make_shape(**kw, act_quant=2), with_norm=cfg.rms_eps is not None)
+    assert both["x_terms"] == 0 and both["act_terms"] == 0
+    assert both["tile_rows"] == exact["tile_rows"]
 
 
 def test_decode_rejects_the_quantised_mode():
     # the mode check runs before any device call
     assert _call("moe_forward_decode", _shape(act_quant=1)) == _lib.MOE_ERR_UNSUPPORTED
+    assert _call("moe_forward_decode", _shape(act_quant=2)) == _lib.MOE_ERR_UNSUPPORTED
     assert _call("moe_forward_decode", _shape(T=64, act_quant=1)) == _lib.MOE_ERR_UNSUPPORTED
 
 

@@ -192,4 +192,4 @@ def test_mode2_collects_the_unrounded_swiglu_output():
     omoe.block_for_config(cfg, layer, x, stats=stats, act_quant=2)
     acts = stats["act"]
     assert len(acts) == len(np.unique(omoe.block_for_config(cfg, layer, x)["idx"]))
-    assert all(a.shape[1] == cfg.F for _, a in acts)
+    assert all(r["a"].shape == (len(r["tokens"]), cfg.F) for r in acts)

@@ -1,5 +1,5 @@
-"""The quantised expert-input mode (act_quant = 1) on the GPU against the
-oracle.
+"""The quantised modes (act_quant = 1: MX-FP4 expert input; 2: and MX-FP4
+SwiGLU output) on the GPU against the oracle.
 
 Bars:
 - the MX-FP4 expert input (codes and scale bytes, moe_act_quant_debug) is
@@ -16,7 +16,9 @@ Bars:
   only float32 accumulation error to the exact mode's FP8-term error of the
   SwiGLU output;
 - the mode changes the output by more than that bound against the exact
-  block, so the test would see a path that ignored the mode.
+  block, so the test would see a path that ignored the mode;
+- mode 2: the same bound plus an allowance, computed from the oracle alone,
+  for SwiGLU values at an MX-FP4 rounding edge (see kEdge below).
 Page: antirez ds4.c `dsv4_fp4_act_quantize_row_inplace_cpu`,
 `dsv4_e2m1fn_dequant_cpu`; goosedump `mixture_of_experts` (`Q8Activation`:
 the expert input quantised once for every expert row).
@@ -29,6 +31,7 @@ import mxfp4_expert_ffn_amd as mx
 from mxfp4_expert_ffn_amd.device import workspace
 from oracle import act_quant as aq
 from oracle import moe as omoe
+from oracle import mxfp4 as omx
 from workloads import config_by_id, make_layer, scaled
 from workloads.gen import make_activations
 
@@ -195,7 +198,6 @@ def test_prefill_block_matches_exact_mode_on_grid_inputs():
     _announce("act_quant prefill: grid inputs, both modes")
     layer = make_layer(cfg)
     rng = np.random.default_rng(9)
-    from oracle import mxfp4 as omx
     codes = rng.integers(0, 16, size=(cfg.T, cfg.H)).astype(np.uint8)
     codes[:, ::32] = 7
     e = rng.integers(-3, 1, size=(cfg.T, cfg.H // 32))
@@ -221,3 +223,96 @@ def test_decode_rejects_the_mode():
         mx.moe_forward_decode(shape, torch.from_numpy(x).cuda(), dl.router_w, dl.router_b,
                               dl.experts_copy(0), out, workspace(shape))
     assert ei.value.code == mx._lib.MOE_ERR_UNSUPPORTED
+
+
+# ---------------------------------------------------------------- mode 2
+# The SwiGLU output is rounded to MX-FP4 on each side from its own float32
+# value: the oracle's from fp64 arithmetic, the GPU's from float32 matrix-core
+# accumulation of exact FP4 x FP4 products. Where a value lies within
+# kEdge x 2^e of an E2M1 decision boundary of its block (scale 2^e), or its
+# block maximum within kEdge x 2^e of the point where the scale changes, the
+# two sides may take neighbouring codes. The bar for a token is then the exact
+# mode's 2e-3 x RMS plus, per such value f of slot j, the route weight times
+# the code step at that boundary times |W_down[:, f]| (every code of the block
+# when its scale is in doubt). kEdge = 2^-13 of the scale, 2e-5 of the block
+# maximum, against float32 accumulation errors near 1e-6 of it. A value whose
+# gate and up were both clamped holds no accumulated product: both sides
+# evaluate limit * sigmoid(alpha * limit) * (+-limit + offset) from the same
+# constants, within a few float32 ulps, so its edge is kEdgeClamped = 2^-18 of
+# the scale (gpt-oss's clamped outputs, 55.99963 on a scale of 16, sit 2.3e-5
+# of the scale below the 3.5 boundary).
+kEdge = 2.0 ** -13
+kEdgeClamped = 2.0 ** -18
+_BOUNDS = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])
+_STEPS = np.array([0.5, 0.5, 0.5, 0.5, 1.0, 1.0, 2.0])
+
+
+def _edge_steps(a64: np.ndarray, clamped: np.ndarray) -> np.ndarray:
+    """Per value of `a` [rows, F]: the code step it may take at a rounding edge
+    (in units of its value), 0 where it is clear of every edge."""
+    rows, F = a64.shape
+    width = np.where(clamped, kEdgeClamped, kEdge).reshape(rows, F // 32, 32)
+    blk = a64.reshape(rows, F // 32, 32)
+    amax = np.maximum(np.abs(blk).max(axis=-1).astype(np.float32), np.float32(aq.AMAX_FLOOR))
+    sc = np.ldexp(1.0, aq.block_exponent(amax))              # [rows, nb]
+    r = np.abs(blk) / sc[..., None]
+    near = np.abs(r[..., None] - _BOUNDS) <= width[..., None]  # [rows, nb, 32, 7]
+    step = np.where(near, _STEPS, 0.0).max(axis=-1) * sc[..., None]
+    # a block maximum at the scale's edge (1.5 x 2^E) may move every code
+    m = amax.astype(np.float64)
+    E = np.floor(np.log2(m)).astype(np.int64)
+    doubt = np.abs(m - 1.5 * np.ldexp(1.0, E)) <= kEdge * sc
+    step = np.where(doubt[..., None], 4.0 * sc[..., None], step)
+    return step.reshape(rows, F)
+
+
+def _edge_allowance(cfg, layer, ref, stats, toks) -> np.ndarray:
+    """[len(toks), H]: the output movement rounding-edge codes may cause."""
+    pos = {int(t): i for i, t in enumerate(toks)}
+    allow = np.zeros((len(toks), cfg.H))
+    for rec in stats["act"]:
+        planes = layer.shared if rec["shared"] else layer.experts
+        wd = np.abs(omx.dequant(planes.down_codes[rec["e"]], planes.down_scales[rec["e"]]))
+        st = _edge_steps(rec["a"], rec["clamped"])
+        for i, t in enumerate(rec["tokens"]):
+            if int(t) not in pos or not st[i].any():
+                continue
+            w = 1.0 if rec["shared"] else float(ref["w"][int(t), rec["slots"][i]])
+            allow[pos[int(t)]] += w * (wd @ st[i])
+    return allow
+
+
+@pytest.mark.parametrize("cid,T,tile", [(1, 8, 16), (3, 128, 16), (5, 1024, 32), (5, 2048, 64)])
+def test_prefill_block_mode2(cid, T, tile):
+    """SwiGLU output quantised too: FP4 x FP4 down products."""
+    cfg = scaled(config_by_id(cid), T=T)
+    _announce(f"act_quant 2 prefill: config {cid} T={T}")
+    layer = make_layer(cfg)
+    x, xb = make_activations(cfg)
+    kw = cfg.shape_kwargs()
+    kw["act_quant"] = 2
+    shape = mx.make_shape(**kw)
+    plan = mx.moe_prefill_plan(shape, with_norm=layer.norm_w is not None)
+    assert plan["tile_rows"] == tile and plan["x_terms"] == 0 and plan["act_terms"] == 0
+    dl = upload(cfg, layer)
+    out, ro = run_forward("prefill", shape, dl, device_input(cfg, x, xb))
+    ro = to_np(ro)
+    out = out.cpu().numpy()
+    toks = np.arange(T) if T <= 128 else np.random.default_rng(T + 2).choice(T, 12, replace=False)
+    stats = {}
+    ref = omoe.block_for_config(cfg, layer, x, tokens=toks, stats=stats, act_quant=2)
+    check_routing(ro["topk_idx"], ro["topk_w"], ref, layer.router_w, layer.router_b,
+                  cfg.route_scale)
+    want = x[toks] + ref["delta"]
+    rms = np.sqrt(np.mean(want.astype(np.float64) ** 2))
+    allow = _edge_allowance(cfg, layer, ref, stats, toks)
+    err = np.abs(out[toks].astype(np.float64) - want)
+    bar = TOL * rms + allow
+    clear = ~allow.any(axis=1)
+    print(f"config {cid} T={T} mode 2: max|err|/rms = {err.max() / rms:.2e}; tokens clear of "
+          f"rounding edges {int(clear.sum())}/{len(toks)}, their max|err|/rms = "
+          f"{(err[clear].max() / rms) if clear.any() else float('nan'):.2e}")
+    assert np.all(err <= bar), f"worst excess {float((err - bar).max()) / rms:.3e} x RMS"
+    # against the mode that keeps the SwiGLU output exact, the difference is real
+    one = omoe.block_for_config(cfg, layer, x, tokens=toks, act_quant=1)
+    assert rel_err(x[toks] + one["delta"], want) > 5 * TOL
