@@ -130,7 +130,10 @@ __device__ __forceinline__ bool find_item(int nrb, int bm, const int32_t *offset
 // LDS holds a step's B pieces in fragment order: piece p = ((term * NG +
 // group) * 8 + chunk) * 16 + column, so the 16 lanes of one k-group read 256
 // contiguous bytes; the B scale bytes sit in lane order, [term][k-group][row].
-// All kTerms terms are staged; the first NT of them meet the A fragments.
+// Only the NT terms that meet the A fragments are staged (three of the four
+// stored: a quarter less B traffic through L2 and LDS per step); when the
+// pieces do not divide evenly over the threads, the last threads reload and
+// rewrite the last piece (the same bytes to the same place).
 template <int NG, int W, int NA, int NT>
 __device__ __forceinline__ void gemm_mainloop(const uint8_t *const (&aq)[NA],
                                               const uint8_t *const (&as)[NA], const ALane &al,
@@ -139,25 +142,31 @@ __device__ __forceinline__ void gemm_mainloop(const uint8_t *const (&aq)[NA],
                                               f32x4_t (&acc)[NA][NG]) {
     using Gm = Geo<NG, W, NA>;
     constexpr int kThreads = Gm::kThreads;
+    constexpr int kPcs = NT * NG * 8 * 16;                    // staged pieces per step
+    constexpr int kPT = (kPcs + kThreads - 1) / kThreads;     // per thread
+    constexpr int kScl = Gm::kRows * NT;                      // staged scale dwords per step
+    static_assert(kScl <= kThreads, "one scale dword per thread at most");
     const int tid = threadIdx.x, lane = tid & 63;
-    // this thread's B pieces: byte offsets from bq at step 0
-    uint32_t soff[Gm::kPerThread];
+    // this thread's B pieces: byte offsets from bq at step 0, and LDS slots
+    uint32_t soff[kPT];
+    int sdp[kPT];
 #pragma unroll
-    for (int i = 0; i < Gm::kPerThread; ++i) {
-        const int p = tid + kThreads * i;
+    for (int i = 0; i < kPT; ++i) {
+        const int p = min(tid + kThreads * i, kPcs - 1);
         const int col = p & 15, chunk = (p >> 4) & 7, grp = (p >> 7) % NG, term = (p >> 7) / NG;
         soff[i] = static_cast<uint32_t>((s_brow[16 * grp + col] * kTerms + term) * Kb + 16 * chunk);
+        sdp[i] = 16 * p;
     }
-    // threads < kScales stage the scale dword (blocks 4s..4s+3) of one (row, term)
-    const bool sc_on = tid < Gm::kScales;
-    const int stok = sc_on ? tid >> 2 : 0, sterm = tid & 3;
+    // threads < kScl stage the scale dword (blocks 4s..4s+3) of one (row, term)
+    const bool sc_on = tid < kScl;
+    const int stok = sc_on ? tid / NT : 0, sterm = tid % NT;
     const uint32_t *ssrc = reinterpret_cast<const uint32_t *>(
         bs + (static_cast<size_t>(s_brow[stok]) * kTerms + sterm) * (Kb / 32));
     const int sdst = sterm * 4 * Gm::kRows + stok;  // byte of k-group h at sdst + h * kRows
     const int ngroups = (n + 15) >> 4;               // row groups holding tile rows
 
     struct BSlot {
-        u32x4_t b[Gm::kPerThread];
+        u32x4_t b[kPT];
         uint32_t s;
     };
     struct ASlot {
@@ -166,7 +175,7 @@ __device__ __forceinline__ void gemm_mainloop(const uint8_t *const (&aq)[NA],
     auto fill_b = [&](BSlot &sl, int step) __attribute__((always_inline)) {
         const int sd = min(step, NS - 1);
 #pragma unroll
-        for (int i = 0; i < Gm::kPerThread; ++i)
+        for (int i = 0; i < kPT; ++i)
             sl.b[i] = *reinterpret_cast<const u32x4_t *>(bq + soff[i] + 128 * sd);
         sl.s = ssrc[sd];
     };
@@ -181,8 +190,7 @@ __device__ __forceinline__ void gemm_mainloop(const uint8_t *const (&aq)[NA],
         uint8_t *buf = sB + L * Gm::kBufBytes;
         uint8_t *sbuf = sBs + L * 4 * Gm::kScales;
 #pragma unroll
-        for (int i = 0; i < Gm::kPerThread; ++i)
-            *reinterpret_cast<u32x4_t *>(buf + 16 * (tid + kThreads * i)) = bsl.b[i];
+        for (int i = 0; i < kPT; ++i) *reinterpret_cast<u32x4_t *>(buf + sdp[i]) = bsl.b[i];
         if (sc_on) {
 #pragma unroll
             for (int h = 0; h < 4; ++h) sbuf[sdst + h * Gm::kRows] = static_cast<uint8_t>(bsl.s >> (8 * h));
@@ -231,8 +239,7 @@ __device__ __forceinline__ void gemm_mainloop(const uint8_t *const (&aq)[NA],
             uint8_t *buf = sB + L * Gm::kBufBytes;
             uint8_t *sbuf = sBs + L * 4 * Gm::kScales;
 #pragma unroll
-            for (int i = 0; i < Gm::kPerThread; ++i)
-                *reinterpret_cast<u32x4_t *>(buf + 16 * (tid + kThreads * i)) = bsl.b[i];
+            for (int i = 0; i < kPT; ++i) *reinterpret_cast<u32x4_t *>(buf + sdp[i]) = bsl.b[i];
             if (sc_on) {
 #pragma unroll
                 for (int h = 0; h < 4; ++h) sbuf[sdst + h * Gm::kRows] = static_cast<uint8_t>(bsl.s >> (8 * h));
