@@ -60,6 +60,7 @@ METRIC = "MoE block tokens/s (decode T=1, prefill T=128/512) + % HBM/MFMA peak"
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
 FP8_PEAK_TFLOPS = 5000.0        # MI355X dense FP8 MFMA: the rate of the FP4 x FP8 scaled MFMA used
 FP4_PEAK_TFLOPS = 10100.0       # MI355X dense FP4 MFMA: the FP4 x FP4 rate (quantised expert input)
+BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA: a bfloat16 expert input taken as it is
 DTYPE = "fp4xfp8"               # MXFP4 weights x FP8-term activations, float32 accumulation
 
 WORKLOADS = {
@@ -321,6 +322,12 @@ class Setup:
                     unit="routed row (token, expert) of the grouped GEMM",
                     active_experts=sum(active) / len(active))
 
+    def gate_up_x_terms(self):
+        """The library's operand choice for the expert input of the gate/up
+        GEMM: FP8 terms (3 or 4), 1 (the bfloat16 input itself) or 0 (MX-FP4)."""
+        cfg = self.cfg
+        return self.mx.moe_prefill_plan(self.shape, with_norm=cfg.rms_eps is not None)["x_terms"]
+
     def issued_flops(self, counts_per_call):
         """Matrix-core flops the dominant kernel issues per launch, from its
         structure: every 16x16x128 block-scaled instruction counts
@@ -342,7 +349,8 @@ class Setup:
         # gate/up GEMM (the library's plan for this shape): per 16-row group of
         # an expert's rows, every gate and up weight tile of every feature block
         # of a work item, every 128-wide K-step, every FP8 term used (one
-        # instruction for the MX-FP4 input: x_terms 0)
+        # instruction for the MX-FP4 input, x_terms 0; four 16x16x32 bf16
+        # instructions, the same flops, for the bfloat16 input, x_terms 1)
         plan = self.mx.moe_prefill_plan(self.shape, with_norm=cfg.rms_eps is not None)
         nt, fwg = plan["x_terms"] or 1, plan["gate_up_features"]
         tiles = -(-pad128(F) // fwg) * (2 * fwg // 16)
@@ -598,9 +606,14 @@ def measure(wl: str, args, steps: int, warmup: int) -> dict:
     kern_s = kern_avg_ms / 1e3
     traffic = traffic_from_profile(kernel, wl)
     # the matrix-core peak of the instruction the kernel issues: FP4 x FP8
-    # (the FP8 rate), or FP4 x FP4 with the MX-FP4 expert input
-    mfma_peak = FP4_PEAK_TFLOPS if setup.act_quant else FP8_PEAK_TFLOPS
-    mfma_dtype = "fp4 (fp4 x fp4 scaled MFMA)" if setup.act_quant else "fp8 (fp4 x fp8 scaled MFMA)"
+    # (the FP8 rate), FP4 x FP4 with the MX-FP4 expert input, or bf16 x bf16
+    # when the gate/up GEMM takes a bfloat16 input as it is
+    if setup.act_quant:
+        mfma_peak, mfma_dtype = FP4_PEAK_TFLOPS, "fp4 (fp4 x fp4 scaled MFMA)"
+    elif kernel == "gate_up_gemm" and setup.gate_up_x_terms() == 1:
+        mfma_peak, mfma_dtype = BF16_PEAK_TFLOPS, "bf16 (weights decoded to bf16 in registers x bf16 input)"
+    else:
+        mfma_peak, mfma_dtype = FP8_PEAK_TFLOPS, "fp8 (fp4 x fp8 scaled MFMA)"
     t_hbm = alg["bytes"] / (HBM_PEAK_GBPS * 1e9)
     t_mfma = alg["flops"] / (mfma_peak * 1e12)
     if kernel.startswith("decode") or t_hbm >= t_mfma:

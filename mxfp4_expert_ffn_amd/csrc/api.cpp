@@ -487,17 +487,19 @@ int moe_forward_prefill(const moe_shape *s, const void *hidden, const float *nor
             return fail(MOE_ERR_UNSUPPORTED, "prefill needs T*(k+n_shared)*4*pad128(F) and T*4*pad128(H) below 2^32");
     }
     const Workspace w = carve(s, static_cast<uint8_t *>(ws));
-    // the FP8 terms of the expert input ride in the router launch in its
-    // GEMV form, else beside the one-workgroup permutation
+    const moe::GemmPlan plan = gemm_plan_of(s, norm_w != nullptr);
+    // the FP8 terms (or MX-FP4 codes) of the expert input ride in the router
+    // launch in its GEMV form, else beside the one-workgroup permutation; a
+    // bfloat16 input taken as it is (x_terms 1) needs neither
+    const bool need_terms = plan.x_terms != 1;
     moe::RouteIn in;
-    const bool router_terms = moe::router_plan(s->T, s->H, s->E).gemv;
+    const bool router_terms = need_terms && moe::router_plan(s->T, s->H, s->E).gemv;
     MOE_TRY(route_front(s, hidden, norm_w, router_w, w, router_terms, nullptr, &in, st));
     MOE_TRY(launch(MOE_KERNEL_TOPK, "topk", st, [&] {
         return moe::launch_topk(w.partial, w.splits, router_b, rs, s->T, s->E, s->k,
                                 s->route_scale, w.idx, w.wts, ro ? ro->topk_idx : nullptr,
                                 ro ? ro->topk_w : nullptr, st);
     }));
-    const moe::GemmPlan plan = gemm_plan_of(s, norm_w != nullptr);
     const int bm = plan.tile_rows;
     const moe::TermsOut tq{w.xq, w.xs, s->act_quant};
     MOE_TRY(launch(MOE_KERNEL_PERMUTE, "permute", st, [&] {
@@ -505,14 +507,15 @@ int moe_forward_prefill(const moe_shape *s, const void *hidden, const float *nor
                                    w.perm, w.inv, w.rank, w.mprefix, ro ? ro->counts : nullptr,
                                    ro ? ro->offsets : nullptr, ro ? ro->perm : nullptr,
                                    ro ? ro->inv : nullptr, ro ? ro->route_counts : nullptr, &in,
-                                   s->H, router_terms ? nullptr : &tq, st);
+                                   s->H, need_terms && !router_terms ? &tq : nullptr, st);
     }));
     const moe::ExpertPtrs ex = expert_ptrs(s, experts);
     const moe::ExpertPtrs sh = expert_ptrs(s, shared);
     const moe::SwigluConsts c{s->swiglu_alpha, s->swiglu_limit, s->swiglu_up_offset};
     const int mt = max_tiles(s, bm);
     MOE_TRY(launch(MOE_KERNEL_GATE_UP_GEMM, "gate_up_gemm", st, [&] {
-        return moe::launch_gate_up_gemm(w.xq, w.xs, s->T, s->H, s->F, s->E, s->k, s->n_shared, ex,
+        const uint8_t *xb = plan.x_terms == 1 ? static_cast<const uint8_t *>(hidden) : w.xq;
+        return moe::launch_gate_up_gemm(xb, w.xs, s->T, s->H, s->F, s->E, s->k, s->n_shared, ex,
                                         sh, c, w.offsets, w.perm, w.mprefix, bm, mt, plan.x_terms,
                                         plan.act_terms == 0, w.act_q, w.act_s, st);
     }));

@@ -191,22 +191,23 @@ hipError_t launch_decode_down(const DecodeArgs &a, hipStream_t s);
 // count.
 struct GemmPlan {
     int tile_rows;         // activation rows per tile
-    int x_terms;           // FP8 terms of the expert input that take part (3 or kTerms), or 0:
-                           // the MX-FP4 expert input of the quantised mode
+    int x_terms;           // FP8 terms of the expert input that take part (3 or kTerms), or 1:
+                           // the bfloat16 input itself (bfloat16 matrix cores), or 0: the
+                           // MX-FP4 expert input of the quantised mode
     int act_terms;         // FP8 terms of the SwiGLU output that take part, or 0: its
                            // MX-FP4 codes (quantised mode 2)
     int gate_up_features;  // features per gate/up workgroup
     int down_rows;         // hidden rows per down workgroup
 };
 // x_bf16_exact: the expert input is a bfloat16 value (no RMSNorm in between),
-// which three terms carry as closely as four.
+// taken as it is by the bfloat16 matrix cores.
 // x_fp4: the quantised expert-input mode; act_fp4: its mode 2 (the SwiGLU
 // output quantised too).
 GemmPlan gemm_plan(int T, int k, int E, int n_shared, int F, bool x_bf16_exact, bool x_fp4,
                    bool act_fp4);
-// x_terms: FP8 terms of the expert input that take part, 3 or kTerms, or 0
-// (MX-FP4 input); act_fp4: the SwiGLU output leaves as MX-FP4 codes (needs
-// x_terms 0).
+// x_terms: FP8 terms of the expert input that take part, 3 or kTerms (xq /
+// xs: the term rows), 1 (xq: the bfloat16 input [T][H] itself), or 0 (MX-FP4
+// input); act_fp4: the SwiGLU output leaves as MX-FP4 codes (needs x_terms 0).
 hipError_t launch_gate_up_gemm(const uint8_t *xq, const uint8_t *xs, int T, int H, int F, int E,
                                int k, int n_shared, const ExpertPtrs &ex, const ExpertPtrs &sh,
                                SwigluConsts c, const int32_t *offsets, const int32_t *perm,

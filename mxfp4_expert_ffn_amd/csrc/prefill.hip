@@ -404,13 +404,141 @@ __device__ __forceinline__ void gemm_mainloop_x4(const uint8_t *const (&aq)[NA],
     }
 }
 
+// Main loop with the bfloat16 expert input itself as operand B (a bfloat16
+// input with no RMSNorm in between): the MXFP4 weights are decoded to
+// bfloat16 in registers with the scaled FP4 converts (exact: an E2M1 value
+// times 2^n is a bfloat16 for scale bytes 1..252) and multiplied on the
+// bfloat16 matrix cores, v_mfma_f32_16x16x32_bf16, one instruction per
+// 32-wide slice of K instead of one per FP8 term: two thirds of the
+// matrix-core time of three terms, and two bytes per activation staged
+// instead of three. The products are exact and accumulate in float32, as on
+// the FP8-term path.
+//
+// K order: an A fragment (16 B per lane) holds the 32 codes of k-group
+// h = l / 16 of its row; instruction j (0..3) of a step takes codes 8j..8j+7
+// of every lane, so lane group h stands for k = 32h + 8j .. 32h + 8j + 7, and
+// B lane (column c, group h) supplies the same k of its row. The result layout
+// is that of the block-scaled instruction (lane l: rows 4 (l / 16) + v of
+// column l % 16).
+//
+// LDS holds a step's B rows, 128 values (256 B) each at a 272-byte stride (the
+// 16 lanes of a k-group read 16 B each from 16 rows on distinct banks); rows
+// are staged 2 steps ahead through two buffers, 16-byte pieces, consecutive
+// threads along a row. A piece at or past K = H loads as zeros (buffer
+// bounds), so the ragged last step adds nothing; x is [T][H] bfloat16.
+constexpr int kBfRow = 272;  // LDS bytes per staged bfloat16 row
+template <int NG>
+__host__ __device__ constexpr int bf_stage_bytes() { return 16 * NG * kBfRow; }
+
+template <int NG, int W, int NA>
+__device__ __forceinline__ void gemm_mainloop_bf(const uint8_t *const (&aq)[NA],
+                                                 const uint8_t *const (&as)[NA], const ALane &al,
+                                                 int NS, const uint8_t *x, int T, int H,
+                                                 const int *s_brow, int n, uint8_t *sB,
+                                                 f32x4_t (&acc)[NA][NG]) {
+    constexpr int kThreads = 64 * W;
+    constexpr int kPcs = NG * 16 * 16;                     // 16-byte pieces per step
+    constexpr int kPT = (kPcs + kThreads - 1) / kThreads;  // per thread
+    constexpr int kBuf = bf_stage_bytes<NG>();
+    constexpr uint32_t kOob = 0x80000000u;                 // past the buffer: loads zeros
+    constexpr int kRawFlags = 0x00020000;
+    const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t *>(x), 0, static_cast<int>(2u * static_cast<uint32_t>(T) * H), kRawFlags);
+    const int tid = threadIdx.x, lane = tid & 63;
+    uint32_t roff[kPT];
+    int kq[kPT], sdp[kPT];
+#pragma unroll
+    for (int i = 0; i < kPT; ++i) {
+        const int p = min(tid + kThreads * i, kPcs - 1);
+        const int r = p >> 4, q = p & 15;
+        roff[i] = 2u * (static_cast<uint32_t>(s_brow[r]) * H + 8u * q);
+        kq[i] = 8 * q;
+        sdp[i] = r * kBfRow + 16 * q;
+    }
+    const int ngroups = (n + 15) >> 4;
+    typedef int bf_i32x4 __attribute__((ext_vector_type(4)));
+    struct BSlot {
+        bf_i32x4 b[kPT];
+    };
+    struct ASlot {
+        AFrag a[NA];
+    };
+    auto fill_b = [&](BSlot &sl, int step) __attribute__((always_inline)) {
+        const int sd = min(step, NS - 1);
+#pragma unroll
+        for (int i = 0; i < kPT; ++i) {
+            const uint32_t o = 128 * sd + kq[i] < H ? roff[i] + 256u * sd : kOob;
+            sl.b[i] = __builtin_amdgcn_raw_buffer_load_b128(xr, o, 0, 0);
+        }
+    };
+    auto fill_a = [&](ASlot &sl, int step) __attribute__((always_inline)) {
+        const int sd = min(step, NS - 1);
+#pragma unroll
+        for (int j = 0; j < NA; ++j) sl.a[j] = load_afrag(aq[j], as[j], al, sd);
+    };
+    const int col = lane & 15, kh = lane >> 4;
+    auto step = [&](auto lbuf, BSlot &bsl, ASlot &asl, int s) __attribute__((always_inline)) {
+        constexpr int L = decltype(lbuf)::value;
+        uint8_t *buf = sB + L * kBuf;
+#pragma unroll
+        for (int i = 0; i < kPT; ++i) *reinterpret_cast<bf_i32x4 *>(buf + sdp[i]) = bsl.b[i];
+        fill_b(bsl, s + 2);
+        __syncthreads();
+        if (s < NS) {  // uniform; no loads inside
+            float sc[NA];
+#pragma unroll
+            for (int jj = 0; jj < NA; ++jj) sc[jj] = e8m0_scale(asl.a[jj].s & 0xffu);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                bf16x8_t abf[NA];
+#pragma unroll
+                for (int jj = 0; jj < NA; ++jj) {
+                    const uint32_t d = j == 0 ? asl.a[jj].q.x
+                                     : j == 1 ? asl.a[jj].q.y
+                                     : j == 2 ? asl.a[jj].q.z
+                                              : asl.a[jj].q.w;
+                    abf[jj] = fp4x8_to_bf16(d, sc[jj]);
+                }
+#pragma unroll
+                for (int g = 0; g < NG; ++g) {
+                    if (g < ngroups) {  // uniform: row groups the tile fills
+                        const bf16x8_t b = *reinterpret_cast<const bf16x8_t *>(
+                            buf + (16 * g + col) * kBfRow + 64 * kh + 16 * j);
+#pragma unroll
+                        for (int jj = 0; jj < NA; ++jj)
+                            acc[jj][g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(abf[jj], b, acc[jj][g], 0, 0, 0);
+                    }
+                }
+            }
+        }
+        fill_a(asl, s + 2);
+    };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    ASlot a0, a1;
+    BSlot b0, b1;
+    fill_b(b0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    fill_a(a0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    fill_b(b1, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    fill_a(a1, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    for (int s0 = 0; s0 < NS; s0 += 2) {
+        step(I0{}, b0, a0, s0);
+        step(I1{}, b1, a1, s0 + 1);
+    }
+}
+
 __device__ __forceinline__ void load_pre(const int32_t *mprefix, int G, int *s_pre) {
     for (int i = threadIdx.x; i <= G; i += blockDim.x) s_pre[i] = mprefix[i];
     __syncthreads();
 }
 
 // gate/up: grid = kXcds-rounded max_tiles x ceil(pad128(F) / kGateUpRows) items;
-// NT FP8 terms of the expert input take part, or (NT = 0) its MX-FP4 codes.
+// NT (3 or 4) FP8 terms of the expert input take part, or (NT = 1) the
+// bfloat16 input itself, or (NT = 0) its MX-FP4 codes.
 // Q4A: the SwiGLU output leaves as MX-FP4 codes (act_q [rows][Fp / 2], one
 // scale byte per 32 values in act_s [rows][Fp / 32]) instead of FP8 terms.
 // 16-row tiles are held to 4 wavefronts per SIMD (128 VGPRs, no spills).
@@ -427,7 +555,7 @@ __global__ __launch_bounds__(64 * W, NG == 1 ? 4 : (W == 4 ? 2 : 1)) void gate_u
     // B staging buffers; after the main loop the workgroup's SwiGLU outputs
     // ([rows][kGateUpRows + 1] floats) reuse them
     constexpr int kActBytes = Gm::kRows * kActStride * 4;
-    constexpr int kStageBytes = 2 * Gm::kBufBytes;
+    constexpr int kStageBytes = NT == 1 ? 2 * bf_stage_bytes<NG>() : 2 * Gm::kBufBytes;
     __shared__ __align__(16) uint8_t sB[kStageBytes > kActBytes ? kStageBytes : kActBytes];
     __shared__ __align__(16) uint8_t sBs[2 * 4 * Gm::kScales];  // dword-read by the FP4 main loop
     __shared__ float s_bias[2][Gm::kGateUpRows];  // gate, up biases of the workgroup's features
@@ -472,6 +600,8 @@ __global__ __launch_bounds__(64 * W, NG == 1 ? 4 : (W == 4 ? 2 : 1)) void gate_u
     const int Kp = pad128(H);
     if constexpr (NT == 0)  // MX-FP4 expert input
         gemm_mainloop_x4<NG, W, NA>(aq, as, al, Kp / 128, xq, xs, Kp, s_brow, tl.n, sB, sBs, acc);
+    else if constexpr (NT == 1)  // the bfloat16 expert input (xq: x [T][H])
+        gemm_mainloop_bf<NG, W, NA>(aq, as, al, Kp / 128, xq, T, H, s_brow, tl.n, sB, acc);
     else
         gemm_mainloop<NG, W, NA, NT>(aq, as, al, Kp / 128, xq, xs, Kp, s_brow, tl.n, sB, sBs, acc);
 
@@ -681,10 +811,12 @@ int items(int nrb, int max_tiles) {
 //  - 32-row tiles (8 wavefronts) from 24 rows on average (the stack, 64 rows
 //    per expert: 7.46 -> 6.98 ms);
 //  - 16-row tiles (4 wavefronts, four per CU) below (the T = 128 layer).
-// Tiles of 32 rows and more take three FP8 terms of the expert input (a
-// fourth does not fit two wavefronts' registers per SIMD at 64 rows and was
-// slower at 32); 16-row tiles take four of a float32 input. An MX-FP4
-// expert input (x_fp4) is one FP4 operand (x_terms 0).
+// A bfloat16 expert input with no RMSNorm in between (x_bf16_exact) is
+// operand B itself on the bfloat16 matrix cores (x_terms 1). Otherwise tiles
+// of 32 rows and more take three FP8 terms of the expert input (a fourth does
+// not fit two wavefronts' registers per SIMD at 64 rows and was slower at
+// 32); 16-row tiles take four of a float32 input. An MX-FP4 expert input
+// (x_fp4) is one FP4 operand (x_terms 0).
 GemmPlan gemm_plan(int T, int k, int E, int n_shared, int F, bool x_bf16_exact, bool x_fp4,
                    bool act_fp4) {
     const double rows = static_cast<double>(T) * (k + n_shared);
@@ -695,7 +827,7 @@ GemmPlan gemm_plan(int T, int k, int E, int n_shared, int F, bool x_bf16_exact, 
     if (avg >= 30.0 && items64 >= 2048.0) p.tile_rows = 64;
     else if (avg >= 24.0) p.tile_rows = 32;
     else p.tile_rows = 16;
-    p.x_terms = x_fp4 ? 0 : (x_bf16_exact || p.tile_rows >= 32) ? 3 : kTerms;
+    p.x_terms = x_fp4 ? 0 : x_bf16_exact ? 1 : p.tile_rows >= 32 ? 3 : kTerms;
     p.act_terms = act_fp4 ? 0 : kDownTerms;
     p.gate_up_features = p.tile_rows == 16 ? 128 : 256;
     p.down_rows = p.tile_rows == 16 ? 256 : 512;
@@ -726,11 +858,14 @@ hipError_t launch_gate_up_gemm(const uint8_t *xq, const uint8_t *xs, int T, int 
         launch_kernel(gate_up_gemm_kernel<NG, W, NA, NT, false>, grid, 64 * (W), s, xq, xs, T, H,  \
                       F, E, k, n_shared, ex, sh, c, offsets, perm, mprefix, act_q, act_s);          \
     } while (0)
-    if (x_terms != 0 && x_terms != 3 && x_terms != kTerms) return hipErrorInvalidValue;
+    if (x_terms < 0 || x_terms == 2 || x_terms > kTerms) return hipErrorInvalidValue;
     switch (tile_rows * 10 + x_terms) {
     case 160: MOE_GU(1, 4, 4, 0); break;
     case 320: MOE_GU(2, 8, 4, 0); break;
     case 640: MOE_GU(4, 8, 4, 0); break;
+    case 161: MOE_GU(1, 4, 4, 1); break;
+    case 321: MOE_GU(2, 8, 4, 1); break;
+    case 641: MOE_GU(4, 8, 4, 1); break;
     case 163: MOE_GU(1, 4, 4, 3); break;
     case 164: MOE_GU(1, 4, 4, 4); break;
     case 323: MOE_GU(2, 8, 4, 3); break;

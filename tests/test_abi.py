@@ -229,7 +229,7 @@ def test_noalloc_scratch_covers_the_decode_workloads():
         assert mx.moe_workspace_bytes(s) <= _lib.MOE_NOALLOC_SCRATCH_BYTES, cid
 
 
-@pytest.mark.parametrize("cid,tile,x_terms", [(1, 16, 4), (3, 16, 4), (4, 32, 3), (5, 64, 3), (6, 64, 3)])
+@pytest.mark.parametrize("cid,tile,x_terms", [(1, 16, 4), (3, 16, 4), (4, 32, 3), (5, 64, 1), (6, 64, 1), (7, 64, 1), (8, 64, 1)])
 def test_prefill_plan_of_the_workloads(cid, tile, x_terms):
     cfg = config_by_id(cid)
     plan = mx.moe_prefill_plan(mx.make_shape(**cfg.shape_kwargs()), with_norm=cfg.rms_eps is not None)
