@@ -416,22 +416,24 @@ __global__ __launch_bounds__(256) void topk_kernel(const double *partial, int S,
 }
 
 // ---------------------------------------------------------------- permutation
-// One workgroup of 1024 threads. Routes r = t*k + j are taken in chunks of
-// 1024; inside a wavefront the lanes holding the same expert are found with
-// nine bit-plane ballots and ranked by lane; per-wave counts are prefix-summed per expert in
-// wave order, so a route's rank counts exactly the earlier routes of its
-// expert: the permutation is stable (ascending token). Then counts, the
-// exclusive scan and the M-tile prefix for the grouped GEMMs (a workgroup
-// scan, one group per thread), perm and inv.
+// One workgroup of 1024 threads, two passes over the routes r = t*k + j.
+// Pass 1 counts each expert's routes (LDS atomics); a workgroup scan gives
+// the groups' offsets and the M-tile prefix for the grouped GEMMs (one group
+// per thread). Pass 2 takes the routes in chunks of 1024: inside a wavefront
+// the lanes holding the same expert are found with nine bit-plane ballots and
+// ranked by lane, per-wave counts are prefix-summed per expert in wave order
+// on top of the expert's running position, so a route's position counts
+// exactly the earlier routes of its expert: the permutation is stable
+// (ascending token). Each route writes perm and inv at once.
 // Group E (when n_shared) is the shared expert: T rows, identity order.
 __global__ __launch_bounds__(1024) void permute_kernel(
-    const int32_t *idx, int T, int E, int k, int n_shared, int bm, int32_t *counts,
+    const int32_t *__restrict__ idx, int T, int E, int k, int n_shared, int bm, int32_t *counts,
     int32_t *offsets, int32_t *perm, int32_t *inv, int32_t *rank, int32_t *mprefix,
     int32_t *out_counts, int32_t *out_offsets, int32_t *out_perm, int32_t *out_inv,
     uint64_t *route_counts, RouteIn qin, int H, int Kp, uint8_t *xq, uint8_t *xs, int fp4) {
     __shared__ int wcnt[16][kMaxE];
     __shared__ int base[kMaxE + 1];
-    __shared__ int start[kMaxE + 2];
+    (void)rank;
     if (blockIdx.x > 0) {
         quantize_terms_wgs(qin, T, H, Kp, xq, xs, 1, fp4);
         return;
@@ -441,17 +443,11 @@ __global__ __launch_bounds__(1024) void permute_kernel(
     const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     for (int e = tid; e < E; e += 1024) base[e] = 0;
     __syncthreads();
-    int e_next = tid < R ? idx[tid] : 0;  // the next chunk's experts load during this one
-    for (int c0 = 0; c0 < R; c0 += 1024) {
-        for (int i = tid; i < 16 * kMaxE; i += 1024) wcnt[i / kMaxE][i % kMaxE] = 0;
-        const int r = c0 + tid;
-        const bool valid = r < R;
-        const int e = e_next;
-        if (r + 1024 < R) e_next = idx[r + 1024];
-        __syncthreads();
-        // lanes holding the same expert: the intersection of the bit-plane
-        // ballots of the expert index (9 planes: E <= 512)
-        static_assert(kMaxE <= 512, "expert indices fit 9 bit planes");
+    // lanes of a wavefront holding the same expert as this one: the
+    // intersection of the bit-plane ballots of the expert index (9 planes:
+    // E <= 512)
+    static_assert(kMaxE <= 512, "expert indices fit 9 bit planes");
+    auto same_expert = [&](int e, bool valid) __attribute__((always_inline)) {
         uint64_t eq = __ballot(valid);
 #pragma unroll
         for (int b = 0; b < 9; ++b) {
@@ -459,25 +455,24 @@ __global__ __launch_bounds__(1024) void permute_kernel(
             const uint64_t plane = __ballot(bit);
             eq &= bit ? plane : ~plane;
         }
-        const int myrank = __popcll(eq & lt_mask);
-        if (valid && myrank == 0) wcnt[w][e] = __popcll(eq);  // the first lane of its expert
-        __syncthreads();
-        for (int ee = tid; ee < E; ee += 1024) {
-            int run = base[ee];
-            for (int ww = 0; ww < 16; ++ww) {
-                const int c = wcnt[ww][ee];
-                wcnt[ww][ee] = run;
-                run += c;
-            }
-            base[ee] = run;
+        return eq;
+    };
+    // pass 1: the experts' route counts (LDS atomics; loads four rounds at a time)
+    for (int r0 = tid; r0 < R; r0 += 4 * 1024) {
+        int ev[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int r = r0 + u * 1024;
+            ev[u] = r < R ? idx[r] : -1;
         }
-        __syncthreads();
-        if (valid) rank[r] = wcnt[w][e] + myrank;
-        __syncthreads();
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            if (ev[u] >= 0) atomicAdd(&base[ev[u]], 1);
     }
+    __syncthreads();
     // counts, their exclusive scan and the tile prefix: one group per thread
     // (G <= kMaxE + 1 <= 1024), wavefront scans, then the totals of the
-    // wavefronts before
+    // wavefronts before; base[g] becomes group g's first position
     const int G = E + n_shared;
     __shared__ int wsum_c[16], wsum_t[16];
     {
@@ -503,8 +498,9 @@ __global__ __launch_bounds__(1024) void permute_kernel(
             pt += wsum_t[ww];
         }
         const int off = pc + sc - c, mt = pt + st - nt;
+        __syncthreads();  // every count is read before base[] turns into offsets
         if (g < G) {
-            start[g] = off;
+            if (g < E) base[g] = off;
             offsets[g] = off;
             mprefix[g] = mt;
             counts[g] = c;
@@ -516,19 +512,43 @@ __global__ __launch_bounds__(1024) void permute_kernel(
             if (out_offsets && g < E) out_offsets[g] = off;
         }
         if (g == G - 1) {
-            start[G] = off + c;
             offsets[G] = off + c;
             mprefix[G] = mt + nt;
         }
         if (out_offsets && g == 0) out_offsets[E] = R;
     }
     __syncthreads();
-    for (int r = tid; r < R; r += 1024) {
-        const int pos = start[idx[r]] + rank[r];
-        perm[pos] = r;
-        inv[r] = pos;
-        if (out_perm) out_perm[pos] = r;
-        if (out_inv) out_inv[r] = pos;
+    // pass 2: positions in chunks of 1024 routes
+    int e_next = tid < R ? idx[tid] : 0;  // the next chunk's experts load during this one
+    for (int c0 = 0; c0 < R; c0 += 1024) {
+        for (int i = tid; i < 16 * kMaxE; i += 1024) wcnt[i / kMaxE][i % kMaxE] = 0;
+        const int r = c0 + tid;
+        const bool valid = r < R;
+        const int e = e_next;
+        if (r + 1024 < R) e_next = idx[r + 1024];
+        __syncthreads();
+        const uint64_t eq = same_expert(e, valid);
+        const int myrank = __popcll(eq & lt_mask);
+        if (valid && myrank == 0) wcnt[w][e] = __popcll(eq);  // the first lane of its expert
+        __syncthreads();
+        for (int ee = tid; ee < E; ee += 1024) {
+            int run = base[ee];
+            for (int ww = 0; ww < 16; ++ww) {
+                const int c = wcnt[ww][ee];
+                wcnt[ww][ee] = run;
+                run += c;
+            }
+            base[ee] = run;
+        }
+        __syncthreads();
+        if (valid) {
+            const int pos = wcnt[w][e] + myrank;
+            perm[pos] = r;
+            inv[r] = pos;
+            if (out_perm) out_perm[pos] = r;
+            if (out_inv) out_inv[r] = pos;
+        }
+        __syncthreads();
     }
 }
 
