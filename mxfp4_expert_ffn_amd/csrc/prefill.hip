@@ -808,8 +808,9 @@ int items(int nrb, int max_tiles) {
 //    weights stream once (DeepSeek-V4 Flash 1.91 -> 1.58 ms per layer, Pro
 //    5.54 -> 4.99 ms); with few items the last round runs mostly empty (the
 //    24-layer stack: 7.46 -> 8.71 ms);
-//  - 32-row tiles (8 wavefronts) from 24 rows on average (the stack, 64 rows
-//    per expert: 7.46 -> 6.98 ms);
+//  - 32-row tiles from 24 rows on average (the stack, 64 rows per expert:
+//    7.46 -> 6.98 ms with 8 wavefronts; with FP8 terms 4 wavefronts and 128
+//    features per gate/up workgroup, two workgroups per CU);
 //  - 16-row tiles (4 wavefronts, four per CU) below (the T = 128 layer).
 // A bfloat16 expert input with no RMSNorm in between (x_bf16_exact) is
 // operand B itself on the bfloat16 matrix cores (x_terms 1). Otherwise tiles
@@ -829,13 +830,17 @@ GemmPlan gemm_plan(int T, int k, int E, int n_shared, int F, bool x_bf16_exact, 
     else p.tile_rows = 16;
     p.x_terms = x_fp4 ? 0 : x_bf16_exact ? 1 : p.tile_rows >= 32 ? 3 : kTerms;
     p.act_terms = act_fp4 ? 0 : kDownTerms;
-    p.gate_up_features = p.tile_rows == 16 ? 128 : 256;
-    p.down_rows = p.tile_rows == 16 ? 256 : 512;
+    p.gate_up_features = p.tile_rows == 16 || (p.tile_rows == 32 && p.x_terms == 3) ? 128 : 256;
+    p.down_rows = p.tile_rows == 64 ? 512 : 256;
     return p;
 }
 
-// 16-row tiles: 4 wavefronts with 4 A fragments each; 32- and 64-row tiles:
-// 8 wavefronts with 4 A fragments each.
+// 16-row tiles: 4 wavefronts with 4 A fragments each (four workgroups per
+// CU); 32-row tiles with FP8 terms, and the 32-row down GEMM: 4 wavefronts,
+// two workgroups per CU (their barriers do not hold each other: 4% faster per
+// gate/up launch than 8 wavefronts on the 24-layer stack, though each
+// workgroup covers half the features); otherwise 8 wavefronts with 4 A
+// fragments each.
 hipError_t launch_gate_up_gemm(const uint8_t *xq, const uint8_t *xs, int T, int H, int F, int E,
                                int k, int n_shared, const ExpertPtrs &ex, const ExpertPtrs &sh,
                                SwigluConsts c, const int32_t *offsets, const int32_t *perm,
@@ -868,7 +873,7 @@ hipError_t launch_gate_up_gemm(const uint8_t *xq, const uint8_t *xs, int T, int 
     case 641: MOE_GU(4, 8, 4, 1); break;
     case 163: MOE_GU(1, 4, 4, 3); break;
     case 164: MOE_GU(1, 4, 4, 4); break;
-    case 323: MOE_GU(2, 8, 4, 3); break;
+    case 323: MOE_GU(2, 4, 4, 3); break;
     case 643: MOE_GU(4, 8, 4, 3); break;
     default: return hipErrorInvalidValue;
     }
@@ -895,7 +900,7 @@ hipError_t launch_down_gemm(const uint8_t *act_q, const uint8_t *act_s, int T, i
     } while (0)
     switch (tile_rows) {
     case 16: MOE_DN(1, 4, 4); break;
-    case 32: MOE_DN(2, 8, 4); break;
+    case 32: MOE_DN(2, 4, 4); break;
     case 64: MOE_DN(4, 8, 4); break;
     default: return hipErrorInvalidValue;
     }

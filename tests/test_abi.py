@@ -235,8 +235,10 @@ def test_prefill_plan_of_the_workloads(cid, tile, x_terms):
     plan = mx.moe_prefill_plan(mx.make_shape(**cfg.shape_kwargs()), with_norm=cfg.rms_eps is not None)
     assert plan["tile_rows"] == tile and plan["x_terms"] == x_terms
     assert plan["act_terms"] == 3
-    assert plan["gate_up_features"] == (128 if tile == 16 else 256)
-    assert plan["down_rows"] == 2 * plan["gate_up_features"]
+    # 16-row tiles and 32-row tiles with FP8 terms: 4-wavefront workgroups
+    four = tile == 16 or (tile == 32 and x_terms == 3)
+    assert plan["gate_up_features"] == (128 if four else 256)
+    assert plan["down_rows"] == (512 if tile == 64 else 256)
 
 
 @pytest.mark.parametrize("cid", [3, 4, 5, 6])
@@ -246,8 +248,12 @@ def test_prefill_plan_of_the_quantised_mode(cid):
     exact = mx.moe_prefill_plan(mx.make_shape(**kw), with_norm=cfg.rms_eps is not None)
     quant = mx.moe_prefill_plan(mx.make_shape(**kw, act_quant=1), with_norm=cfg.rms_eps is not None)
     assert quant["x_terms"] == 0
-    assert {k: v for k, v in quant.items() if k != "x_terms"} == \
-        {k: v for k, v in exact.items() if k != "x_terms"}
+    # same tiling; the gate/up workgroup width follows the operand (4-wavefront
+    # workgroups only for 32-row tiles with FP8 terms)
+    skip = ("x_terms", "gate_up_features")
+    assert {k: v for k, v in quant.items() if k not in skip} == \
+        {k: v for k, v in exact.items() if k not in skip}
+    assert quant["gate_up_features"] == (128 if quant["tile_rows"] == 16 else 256)
     both = mx.moe_prefill_plan(mx.make_shape(**kw, act_quant=2), with_norm=cfg.rms_eps is not None)
     assert both["x_terms"] == 0 and both["act_terms"] == 0
     assert both["tile_rows"] == exact["tile_rows"]
