@@ -539,7 +539,7 @@ def route_locality(setup) -> dict:
 # the default run: the decode headline, then these workloads nested under
 # "workloads" (each with its own step count)
 SUITE = (("prefill", "prefill_T128"), ("stack", "stack_T512"), ("ds4", "ds4"), ("ds4_q4", "ds4_q4"),
-         ("ds4_selbias", "ds4_selbias"), ("ds4_hash", "ds4_hash"))
+         ("ds4_q4a", "ds4_q4a"), ("ds4_selbias", "ds4_selbias"), ("ds4_hash", "ds4_hash"))
 
 
 def measure(wl: str, args, steps: int, warmup: int) -> dict:
@@ -620,6 +620,14 @@ def measure(wl: str, args, steps: int, warmup: int) -> dict:
         achieved, peak, unit, bound = alg["bytes"] / kern_s / 1e9, HBM_PEAK_GBPS, "GB/s", "hbm"
     else:
         achieved, peak, unit, bound = alg["flops"] / kern_s / 1e12, mfma_peak, "TFLOP/s", "mfma"
+    # how the gate/up GEMM takes the expert input (decode: four FP8 terms)
+    xt = setup.gate_up_x_terms() if setup.mode == "prefill" else None
+    if setup.act_quant:
+        expert_input = "mxfp4 (rounded once)"
+    elif xt == 1:
+        expert_input = "exact (bf16 as it is; weights decoded to bf16 in registers)"
+    else:
+        expert_input = "exact (fp8 terms)"
     block_bytes = setup.block_bytes_per_step(counts)
     block_gbps = block_bytes / (ms_per_step / 1e3) / 1e9
     nominal_tf = alg["flops"] / kern_s / 1e12
@@ -636,7 +644,7 @@ def measure(wl: str, args, steps: int, warmup: int) -> dict:
             "k": cfg.k, "n_shared": cfg.n_shared, "layers": cfg.layers,
             "tokens_per_step": setup.tokens_per_step, "weights": "mxfp4 (e2m1 + e8m0/32) + fp32 bias",
             "activations": cfg.act_dtype, "weight_copies": setup.copies,
-            "expert_input": "mxfp4 (rounded once)" if setup.act_quant else "exact (fp8 terms)",
+            "expert_input": expert_input,
             "swiglu_output": "mxfp4" if setup.act_quant == 2 else "exact (fp8 terms)",
             "launch": "eager" if graphs is None else "hip_graph",
             "route_profile": args.route_profile,
