@@ -29,9 +29,12 @@
  *   value with one E8M0 scale per 32 values and term; n terms carry a value
  *   to within about 2^-4n of its block's largest magnitude. Decode uses four
  *   terms everywhere; prefill uses three for the SwiGLU output and, for the
- *   expert input, four on 16-row tiles and three on larger tiles or for a
- *   bfloat16 input without RMSNorm (moe_prefill_plan tells which). Products
- *   accumulate in float32. Router logits are accumulated in float64.
+ *   expert input, four on 16-row tiles and three on larger tiles. A bfloat16
+ *   expert input without RMSNorm is not split in prefill: the weights are
+ *   decoded to bfloat16 in registers (exact for scale bytes 1..252) and meet
+ *   the input on the bfloat16 matrix cores (moe_prefill_plan tells which
+ *   path a shape takes). Products accumulate in float32. Router logits are
+ *   accumulated in float64.
  * - Shape limits: 1 <= E <= 512, 1 <= k <= min(E, 8), H and F multiples of
  *   32 and at most 16384, 0 <= T, n_shared in {0, 1}. Decode additionally
  *   needs T <= 64 and H, F <= 8192. With T = 0 a call only validates the
@@ -368,8 +371,10 @@ int moe_forward_decode_noalloc(const moe_shape *shape, const void *hidden, const
  * this library's tiling of those per-expert row groups. */
 typedef struct moe_prefill_plan_t {
     int32_t tile_rows;         /* routed rows of one expert per tile: 16, 32 or 64 */
-    int32_t x_terms;           /* FP8 terms of the expert input in the gate/up products;
-                                  0: the MX-FP4 expert input (act_quant = 1), one FP4 operand */
+    int32_t x_terms;           /* FP8 terms of the expert input in the gate/up products (3 or 4);
+                                  1: a bfloat16 input with no RMSNorm, taken as it is by the
+                                  bfloat16 matrix cores against weights decoded to bfloat16;
+                                  0: the MX-FP4 expert input (act_quant >= 1), one FP4 operand */
     int32_t act_terms;         /* FP8 terms of the SwiGLU output in the down products;
                                   0: its MX-FP4 codes (act_quant = 2) */
     int32_t gate_up_features;  /* features (gate and up rows each) per gate/up work item */
