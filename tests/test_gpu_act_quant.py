@@ -177,7 +177,7 @@ def test_prefill_block(cid, T, tile):
     out, ro = run_forward("prefill", shape, dl, device_input(cfg, x, xb))
     ro = to_np(ro)
     out = out.cpu().numpy()
-    toks = None if T <= 512 else np.random.default_rng(T).choice(T, 16, replace=False)
+    toks = None if T <= 512 else np.random.default_rng(T).choice(T, 48, replace=False)
     ref = omoe.block_for_config(cfg, layer, x, tokens=toks, act_quant=1)
     check_routing(ro["topk_idx"], ro["topk_w"], ref, layer.router_w, layer.router_b,
                   cfg.route_scale)

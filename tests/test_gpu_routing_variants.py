@@ -67,7 +67,7 @@ def test_route_parity(cid, T):
         assert np.mean(np.any(plain != ref["idx"], axis=1)) > 0.2
 
 
-@pytest.mark.parametrize("cid,T,sample", [(7, 2048, 16), (8, 2048, 16), (7, 256, None),
+@pytest.mark.parametrize("cid,T,sample", [(7, 2048, 48), (8, 2048, 48), (7, 256, None),
                                           (8, 256, None)])
 def test_prefill_block(cid, T, sample):
     cfg = scaled(config_by_id(cid), T=T)
