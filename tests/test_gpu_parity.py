@@ -367,6 +367,11 @@ EDGE = {
     "max_F": _small(1, T=3, H=64, F=16384, E=2, k=1),
     # the largest decode batch, bf16 input with a shared expert
     "decode_T64": _small(5, T=64, H=256, F=128, E=12, k=6),
+    # the prefill gate/up's bfloat16 operand on widths that end in a partial
+    # 128-wide step: 32-row tiles over H = 2880 (22.5 steps), and 16-row
+    # tiles over H = 96 (one partial step)
+    "bf16_ragged_K": _small(5, T=45, H=2880, F=352, E=8, k=4),
+    "bf16_narrow": _small(5, T=11, H=96, F=160, E=6, k=3),
 }
 
 
