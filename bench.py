@@ -310,13 +310,21 @@ class Setup:
             byts = active * 2 * (mat + 4 * F) + T * terms(H) + routes * terms(F) + T * splits * E * 8
             return dict(bytes=byts, flops=routes * 4 * H * F, units=routes,
                         unit="route (token, selected expert)", active_experts=active)
-        # gate/up GEMM: weights of every active expert once, x terms (or the
-        # MX-FP4 input: codes + scales) once, act terms out
+        # gate/up GEMM: weights of every active expert once, the expert input
+        # once (its FP8 terms that take part, the bfloat16 rows themselves, or
+        # the MX-FP4 codes + scales), the SwiGLU output's three FP8 terms (or
+        # its MX-FP4 codes) out
         T = cfg.T
         active = [sum(1 for c in counts if c > 0) + cfg.n_shared for counts in counts_per_call]
         rows = T * k + T * cfg.n_shared
-        x_in = T * pad128(H) * 17 // 32 if self.act_quant else T * terms(H)
-        act_out = rows * pad128(F) * 17 // 32 if self.act_quant == 2 else rows * terms(F)
+        xt = self.gate_up_x_terms()
+        if self.act_quant:
+            x_in = T * pad128(H) * 17 // 32
+        elif xt == 1:
+            x_in = T * H * 2
+        else:
+            x_in = T * terms(H) * xt // 4
+        act_out = rows * pad128(F) * 17 // 32 if self.act_quant == 2 else rows * terms(F) * 3 // 4
         per = [a * 2 * (mat + 4 * F) + x_in + act_out for a in active]
         return dict(bytes=sum(per) / len(per), flops=4.0 * rows * H * F, units=rows,
                     unit="routed row (token, expert) of the grouped GEMM",

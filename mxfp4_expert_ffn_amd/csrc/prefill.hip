@@ -674,7 +674,7 @@ __global__ __launch_bounds__(64 * W, NG == 1 ? 4 : (W == 4 ? 2 : 1)) void gate_u
             if (on[u] && fb[u] < Fp) {
                 const size_t p = static_cast<size_t>(tl.p0 + row[u]);
 #pragma unroll
-                for (int n = 0; n < kTerms; ++n) {
+                for (int n = 0; n < kDownTerms; ++n) {  // the terms the down GEMM reads
                     act_q[(p * kTerms + n) * Fp + fb[u] + i] = static_cast<uint8_t>(codes[u] >> (8 * n));
                     if (i == 0)
                         act_s[(p * kTerms + n) * nbp + fb[u] / 32] = static_cast<uint8_t>(scales[u] >> (8 * n));
