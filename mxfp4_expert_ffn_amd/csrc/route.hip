@@ -570,7 +570,7 @@ RouterPlan router_plan(int T, int H, int E) {
         return p;
     }
     const int tiles = ((T + 63) / 64) * ((E + 63) / 64);
-    int want = (512 + tiles - 1) / tiles;
+    int want = (1024 + tiles - 1) / tiles;
     want = want < 1 ? 1 : (want > kRouterMaxSplits ? kRouterMaxSplits : want);
     const int units = H / 32;
     if (want > units) want = units;
