@@ -545,9 +545,11 @@ __device__ __forceinline__ void load_pre(const int32_t *mprefix, int G, int *s_p
 // Q4A: the SwiGLU output leaves as MX-FP4 codes (act_q [rows][Fp / 2], one
 // scale byte per 32 values in act_s [rows][Fp / 32]) instead of FP8 terms.
 // 16-row tiles are held to 4 wavefronts per SIMD (128 VGPRs, no spills),
-// 32-row FP8-term tiles in 4-wavefront workgroups to 3 (168 VGPRs).
+// 32-row FP8-term tiles in 4-wavefront workgroups to 3 (168 VGPRs), 64-row
+// bfloat16-operand tiles with 2 A fragments per wavefront to 4 (two
+// 8-wavefront workgroups per CU).
 template <int NG, int W, int NA, int NT, bool Q4A>
-__global__ __launch_bounds__(64 * W, NG == 1 ? 4 : (W == 4 ? (NG == 2 && NT >= 3 ? 3 : 2) : 1)) void gate_up_gemm_kernel(
+__global__ __launch_bounds__(64 * W, NG == 1 ? 4 : (W == 4 ? (NG == 2 && NT >= 3 ? 3 : 2) : (NT == 1 && NA == 2 ? 4 : 1))) void gate_up_gemm_kernel(
     const uint8_t *xq, const uint8_t *xs, int T, int H, int F, int E, int k, int n_shared,
     ExpertPtrs ex, ExpertPtrs sh, SwigluConsts sc, const int32_t *offsets, const int32_t *perm,
     const int32_t *mprefix, uint8_t *act_q, uint8_t *act_s) {
@@ -834,17 +836,24 @@ GemmPlan gemm_plan(int T, int k, int E, int n_shared, int F, bool x_bf16_exact, 
     else p.tile_rows = 16;
     p.x_terms = x_fp4 ? 0 : x_bf16_exact ? 1 : p.tile_rows >= 32 ? 3 : kTerms;
     p.act_terms = act_fp4 ? 0 : kDownTerms;
-    p.gate_up_features = p.tile_rows == 16 || (p.tile_rows == 32 && p.x_terms == 3) ? 128 : 256;
+    // 128 features: 4-wavefront workgroups, or 8 wavefronts of two A
+    // fragments (64-row tiles with the bfloat16 operand)
+    p.gate_up_features = p.tile_rows == 16 || (p.tile_rows == 32 && p.x_terms == 3) ||
+                                 (p.tile_rows == 64 && p.x_terms == 1)
+                             ? 128
+                             : 256;
     p.down_rows = p.tile_rows == 64 ? 512 : 256;
     return p;
 }
 
 // 16-row tiles: 4 wavefronts with 4 A fragments each (four workgroups per
 // CU); 32-row tiles with FP8 terms, and the 32-row down GEMM: 4 wavefronts,
-// two workgroups per CU (their barriers do not hold each other: 4% faster per
-// gate/up launch than 8 wavefronts on the 24-layer stack, though each
-// workgroup covers half the features); otherwise 8 wavefronts with 4 A
-// fragments each.
+// three workgroups per CU (their barriers do not hold each other: 4% faster
+// per gate/up launch than 8 wavefronts on the 24-layer stack, though each
+// workgroup covers half the features); 64-row tiles with the bfloat16
+// operand: 8 wavefronts with 2 A fragments each (96 VGPRs, two workgroups per
+// CU: DeepSeek-V4-Flash gate/up 664 -> 593 us against 4 fragments and one
+// workgroup per CU); otherwise 8 wavefronts with 4 A fragments each.
 hipError_t launch_gate_up_gemm(const uint8_t *xq, const uint8_t *xs, int T, int H, int F, int E,
                                int k, int n_shared, const ExpertPtrs &ex, const ExpertPtrs &sh,
                                SwigluConsts c, const int32_t *offsets, const int32_t *perm,
@@ -874,7 +883,7 @@ hipError_t launch_gate_up_gemm(const uint8_t *xq, const uint8_t *xs, int T, int 
     case 640: MOE_GU(4, 8, 4, 0); break;
     case 161: MOE_GU(1, 4, 4, 1); break;
     case 321: MOE_GU(2, 8, 4, 1); break;
-    case 641: MOE_GU(4, 8, 4, 1); break;
+    case 641: MOE_GU(4, 8, 2, 1); break;
     case 163: MOE_GU(1, 4, 4, 3); break;
     case 164: MOE_GU(1, 4, 4, 4); break;
     case 323: MOE_GU(2, 4, 4, 3); break;

@@ -235,9 +235,10 @@ def test_prefill_plan_of_the_workloads(cid, tile, x_terms):
     plan = mx.moe_prefill_plan(mx.make_shape(**cfg.shape_kwargs()), with_norm=cfg.rms_eps is not None)
     assert plan["tile_rows"] == tile and plan["x_terms"] == x_terms
     assert plan["act_terms"] == 3
-    # 16-row tiles and 32-row tiles with FP8 terms: 4-wavefront workgroups
-    four = tile == 16 or (tile == 32 and x_terms == 3)
-    assert plan["gate_up_features"] == (128 if four else 256)
+    # 16-row tiles and 32-row tiles with FP8 terms (4-wavefront workgroups),
+    # 64-row tiles with the bfloat16 operand (two A fragments per wavefront)
+    narrow = tile == 16 or (tile == 32 and x_terms == 3) or (tile == 64 and x_terms == 1)
+    assert plan["gate_up_features"] == (128 if narrow else 256)
     assert plan["down_rows"] == (512 if tile == 64 else 256)
 
 
