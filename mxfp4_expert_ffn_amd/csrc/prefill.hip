@@ -546,10 +546,10 @@ __device__ __forceinline__ void load_pre(const int32_t *mprefix, int G, int *s_p
 // scale byte per 32 values in act_s [rows][Fp / 32]) instead of FP8 terms.
 // 16-row tiles are held to 4 wavefronts per SIMD (128 VGPRs, no spills),
 // 32-row FP8-term tiles in 4-wavefront workgroups to 3 (168 VGPRs), 64-row
-// bfloat16-operand tiles with 2 A fragments per wavefront to 4 (two
-// 8-wavefront workgroups per CU).
+// tiles with the bfloat16 or MX-FP4 operand and 2 A fragments per wavefront
+// to 4 (two 8-wavefront workgroups per CU).
 template <int NG, int W, int NA, int NT, bool Q4A>
-__global__ __launch_bounds__(64 * W, NG == 1 ? 4 : (W == 4 ? (NG == 2 && NT >= 3 ? 3 : 2) : (NT == 1 && NA == 2 ? 4 : 1))) void gate_up_gemm_kernel(
+__global__ __launch_bounds__(64 * W, NG == 1 ? 4 : (W == 4 ? (NG == 2 && NT >= 3 ? 3 : 2) : (NT <= 1 && NA == 2 ? 4 : 1))) void gate_up_gemm_kernel(
     const uint8_t *xq, const uint8_t *xs, int T, int H, int F, int E, int k, int n_shared,
     ExpertPtrs ex, ExpertPtrs sh, SwigluConsts sc, const int32_t *offsets, const int32_t *perm,
     const int32_t *mprefix, uint8_t *act_q, uint8_t *act_s) {
@@ -692,8 +692,9 @@ __global__ __launch_bounds__(64 * W, NG == 1 ? 4 : (W == 4 ? (NG == 2 && NT >= 3
 
 // down: grid = kXcds-rounded max_tiles x ceil(H / kDownRows) items. A4: the
 // activation rows are MX-FP4 codes (FP4 x FP4 products) instead of FP8 terms.
+// With MX-FP4 rows and 2 A fragments per wavefront: 4 wavefronts per SIMD.
 template <int NG, int W, int NA, bool A4>
-__global__ __launch_bounds__(64 * W) void down_gemm_kernel(
+__global__ __launch_bounds__(64 * W, A4 && NA == 2 ? 4 : 1) void down_gemm_kernel(
     const uint8_t *act_q, const uint8_t *act_s, int T, int H, int F, int E, int k, int n_shared,
     ExpertPtrs ex, ExpertPtrs sh, const int32_t *offsets, const int32_t *perm, const float *wts,
     const int32_t *mprefix, float *y) {
@@ -837,12 +838,12 @@ GemmPlan gemm_plan(int T, int k, int E, int n_shared, int F, bool x_bf16_exact, 
     p.x_terms = x_fp4 ? 0 : x_bf16_exact ? 1 : p.tile_rows >= 32 ? 3 : kTerms;
     p.act_terms = act_fp4 ? 0 : kDownTerms;
     // 128 features: 4-wavefront workgroups, or 8 wavefronts of two A
-    // fragments (64-row tiles with the bfloat16 operand)
+    // fragments (64-row tiles with the bfloat16 or MX-FP4 operand)
     p.gate_up_features = p.tile_rows == 16 || (p.tile_rows == 32 && p.x_terms == 3) ||
-                                 (p.tile_rows == 64 && p.x_terms == 1)
+                                 (p.tile_rows == 64 && p.x_terms <= 1)
                              ? 128
                              : 256;
-    p.down_rows = p.tile_rows == 64 ? 512 : 256;
+    p.down_rows = p.tile_rows == 64 && p.act_terms != 0 ? 512 : 256;
     return p;
 }
 
@@ -880,7 +881,7 @@ hipError_t launch_gate_up_gemm(const uint8_t *xq, const uint8_t *xs, int T, int 
     switch (tile_rows * 10 + x_terms) {
     case 160: MOE_GU(1, 4, 4, 0); break;
     case 320: MOE_GU(2, 8, 4, 0); break;
-    case 640: MOE_GU(4, 8, 4, 0); break;
+    case 640: MOE_GU(4, 8, 2, 0); break;
     case 161: MOE_GU(1, 4, 4, 1); break;
     case 321: MOE_GU(2, 8, 4, 1); break;
     case 641: MOE_GU(4, 8, 2, 1); break;
@@ -899,22 +900,21 @@ hipError_t launch_down_gemm(const uint8_t *act_q, const uint8_t *act_s, int T, i
                             const int32_t *offsets, const int32_t *perm, const float *wts,
                             const int32_t *mprefix, int tile_rows, int max_tiles, bool act_fp4,
                             float *y, hipStream_t s) {
-#define MOE_DN(NG, W, NA)                                                                           \
+#define MOE_DN(NG, W, NA, A4)                                                                       \
     do {                                                                                            \
         using Gm = Geo<NG, W, NA>;                                                                  \
         const int grid = items((H + Gm::kDownRows - 1) / Gm::kDownRows, max_tiles);                 \
         if (grid == 0) return hipSuccess;                                                           \
-        if (act_fp4)                                                                                \
-            launch_kernel(down_gemm_kernel<NG, W, NA, true>, grid, 64 * (W), s, act_q, act_s, T, H,  \
-                          F, E, k, n_shared, ex, sh, offsets, perm, wts, mprefix, y);               \
-        else                                                                                        \
-            launch_kernel(down_gemm_kernel<NG, W, NA, false>, grid, 64 * (W), s, act_q, act_s, T, H, \
-                          F, E, k, n_shared, ex, sh, offsets, perm, wts, mprefix, y);               \
+        launch_kernel(down_gemm_kernel<NG, W, NA, A4>, grid, 64 * (W), s, act_q, act_s, T, H, F, E, \
+                      k, n_shared, ex, sh, offsets, perm, wts, mprefix, y);                         \
     } while (0)
-    switch (tile_rows) {
-    case 16: MOE_DN(1, 4, 4); break;
-    case 32: MOE_DN(2, 4, 4); break;
-    case 64: MOE_DN(4, 8, 4); break;
+    switch (tile_rows * 2 + (act_fp4 ? 1 : 0)) {
+    case 32: MOE_DN(1, 4, 4, false); break;
+    case 33: MOE_DN(1, 4, 4, true); break;
+    case 64: MOE_DN(2, 4, 4, false); break;
+    case 65: MOE_DN(2, 4, 4, true); break;
+    case 128: MOE_DN(4, 8, 4, false); break;
+    case 129: MOE_DN(4, 8, 2, true); break;  // 97 VGPRs: two workgroups per CU
     default: return hipErrorInvalidValue;
     }
 #undef MOE_DN

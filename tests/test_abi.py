@@ -236,8 +236,9 @@ def test_prefill_plan_of_the_workloads(cid, tile, x_terms):
     assert plan["tile_rows"] == tile and plan["x_terms"] == x_terms
     assert plan["act_terms"] == 3
     # 16-row tiles and 32-row tiles with FP8 terms (4-wavefront workgroups),
-    # 64-row tiles with the bfloat16 operand (two A fragments per wavefront)
-    narrow = tile == 16 or (tile == 32 and x_terms == 3) or (tile == 64 and x_terms == 1)
+    # 64-row tiles with the bfloat16 or MX-FP4 operand (two A fragments per
+    # wavefront)
+    narrow = tile == 16 or (tile == 32 and x_terms == 3) or (tile == 64 and x_terms <= 1)
     assert plan["gate_up_features"] == (128 if narrow else 256)
     assert plan["down_rows"] == (512 if tile == 64 else 256)
 
@@ -254,10 +255,13 @@ def test_prefill_plan_of_the_quantised_mode(cid):
     skip = ("x_terms", "gate_up_features")
     assert {k: v for k, v in quant.items() if k not in skip} == \
         {k: v for k, v in exact.items() if k not in skip}
-    assert quant["gate_up_features"] == (128 if quant["tile_rows"] == 16 else 256)
+    assert quant["gate_up_features"] == (256 if quant["tile_rows"] == 32 else 128)
+    assert quant["down_rows"] == exact["down_rows"]
     both = mx.moe_prefill_plan(mx.make_shape(**kw, act_quant=2), with_norm=cfg.rms_eps is not None)
     assert both["x_terms"] == 0 and both["act_terms"] == 0
     assert both["tile_rows"] == exact["tile_rows"]
+    # MX-FP4 down rows on 64-row tiles: two A fragments per wavefront
+    assert both["down_rows"] == 256
 
 
 def test_decode_rejects_the_quantised_mode():
