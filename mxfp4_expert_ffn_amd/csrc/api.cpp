@@ -107,7 +107,7 @@ struct Workspace {
     int splits;
     int32_t *idx;
     float *wts;
-    int32_t *counts, *offsets, *mprefix, *perm, *inv, *rank;
+    int32_t *counts, *offsets, *mprefix, *perm, *inv;
     // FP8 terms (codes, E8M0 scales) of the expert input [T] and of the
     // SwiGLU output [T*k + T*n_shared] (route order in decode, position
     // order in prefill)
@@ -138,7 +138,6 @@ Workspace carve(const moe_shape *s, uint8_t *base) {
     w.mprefix = reinterpret_cast<int32_t *>(take((E + 2) * 4));
     w.perm = reinterpret_cast<int32_t *>(take(R * 4));
     w.inv = reinterpret_cast<int32_t *>(take(R * 4));
-    w.rank = reinterpret_cast<int32_t *>(take(R * 4));
     w.xq = take(T * moe::kTerms * Hp);
     w.xs = take(T * moe::kTerms * Hp / 32);
     w.act_q = take((R + T * ns) * moe::kTerms * Fp);
@@ -386,7 +385,7 @@ int moe_route(const moe_shape *s, const void *x, const float *norm_w, const floa
                                 s->route_scale, w.idx, w.wts, out->topk_idx, out->topk_w, st);
     }));
     MOE_TRY(launch(MOE_KERNEL_PERMUTE, "permute", st, [&] { return moe::launch_permute(w.idx, s->T, s->E, s->k, 0, 16, w.counts, w.offsets, w.perm,
-                                          w.inv, w.rank, w.mprefix, out->counts, out->offsets,
+                                          w.inv, w.mprefix, out->counts, out->offsets,
                                           out->perm, out->inv, out->route_counts, nullptr, s->H,
                                           nullptr, st); }));
     return ok();
@@ -466,7 +465,7 @@ int moe_forward_decode(const moe_shape *s, const void *hidden, const float *norm
     if (ro && (ro->counts || ro->offsets || ro->perm || ro->inv))
         MOE_TRY(launch(MOE_KERNEL_PERMUTE, "permute", st, [&] {
             return moe::launch_permute(w.idx, s->T, s->E, s->k, 0, 16, w.counts, w.offsets, w.perm,
-                                       w.inv, w.rank, w.mprefix, ro->counts, ro->offsets,
+                                       w.inv, w.mprefix, ro->counts, ro->offsets,
                                        ro->perm, ro->inv, nullptr, nullptr, s->H, nullptr, st);
         }));
     return ok();
@@ -504,7 +503,7 @@ int moe_forward_prefill(const moe_shape *s, const void *hidden, const float *nor
     const moe::TermsOut tq{w.xq, w.xs, s->act_quant};
     MOE_TRY(launch(MOE_KERNEL_PERMUTE, "permute", st, [&] {
         return moe::launch_permute(w.idx, s->T, s->E, s->k, s->n_shared, bm, w.counts, w.offsets,
-                                   w.perm, w.inv, w.rank, w.mprefix, ro ? ro->counts : nullptr,
+                                   w.perm, w.inv, w.mprefix, ro ? ro->counts : nullptr,
                                    ro ? ro->offsets : nullptr, ro ? ro->perm : nullptr,
                                    ro ? ro->inv : nullptr, ro ? ro->route_counts : nullptr, &in,
                                    s->H, need_terms && !router_terms ? &tq : nullptr, st);

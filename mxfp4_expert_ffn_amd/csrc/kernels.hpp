@@ -147,7 +147,7 @@ hipError_t launch_topk(const double *partial, int S, const float *bias, const Ro
 constexpr int kPermuteQuantizeWgs = 512;
 hipError_t launch_permute(const int32_t *idx, int T, int E, int k, int n_shared, int tile_rows,
                           int32_t *counts, int32_t *offsets, int32_t *perm, int32_t *inv,
-                          int32_t *rank, int32_t *mprefix, int32_t *out_counts,
+                          int32_t *mprefix, int32_t *out_counts,
                           int32_t *out_offsets, int32_t *out_perm, int32_t *out_inv,
                           uint64_t *route_counts, const RouteIn *qin, int H,
                           const TermsOut *terms, hipStream_t s);

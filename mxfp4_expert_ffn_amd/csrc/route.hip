@@ -428,12 +428,11 @@ __global__ __launch_bounds__(256) void topk_kernel(const double *partial, int S,
 // Group E (when n_shared) is the shared expert: T rows, identity order.
 __global__ __launch_bounds__(1024) void permute_kernel(
     const int32_t *__restrict__ idx, int T, int E, int k, int n_shared, int bm, int32_t *counts,
-    int32_t *offsets, int32_t *perm, int32_t *inv, int32_t *rank, int32_t *mprefix,
+    int32_t *offsets, int32_t *perm, int32_t *inv, int32_t *mprefix,
     int32_t *out_counts, int32_t *out_offsets, int32_t *out_perm, int32_t *out_inv,
     uint64_t *route_counts, RouteIn qin, int H, int Kp, uint8_t *xq, uint8_t *xs, int fp4) {
     __shared__ int wcnt[16][kMaxE];
     __shared__ int base[kMaxE + 1];
-    (void)rank;
     if (blockIdx.x > 0) {
         quantize_terms_wgs(qin, T, H, Kp, xq, xs, 1, fp4);
         return;
@@ -644,7 +643,7 @@ hipError_t launch_topk(const double *partial, int S, const float *bias, const Ro
 
 hipError_t launch_permute(const int32_t *idx, int T, int E, int k, int n_shared, int tile_rows,
                           int32_t *counts,
-                          int32_t *offsets, int32_t *perm, int32_t *inv, int32_t *rank,
+                          int32_t *offsets, int32_t *perm, int32_t *inv,
                           int32_t *mprefix, int32_t *out_counts, int32_t *out_offsets,
                           int32_t *out_perm, int32_t *out_inv, uint64_t *route_counts,
                           const RouteIn *qin, int H, const TermsOut *terms, hipStream_t s) {
@@ -656,7 +655,7 @@ hipError_t launch_permute(const int32_t *idx, int T, int E, int k, int n_shared,
     }
     const RouteIn none{nullptr, 0, nullptr, nullptr, nullptr};
     launch_kernel(permute_kernel, 1 + qwgs, 1024, s, idx, T, E, k, n_shared, tile_rows, counts,
-                  offsets, perm, inv, rank, mprefix, out_counts, out_offsets, out_perm, out_inv,
+                  offsets, perm, inv, mprefix, out_counts, out_offsets, out_perm, out_inv,
                   route_counts, terms ? *qin : none, H, Kp, terms ? terms->q : nullptr,
                   terms ? terms->scales : nullptr, terms ? terms->fp4 : 0);
     return hipGetLastError();
