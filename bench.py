@@ -762,7 +762,7 @@ def main():
                     help="also run one device copy of this many GiB (PMC byte calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(run with --gpus 1).", file=sys.stderr)
         sys.exit(2)
     head = "decode" if args.workload == "suite" else args.workload
