@@ -42,10 +42,13 @@ def _eager_noise(xd, dl, shape, ws):
     other.fill_(0.5)
 
 
-@pytest.mark.parametrize("cid,T", [(3, 128), (5, 256), (4, 96)])
+# (5, 2048): the DeepSeek-V4-Flash layer at full size, the kernels its bench
+# line replays (bf16 operand on 64-row tiles, two workgroups per CU)
+@pytest.mark.parametrize("cid,T", [(3, 128), (5, 256), (4, 96), (5, 2048)])
 def test_prefill_graph_replays_equal_eager(cid, T):
-    cfg = config_by_id(cid) if (cid, T) == (3, 128) else scaled(config_by_id(cid), T=T, H=512, F=256,
-                                                                     E=min(config_by_id(cid).E, 16))
+    full = (cid, T) in ((3, 128), (5, 2048))
+    cfg = config_by_id(cid) if full else scaled(config_by_id(cid), T=T, H=512, F=256,
+                                                E=min(config_by_id(cid).E, 16))
     _announce(f"graph replay: prefill config {cid} T={T}")
     layer = make_layer(cfg)
     x, xb = make_activations(cfg, rows=cfg.T)
