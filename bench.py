@@ -636,6 +636,11 @@ def measure(wl: str, args, steps: int, warmup: int) -> dict:
         expert_input = "exact (bf16 as it is; weights decoded to bf16 in registers)"
     else:
         expert_input = "exact (fp8 terms)"
+    # the arithmetic the path computes in: MXFP4 weights against FP8 terms,
+    # the bfloat16 input (weights decoded to bf16), or MX-FP4 activations
+    gate_dt = {1: "bf16", 0: "fp4xfp4"}.get(xt, DTYPE) if setup.mode == "prefill" else DTYPE
+    down_dt = "fp4xfp4" if setup.act_quant == 2 else DTYPE
+    dtype = gate_dt if gate_dt == down_dt else f"{gate_dt} (gate/up), {down_dt} (down)"
     block_bytes = setup.block_bytes_per_step(counts)
     block_gbps = block_bytes / (ms_per_step / 1e3) / 1e9
     nominal_tf = alg["flops"] / kern_s / 1e12
@@ -644,6 +649,7 @@ def measure(wl: str, args, steps: int, warmup: int) -> dict:
     result = {
         "value": round(value, 1),
         "unit": "tokens/s",
+        "dtype": dtype,
         "steps": steps,
         "warmup": warmup,
         "ms_per_step": round(ms_per_step, 4),
@@ -786,7 +792,7 @@ def main():
     result = {
         "metric": METRIC, "value": r.pop("value"), "unit": r.pop("unit"), "n_gpus": 1,
         "steps": r.pop("steps"), "warmup": r.pop("warmup"), "ms_per_step": r.pop("ms_per_step"),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": DTYPE,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": r.pop("dtype"),
         "data": "synthetic",
     }
     result.update(r)
