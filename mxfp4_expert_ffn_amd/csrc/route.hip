@@ -71,83 +71,196 @@ __global__ __launch_bounds__(256) void rms_inv_kernel(const void *x, int H, floa
     }
 }
 
+// ---------------------------------------------------------------- four values per lane
+// The block splits of fp8_terms_group and fp4_act_code for a block of 32
+// values held four per lane by a group of 8 consecutive lanes (lane j of the
+// group: values 4j .. 4j + 3): the same arithmetic value by value, with the
+// block maximum taken over the group. The 8 lanes of a group take part
+// together.
+
+// Maximum over each group of 8 consecutive lanes of a value that is >= 0,
+// returned to all 8: DPP swaps inside each quad, then the mirror inside the
+// group of 8 (lane i and lane 7 - i sit in different quads).
+__device__ __forceinline__ float group8_max(float v) {
+    v = fmaxf(v, __builtin_amdgcn_update_dpp(0.0f, v, 0xB1, 0xf, 0xf, false));    // quad_perm [1,0,3,2]
+    v = fmaxf(v, __builtin_amdgcn_update_dpp(0.0f, v, 0x4E, 0xf, 0xf, false));    // quad_perm [2,3,0,1]
+    return fmaxf(v, __builtin_amdgcn_update_dpp(0.0f, v, 0x141, 0xf, 0xf, false));  // row_half_mirror
+}
+
+__device__ __forceinline__ float abs_max4(const float (&v)[4]) {
+    return fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
+}
+
+// codes[n]: term n of the lane's four values (value m in byte m); scales:
+// the scale byte of term n in byte n.
+__device__ __forceinline__ void fp8_terms_group4(const float (&v)[4], uint32_t (&codes)[kTerms],
+                                                 uint32_t &scales) {
+    const float amax = group8_max(abs_max4(v));
+    const int e0 = static_cast<int>((__float_as_uint(amax) >> 23) & 0xffu) - 127 - 7;
+    float r[4] = {v[0], v[1], v[2], v[3]};
+    scales = 0;
+#pragma unroll
+    for (int n = 0; n < kTerms; ++n) {
+        int e = e0 - 4 * n;
+        e = e < -126 ? -126 : (e > 127 ? 127 : e);
+        uint32_t c = 0;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const uint32_t q = e4m3_encode(r[m] * pow2f(-e));
+            r[m] -= e4m3_decode(q) * pow2f(e);
+            c |= q << (8 * m);
+        }
+        codes[n] = c;
+        scales |= static_cast<uint32_t>(e + 127) << (8 * n);
+    }
+}
+
+// The lane's four E2M1 codes packed in 16 bits (value m in bits 4m .. 4m + 3,
+// so the low nibble of each byte is the even element) and the block's scale
+// byte.
+__device__ __forceinline__ uint32_t fp4_act_codes4(const float (&v)[4], uint32_t &scale_byte) {
+    const float amax = fmaxf(group8_max(abs_max4(v)), 7.052966104933725e-38f);  // 6 * 2^-126
+    const uint32_t bits = __float_as_uint(amax);
+    const int E = static_cast<int>((bits >> 23) & 0xffu) - 127;
+    const int e = (bits & 0x7fffffu) <= 0x400000u ? E - 2 : E - 1;  // amax <= 1.5 * 2^E: 6 * 2^(E-2) fits
+    scale_byte = static_cast<uint32_t>(e + 127);
+    uint32_t c = 0;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        const float a = fminf(fabsf(v[m]) * pow2f(-e), 6.0f);
+        // nearest of {0, .5, 1, 1.5, 2, 3, 4, 6}; a midpoint goes to the even index
+        const uint32_t idx = static_cast<uint32_t>(a > 0.25f) + static_cast<uint32_t>(a >= 0.75f) +
+                             static_cast<uint32_t>(a > 1.25f) + static_cast<uint32_t>(a >= 1.75f) +
+                             static_cast<uint32_t>(a > 2.5f) + static_cast<uint32_t>(a >= 3.5f) +
+                             static_cast<uint32_t>(a > 5.0f);
+        c |= (idx | (v[m] < 0.0f ? 8u : 0u)) << (4 * m);
+    }
+    return c;
+}
+
 // ---------------------------------------------------------------- FP8 terms
 // Quantisation of the expert input into FP8 terms for the block-scaled
-// matrix-core kernels, done by the workgroups past a router launch's own:
-// one half-wavefront per 32-value block of k (the unit an E8M0 scale of the
-// instruction's operand covers); codes go to xq[t][n][k] (zero past H),
-// scales to xs[t][n][k / 32]. With a norm the value is
-// float32((x * inv[t]) * gamma[k]). With a seed buffer the raw input value is
-// also stored there as float32 (decode's residual: the store rides on the load
-// the quantisation makes anyway, ahead of every expert launch).
+// matrix-core kernels, done by the workgroups past a router launch's or the
+// permutation launch's own. A 32-value block of k (the unit an E8M0 scale of
+// the instruction's operand covers) belongs to a group of lanes: 32 lanes of
+// one value each (VPL 1: the few blocks of a small batch, where the chain of
+// one lane is the launch's latency), or 8 lanes of four consecutive values
+// each (VPL 4: a quarter of the instructions, 16-byte loads and 4-byte stores
+// for a large batch; the stack's and DeepSeek-V4's quantisation 2x faster).
+// Codes go to xq[t][n][k] (zero past H), scales to xs[t][n][k / 32]. With a
+// norm the value is float32((x * inv[t]) * gamma[k]). With a seed buffer the
+// raw input value is also stored there as float32 (decode's residual: the
+// store rides on the load the quantisation makes anyway, ahead of every
+// expert launch). H is a multiple of 32, so a block is all in or all out.
 
-// The lane's value of block gidx (0 past the last block or past H).
-__device__ __forceinline__ float quantize_input(const RouteIn &in, int T, int H, int nb,
-                                                int gidx) {
-    const int i = threadIdx.x & 31;
-    if (gidx >= T * nb) return 0.f;
-    const int t = gidx / nb, kk = 32 * (gidx - t * nb) + i;
-    if (kk >= H) return 0.f;
+// The lane's VPL values of block gidx (zeros past the last block or past H).
+template <int VPL>
+__device__ __forceinline__ void quantize_input(const RouteIn &in, int T, int H, int nb, int gidx,
+                                               float (&v)[VPL]) {
+#pragma unroll
+    for (int m = 0; m < VPL; ++m) v[m] = 0.f;
+    if (gidx >= T * nb) return;
+    const int t = gidx / nb, kk = 32 * (gidx - t * nb) + VPL * (threadIdx.x & (32 / VPL - 1));
+    if (kk >= H) return;
     const size_t at = static_cast<size_t>(t) * H + kk;
-    const double x = in.bf16 ? load_in<1>(in.x, at) : load_in<0>(in.x, at);
-    if (in.seed) in.seed[at] = static_cast<float>(x);  // exact: the input is f32 or bf16
-    return in.inv ? static_cast<float>(x * in.inv[t] * static_cast<double>(in.gamma[kk]))
-                  : static_cast<float>(x);
+    double x[VPL];
+    if constexpr (VPL == 1) {
+        x[0] = in.bf16 ? load_in<1>(in.x, at) : load_in<0>(in.x, at);
+        if (in.seed) in.seed[at] = static_cast<float>(x[0]);  // exact: the input is f32 or bf16
+    } else {
+        if (in.bf16) load4<1>(in.x, at, x);
+        else load4<0>(in.x, at, x);
+        if (in.seed)
+            *reinterpret_cast<float4 *>(in.seed + at) =
+                make_float4(static_cast<float>(x[0]), static_cast<float>(x[1]), static_cast<float>(x[2]),
+                            static_cast<float>(x[3]));
+    }
+    if (in.inv) {
+        const double iv = in.inv[t];
+        float g[VPL];
+        if constexpr (VPL == 1) {
+            g[0] = in.gamma[kk];
+        } else {
+            const float4 g4 = *reinterpret_cast<const float4 *>(in.gamma + kk);
+            g[0] = g4.x; g[1] = g4.y; g[2] = g4.z; g[3] = g4.w;
+        }
+#pragma unroll
+        for (int m = 0; m < VPL; ++m) v[m] = static_cast<float>(x[m] * iv * static_cast<double>(g[m]));
+    } else {
+#pragma unroll
+        for (int m = 0; m < VPL; ++m) v[m] = static_cast<float>(x[m]);
+    }
 }
 
-// Terms of block gidx from the lanes' values; every lane of the wavefront
-// takes part (the group maximum is a half-wavefront reduction). fp4: the
+// Terms of block gidx from the group's values; the group's lanes take part
+// together (VPL 1: the whole wavefront, one half-wavefront maximum). fp4: the
 // MX-FP4 round trip instead, codes packed two per byte in xq[t][Kp / 2] and
 // the block's scale byte in xs[t][Kp / 32].
-__device__ __forceinline__ void quantize_store(float v, int T, int nb, int Kp, uint8_t *xq,
+template <int VPL>
+__device__ __forceinline__ void quantize_store(const float (&v)[VPL], int T, int nb, int Kp, uint8_t *xq,
                                                uint8_t *xs, int gidx, int fp4) {
-    const int i = threadIdx.x & 31;
+    const int j = threadIdx.x & (32 / VPL - 1);  // the lane in its group
+    const bool real = VPL == 1 ? gidx < T * nb : true;
+    const int t = gidx / nb, blk = gidx - t * nb;
     if (fp4) {
         uint32_t sbyte;
-        const uint32_t pair = fp4_pack_pair(fp4_act_code(v, sbyte));
-        if (gidx < T * nb) {
-            const int t = gidx / nb, blk = gidx - t * nb;
-            if ((i & 1) == 0)
-                xq[static_cast<size_t>(t) * (Kp / 2) + 16 * blk + (i >> 1)] = static_cast<uint8_t>(pair);
-            if (i == 0) xs[static_cast<size_t>(t) * nb + blk] = static_cast<uint8_t>(sbyte);
+        if constexpr (VPL == 1) {
+            const uint32_t pair = fp4_pack_pair(fp4_act_code(v[0], sbyte));
+            if (real && (j & 1) == 0)
+                xq[static_cast<size_t>(t) * (Kp / 2) + 16 * blk + (j >> 1)] = static_cast<uint8_t>(pair);
+        } else {
+            const uint32_t c = fp4_act_codes4(v, sbyte);
+            *reinterpret_cast<uint16_t *>(xq + static_cast<size_t>(t) * (Kp / 2) + 16 * blk + 2 * j) =
+                static_cast<uint16_t>(c);
         }
+        if (real && j == 0) xs[static_cast<size_t>(t) * nb + blk] = static_cast<uint8_t>(sbyte);
         return;
     }
-    uint32_t codes, scales;
-    fp8_terms_group(v, codes, scales);
-    if (gidx < T * nb) {
-        const int t = gidx / nb, blk = gidx - t * nb;
-        const int kk = 32 * blk + i;
+    uint32_t codes[kTerms], scales;
+    if constexpr (VPL == 1) {
+        uint32_t packed;
+        fp8_terms_group(v[0], packed, scales);
 #pragma unroll
-        for (int n = 0; n < kTerms; ++n) {
-            xq[(static_cast<size_t>(t) * kTerms + n) * Kp + kk] = static_cast<uint8_t>(codes >> (8 * n));
-            if (i == 0)
-                xs[(static_cast<size_t>(t) * kTerms + n) * nb + blk] = static_cast<uint8_t>(scales >> (8 * n));
-        }
+        for (int n = 0; n < kTerms; ++n) codes[n] = (packed >> (8 * n)) & 0xffu;
+    } else {
+        fp8_terms_group4(v, codes, scales);
+    }
+    if (!real) return;
+    const int kk = 32 * blk + VPL * j;
+#pragma unroll
+    for (int n = 0; n < kTerms; ++n) {
+        uint8_t *dst = xq + (static_cast<size_t>(t) * kTerms + n) * Kp + kk;
+        if constexpr (VPL == 1) *dst = static_cast<uint8_t>(codes[n]);
+        else *reinterpret_cast<uint32_t *>(dst) = codes[n];
+        if (j == 0) xs[(static_cast<size_t>(t) * kTerms + n) * nb + blk] = static_cast<uint8_t>(scales >> (8 * n));
     }
 }
 
-// Workgroups [first, gridDim.x) of a router or permutation launch:
-// blockDim.x / 32 blocks of 32 values per workgroup and round, in a
-// grid-stride loop that loads kU rounds before it quantises them. The loop
-// and its guards are per wavefront (both halves together), as the group
-// maximum needs.
+// Workgroups [first, gridDim.x) of a launch: blockDim.x * VPL / 32 blocks of
+// 32 values per workgroup and round, in a grid-stride loop that loads kU
+// rounds before it quantises them. The loop and its guards are per group of
+// lanes (VPL 1: per wavefront, both halves together, as the half-wavefront
+// maximum needs).
+template <int VPL>
 __device__ __forceinline__ void quantize_terms_wgs(const RouteIn &in, int T, int H, int Kp,
                                                    uint8_t *xq, uint8_t *xs, int first, int fp4) {
+    static_assert(VPL == 1 || VPL == 4, "one or four values per lane");
     constexpr int kU = 4;
+    constexpr int kLanes = 32 / VPL;  // lanes per block
     const int nb = Kp / 32;
     const int total = T * nb;
-    const int half = (threadIdx.x >> 5) & 1;
-    const int per_wg = static_cast<int>(blockDim.x) / 32;
+    const int per_wg = static_cast<int>(blockDim.x) / kLanes;
     const int stride = (static_cast<int>(gridDim.x) - first) * per_wg;
-    for (int g0 = (static_cast<int>(blockIdx.x) - first) * per_wg + 2 * (threadIdx.x >> 6);
-         g0 < total; g0 += kU * stride) {
-        float v[kU];
+    // VPL 1: the wavefront's two blocks are g0 (lanes 0..31) and g0 + 1
+    const int lead = VPL == 1 ? 2 * (static_cast<int>(threadIdx.x) >> 6) : static_cast<int>(threadIdx.x) / kLanes;
+    const int half = VPL == 1 ? (static_cast<int>(threadIdx.x) >> 5) & 1 : 0;
+    for (int g0 = (static_cast<int>(blockIdx.x) - first) * per_wg + lead; g0 < total; g0 += kU * stride) {
+        float v[kU][VPL];
 #pragma unroll
-        for (int u = 0; u < kU; ++u) v[u] = quantize_input(in, T, H, nb, g0 + u * stride + half);
+        for (int u = 0; u < kU; ++u) quantize_input<VPL>(in, T, H, nb, g0 + u * stride + half, v[u]);
 #pragma unroll
         for (int u = 0; u < kU; ++u)
-            if (g0 + u * stride < total) quantize_store(v[u], T, nb, Kp, xq, xs, g0 + u * stride + half, fp4);
+            if (g0 + u * stride < total) quantize_store<VPL>(v[u], T, nb, Kp, xq, xs, g0 + u * stride + half, fp4);
     }
 }
 
@@ -170,7 +283,7 @@ __global__ __launch_bounds__(256) void router_gemv_kernel(RouteIn in, const floa
     constexpr int NV = kRouterGemvSlice / 256;  // float4 per lane
     const int lane = threadIdx.x & 63;
     if (static_cast<int>(blockIdx.x) >= router_wgs) {
-        quantize_terms_wgs(in, T, H, Kp, xq, xs, router_wgs, fp4);
+        quantize_terms_wgs<1>(in, T, H, Kp, xq, xs, router_wgs, fp4);
         return;
     }
     const int item = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -247,7 +360,7 @@ __global__ __launch_bounds__(256) void router_tiled_kernel(RouteIn in, const flo
     __shared__ __align__(16) float wsm[2][32][64 + kPad];  // [k][expert]
     const int b = blockIdx.x;
     if (b >= router_wgs) {
-        quantize_terms_wgs(in, T, H, Kp, xq, xs, router_wgs, fp4);
+        quantize_terms_wgs<4>(in, T, H, Kp, xq, xs, router_wgs, fp4);
         return;
     }
     const int tid = threadIdx.x;
@@ -434,7 +547,7 @@ __global__ __launch_bounds__(1024) void permute_kernel(
     __shared__ int wcnt[16][kMaxE];
     __shared__ int base[kMaxE + 1];
     if (blockIdx.x > 0) {
-        quantize_terms_wgs(qin, T, H, Kp, xq, xs, 1, fp4);
+        quantize_terms_wgs<4>(qin, T, H, Kp, xq, xs, 1, fp4);
         return;
     }
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
@@ -601,8 +714,10 @@ void router_launch(const RouterPlan &p, const RouteIn &in, const float *w, int T
 hipError_t launch_router(const RouteIn &in, const float *w, int T, int H, int E, double *partial,
                          const TermsOut *terms, hipStream_t s) {
     const RouterPlan p = router_plan(T, H, E);
-    // quantisation workgroups: one round of 8 blocks of 32 values each
-    const int qwant = terms ? (T * (pad128(H) / 32) + 7) / 8 : 0;
+    // quantisation workgroups, one round each: 8 blocks of 32 values beside the
+    // GEMV (one value per lane), 32 beside the tiled router (four per lane)
+    const int per_wg = p.gemv ? 8 : 32;
+    const int qwant = terms ? (T * (pad128(H) / 32) + per_wg - 1) / per_wg : 0;
     uint8_t *xq = terms ? terms->q : nullptr;
     uint8_t *xs = terms ? terms->scales : nullptr;
     const int fp4 = terms ? terms->fp4 : 0;
@@ -621,13 +736,13 @@ namespace {
 // so that rows are packed without padding).
 __global__ __launch_bounds__(256) void act_fp4_kernel(RouteIn in, int T, int H, uint8_t *q,
                                                       uint8_t *scales) {
-    quantize_terms_wgs(in, T, H, H, q, scales, 0, 1);
+    quantize_terms_wgs<4>(in, T, H, H, q, scales, 0, 1);
 }
 }  // namespace
 
 hipError_t launch_act_fp4(const RouteIn &in, int T, int H, uint8_t *q, uint8_t *scales,
                           hipStream_t s) {
-    const int want = (T * (H / 32) + 7) / 8;  // one round of 8 blocks per workgroup
+    const int want = (T * (H / 32) + 31) / 32;  // one round of 32 blocks per workgroup
     launch_kernel(act_fp4_kernel, want < kQuantizeMaxWgs ? want : kQuantizeMaxWgs, 256, s, in, T, H,
                   q, scales);
     return hipGetLastError();
@@ -650,7 +765,7 @@ hipError_t launch_permute(const int32_t *idx, int T, int E, int k, int n_shared,
     const int Kp = pad128(H);
     int qwgs = 0;
     if (terms) {
-        const int want = (T * (Kp / 32) + 31) / 32;  // one round of 32 blocks each
+        const int want = (T * (Kp / 32) + 127) / 128;  // one round of 128 blocks each
         qwgs = want < kPermuteQuantizeWgs ? want : kPermuteQuantizeWgs;
     }
     const RouteIn none{nullptr, 0, nullptr, nullptr, nullptr};
