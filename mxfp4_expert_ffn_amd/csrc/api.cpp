@@ -488,7 +488,7 @@ int moe_forward_prefill(const moe_shape *s, const void *hidden, const float *nor
     const Workspace w = carve(s, static_cast<uint8_t *>(ws));
     const moe::GemmPlan plan = gemm_plan_of(s, norm_w != nullptr);
     // the FP8 terms (or MX-FP4 codes) of the expert input ride in the router
-    // launch in its GEMV form, else beside the one-workgroup permutation; a
+    // launch in its GEMV form, else beside the permutation's workgroups; a
     // bfloat16 input taken as it is (x_terms 1) needs neither
     const bool need_terms = plan.x_terms != 1;
     moe::RouteIn in;

@@ -142,8 +142,8 @@ hipError_t launch_topk(const double *partial, int S, const float *bias, const Ro
 // mprefix[g] = tiles of tile_rows rows before group g (groups: E experts,
 // then the shared expert's T rows when n_shared). With `terms` (and `qin`,
 // the expert input) the launch's other workgroups make the FP8 terms, as
-// launch_router would; the permutation itself is one workgroup, so they run
-// on otherwise idle compute units.
+// launch_router would; the permutation itself is one workgroup per 1024
+// routes, so they run on otherwise idle compute units.
 constexpr int kPermuteQuantizeWgs = 512;
 hipError_t launch_permute(const int32_t *idx, int T, int E, int k, int n_shared, int tile_rows,
                           int32_t *counts, int32_t *offsets, int32_t *perm, int32_t *inv,

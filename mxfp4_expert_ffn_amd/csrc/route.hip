@@ -529,62 +529,81 @@ __global__ __launch_bounds__(256) void topk_kernel(const double *partial, int S,
 }
 
 // ---------------------------------------------------------------- permutation
-// One workgroup of 1024 threads, two passes over the routes r = t*k + j.
-// Pass 1 counts each expert's routes (LDS atomics); a workgroup scan gives
-// the groups' offsets and the M-tile prefix for the grouped GEMMs (one group
-// per thread). Pass 2 takes the routes in chunks of 1024: inside a wavefront
-// the lanes holding the same expert are found with nine bit-plane ballots and
-// ranked by lane, per-wave counts are prefix-summed per expert in wave order
-// on top of the expert's running position, so a route's position counts
-// exactly the earlier routes of its expert: the permutation is stable
-// (ascending token). Each route writes perm and inv at once.
+// Workgroups of 1024 threads, one per chunk of 1024 routes r = t*k + j (the
+// workgroups past them quantise the expert input). Every chunk workgroup
+// counts all routes per expert (LDS atomics), and apart the routes before its
+// chunk; a workgroup scan of the counts gives the groups' offsets and the
+// M-tile prefix for the grouped GEMMs (one group per thread; workgroup 0
+// writes them). Its chunk's routes then start at offset + earlier routes of
+// their expert: inside a wavefront the lanes holding the same expert are found
+// with nine bit-plane ballots and ranked by lane, and per-wave counts are
+// prefix-summed per expert in wave order, so a route's position counts exactly
+// the earlier routes of its expert: the permutation is stable (ascending
+// token), the same from every chunk in parallel as in one pass. Each route
+// writes perm and inv at once.
 // Group E (when n_shared) is the shared expert: T rows, identity order.
 __global__ __launch_bounds__(1024) void permute_kernel(
-    const int32_t *__restrict__ idx, int T, int E, int k, int n_shared, int bm, int32_t *counts,
-    int32_t *offsets, int32_t *perm, int32_t *inv, int32_t *mprefix,
+    const int32_t *__restrict__ idx, int T, int E, int k, int n_shared, int bm, int nchunks,
+    int32_t *counts, int32_t *offsets, int32_t *perm, int32_t *inv, int32_t *mprefix,
     int32_t *out_counts, int32_t *out_offsets, int32_t *out_perm, int32_t *out_inv,
     uint64_t *route_counts, RouteIn qin, int H, int Kp, uint8_t *xq, uint8_t *xs, int fp4) {
     __shared__ int wcnt[16][kMaxE];
     __shared__ int base[kMaxE + 1];
-    if (blockIdx.x > 0) {
-        quantize_terms_wgs<4>(qin, T, H, Kp, xq, xs, 1, fp4);
+    __shared__ int before[kMaxE];
+    const int chunk = static_cast<int>(blockIdx.x);
+    if (chunk >= nchunks) {
+        quantize_terms_wgs<4>(qin, T, H, Kp, xq, xs, nchunks, fp4);
         return;
     }
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
-    const int R = T * k;
+    const int R = T * k, c0 = chunk * 1024;
+    const bool writer = chunk == 0;  // workgroup 0 writes the counts, offsets and prefix
     const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    for (int e = tid; e < E; e += 1024) base[e] = 0;
+    for (int e = tid; e < E; e += 1024) {
+        base[e] = 0;
+        before[e] = 0;
+    }
+    // this chunk's route (its expert loads during the counting)
+    const int r = c0 + tid;
+    const bool valid = r < R;
+    const int e = valid ? idx[r] : 0;
     __syncthreads();
     // lanes of a wavefront holding the same expert as this one: the
     // intersection of the bit-plane ballots of the expert index (9 planes:
     // E <= 512)
     static_assert(kMaxE <= 512, "expert indices fit 9 bit planes");
-    auto same_expert = [&](int e, bool valid) __attribute__((always_inline)) {
-        uint64_t eq = __ballot(valid);
+    auto same_expert = [&](int ex, bool on) __attribute__((always_inline)) {
+        uint64_t eq = __ballot(on);
 #pragma unroll
-        for (int b = 0; b < 9; ++b) {
-            const bool bit = (e >> b) & 1;
+        for (int bt = 0; bt < 9; ++bt) {
+            const bool bit = (ex >> bt) & 1;
             const uint64_t plane = __ballot(bit);
             eq &= bit ? plane : ~plane;
         }
         return eq;
     };
-    // pass 1: the experts' route counts (LDS atomics; loads four rounds at a time)
+    // the experts' route counts, and those of the routes before this chunk
+    // (LDS atomics; loads four rounds at a time)
     for (int r0 = tid; r0 < R; r0 += 4 * 1024) {
         int ev[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-            const int r = r0 + u * 1024;
-            ev[u] = r < R ? idx[r] : -1;
+            const int rr = r0 + u * 1024;
+            ev[u] = rr < R ? idx[rr] : -1;
         }
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
-            if (ev[u] >= 0) atomicAdd(&base[ev[u]], 1);
+        for (int u = 0; u < 4; ++u) {
+            if (ev[u] >= 0) {
+                atomicAdd(&base[ev[u]], 1);
+                if (r0 + u * 1024 < c0) atomicAdd(&before[ev[u]], 1);
+            }
+        }
     }
     __syncthreads();
     // counts, their exclusive scan and the tile prefix: one group per thread
     // (G <= kMaxE + 1 <= 1024), wavefront scans, then the totals of the
-    // wavefronts before; base[g] becomes group g's first position
+    // wavefronts before; base[g] becomes the first position of group g's
+    // routes in this chunk
     const int G = E + n_shared;
     __shared__ int wsum_c[16], wsum_t[16];
     {
@@ -610,57 +629,49 @@ __global__ __launch_bounds__(1024) void permute_kernel(
             pt += wsum_t[ww];
         }
         const int off = pc + sc - c, mt = pt + st - nt;
-        __syncthreads();  // every count is read before base[] turns into offsets
-        if (g < G) {
-            if (g < E) base[g] = off;
-            offsets[g] = off;
-            mprefix[g] = mt;
-            counts[g] = c;
-            if (out_counts && g < E) out_counts[g] = c;
-            // route profile: this call's selections of expert g (one atomic per expert)
-            if (route_counts && g < E && c > 0)
-                atomicAdd(reinterpret_cast<unsigned long long *>(route_counts + g),
-                          static_cast<unsigned long long>(c));
-            if (out_offsets && g < E) out_offsets[g] = off;
+        __syncthreads();  // every count is read before base[] turns into positions
+        if (g < E) base[g] = off + before[g];
+        if (writer) {
+            if (g < G) {
+                offsets[g] = off;
+                mprefix[g] = mt;
+                counts[g] = c;
+                if (out_counts && g < E) out_counts[g] = c;
+                // route profile: this call's selections of expert g (one atomic per expert)
+                if (route_counts && g < E && c > 0)
+                    atomicAdd(reinterpret_cast<unsigned long long *>(route_counts + g),
+                              static_cast<unsigned long long>(c));
+                if (out_offsets && g < E) out_offsets[g] = off;
+            }
+            if (g == G - 1) {
+                offsets[G] = off + c;
+                mprefix[G] = mt + nt;
+            }
+            if (out_offsets && g == 0) out_offsets[E] = R;
         }
-        if (g == G - 1) {
-            offsets[G] = off + c;
-            mprefix[G] = mt + nt;
+    }
+    // positions of this chunk's routes
+    for (int i = tid; i < 16 * kMaxE; i += 1024) wcnt[i / kMaxE][i % kMaxE] = 0;
+    __syncthreads();
+    const uint64_t eq = same_expert(e, valid);
+    const int myrank = __popcll(eq & lt_mask);
+    if (valid && myrank == 0) wcnt[w][e] = __popcll(eq);  // the first lane of its expert
+    __syncthreads();
+    for (int ee = tid; ee < E; ee += 1024) {
+        int run = base[ee];
+        for (int ww = 0; ww < 16; ++ww) {
+            const int c = wcnt[ww][ee];
+            wcnt[ww][ee] = run;
+            run += c;
         }
-        if (out_offsets && g == 0) out_offsets[E] = R;
     }
     __syncthreads();
-    // pass 2: positions in chunks of 1024 routes
-    int e_next = tid < R ? idx[tid] : 0;  // the next chunk's experts load during this one
-    for (int c0 = 0; c0 < R; c0 += 1024) {
-        for (int i = tid; i < 16 * kMaxE; i += 1024) wcnt[i / kMaxE][i % kMaxE] = 0;
-        const int r = c0 + tid;
-        const bool valid = r < R;
-        const int e = e_next;
-        if (r + 1024 < R) e_next = idx[r + 1024];
-        __syncthreads();
-        const uint64_t eq = same_expert(e, valid);
-        const int myrank = __popcll(eq & lt_mask);
-        if (valid && myrank == 0) wcnt[w][e] = __popcll(eq);  // the first lane of its expert
-        __syncthreads();
-        for (int ee = tid; ee < E; ee += 1024) {
-            int run = base[ee];
-            for (int ww = 0; ww < 16; ++ww) {
-                const int c = wcnt[ww][ee];
-                wcnt[ww][ee] = run;
-                run += c;
-            }
-            base[ee] = run;
-        }
-        __syncthreads();
-        if (valid) {
-            const int pos = wcnt[w][e] + myrank;
-            perm[pos] = r;
-            inv[r] = pos;
-            if (out_perm) out_perm[pos] = r;
-            if (out_inv) out_inv[r] = pos;
-        }
-        __syncthreads();
+    if (valid) {
+        const int pos = wcnt[w][e] + myrank;
+        perm[pos] = r;
+        inv[r] = pos;
+        if (out_perm) out_perm[pos] = r;
+        if (out_inv) out_inv[r] = pos;
     }
 }
 
@@ -769,7 +780,8 @@ hipError_t launch_permute(const int32_t *idx, int T, int E, int k, int n_shared,
         qwgs = want < kPermuteQuantizeWgs ? want : kPermuteQuantizeWgs;
     }
     const RouteIn none{nullptr, 0, nullptr, nullptr, nullptr};
-    launch_kernel(permute_kernel, 1 + qwgs, 1024, s, idx, T, E, k, n_shared, tile_rows, counts,
+    const int nchunks = (T * k + 1023) / 1024;
+    launch_kernel(permute_kernel, nchunks + qwgs, 1024, s, idx, T, E, k, n_shared, tile_rows, nchunks, counts,
                   offsets, perm, inv, mprefix, out_counts, out_offsets, out_perm, out_inv,
                   route_counts, terms ? *qin : none, H, Kp, terms ? terms->q : nullptr,
                   terms ? terms->scales : nullptr, terms ? terms->fp4 : 0);
