@@ -121,6 +121,35 @@ def test_route_parity(cid, T):
     check_permutation(got, got["topk_idx"], cfg.E)
 
 
+# routes (T * k) at and around the 1024-route chunks the permutation works in,
+# with the largest expert count and with every token's first choice forced onto
+# one expert (its count spans chunks)
+@pytest.mark.parametrize("T,k,E,skew", [(1023, 1, 8, False), (1024, 1, 16, False), (1025, 1, 16, False),
+                                        (512, 2, 512, False), (683, 3, 300, False), (700, 3, 24, True),
+                                        (2048, 6, 257, True)])
+def test_permutation_at_chunk_edges(T, k, E, skew):
+    _announce(f"permutation T={T} k={k} E={E} skew={skew}")
+    H = 64
+    rng = np.random.default_rng(T * 31 + E)
+    rw = rng.normal(0.0, 0.05, size=(E, H)).astype(np.float32)
+    rb = rng.normal(0.0, 0.05, size=E).astype(np.float32)
+    if skew:
+        rb[E // 3] = 50.0  # every token's first choice
+    x = rng.normal(0.0, 1.0, size=(T, H)).astype(np.float32)
+    shape = mx.make_shape(T, H, 32, E, k)
+    ro = route_buffers(T, k, E)
+    mx.moe_route(shape, torch.from_numpy(x).cuda(), torch.from_numpy(rw).cuda(),
+                 torch.from_numpy(rb).cuda(), ro, workspace(shape))
+    torch.cuda.synchronize()
+    got = to_np(ro)
+    if skew:
+        assert np.all(got["topk_idx"][:, 0] == E // 3)
+    logits, idx, w, _ = omoe.route(x.astype(np.float64), rw, rb, k, 1.0)
+    check_routing(got["topk_idx"], got["topk_w"], dict(logits=logits, idx=idx, w=w, xn=x.astype(np.float64)),
+                  rw, rb, 1.0)
+    check_permutation(got, got["topk_idx"], E)
+
+
 def test_route_ties_go_to_lowest_index():
     _announce("route ties")
     T, H, E, k = 5, 64, 16, 4
